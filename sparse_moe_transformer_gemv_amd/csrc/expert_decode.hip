@@ -1,0 +1,367 @@
+// expert_decode.hip -- bandwidth-bound expert kernels for decode-sized token
+// counts (gfx950).
+//
+// Decoding reads each selected expert's weights once per step, so the time is
+// set by weight bytes over HBM bandwidth [kongchang.com, "Recursive
+// Open-Sources Flint: A 40B MoE Local Coding Model with 2.5B Active
+// Parameters", section "125+ tokens/s: The Practical Threshold for Local
+// Inference"; futurpulse.com, "Flint model: local coding with fewer active
+// parameters", section "How does Flint use 39.8B parameters efficiently?":
+// only the routed group and the shared expert are read per token].
+//
+// The kernels are weight-stationary: every active (group, row block) work
+// item streams its weight rows from HBM exactly once with 16-byte-per-lane
+// coalesced loads and applies them to all tokens routed to that group (token
+// vectors come through L1/L2).  Groups are the experts with at least one token
+// plus the shared expert, listed by the router's counting sort.
+//
+//   gate/up:  h[slot][j] = SiLU(G_j . x_t) * (U_j . x_t)      (fp32 out)
+//   down:     y[slot][n] = w_slot * (D_n . h[slot])           (fp32 out)
+//
+// Weight formats: fp32, bf16, and NVFP4 (E2M1 codes with one E4M3 scale per
+// 16 elements and an fp32 tensor scale [evermx.com, "Recursive Flint:
+// Open-Weight MoE Coding Model, 2.5B Active", Feature Overview,
+// "Quantization"]; decoded in registers).
+#include "flint_internal.hpp"
+
+namespace flint {
+
+// ---------------------------------------------------------------------------
+// Weight chunk loaders: VEC consecutive elements of one row starting at k0
+// (k0 a multiple of VEC), returned as fp32.
+// ---------------------------------------------------------------------------
+template <int WT> struct WChunk;
+
+template <> struct WChunk<DT_F32> {
+    static constexpr int VEC = 4;
+    uint4 raw;
+    __device__ __forceinline__ void load(const void* row, const uint8_t*, int k0) {
+        raw = *reinterpret_cast<const uint4*>(static_cast<const float*>(row) + k0);
+    }
+    __device__ __forceinline__ void decode(float v[VEC], float) const {
+        v[0] = __uint_as_float(raw.x); v[1] = __uint_as_float(raw.y);
+        v[2] = __uint_as_float(raw.z); v[3] = __uint_as_float(raw.w);
+    }
+};
+
+template <> struct WChunk<DT_BF16> {
+    static constexpr int VEC = 8;
+    uint4 raw;
+    __device__ __forceinline__ void load(const void* row, const uint8_t*, int k0) {
+        raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(row) + k0);
+    }
+    __device__ __forceinline__ void decode(float v[VEC], float) const {
+        v[0] = bf16_lo(raw.x); v[1] = bf16_hi(raw.x); v[2] = bf16_lo(raw.y); v[3] = bf16_hi(raw.y);
+        v[4] = bf16_lo(raw.z); v[5] = bf16_hi(raw.z); v[6] = bf16_lo(raw.w); v[7] = bf16_hi(raw.w);
+    }
+};
+
+// E2M1 magnitude codes 0..7 -> 0, 0.5, 1, 1.5, 2, 3, 4, 6 (OCP MX): exponent
+// field e (bias 1) and mantissa bit m; e == 0 is subnormal (0.5 * m).
+__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
+    const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+    float mag = e ? __uint_as_float(((e + 126u) << 23) | (m << 22)) : 0.5f * (float)m;
+    return (c & 8u) ? -mag : mag;
+}
+
+// E4M3 (OCP FP8 "E4M3FN") -> fp32: bias 7, subnormals 0.m * 2^-6, S.1111.111 = NaN.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+    const uint32_t s = c >> 7, e = (c >> 3) & 15u, m = c & 7u;
+    float v;
+    if (e == 15u && m == 7u) v = __uint_as_float(0x7FC00000u);
+    else if (e == 0u) v = (float)m * 0.001953125f;  // m/8 * 2^-6
+    else v = __uint_as_float(((e + 120u) << 23) | (m << 20));
+    return s ? -v : v;
+}
+
+template <> struct WChunk<DT_NVFP4> {
+    static constexpr int VEC = 16;  // one block-scale group per chunk
+    uint2 raw;                      // 16 E2M1 codes, even element in the low nibble
+    uint32_t sc;                    // E4M3 block-scale code
+    __device__ __forceinline__ void load(const void* row, const uint8_t* srow, int k0) {
+        raw = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(row) + k0 / 2);
+        sc = srow[k0 / 16];
+    }
+    __device__ __forceinline__ void decode(float v[VEC], float tscale) const {
+        const float s = e4m3_to_f32(sc) * tscale;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            v[i] = e2m1_to_f32(raw.x >> (4 * i)) * s;
+            v[8 + i] = e2m1_to_f32(raw.y >> (4 * i)) * s;
+        }
+    }
+};
+
+// Row pointers of expert matrices.  Element offsets for fp32/bf16, byte
+// offsets for NVFP4 codes (2 per byte) and scales (1 per 16 elements).
+template <int WT>
+__device__ __forceinline__ const void* row_ptr(const void* base, size_t row, int K) {
+    if constexpr (WT == DT_F32) return static_cast<const float*>(base) + row * K;
+    else if constexpr (WT == DT_BF16) return static_cast<const uint16_t*>(base) + row * K;
+    else return static_cast<const uint8_t*>(base) + row * (K / 2);
+}
+
+template <typename ActT, int VEC>
+__device__ __forceinline__ void load_act(const ActT* x, float v[VEC]) {
+    if constexpr (sizeof(ActT) == 4) {
+#pragma unroll
+        for (int i = 0; i < VEC; i += 4) {
+            float4 a = *reinterpret_cast<const float4*>(x + i);
+            v[i] = a.x; v[i + 1] = a.y; v[i + 2] = a.z; v[i + 3] = a.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < VEC; i += 8) {
+            uint4 a = *reinterpret_cast<const uint4*>(x + i);
+            v[i] = bf16_lo(a.x); v[i + 1] = bf16_hi(a.x); v[i + 2] = bf16_lo(a.y);
+            v[i + 3] = bf16_hi(a.y); v[i + 4] = bf16_lo(a.z); v[i + 5] = bf16_hi(a.z);
+            v[i + 6] = bf16_lo(a.w); v[i + 7] = bf16_hi(a.w);
+        }
+    }
+}
+
+template <int VEC>
+__device__ __forceinline__ void load_h(const float* h, float v[VEC]) {
+#pragma unroll
+    for (int i = 0; i < VEC; i += 4) {
+        float4 a = *reinterpret_cast<const float4*>(h + i);
+        v[i] = a.x; v[i + 1] = a.y; v[i + 2] = a.z; v[i + 3] = a.w;
+    }
+}
+
+struct ExpertParams {
+    Dims dm;
+    const void* x;
+    WeightPtrs routed, shared;
+    Workspace ws;
+    int hstride;  // row stride of h (max(f, fs))
+};
+
+// ---------------------------------------------------------------------------
+// gate/up + SwiGLU.  Block = 4 waves, each wave owns FPW features (FPW gate
+// rows and the matching FPW up rows); work item = (group, block of 4*FPW
+// features).  Tokens of the group are processed TG at a time.
+// ---------------------------------------------------------------------------
+constexpr int kFPW = 2;
+constexpr int kFPB = 4 * kFPW;
+constexpr int kTG = 4;
+
+template <typename ActT, int WT>
+__global__ __launch_bounds__(256) void gateup_decode_kernel(ExpertParams p) {
+    using W = WChunk<WT>;
+    constexpr int VEC = W::VEC;
+    constexpr int NR = 2 * kFPW;  // rows per wave
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int fmax = max(p.dm.f, p.dm.fs);
+    const int fblocks = (fmax + kFPB - 1) / kFPB;
+    const int gi = blockIdx.x / fblocks, fb = blockIdx.x % fblocks;
+    if (gi >= *p.ws.n_groups) return;
+    const int4 g = p.ws.groups[gi];  // {expert, first sorted index, rows, first slot}
+    const bool is_shared = g.x == p.dm.E;
+    const int F = is_shared ? p.dm.fs : p.dm.f;
+    const int j0 = fb * kFPB + wave * kFPW;
+    if (j0 >= F) return;
+    const int d = p.dm.d;
+    const WeightPtrs& wp = is_shared ? p.shared : p.routed;
+    const size_t e = is_shared ? 0 : (size_t)g.x;
+    const size_t row0 = e * 2 * F;  // first gate_up row of this expert
+    float tsc[NR];
+    const void* rows[NR];
+    const uint8_t* srows[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        // rows 0..FPW-1: gate j0+r; rows FPW..: up j0+r-FPW
+        const size_t rr = row0 + (r < kFPW ? (size_t)(j0 + r) : (size_t)(F + j0 + r - kFPW));
+        rows[r] = row_ptr<WT>(wp.gu, rr, d);
+        srows[r] = (WT == DT_NVFP4) ? wp.gus + rr * (d / 16) : nullptr;
+        tsc[r] = (WT == DT_NVFP4) ? wp.ts[e * 3 + (r < kFPW ? 0 : 1)] : 1.f;
+    }
+    const ActT* x = static_cast<const ActT*>(p.x);
+    const int kT = p.dm.k * p.dm.T;
+    (void)kT;
+    for (int r0 = 0; r0 < g.z; r0 += kTG) {
+        int tok[kTG];
+#pragma unroll
+        for (int tt = 0; tt < kTG; ++tt) {
+            const int r = r0 + tt;
+            tok[tt] = (r < g.z) ? (is_shared ? r : p.ws.sorted_pair[g.y + r] / p.dm.k) : -1;
+        }
+        float acc[kTG][NR];
+#pragma unroll
+        for (int tt = 0; tt < kTG; ++tt)
+#pragma unroll
+            for (int r = 0; r < NR; ++r) acc[tt][r] = 0.f;
+        for (int k0 = lane * VEC; k0 < d; k0 += 64 * VEC) {
+            W wc[NR];
+#pragma unroll
+            for (int r = 0; r < NR; ++r) wc[r].load(rows[r], srows[r], k0);
+#pragma unroll
+            for (int tt = 0; tt < kTG; ++tt) {
+                if (tok[tt] < 0) continue;
+                float xv[VEC];
+                load_act<ActT, VEC>(x + (size_t)tok[tt] * d + k0, xv);
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    float wv[VEC];
+                    wc[r].decode(wv, tsc[r]);
+                    float a = acc[tt][r];
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) a = fmaf(wv[v], xv[v], a);
+                    acc[tt][r] = a;
+                }
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < kTG; ++tt) {
+            if (tok[tt] < 0) continue;  // uniform across the wave
+            float s[NR];
+#pragma unroll
+            for (int r = 0; r < NR; ++r) s[r] = wave_sum(acc[tt][r]);
+            if (lane < kFPW) {
+                float gv = s[0], uv = s[kFPW];
+#pragma unroll
+                for (int q = 1; q < kFPW; ++q)
+                    if (lane == q) { gv = s[q]; uv = s[kFPW + q]; }
+                float* hrow = static_cast<float*>(p.ws.h) + (size_t)(g.w + r0 + tt) * p.hstride;
+                hrow[j0 + lane] = silu_f32(gv) * uv;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// down.  Block = 4 waves x kRPW output rows; work item = (group, block of
+// 4*kRPW rows of d).  Each lane reads VEC elements of a row of D (K = F).
+// ---------------------------------------------------------------------------
+constexpr int kRPW = 4;
+constexpr int kRPB = 4 * kRPW;
+
+template <int WT>
+__global__ __launch_bounds__(256) void down_decode_kernel(ExpertParams p) {
+    using W = WChunk<WT>;
+    constexpr int VEC = W::VEC;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int d = p.dm.d;
+    const int rblocks = (d + kRPB - 1) / kRPB;
+    const int gi = blockIdx.x / rblocks, rb = blockIdx.x % rblocks;
+    if (gi >= *p.ws.n_groups) return;
+    const int4 g = p.ws.groups[gi];
+    const bool is_shared = g.x == p.dm.E;
+    const int F = is_shared ? p.dm.fs : p.dm.f;
+    const int n0 = rb * kRPB + wave * kRPW;
+    if (n0 >= d) return;
+    const WeightPtrs& wp = is_shared ? p.shared : p.routed;
+    const size_t e = is_shared ? 0 : (size_t)g.x;
+    const void* rows[kRPW];
+    const uint8_t* srows[kRPW];
+    const float tsc = (WT == DT_NVFP4) ? wp.ts[e * 3 + 2] : 1.f;
+#pragma unroll
+    for (int r = 0; r < kRPW; ++r) {
+        const size_t rr = e * (size_t)d + (size_t)(n0 + r);
+        rows[r] = row_ptr<WT>(wp.dn, rr, F);
+        srows[r] = (WT == DT_NVFP4) ? wp.dns + rr * (F / 16) : nullptr;
+    }
+    const float* h = static_cast<const float*>(p.ws.h);
+    float* y = static_cast<float*>(p.ws.y);
+    for (int r0 = 0; r0 < g.z; r0 += kTG) {
+        int slot[kTG];
+        float wslot[kTG];
+#pragma unroll
+        for (int tt = 0; tt < kTG; ++tt) {
+            const int r = r0 + tt;
+            slot[tt] = (r < g.z) ? g.w + r : -1;
+            wslot[tt] = (r < g.z && !is_shared) ? p.ws.wts[p.ws.sorted_pair[g.y + r]] : 1.f;
+        }
+        float acc[kTG][kRPW];
+#pragma unroll
+        for (int tt = 0; tt < kTG; ++tt)
+#pragma unroll
+            for (int r = 0; r < kRPW; ++r) acc[tt][r] = 0.f;
+        for (int k0 = lane * VEC; k0 < F; k0 += 64 * VEC) {
+            W wc[kRPW];
+#pragma unroll
+            for (int r = 0; r < kRPW; ++r) wc[r].load(rows[r], srows[r], k0);
+#pragma unroll
+            for (int tt = 0; tt < kTG; ++tt) {
+                if (slot[tt] < 0) continue;
+                float hv[VEC];
+                load_h<VEC>(h + (size_t)slot[tt] * p.hstride + k0, hv);
+#pragma unroll
+                for (int r = 0; r < kRPW; ++r) {
+                    float wv[VEC];
+                    wc[r].decode(wv, tsc);
+                    float a = acc[tt][r];
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) a = fmaf(wv[v], hv[v], a);
+                    acc[tt][r] = a;
+                }
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < kTG; ++tt) {
+            if (slot[tt] < 0) continue;
+            float s[kRPW];
+#pragma unroll
+            for (int r = 0; r < kRPW; ++r) s[r] = wave_sum(acc[tt][r]);
+            if (lane < kRPW) {
+                float v = s[0];
+#pragma unroll
+                for (int q = 1; q < kRPW; ++q)
+                    if (lane == q) v = s[q];
+                y[(size_t)slot[tt] * d + n0 + lane] = wslot[tt] * v;
+            }
+        }
+    }
+}
+
+static int max_groups(const Dims& dm) {
+    const int routed = dm.k * dm.T < dm.E ? dm.k * dm.T : dm.E;
+    return routed + (dm.fs > 0 ? 1 : 0);
+}
+
+static ExpertParams make_params(const LayerArgs& a, const Workspace& w) {
+    ExpertParams p;
+    p.dm = a.dm;
+    p.x = a.x;
+    p.routed = a.routed;
+    p.shared = a.shared;
+    p.ws = w;
+    p.hstride = a.dm.f > a.dm.fs ? a.dm.f : a.dm.fs;
+    return p;
+}
+
+hipError_t launch_gateup_decode(const LayerArgs& a, const Workspace& w, hipStream_t s) {
+    ExpertParams p = make_params(a, w);
+    const int fblocks = (p.hstride + kFPB - 1) / kFPB;
+    dim3 grid(max_groups(a.dm) * fblocks);
+    const bool f32 = a.dm.act == DT_F32;
+    switch (a.dm.wdt) {
+    case DT_F32:
+        if (f32) hipLaunchKernelGGL((gateup_decode_kernel<float, DT_F32>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((gateup_decode_kernel<uint16_t, DT_F32>), grid, dim3(256), 0, s, p);
+        break;
+    case DT_BF16:
+        if (f32) hipLaunchKernelGGL((gateup_decode_kernel<float, DT_BF16>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((gateup_decode_kernel<uint16_t, DT_BF16>), grid, dim3(256), 0, s, p);
+        break;
+    default:
+        if (f32) hipLaunchKernelGGL((gateup_decode_kernel<float, DT_NVFP4>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((gateup_decode_kernel<uint16_t, DT_NVFP4>), grid, dim3(256), 0, s, p);
+        break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_down_decode(const LayerArgs& a, const Workspace& w, hipStream_t s) {
+    ExpertParams p = make_params(a, w);
+    const int rblocks = (a.dm.d + kRPB - 1) / kRPB;
+    dim3 grid(max_groups(a.dm) * rblocks);
+    switch (a.dm.wdt) {
+    case DT_F32: hipLaunchKernelGGL(down_decode_kernel<DT_F32>, grid, dim3(256), 0, s, p); break;
+    case DT_BF16: hipLaunchKernelGGL(down_decode_kernel<DT_BF16>, grid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL(down_decode_kernel<DT_NVFP4>, grid, dim3(256), 0, s, p); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace flint

@@ -1,0 +1,412 @@
+// flint_moe.cpp -- host side of libflint_moe.so: the C ABI declared in
+// include/flint_moe.h.  Argument validation (before any HIP call), device
+// check, workspace carving, decode/prefill path choice and kernel enqueueing
+// on the caller's stream.  No allocation, host synchronisation or
+// device-to-host read happens inside flint_moe_forward.
+#include "flint_moe.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "flint_internal.hpp"
+
+using namespace flint;
+
+struct flint_moe {
+    flint_moe_config cfg;
+    int device;
+    void* mem;
+    size_t mem_bytes;
+    Workspace ws;
+    int last_T;
+    int decode_max_t;
+    // measurement hook
+    int prof_kernel;
+    int prof_cap;
+    int prof_n;
+    std::vector<hipEvent_t> prof_ev;  // 2 per launch
+};
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+flint_status fail(flint_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+flint_status ok() {
+    g_err[0] = '\0';
+    return FLINT_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t act_size(int dt) { return dt == FLINT_F32 ? 4 : 2; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+flint_status check_config(const flint_moe_config* c) {
+    if (!c) return fail(FLINT_ERR_INVALID_ARG, "config is NULL");
+    if (c->struct_size != sizeof(flint_moe_config))
+        return fail(FLINT_ERR_INVALID_ARG, "config.struct_size %u != %zu", c->struct_size,
+                    sizeof(flint_moe_config));
+    if (c->d_model <= 0 || c->d_model % 64 || c->d_model > 16384)
+        return fail(FLINT_ERR_INVALID_ARG, "d_model %d: need a positive multiple of 64, <= 16384",
+                    c->d_model);
+    if (c->n_experts < 1 || c->n_experts > 256)
+        return fail(FLINT_ERR_INVALID_ARG, "n_experts %d: need 1..256", c->n_experts);
+    if (c->top_k < 1 || c->top_k > 8 || c->top_k > c->n_experts)
+        return fail(FLINT_ERR_INVALID_ARG, "top_k %d: need 1..min(8, n_experts)", c->top_k);
+    if (c->d_ff <= 0 || c->d_ff % 32 || c->d_ff > 16384)
+        return fail(FLINT_ERR_INVALID_ARG, "d_ff %d: need a positive multiple of 32, <= 16384",
+                    c->d_ff);
+    if (c->d_ff_shared < 0 || c->d_ff_shared % 32 || c->d_ff_shared > 16384)
+        return fail(FLINT_ERR_INVALID_ARG, "d_ff_shared %d: need 0 or a multiple of 32",
+                    c->d_ff_shared);
+    if (c->act_dtype != FLINT_F32 && c->act_dtype != FLINT_BF16)
+        return fail(FLINT_ERR_INVALID_ARG, "act_dtype %d: need FLINT_F32 or FLINT_BF16",
+                    c->act_dtype);
+    if (c->weight_dtype != FLINT_F32 && c->weight_dtype != FLINT_BF16 &&
+        c->weight_dtype != FLINT_NVFP4)
+        return fail(FLINT_ERR_INVALID_ARG, "weight_dtype %d unknown", c->weight_dtype);
+    if (c->max_tokens < 1 || c->max_tokens > 65536)
+        return fail(FLINT_ERR_INVALID_ARG, "max_tokens %d: need 1..65536", c->max_tokens);
+    if (c->flags & ~(FLINT_FORCE_DECODE_PATH | FLINT_FORCE_PREFILL_PATH))
+        return fail(FLINT_ERR_INVALID_ARG, "unknown flags 0x%x", c->flags);
+    if ((c->flags & FLINT_FORCE_DECODE_PATH) && (c->flags & FLINT_FORCE_PREFILL_PATH))
+        return fail(FLINT_ERR_INVALID_ARG, "both path-forcing flags set");
+    if ((c->flags & FLINT_FORCE_PREFILL_PATH) &&
+        (c->act_dtype != FLINT_BF16 || c->weight_dtype != FLINT_BF16))
+        return fail(FLINT_ERR_UNSUPPORTED, "the grouped-MFMA path needs bf16 activations and weights");
+    return FLINT_OK;
+}
+
+flint_status check_device(int* dev_out) {
+    int n = 0;
+    hipError_t e = hipGetDeviceCount(&n);
+    if (e != hipSuccess || n < 1) {
+        (void)hipGetLastError();
+        return fail(FLINT_ERR_NO_DEVICE, "no HIP device (%s)", hipGetErrorString(e));
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(FLINT_ERR_NO_DEVICE, "hipGetDevice failed");
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return fail(FLINT_ERR_NO_DEVICE, "hipGetDeviceProperties failed");
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(FLINT_ERR_NO_DEVICE, "device %d is %s; this library is built for gfx950", dev,
+                    prop.gcnArchName);
+    *dev_out = dev;
+    return FLINT_OK;
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Lay the workspace out in `base` (nullptr: just measure).
+size_t carve(const flint_moe_config& c, char* base, Workspace* w) {
+    const size_t Tm = (size_t)c.max_tokens, E = (size_t)c.n_experts, k = (size_t)c.top_k;
+    const size_t fmax = (size_t)(c.d_ff > c.d_ff_shared ? c.d_ff : c.d_ff_shared);
+    const size_t slots = (k + 1) * Tm;
+    const size_t max_tiles = slots / kPrefillBM + E + 2;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off = align_up(off + bytes, 256);
+        return base ? static_cast<void*>(base + o) : nullptr;
+    };
+    w->logits = static_cast<float*>(take(Tm * E * 4));
+    w->sel = static_cast<int*>(take(Tm * k * 4));
+    w->wts = static_cast<float*>(take(Tm * k * 4));
+    w->counts = static_cast<int*>(take(E * 4));
+    w->offsets = static_cast<int*>(take((E + 1) * 4));
+    w->sorted_pair = static_cast<int*>(take(Tm * k * 4));
+    w->pair_pos = static_cast<int*>(take(Tm * k * 4));
+    w->groups = static_cast<int4*>(take((E + 1) * 16));
+    w->n_groups = static_cast<int*>(take(4));
+    w->tiles = static_cast<int2*>(take(max_tiles * 8));
+    w->n_tiles = static_cast<int*>(take(4));
+    w->counter = static_cast<int*>(take(4));
+    w->h = take(slots * fmax * 4);
+    w->y = take(slots * (size_t)c.d_model * 4);
+    w->max_tiles = (int)max_tiles;
+    return off;
+}
+
+flint_status hip_fail(hipError_t e, const char* what) {
+    return fail(FLINT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+flint_status check_weights(const flint_moe_config& c, const flint_expert_weights* w,
+                           const char* name) {
+    if (!w) return fail(FLINT_ERR_INVALID_ARG, "%s weights are NULL", name);
+    if (!w->gate_up || !w->down)
+        return fail(FLINT_ERR_INVALID_ARG, "%s gate_up/down pointer is NULL", name);
+    if (!aligned(w->gate_up, 16) || !aligned(w->down, 16))
+        return fail(FLINT_ERR_INVALID_ARG, "%s gate_up/down must be 16-byte aligned", name);
+    if (c.weight_dtype == FLINT_NVFP4) {
+        if (!w->gate_up_scales || !w->down_scales || !w->tensor_scales)
+            return fail(FLINT_ERR_INVALID_ARG, "%s: NVFP4 weights need scale pointers", name);
+        if (!aligned(w->tensor_scales, 4))
+            return fail(FLINT_ERR_INVALID_ARG, "%s tensor_scales must be 4-byte aligned", name);
+    } else if (w->gate_up_scales || w->down_scales || w->tensor_scales) {
+        return fail(FLINT_ERR_INVALID_ARG, "%s: scale pointers must be NULL unless NVFP4", name);
+    }
+    return FLINT_OK;
+}
+
+struct Timer {
+    flint_moe* h;
+    int id;
+    hipStream_t s;
+    bool on;
+    Timer(flint_moe* h_, int id_, hipStream_t s_) : h(h_), id(id_), s(s_), on(false) {
+        if (h->prof_kernel == id && h->prof_n < h->prof_cap) {
+            on = true;
+            (void)hipEventRecord(h->prof_ev[2 * h->prof_n], s);
+        }
+    }
+    ~Timer() {
+        if (on) {
+            (void)hipEventRecord(h->prof_ev[2 * h->prof_n + 1], s);
+            h->prof_n++;
+        }
+    }
+};
+
+}  // namespace
+
+extern "C" {
+
+const char* flint_status_string(flint_status s) {
+    switch (s) {
+    case FLINT_OK: return "FLINT_OK";
+    case FLINT_ERR_INVALID_ARG: return "FLINT_ERR_INVALID_ARG";
+    case FLINT_ERR_UNSUPPORTED: return "FLINT_ERR_UNSUPPORTED";
+    case FLINT_ERR_OUT_OF_MEMORY: return "FLINT_ERR_OUT_OF_MEMORY";
+    case FLINT_ERR_NO_DEVICE: return "FLINT_ERR_NO_DEVICE";
+    case FLINT_ERR_HIP: return "FLINT_ERR_HIP";
+    }
+    return "FLINT_ERR_UNKNOWN";
+}
+
+const char* flint_last_error(void) { return g_err; }
+
+flint_status flint_moe_create(const flint_moe_config* cfg, flint_moe_t* out) {
+    if (!out) return fail(FLINT_ERR_INVALID_ARG, "out handle pointer is NULL");
+    *out = nullptr;
+    flint_status st = check_config(cfg);
+    if (st != FLINT_OK) return st;
+    int dev = 0;
+    st = check_device(&dev);
+    if (st != FLINT_OK) return st;
+    flint_moe* h = new (std::nothrow) flint_moe();
+    if (!h) return fail(FLINT_ERR_OUT_OF_MEMORY, "host allocation failed");
+    h->cfg = *cfg;
+    h->device = dev;
+    h->last_T = 0;
+    h->prof_kernel = -1;
+    h->prof_cap = 0;
+    h->prof_n = 0;
+    h->decode_max_t = 64;
+    if (const char* s = std::getenv("FLINT_MOE_DECODE_MAX_T")) h->decode_max_t = std::atoi(s);
+    Workspace dummy{};
+    h->mem_bytes = carve(*cfg, nullptr, &dummy);
+    const size_t bytes = h->mem_bytes;
+    hipError_t e = hipMalloc(&h->mem, bytes);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        delete h;
+        return fail(FLINT_ERR_OUT_OF_MEMORY, "workspace of %zu bytes: %s", bytes,
+                    hipGetErrorString(e));
+    }
+    carve(*cfg, static_cast<char*>(h->mem), &h->ws);
+    // zero everything once: the last-block ticket must start at 0
+    e = hipMemset(h->mem, 0, h->mem_bytes);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        (void)hipFree(h->mem);
+        delete h;
+        return hip_fail(e, "workspace init");
+    }
+    *out = h;
+    return ok();
+}
+
+flint_status flint_moe_destroy(flint_moe_t h) {
+    if (!h) return fail(FLINT_ERR_INVALID_ARG, "handle is NULL");
+    (void)hipDeviceSynchronize();
+    for (hipEvent_t ev : h->prof_ev) (void)hipEventDestroy(ev);
+    hipError_t e = hipFree(h->mem);
+    delete h;
+    if (e != hipSuccess) return hip_fail(e, "hipFree");
+    return ok();
+}
+
+flint_status flint_moe_forward(flint_moe_t h, int32_t T, const void* hidden, const float* router_w,
+                               const float* router_bias, const flint_expert_weights* experts,
+                               const flint_expert_weights* shared, const float* residual,
+                               void* out, hipStream_t stream) {
+    if (!h) return fail(FLINT_ERR_INVALID_ARG, "handle is NULL");
+    const flint_moe_config& c = h->cfg;
+    if (T < 0 || T > c.max_tokens)
+        return fail(FLINT_ERR_INVALID_ARG, "T=%d outside 0..max_tokens=%d", T, c.max_tokens);
+    if (T == 0) return ok();  // nothing to read or write
+    if (!hidden || !router_w || !out)
+        return fail(FLINT_ERR_INVALID_ARG, "hidden, router_w and out must be non-NULL");
+    if (!aligned(hidden, 16) || !aligned(out, 16) || !aligned(router_w, 16) ||
+        (residual && !aligned(residual, 16)) || (router_bias && !aligned(router_bias, 4)))
+        return fail(FLINT_ERR_INVALID_ARG, "tensors must be 16-byte aligned (bias 4-byte)");
+    flint_status st = check_weights(c, experts, "routed");
+    if (st != FLINT_OK) return st;
+    if (c.d_ff_shared > 0) {
+        st = check_weights(c, shared, "shared");
+        if (st != FLINT_OK) return st;
+    } else if (shared) {
+        return fail(FLINT_ERR_INVALID_ARG, "shared weights given but d_ff_shared == 0");
+    }
+    const size_t xbytes = (size_t)T * c.d_model * act_size(c.act_dtype);
+    const size_t obytes = (size_t)T * c.d_model * (residual ? 4 : act_size(c.act_dtype));
+    if (overlap(hidden, xbytes, out, obytes))
+        return fail(FLINT_ERR_INVALID_ARG, "out overlaps hidden");
+    if (residual && residual != out &&
+        overlap(residual, (size_t)T * c.d_model * 4, out, obytes))
+        return fail(FLINT_ERR_INVALID_ARG, "out partially overlaps residual");
+
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
+        return fail(FLINT_ERR_INVALID_ARG, "current device %d is not the handle's device %d", dev,
+                    h->device);
+
+    LayerArgs a;
+    a.dm = Dims{T, c.d_model, c.n_experts, c.top_k, c.d_ff, c.d_ff_shared, c.act_dtype,
+                c.weight_dtype};
+    a.x = hidden;
+    a.wr = router_w;
+    a.bias = router_bias;
+    a.routed = WeightPtrs{experts->gate_up, experts->down, experts->gate_up_scales,
+                          experts->down_scales, experts->tensor_scales};
+    a.shared = shared ? WeightPtrs{shared->gate_up, shared->down, shared->gate_up_scales,
+                                   shared->down_scales, shared->tensor_scales}
+                      : WeightPtrs{nullptr, nullptr, nullptr, nullptr, nullptr};
+    a.residual = residual;
+    a.out = out;
+
+    const bool mfma_ok = c.act_dtype == FLINT_BF16 && c.weight_dtype == FLINT_BF16;
+    bool prefill = false;
+    if (c.flags & FLINT_FORCE_PREFILL_PATH) prefill = true;
+    else if (!(c.flags & FLINT_FORCE_DECODE_PATH)) prefill = mfma_ok && T > h->decode_max_t;
+    if (prefill) return fail(FLINT_ERR_UNSUPPORTED, "grouped-MFMA path not built yet");
+
+    hipError_t e;
+    {
+        Timer tm(h, FLINT_KERNEL_ROUTE, stream);
+        e = launch_route_decode(a, h->ws, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "route kernel");
+    {
+        Timer tm(h, FLINT_KERNEL_EXPERT_UP, stream);
+        e = launch_gateup_decode(a, h->ws, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "gate/up kernel");
+    {
+        Timer tm(h, FLINT_KERNEL_EXPERT_DOWN, stream);
+        e = launch_down_decode(a, h->ws, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "down kernel");
+    {
+        Timer tm(h, FLINT_KERNEL_COMBINE, stream);
+        e = launch_combine(a, h->ws, false, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "combine kernel");
+    h->last_T = T;
+    return ok();
+}
+
+flint_status flint_moe_get_routing(flint_moe_t h, int32_t* idx, float* weights,
+                                   int32_t* sorted_pair, int32_t* counts, float* logits,
+                                   int32_t* T_out, hipStream_t stream) {
+    if (!h) return fail(FLINT_ERR_INVALID_ARG, "handle is NULL");
+    const size_t T = (size_t)h->last_T, k = (size_t)h->cfg.top_k, E = (size_t)h->cfg.n_experts;
+    if (T_out) *T_out = (int32_t)T;
+    if (T == 0) return ok();
+    struct Copy {
+        void* dst;
+        const void* src;
+        size_t bytes;
+    } copies[] = {{idx, h->ws.sel, T * k * 4},
+                  {weights, h->ws.wts, T * k * 4},
+                  {sorted_pair, h->ws.sorted_pair, T * k * 4},
+                  {counts, h->ws.counts, E * 4},
+                  {logits, h->ws.logits, T * E * 4}};
+    for (const Copy& cp : copies) {
+        if (!cp.dst) continue;
+        hipError_t e = hipMemcpyAsync(cp.dst, cp.src, cp.bytes, hipMemcpyDeviceToDevice, stream);
+        if (e != hipSuccess) return hip_fail(e, "routing copy");
+    }
+    return ok();
+}
+
+flint_status flint_moe_profile_begin(flint_moe_t h, int32_t kernel_id, int32_t n_launches) {
+    if (!h) return fail(FLINT_ERR_INVALID_ARG, "handle is NULL");
+    if (kernel_id < 0 || kernel_id >= FLINT_KERNEL_COUNT || n_launches < 1 || n_launches > 100000)
+        return fail(FLINT_ERR_INVALID_ARG, "kernel_id %d / n_launches %d out of range", kernel_id,
+                    n_launches);
+    while ((int)h->prof_ev.size() < 2 * n_launches) {
+        hipEvent_t ev;
+        hipError_t e = hipEventCreate(&ev);
+        if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+        h->prof_ev.push_back(ev);
+    }
+    h->prof_kernel = kernel_id;
+    h->prof_cap = n_launches;
+    h->prof_n = 0;
+    return ok();
+}
+
+flint_status flint_moe_profile_end(flint_moe_t h, float* ms_out, int32_t cap, int32_t* n_out) {
+    if (!h) return fail(FLINT_ERR_INVALID_ARG, "handle is NULL");
+    const int n = h->prof_n;
+    h->prof_kernel = -1;
+    int w = 0;
+    for (int i = 0; i < n; ++i) {
+        hipError_t e = hipEventSynchronize(h->prof_ev[2 * i + 1]);
+        if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+        float ms = 0.f;
+        e = hipEventElapsedTime(&ms, h->prof_ev[2 * i], h->prof_ev[2 * i + 1]);
+        if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+        if (ms_out && w < cap) ms_out[w++] = ms;
+    }
+    if (n_out) *n_out = w;
+    h->prof_n = 0;
+    return ok();
+}
+
+flint_status flint_rmsnorm_forward(int32_t T, int32_t d, const float* in, float eps,
+                                   void* out_bf16, hipStream_t stream) {
+    if (T < 0 || d <= 0 || d % 64 || !in || !out_bf16 || !(eps >= 0.f))
+        return fail(FLINT_ERR_INVALID_ARG, "rmsnorm: bad T=%d d=%d or pointers", T, d);
+    if (!aligned(in, 16) || !aligned(out_bf16, 16))
+        return fail(FLINT_ERR_INVALID_ARG, "rmsnorm: tensors must be 16-byte aligned");
+    if (overlap(in, (size_t)T * d * 4, out_bf16, (size_t)T * d * 2))
+        return fail(FLINT_ERR_INVALID_ARG, "rmsnorm: out overlaps in");
+    if (T == 0) return ok();
+    hipError_t e = launch_rmsnorm(T, d, in, eps, out_bf16, stream);
+    if (e != hipSuccess) return hip_fail(e, "rmsnorm kernel");
+    return ok();
+}
+
+}  // extern "C"

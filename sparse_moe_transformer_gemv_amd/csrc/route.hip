@@ -1,0 +1,368 @@
+// route.hip -- router logits, top-k selection and the counting-sort token
+// permutation of the MoE layer (gfx950).
+//
+// Selection: per token, the k largest of the E router logits, ties to the
+// lower expert index; weights are the softmax of the chosen logits, i.e. the
+// full softmax renormalised over the chosen k.  The pages fix 256 experts with
+// 6 chosen per token [evermx.com, "Recursive Flint: Open-Weight MoE Coding
+// Model, 2.5B Active", Feature Overview, "Sparse architecture"]; the softmax,
+// renormalisation and tie rule are the readings this library takes where the
+// pages are silent.
+//
+// Permutation: the k*T (token, slot) pairs are stably sorted by expert, so the
+// tokens of one expert are contiguous and in token order; per-expert counts,
+// offsets and the inverse map feed the expert kernels and the combine.  Ranks
+// come from ballot-based matching inside each wavefront plus per-wave LDS
+// histograms, so the order never depends on atomic timing.
+#include "flint_internal.hpp"
+
+namespace flint {
+
+// ---------------------------------------------------------------------------
+// Router logits for one expert row and a run of tokens: one wavefront per
+// expert, lanes stride K with float4 loads, token groups of 8 accumulators.
+// ---------------------------------------------------------------------------
+template <typename ActT>
+__device__ __forceinline__ void load_act4(const ActT* x, float v[4]);
+
+template <>
+__device__ __forceinline__ void load_act4<float>(const float* x, float v[4]) {
+    float4 a = *reinterpret_cast<const float4*>(x);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+}
+
+template <>
+__device__ __forceinline__ void load_act4<uint16_t>(const uint16_t* x, float v[4]) {
+    uint2 a = *reinterpret_cast<const uint2*>(x);
+    v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x); v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
+}
+
+template <typename ActT>
+__device__ void router_row_logits(const ActT* __restrict__ x, const float* __restrict__ wrow,
+                                  float b, int t_begin, int t_end, int d, int E, int e,
+                                  float* __restrict__ logits, int lane) {
+    constexpr int TG = 8;
+    for (int t0 = t_begin; t0 < t_end; t0 += TG) {
+        float acc[TG];
+#pragma unroll
+        for (int i = 0; i < TG; ++i) acc[i] = 0.f;
+        for (int k0 = lane * 4; k0 < d; k0 += 256) {
+            float4 w = *reinterpret_cast<const float4*>(wrow + k0);
+#pragma unroll
+            for (int tt = 0; tt < TG; ++tt) {
+                if (t0 + tt < t_end) {
+                    float xv[4];
+                    load_act4<ActT>(x + (size_t)(t0 + tt) * d + k0, xv);
+                    float a = acc[tt];
+                    a = fmaf(w.x, xv[0], a);
+                    a = fmaf(w.y, xv[1], a);
+                    a = fmaf(w.z, xv[2], a);
+                    a = fmaf(w.w, xv[3], a);
+                    acc[tt] = a;
+                }
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < TG; ++tt) {
+            float v = wave_sum(acc[tt]);
+            if (lane == 0 && t0 + tt < t_end) logits[(size_t)(t0 + tt) * E + e] = v + b;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Top-k of one token by one wavefront.  Lane l holds logits e = l + 64 i.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        float ov = __shfl_xor(v, off, 64);
+        int oi = __shfl_xor(i, off, 64);
+        if (ov > v || (ov == v && oi < i)) {
+            v = ov;
+            i = oi;
+        }
+    }
+}
+
+__device__ void wave_topk_token(const float* __restrict__ lrow, int E, int k, int lane,
+                                int* __restrict__ sel_out, float* __restrict__ w_out) {
+    constexpr int NONE = 0x7FFFFFFF;
+    float lv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int e = lane + 64 * i;
+        lv[i] = (e < E) ? lrow[e] : 0.f;
+    }
+    unsigned taken = 0;
+    float my_v = 0.f;
+    int my_e = 0;
+    for (int j = 0; j < k; ++j) {
+        float bv = -INFINITY;
+        int bi = NONE;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int e = lane + 64 * i;
+            if (e < E && !((taken >> i) & 1u)) {
+                // strictly greater keeps the lower index on equal logits
+                if (bi == NONE || lv[i] > bv) {
+                    bv = lv[i];
+                    bi = e;
+                }
+            }
+        }
+        wave_argmax(bv, bi);
+        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+        if (lane == j) {
+            my_v = bv;
+            my_e = bi;
+        }
+    }
+    // weights: softmax over the chosen logits; slot 0 holds the largest
+    float l0 = __shfl(my_v, 0, 64);
+    float p = (lane < k) ? expf(my_v - l0) : 0.f;
+    float s = wave_sum(p);
+    if (lane < k) {
+        sel_out[lane] = my_e;
+        w_out[lane] = p / s;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Stable counting sort of P pair keys (expert ids < E <= 256) by one block.
+// Writes counts[E], offsets[E+1], sorted_pair[P], pair_pos[P], the active
+// group list and (if bm > 0) the prefill tile list.
+// s_hist: LDS [NW*E]; s_off: LDS [E+1].
+// ---------------------------------------------------------------------------
+template <int NT>
+__device__ void block_sort_and_groups(const int* __restrict__ keys, int P, int E, int T, int k,
+                                      bool has_shared, int bm, const Workspace& ws, int* s_hist,
+                                      int* s_off) {
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const unsigned long long lt = (1ull << lane) - 1ull;
+
+    for (int i = tid; i < NW * E; i += NT) s_hist[i] = 0;
+    __syncthreads();
+    const int S = (((P + NW - 1) / NW) + 63) & ~63;
+    const int b0 = min(P, w * S), b1 = min(P, b0 + S);
+    for (int i = b0 + lane; i < b1; i += 64) atomicAdd(&s_hist[w * E + keys[i]], 1);
+    __syncthreads();
+
+    // per-expert totals and their exclusive scan (wave 0; 4 experts per lane)
+    if (w == 0) {
+        int c[4];
+        int local = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int e = lane * 4 + i, s = 0;
+            if (e < E)
+                for (int ww = 0; ww < NW; ++ww) s += s_hist[ww * E + e];
+            c[i] = s;
+            local += s;
+        }
+        int inc = local;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            int v = __shfl_up(inc, off, 64);
+            if (lane >= off) inc += v;
+        }
+        int run = inc - local;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int e = lane * 4 + i;
+            if (e < E) {
+                s_off[e] = run;
+                ws.offsets[e] = run;
+                ws.counts[e] = c[i];
+            }
+            run += c[i];
+        }
+        if (lane == 63) {
+            s_off[E] = inc;
+            ws.offsets[E] = inc;
+        }
+    }
+    __syncthreads();
+    // turn per-wave counts into per-wave base positions
+    for (int e = tid; e < E; e += NT) {
+        int run = s_off[e];
+        for (int ww = 0; ww < NW; ++ww) {
+            int c = s_hist[ww * E + e];
+            s_hist[ww * E + e] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    // ordered scatter: rank inside each 64-pair chunk by ballot matching
+    for (int c0 = b0; c0 < b1; c0 += 64) {
+        const int i = c0 + lane;
+        const bool valid = i < b1;
+        const int key = valid ? keys[i] : 0;
+        unsigned long long m = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const bool bit = (key >> b) & 1;
+            const unsigned long long bb = __ballot(valid && bit);
+            m &= bit ? bb : ~bb;
+        }
+        if (valid) {
+            const int pos = s_hist[w * E + key] + __popcll(m & lt);
+            ws.sorted_pair[pos] = i;
+            ws.pair_pos[i] = pos;
+        }
+        // the highest lane of each key group advances that key's base
+        if (valid && (m >> lane) == 1ull) s_hist[w * E + key] += __popcll(m);
+    }
+    __syncthreads();
+
+    // active groups (experts with tokens, ascending), then the shared group;
+    // with bm > 0 also the prefill tile list, ceil(rows / bm) tiles per group
+    if (w == 0) {
+        int n = 0, ntile = 0;
+        for (int e0 = 0; e0 < E; e0 += 64) {
+            const int e = e0 + lane;
+            const int c = (e < E) ? s_off[e + 1] - s_off[e] : 0;
+            const unsigned long long act = __ballot(c > 0);
+            const int gidx = n + __popcll(act & lt);
+            if (c > 0) ws.groups[gidx] = make_int4(e, s_off[e], c, s_off[e]);
+            if (bm > 0) {
+                const int nt = (c + bm - 1) / bm;
+                int inc = nt;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const int v = __shfl_up(inc, off, 64);
+                    if (lane >= off) inc += v;
+                }
+                const int pos = ntile + inc - nt;
+                for (int t = 0; t < nt; ++t) ws.tiles[pos + t] = make_int2(gidx, t * bm);
+                ntile += __shfl(inc, 63, 64);
+            }
+            n += __popcll(act);
+        }
+        if (has_shared) {
+            if (lane == 0) ws.groups[n] = make_int4(E, 0, T, k * T);
+            if (bm > 0) {
+                const int nt = (T + bm - 1) / bm;
+                for (int t = lane; t < nt; t += 64) ws.tiles[ntile + t] = make_int2(n, t * bm);
+                ntile += nt;
+            }
+            n += 1;
+        }
+        if (lane == 0) {
+            *ws.n_groups = n;
+            if (bm > 0) *ws.n_tiles = ntile;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Decode path, one launch: router GEMV over all experts, then the last block
+// to finish runs top-k for every token and the counting sort.
+// ---------------------------------------------------------------------------
+struct RouteDecodeParams {
+    const void* x;
+    const float* wr;
+    const float* bias;
+    int T, d, E, k;
+    int has_shared;
+    Workspace ws;
+};
+
+template <typename ActT>
+__global__ __launch_bounds__(256) void route_decode_kernel(RouteDecodeParams p) {
+    __shared__ int s_hist[4 * 256];
+    __shared__ int s_off[257];
+    __shared__ int s_last;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int e = blockIdx.x * 4 + wave;
+    if (e < p.E)
+        router_row_logits<ActT>(static_cast<const ActT*>(p.x), p.wr + (size_t)e * p.d,
+                                p.bias ? p.bias[e] : 0.f, 0, p.T, p.d, p.E, e, p.ws.logits, lane);
+    // publish this block's logits, then take a ticket
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = (atomicAdd(p.ws.counter, 1) == (int)gridDim.x - 1);
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();  // acquire: every other block's logits are visible
+    if (threadIdx.x == 0) atomicExch(p.ws.counter, 0);
+    for (int t = wave; t < p.T; t += 4)
+        wave_topk_token(p.ws.logits + (size_t)t * p.E, p.E, p.k, lane, p.ws.sel + (size_t)t * p.k,
+                        p.ws.wts + (size_t)t * p.k);
+    __threadfence();
+    __syncthreads();
+    block_sort_and_groups<256>(p.ws.sel, p.k * p.T, p.E, p.T, p.k, p.has_shared != 0, 0, p.ws,
+                               s_hist, s_off);
+}
+
+hipError_t launch_route_decode(const LayerArgs& a, const Workspace& w, hipStream_t s) {
+    RouteDecodeParams p{a.x, a.wr, a.bias, a.dm.T, a.dm.d, a.dm.E, a.dm.k, a.dm.fs > 0, w};
+    dim3 grid((a.dm.E + 3) / 4);
+    if (a.dm.act == DT_F32)
+        hipLaunchKernelGGL(route_decode_kernel<float>, grid, dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL(route_decode_kernel<uint16_t>, grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Prefill path: logits (token blocks x expert blocks), top-k (a wave per
+// token), then one block sorts.
+// ---------------------------------------------------------------------------
+constexpr int kLogitTokensPerBlock = 64;
+
+template <typename ActT>
+__global__ __launch_bounds__(256) void router_logits_kernel(RouteDecodeParams p) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int e = blockIdx.x * 4 + wave;
+    const int t0 = blockIdx.y * kLogitTokensPerBlock;
+    const int t1 = min(p.T, t0 + kLogitTokensPerBlock);
+    if (e < p.E)
+        router_row_logits<ActT>(static_cast<const ActT*>(p.x), p.wr + (size_t)e * p.d,
+                                p.bias ? p.bias[e] : 0.f, t0, t1, p.d, p.E, e, p.ws.logits, lane);
+}
+
+hipError_t launch_router_logits(const LayerArgs& a, const Workspace& w, hipStream_t s) {
+    RouteDecodeParams p{a.x, a.wr, a.bias, a.dm.T, a.dm.d, a.dm.E, a.dm.k, a.dm.fs > 0, w};
+    dim3 grid((a.dm.E + 3) / 4, (a.dm.T + kLogitTokensPerBlock - 1) / kLogitTokensPerBlock);
+    if (a.dm.act == DT_F32)
+        hipLaunchKernelGGL(router_logits_kernel<float>, grid, dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL(router_logits_kernel<uint16_t>, grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void topk_kernel(RouteDecodeParams p) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t < p.T)
+        wave_topk_token(p.ws.logits + (size_t)t * p.E, p.E, p.k, lane, p.ws.sel + (size_t)t * p.k,
+                        p.ws.wts + (size_t)t * p.k);
+}
+
+hipError_t launch_topk(const LayerArgs& a, const Workspace& w, hipStream_t s) {
+    RouteDecodeParams p{a.x, a.wr, a.bias, a.dm.T, a.dm.d, a.dm.E, a.dm.k, a.dm.fs > 0, w};
+    hipLaunchKernelGGL(topk_kernel, dim3((a.dm.T + 3) / 4), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+struct SortParams {
+    int T, E, k, has_shared, bm;
+    Workspace ws;
+};
+
+__global__ __launch_bounds__(1024) void sort_kernel(SortParams p) {
+    __shared__ int s_hist[16 * 256];
+    __shared__ int s_off[257];
+    block_sort_and_groups<1024>(p.ws.sel, p.k * p.T, p.E, p.T, p.k, p.has_shared != 0, p.bm, p.ws,
+                                s_hist, s_off);
+}
+
+hipError_t launch_sort(const LayerArgs& a, const Workspace& w, int bm, hipStream_t s) {
+    SortParams p{a.dm.T, a.dm.E, a.dm.k, a.dm.fs > 0, bm, w};
+    hipLaunchKernelGGL(sort_kernel, dim3(1), dim3(1024), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace flint

@@ -1,0 +1,239 @@
+"""ctypes binding of libflint_moe.so (argument marshalling only).
+
+Every step of the layer runs in the library's HIP kernels; this module only
+checks that tensors live on the GPU and are contiguous, passes their device
+pointers and the current HIP stream, and turns status codes into exceptions.
+PyTorch provides device memory and streams, nothing else.  If the library is
+missing the import fails loudly: there is no CPU fallback.
+
+Names follow the C ABI (include/flint_moe.h): flint_moe_create,
+flint_moe_forward, flint_moe_get_routing, flint_moe_destroy,
+flint_rmsnorm_forward, plus a small MoELayer wrapper around a handle.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libflint_moe.so")
+
+FLINT_OK, FLINT_ERR_INVALID_ARG, FLINT_ERR_UNSUPPORTED = 0, 1, 2
+FLINT_ERR_OUT_OF_MEMORY, FLINT_ERR_NO_DEVICE, FLINT_ERR_HIP = 3, 4, 5
+FLINT_F32, FLINT_BF16, FLINT_NVFP4 = 0, 1, 2
+FLINT_FORCE_DECODE_PATH, FLINT_FORCE_PREFILL_PATH = 0x1, 0x2
+KERNEL_ROUTE, KERNEL_SORT, KERNEL_EXPERT_UP, KERNEL_EXPERT_DOWN, KERNEL_COMBINE = range(5)
+
+EXPORTED = [
+    "flint_moe_create", "flint_moe_forward", "flint_moe_get_routing", "flint_moe_profile_begin",
+    "flint_moe_profile_end", "flint_moe_destroy", "flint_status_string", "flint_last_error",
+    "flint_rmsnorm_forward",
+]
+
+
+class FlintError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__("%s: %s" % (_status_name(status), detail))
+        self.status = status
+
+
+class flint_moe_config(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("d_model", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("d_ff", ctypes.c_int32), ("d_ff_shared", ctypes.c_int32),
+                ("act_dtype", ctypes.c_int32), ("weight_dtype", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class flint_expert_weights(ctypes.Structure):
+    _fields_ = [("gate_up", ctypes.c_void_p), ("down", ctypes.c_void_p),
+                ("gate_up_scales", ctypes.c_void_p), ("down_scales", ctypes.c_void_p),
+                ("tensor_scales", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libflint_moe.so and declare the C signatures (no device call)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError("libflint_moe.so is not built (%s); run "
+                          "`python -m sparse_moe_transformer_gemv_amd.build`" % path)
+    L = ctypes.CDLL(path)
+    vp, i32, u32, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_int
+    L.flint_moe_create.argtypes = [ctypes.POINTER(flint_moe_config), ctypes.POINTER(vp)]
+    L.flint_moe_create.restype = st
+    L.flint_moe_forward.argtypes = [vp, i32, vp, vp, vp, ctypes.POINTER(flint_expert_weights),
+                                    ctypes.POINTER(flint_expert_weights), vp, vp, vp]
+    L.flint_moe_forward.restype = st
+    L.flint_moe_get_routing.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(i32), vp]
+    L.flint_moe_get_routing.restype = st
+    L.flint_moe_profile_begin.argtypes = [vp, i32, i32]
+    L.flint_moe_profile_begin.restype = st
+    L.flint_moe_profile_end.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i32,
+                                        ctypes.POINTER(i32)]
+    L.flint_moe_profile_end.restype = st
+    L.flint_moe_destroy.argtypes = [vp]
+    L.flint_moe_destroy.restype = st
+    L.flint_status_string.argtypes = [st]
+    L.flint_status_string.restype = ctypes.c_char_p
+    L.flint_last_error.argtypes = []
+    L.flint_last_error.restype = ctypes.c_char_p
+    L.flint_rmsnorm_forward.argtypes = [i32, i32, vp, ctypes.c_float, vp, vp]
+    L.flint_rmsnorm_forward.restype = st
+    _lib = L
+    return L
+
+
+def _status_name(s: int) -> str:
+    try:
+        return load_library().flint_status_string(s).decode()
+    except Exception:  # noqa: BLE001 - only used to label an error
+        return "status %d" % s
+
+
+def _check(status: int):
+    if status != FLINT_OK:
+        raise FlintError(status, load_library().flint_last_error().decode())
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    return t.data_ptr()
+
+
+_TORCH_ACT = {FLINT_F32: torch.float32, FLINT_BF16: torch.bfloat16}
+_TORCH_W = {FLINT_F32: torch.float32, FLINT_BF16: torch.bfloat16, FLINT_NVFP4: torch.uint8}
+
+
+@dataclass
+class ExpertWeights:
+    """Device tensors of one expert set (layouts as in include/flint_moe.h)."""
+    gate_up: torch.Tensor
+    down: torch.Tensor
+    gate_up_scales: Optional[torch.Tensor] = None
+    down_scales: Optional[torch.Tensor] = None
+    tensor_scales: Optional[torch.Tensor] = None
+
+    def as_c(self, wdtype: int) -> flint_expert_weights:
+        wt = _TORCH_W[wdtype]
+        return flint_expert_weights(
+            _ptr(self.gate_up, "gate_up", wt), _ptr(self.down, "down", wt),
+            _ptr(self.gate_up_scales, "gate_up_scales", torch.uint8),
+            _ptr(self.down_scales, "down_scales", torch.uint8),
+            _ptr(self.tensor_scales, "tensor_scales", torch.float32))
+
+
+def flint_moe_create(cfg: flint_moe_config) -> ctypes.c_void_p:
+    h = ctypes.c_void_p()
+    _check(load_library().flint_moe_create(ctypes.byref(cfg), ctypes.byref(h)))
+    return h
+
+
+def flint_moe_destroy(h) -> None:
+    _check(load_library().flint_moe_destroy(h))
+
+
+def flint_rmsnorm_forward(x: torch.Tensor, eps: float = 1e-6,
+                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16(x / sqrt(mean(x^2) + eps)) per row; x [T, d] fp32 on the GPU."""
+    if x.dim() != 2:
+        raise ValueError("x must be [T, d]")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    _check(load_library().flint_rmsnorm_forward(x.shape[0], x.shape[1],
+                                                _ptr(x, "x", torch.float32), eps,
+                                                _ptr(out, "out", torch.bfloat16), _stream()))
+    return out
+
+
+class MoELayer:
+    """One handle (workspace) of the MoE layer; serves any number of weight sets."""
+
+    def __init__(self, d_model: int, n_experts: int = 256, top_k: int = 6, d_ff: int = 512,
+                 d_ff_shared: int = 512, act_dtype: int = FLINT_BF16,
+                 weight_dtype: int = FLINT_BF16, max_tokens: int = 64, flags: int = 0):
+        load_library()
+        self.cfg = flint_moe_config(ctypes.sizeof(flint_moe_config), d_model, n_experts, top_k,
+                                    d_ff, d_ff_shared, act_dtype, weight_dtype, max_tokens, flags)
+        self.handle = flint_moe_create(self.cfg)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            flint_moe_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001 - interpreter shutdown
+            pass
+
+    def forward(self, x: torch.Tensor, router_w: torch.Tensor, experts: ExpertWeights,
+                shared: Optional[ExpertWeights], router_bias: Optional[torch.Tensor] = None,
+                residual: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        c = self.cfg
+        if x.dim() != 2 or x.shape[1] != c.d_model:
+            raise ValueError("x must be [T, %d]" % c.d_model)
+        T = x.shape[0]
+        if out is None:
+            odt = torch.float32 if residual is not None else _TORCH_ACT[c.act_dtype]
+            out = torch.empty((T, c.d_model), dtype=odt, device=x.device)
+        ew = experts.as_c(c.weight_dtype)
+        sw = shared.as_c(c.weight_dtype) if shared is not None else None
+        _check(load_library().flint_moe_forward(
+            self.handle, T, _ptr(x, "x", _TORCH_ACT[c.act_dtype]),
+            _ptr(router_w, "router_w", torch.float32),
+            _ptr(router_bias, "router_bias", torch.float32), ctypes.byref(ew),
+            ctypes.byref(sw) if sw is not None else None,
+            _ptr(residual, "residual", torch.float32), _ptr(out, "out"), _stream()))
+        return out
+
+    __call__ = forward
+
+    def routing(self) -> dict:
+        """Routing of the last forward: idx, weights, sorted_pair, counts, logits."""
+        c = self.cfg
+        T = ctypes.c_int32(0)
+        _check(load_library().flint_moe_get_routing(self.handle, None, None, None, None, None,
+                                                    ctypes.byref(T), _stream()))
+        T = T.value
+        dev = torch.device("cuda", torch.cuda.current_device())
+        r = {"idx": torch.empty((T, c.top_k), dtype=torch.int32, device=dev),
+             "weights": torch.empty((T, c.top_k), dtype=torch.float32, device=dev),
+             "sorted_pair": torch.empty((T * c.top_k,), dtype=torch.int32, device=dev),
+             "counts": torch.empty((c.n_experts,), dtype=torch.int32, device=dev),
+             "logits": torch.empty((T, c.n_experts), dtype=torch.float32, device=dev)}
+        _check(load_library().flint_moe_get_routing(
+            self.handle, r["idx"].data_ptr(), r["weights"].data_ptr(),
+            r["sorted_pair"].data_ptr(), r["counts"].data_ptr(), r["logits"].data_ptr(), None,
+            _stream()))
+        return r
+
+    def profile_begin(self, kernel_id: int, n_launches: int) -> None:
+        _check(load_library().flint_moe_profile_begin(self.handle, kernel_id, n_launches))
+
+    def profile_end(self, cap: int = 100000) -> list:
+        buf = (ctypes.c_float * cap)()
+        n = ctypes.c_int32(0)
+        _check(load_library().flint_moe_profile_end(self.handle, buf, cap, ctypes.byref(n)))
+        return [buf[i] for i in range(n.value)]

@@ -1,0 +1,192 @@
+"""GPU parity: the HIP layer (through the C ABI) against the fp64 oracle.
+
+Reduced shapes span several work items with ragged tails; the full-size
+cases are the workloads the benchmark times, compared on every token (decode)
+or on sampled tokens (prefill).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import (check_permutation, compare, dev_array, dev_layer, make_layer_obj,
+                         out_host, run_gpu, run_oracle, x_device)
+from sparse_moe_transformer_gemv_amd import FLINT_FORCE_DECODE_PATH, FlintError
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(cfg_id, T, max_tokens=None, flags=0, draw=0, **override):
+    L = synth.layer(cfg_id, **override)
+    c = L["cfg"]
+    x = synth.hidden(cfg_id, T, c["d"], c["act"], draw=draw)
+    layer = make_layer_obj(c, max_tokens or T, flags)
+    D = dev_layer(L)
+    out, rout = run_gpu(layer, D, x)
+    ref = run_oracle(L, x)
+    rep = compare(out, rout, ref, c["k"], c["wdtype"], out_bf16=c["act"] == synth.BF16)
+    check_permutation(rout, T, c["k"], c["E"])
+    print("case cfg=%d T=%d %s -> %s" % (cfg_id, T, override, rep), flush=True)
+    return L, x, layer, D, out, rout, ref
+
+
+def test_tiny_f32_workload():
+    _case(0, 64)
+
+
+@pytest.mark.parametrize("T", [1, 3, 17, 64])
+def test_small_bf16_decode(T):
+    _case(1, T, d=256, E=64, f=64, fs=96)
+
+
+@pytest.mark.parametrize("T", [1, 5, 40])
+def test_small_nvfp4_decode(T):
+    _case(4, T, d=256, E=32, k=4, f=64, fs=64)
+
+
+def test_f32_activations_bf16_weights():
+    _case(1, 9, d=192, E=48, f=32, fs=64, act=synth.F32)
+
+
+def test_no_shared_expert():
+    L = synth.layer(1, d=128, E=16, f=32, fs=32)
+    L["shared"] = None
+    c = dict(L["cfg"], fs=0)
+    L["cfg"] = c
+    x = synth.hidden(1, 7, 128, synth.BF16)
+    layer = make_layer_obj(c, 8)
+    out, rout = run_gpu(layer, dev_layer(L), x)
+    ref = oracle.moe_forward(x, L["router_w"], L["experts"], None, top_k=c["k"],
+                             wdtype=synth.BF16)
+    compare(out, rout, ref, c["k"], synth.BF16, out_bf16=True)
+
+
+def test_odd_expert_count_and_k8():
+    _case(1, 20, d=128, E=100, k=8, f=32, fs=32)
+
+
+def test_top1():
+    _case(1, 11, d=128, E=64, k=1, f=32, fs=32)
+
+
+def test_equal_logits_pick_lowest_indices():
+    L = synth.layer(1, d=128, E=64, f=32, fs=32)
+    L["router_w"] = np.zeros_like(L["router_w"])
+    c = L["cfg"]
+    x = synth.hidden(1, 5, 128, synth.BF16)
+    layer = make_layer_obj(c, 5)
+    out, rout = run_gpu(layer, dev_layer(L), x)
+    assert np.array_equal(rout["idx"], np.tile(np.arange(6), (5, 1)))
+    assert np.allclose(rout["weights"], 1.0 / 6, atol=1e-7)
+    ref = run_oracle(L, x)
+    # every gap is 0 here, so compare the outputs directly
+    err = np.abs(out - ref["out"]).max()
+    assert err <= 2e-2 * np.sqrt(np.mean(ref["out"] ** 2))
+
+
+def test_zero_tokens_is_a_noop():
+    L = synth.layer(1, d=128, E=16, f=32, fs=32)
+    layer = make_layer_obj(L["cfg"], 4)
+    D = dev_layer(L)
+    x = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    layer.forward(x, D["router_w"], D["experts"], D["shared"], out=out)
+    torch.cuda.synchronize()
+
+
+def test_too_many_tokens_rejected():
+    L = synth.layer(1, d=128, E=16, f=32, fs=32)
+    layer = make_layer_obj(L["cfg"], 4)
+    D = dev_layer(L)
+    x = x_device(synth.hidden(1, 5, 128, synth.BF16))
+    with pytest.raises(FlintError):
+        layer.forward(x, D["router_w"], D["experts"], D["shared"])
+
+
+def test_residual_gives_fp32_sum():
+    L = synth.layer(1, d=256, E=32, f=64, fs=64)
+    c = L["cfg"]
+    x = synth.hidden(1, 6, 256, synth.BF16)
+    res = np.random.default_rng(3).standard_normal((6, 256)).astype(np.float32)
+    layer = make_layer_obj(c, 6)
+    D = dev_layer(L)
+    rd = dev_array(res)
+    out, rout = run_gpu(layer, D, x, residual=rd)
+    ref = run_oracle(L, x)
+    ref = dict(ref, out=ref["out"] + res.astype(np.float64))
+    compare(out, rout, ref, c["k"], synth.BF16, out_bf16=False)
+    # in place: out aliases the residual
+    layer.forward(x_device(x), D["router_w"], D["experts"], D["shared"], residual=rd, out=rd)
+    torch.cuda.synchronize()
+    assert np.abs(out_host(rd) - out).max() <= 1e-6 * np.abs(out).max()
+
+
+def test_rmsnorm_kernel():
+    from sparse_moe_transformer_gemv_amd import flint_rmsnorm_forward
+    h = np.random.default_rng(4).standard_normal((32, 2048)).astype(np.float32) * 3
+    out = flint_rmsnorm_forward(dev_array(h), 1e-6)
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    want = oracle.round_to_bf16(oracle.rmsnorm(h.astype(np.float64), 1e-6))
+    # fp32 vs fp64 arithmetic may land on the other side of a bf16 midpoint
+    diff = np.abs(got.astype(np.int32) - want.astype(np.int32))
+    assert diff.max() <= 1 and (diff > 0).mean() < 1e-3
+
+
+def test_deterministic_repeat():
+    L = synth.layer(1, d=256, E=64, f=64, fs=64)
+    c = L["cfg"]
+    x = synth.hidden(1, 33, 256, synth.BF16)
+    layer = make_layer_obj(c, 64)
+    D = dev_layer(L)
+    a, ra = run_gpu(layer, D, x)
+    b, rb = run_gpu(layer, D, x)
+    assert np.array_equal(a, b)
+    assert np.array_equal(ra["sorted_pair"], rb["sorted_pair"])
+
+
+# ----------------------------------------------------------- full-size workloads
+
+@pytest.fixture(scope="module")
+def decode_layer():
+    L = synth.layer(1)
+    return L, dev_layer(L)
+
+
+@pytest.mark.parametrize("T", [1, 4, 16, 64])
+def test_full_decode_bf16(decode_layer, T):
+    L, D = decode_layer
+    c = L["cfg"]
+    x = synth.hidden(1, T, c["d"], c["act"])
+    layer = make_layer_obj(c, 64)
+    out, rout = run_gpu(layer, D, x)
+    ref = run_oracle(L, x)
+    rep = compare(out, rout, ref, c["k"], c["wdtype"], out_bf16=True)
+    check_permutation(rout, T, c["k"], c["E"])
+    # the same layer with an fp32 output (zero fp32 residual): the plain bound
+    zero = torch.zeros((T, c["d"]), dtype=torch.float32, device="cuda")
+    out32, rout32 = run_gpu(layer, D, x, residual=zero)
+    rep32 = compare(out32, rout32, ref, c["k"], c["wdtype"], out_bf16=False)
+    print("decode bf16 T=%d: %s | fp32 out: %s" % (T, rep, rep32), flush=True)
+
+
+@pytest.fixture(scope="module")
+def fp4_layer():
+    L = synth.layer(4)
+    return L, dev_layer(L)
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_full_decode_nvfp4(fp4_layer, T):
+    L, D = fp4_layer
+    c = L["cfg"]
+    x = synth.hidden(4, T, c["d"], c["act"])
+    layer = make_layer_obj(c, 16)
+    out, rout = run_gpu(layer, D, x)
+    ref = run_oracle(L, x)
+    rep = compare(out, rout, ref, c["k"], c["wdtype"], out_bf16=True)
+    zero = torch.zeros((T, c["d"]), dtype=torch.float32, device="cuda")
+    out32, rout32 = run_gpu(layer, D, x, residual=zero)
+    rep32 = compare(out32, rout32, ref, c["k"], c["wdtype"], out_bf16=False)
+    print("decode nvfp4 T=%d: %s | fp32 out: %s" % (T, rep, rep32), flush=True)
