@@ -314,6 +314,165 @@ __global__ __launch_bounds__(256) void down_decode_kernel(ExpertParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 x bf16 fast path on the matrix cores.  The MFMA is only the dot-product
+// engine here (the kernels stay bound by weight bytes): a 16x16x32 step
+// consumes 16 weight rows x 32 k (1 KiB) against up to 16 tokens, with no
+// cross-lane reduction and no VALU conversion.  Weight fragments are loaded
+// straight from HBM in the MFMA layout (each row contributes 64 contiguous
+// bytes per load instruction) and stay in registers while every token tile of
+// the group streams past.  K is split over the 4 waves of a block; the partial
+// tiles are summed through LDS in a fixed order.
+// ---------------------------------------------------------------------------
+
+// gate/up: block = (group, 8 features): B columns 0..7 are gate rows j0..j0+7,
+// columns 8..15 the matching up rows.  NSTEP = k steps per wave = d / 128.
+template <int NSTEP>
+__global__ __launch_bounds__(256) void gateup_mfma_kernel(ExpertParams p) {
+    __shared__ float s_part[4][256];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = lane & 15, q = lane >> 4;
+    const int d = p.dm.d;
+    const int fblocks = p.hstride / 8;
+    const int gi = blockIdx.x / fblocks, fb = blockIdx.x % fblocks;
+    if (gi >= *p.ws.n_groups) return;
+    const int4 g = p.ws.groups[gi];
+    const bool is_shared = g.x == p.dm.E;
+    const int F = is_shared ? p.dm.fs : p.dm.f;
+    const int j0 = fb * 8;
+    if (j0 >= F) return;
+    const size_t e = is_shared ? 0 : (size_t)g.x;
+    const uint16_t* gu = static_cast<const uint16_t*>(is_shared ? p.shared.gu : p.routed.gu);
+    const size_t wr = e * 2 * F + (row < 8 ? (size_t)(j0 + row) : (size_t)(F + j0 + row - 8));
+    const int kbeg = wave * (d / 4);
+    const uint16_t* wrow = gu + wr * d + kbeg + 8 * q;
+    uint4 b[NSTEP];
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) b[s] = *reinterpret_cast<const uint4*>(wrow + 32 * s);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint16_t* x = static_cast<const uint16_t*>(p.x);
+    float* h = static_cast<float*>(p.ws.h);
+    for (int r0 = 0; r0 < g.z; r0 += 16) {
+        const int m = r0 + row;
+        const int tok = (m < g.z) ? (is_shared ? m : p.ws.sorted_pair[g.y + m] / p.dm.k) : -1;
+        const uint16_t* xr = x + (size_t)(tok < 0 ? 0 : tok) * d + kbeg + 8 * q;
+        floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+        // loads are unconditional (row 0 stands in for padding rows) so they
+        // issue back to back; padding rows are zeroed afterwards
+        uint4 a[NSTEP];
+#pragma unroll
+        for (int s = 0; s < NSTEP; ++s) a[s] = *reinterpret_cast<const uint4*>(xr + 32 * s);
+        __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the first MFMA
+        const uint32_t keep = tok >= 0 ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+        for (int s = 0; s < NSTEP; ++s) {
+            const uint4 av = make_uint4(a[s].x & keep, a[s].y & keep, a[s].z & keep, a[s].w & keep);
+            acc = mfma16x16x32(av, b[s], acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_part[wave][(4 * q + i) * 16 + row] = acc[i];
+        __syncthreads();
+        const int mm = tid >> 4, n = tid & 15;
+        if (n < 8 && r0 + mm < g.z) {
+            const int gi_ = mm * 16 + n, ui_ = gi_ + 8;
+            const float gv = ((s_part[0][gi_] + s_part[1][gi_]) + s_part[2][gi_]) + s_part[3][gi_];
+            const float uv = ((s_part[0][ui_] + s_part[1][ui_]) + s_part[2][ui_]) + s_part[3][ui_];
+            h[(size_t)(g.w + r0 + mm) * p.hstride + j0 + n] = silu_f32(gv) * uv;
+        }
+        __syncthreads();
+    }
+}
+
+// down: block = (group, NT tiles of 16 output rows); K = F split over the
+// waves, NSMAX >= F / 128 k steps per wave.  h is fp32; it enters the MFMA
+// as hi + lo bf16 parts (relative error about 2^-17), the weights exactly.
+template <int NSMAX, int NT>
+__global__ __launch_bounds__(256) void down_mfma_kernel(ExpertParams p) {
+    __shared__ float s_part[4][NT][256];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = lane & 15, q = lane >> 4;
+    const int d = p.dm.d;
+    const int rblocks = d / (16 * NT);
+    const int gi = blockIdx.x / rblocks, rb = blockIdx.x % rblocks;
+    if (gi >= *p.ws.n_groups) return;
+    const int4 g = p.ws.groups[gi];
+    const bool is_shared = g.x == p.dm.E;
+    const int F = is_shared ? p.dm.fs : p.dm.f;
+    const int nsteps = F / 128;
+    const int kbeg = wave * (F / 4);
+    const size_t e = is_shared ? 0 : (size_t)g.x;
+    const uint16_t* dn = static_cast<const uint16_t*>(is_shared ? p.shared.dn : p.routed.dn);
+    const int n0 = rb * 16 * NT;
+    uint4 b[NT][NSMAX];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const uint16_t* drow = dn + (e * d + (size_t)(n0 + 16 * t + row)) * F + kbeg + 8 * q;
+#pragma unroll
+        for (int s = 0; s < NSMAX; ++s)
+            b[t][s] = s < nsteps ? *reinterpret_cast<const uint4*>(drow + 32 * s)
+                                 : make_uint4(0, 0, 0, 0);
+    }
+    const float* h = static_cast<const float*>(p.ws.h);
+    float* y = static_cast<float*>(p.ws.y);
+    for (int r0 = 0; r0 < g.z; r0 += 16) {
+        const int m = r0 + row;
+        const bool ok = m < g.z;
+        const float* hr = h + (size_t)(g.w + (ok ? m : 0)) * p.hstride + kbeg + 8 * q;
+        floatx4_t acc[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        // unconditional loads (slot row of token 0 stands in for padding rows)
+        float4 hv0[NSMAX], hv1[NSMAX];
+#pragma unroll
+        for (int s = 0; s < NSMAX; ++s) {
+            if (s < nsteps) {
+                hv0[s] = *reinterpret_cast<const float4*>(hr + 32 * s);
+                hv1[s] = *reinterpret_cast<const float4*>(hr + 32 * s + 4);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the first MFMA
+        const float keep = ok ? 1.f : 0.f;
+#pragma unroll
+        for (int s = 0; s < NSMAX; ++s) {
+            if (s >= nsteps) break;
+            const float v[8] = {hv0[s].x * keep, hv0[s].y * keep, hv0[s].z * keep, hv0[s].w * keep,
+                                hv1[s].x * keep, hv1[s].y * keep, hv1[s].z * keep, hv1[s].w * keep};
+            uint4 ahi, alo;
+            split2_bf16(v, ahi, alo);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                acc[t] = mfma16x16x32(ahi, b[t][s], acc[t]);
+                acc[t] = mfma16x16x32(alo, b[t][s], acc[t]);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s_part[wave][t][(4 * q + i) * 16 + row] = acc[t][i];
+        __syncthreads();
+        const int mm = tid >> 4, n = tid & 15;
+        if (r0 + mm < g.z) {
+            const float ws = is_shared ? 1.f : p.ws.wts[p.ws.sorted_pair[g.y + r0 + mm]];
+            float* yr = y + (size_t)(g.w + r0 + mm) * d + n0 + n;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const float v = ((s_part[0][t][tid] + s_part[1][t][tid]) + s_part[2][t][tid]) +
+                                s_part[3][t][tid];
+                yr[16 * t] = ws * v;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+bool decode_mfma_ok(const Dims& dm) {
+    const int fmax = dm.f > dm.fs ? dm.f : dm.fs;
+    const int ns = dm.d / 128;
+    return dm.act == DT_BF16 && dm.wdt == DT_BF16 && dm.d % 128 == 0 &&
+           (ns == 1 || ns == 2 || ns == 4 || ns == 8 || ns == 16) && dm.f % 128 == 0 &&
+           dm.fs % 128 == 0 && fmax <= 1024 && dm.d % 32 == 0;
+}
+
 static int max_groups(const Dims& dm) {
     const int routed = dm.k * dm.T < dm.E ? dm.k * dm.T : dm.E;
     return routed + (dm.fs > 0 ? 1 : 0);
@@ -332,6 +491,17 @@ static ExpertParams make_params(const LayerArgs& a, const Workspace& w) {
 
 hipError_t launch_gateup_decode(const LayerArgs& a, const Workspace& w, hipStream_t s) {
     ExpertParams p = make_params(a, w);
+    if (decode_mfma_ok(a.dm)) {
+        dim3 grid(max_groups(a.dm) * (p.hstride / 8));
+        switch (a.dm.d / 128) {
+        case 1: hipLaunchKernelGGL(gateup_mfma_kernel<1>, grid, dim3(256), 0, s, p); break;
+        case 2: hipLaunchKernelGGL(gateup_mfma_kernel<2>, grid, dim3(256), 0, s, p); break;
+        case 4: hipLaunchKernelGGL(gateup_mfma_kernel<4>, grid, dim3(256), 0, s, p); break;
+        case 8: hipLaunchKernelGGL(gateup_mfma_kernel<8>, grid, dim3(256), 0, s, p); break;
+        default: hipLaunchKernelGGL(gateup_mfma_kernel<16>, grid, dim3(256), 0, s, p); break;
+        }
+        return hipGetLastError();
+    }
     const int fblocks = (p.hstride + kFPB - 1) / kFPB;
     dim3 grid(max_groups(a.dm) * fblocks);
     const bool f32 = a.dm.act == DT_F32;
@@ -354,6 +524,18 @@ hipError_t launch_gateup_decode(const LayerArgs& a, const Workspace& w, hipStrea
 
 hipError_t launch_down_decode(const LayerArgs& a, const Workspace& w, hipStream_t s) {
     ExpertParams p = make_params(a, w);
+    if (decode_mfma_ok(a.dm)) {
+        constexpr int NT = 2;
+        dim3 grid(max_groups(a.dm) * (a.dm.d / (16 * NT)));
+        switch ((p.hstride + 127) / 128) {
+        case 1: hipLaunchKernelGGL((down_mfma_kernel<1, NT>), grid, dim3(256), 0, s, p); break;
+        case 2: hipLaunchKernelGGL((down_mfma_kernel<2, NT>), grid, dim3(256), 0, s, p); break;
+        case 3:
+        case 4: hipLaunchKernelGGL((down_mfma_kernel<4, NT>), grid, dim3(256), 0, s, p); break;
+        default: hipLaunchKernelGGL((down_mfma_kernel<8, NT>), grid, dim3(256), 0, s, p); break;
+        }
+        return hipGetLastError();
+    }
     const int rblocks = (a.dm.d + kRPB - 1) / kRPB;
     dim3 grid(max_groups(a.dm) * rblocks);
     switch (a.dm.wdt) {

@@ -30,7 +30,7 @@ struct Workspace {
     int* n_groups;       // [1]
     int2* tiles;         // [max_tiles] prefill m-tiles {group, first row}
     int* n_tiles;        // [1]
-    int* counter;        // [1] last-block ticket, zero between launches
+    int* counter;        // [1 + ceil(Tm/16)] last-block tickets, zero between launches
     void* h;             // [(k+1)*Tm][fmax]: fp32 (decode) or bf16 (prefill)
     void* y;             // [(k+1)*Tm][d]:    fp32 (decode) or bf16 (prefill)
     int max_tiles;
@@ -62,6 +62,8 @@ struct LayerArgs {
 
 // Launchers (each enqueues exactly one kernel on `s`).
 hipError_t launch_route_decode(const LayerArgs& a, const Workspace& w, hipStream_t s);
+hipError_t launch_route_mfma(const LayerArgs& a, const Workspace& w, bool do_sort, hipStream_t s);
+bool route_mfma_ok(const Dims& dm);
 hipError_t launch_router_logits(const LayerArgs& a, const Workspace& w, hipStream_t s);
 hipError_t launch_topk(const LayerArgs& a, const Workspace& w, hipStream_t s);
 hipError_t launch_sort(const LayerArgs& a, const Workspace& w, int bm, hipStream_t s);
@@ -99,6 +101,93 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+
+// Cross-workgroup hand-off inside one kernel without full device fences.
+// Data that another workgroup reads later in the same kernel is written and
+// read with agent-scope relaxed atomics (device-coherent, so no L2 writeback
+// or invalidate is needed for it); the writer waits for its stores to
+// complete (vmcnt 0) before the workgroup barrier that precedes its ticket,
+// and the reader issues its loads only after its ticket has returned.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(int* p, int v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_agent(const int* p) {
+    return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
+
+// All threads: finish this workgroup's hand-off stores, then thread 0 takes a
+// ticket; returns true (in every thread) for the workgroup that arrives last.
+__device__ __forceinline__ bool last_arrival(int* counter, int n_arrivals, int* s_flag) {
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int t = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = t == n_arrivals - 1;
+        if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = last;
+    }
+    __syncthreads();
+    return *s_flag != 0;
+}
+
+// MFMA operand types (gfx950 v_mfma_f32_16x16x32_bf16).  Lane l of a wave
+// supplies A row (l & 15) and B column (l & 15), each with the 8 consecutive
+// k values 8*(l >> 4) .. +7 of a 32-wide k step; the 16x16 fp32 result puts
+// rows 4*(l >> 4) .. +3 of column (l & 15) in lane l.
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float floatx4_t;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ floatx4_t mfma16x16x32(uint4 a, uint4 b, floatx4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Exact split of 8 fp32 values into hi + mid + lo bf16 parts (hi = RNE(v),
+// mid = RNE(v - hi), lo = v - hi - mid, which fits bf16 exactly for normal
+// inputs): a bf16 x bf16 MFMA over the three parts reproduces an fp32 operand.
+__device__ __forceinline__ void split3_bf16(const float v[8], uint4& hi, uint4& mid, uint4& lo) {
+    uint32_t h[4], m[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float a = v[2 * i], b = v[2 * i + 1];
+        uint16_t ah = f32_to_bf16(a), bh = f32_to_bf16(b);
+        float ar = a - bf16_to_f32(ah), br = b - bf16_to_f32(bh);
+        uint16_t am = f32_to_bf16(ar), bm = f32_to_bf16(br);
+        float ar2 = ar - bf16_to_f32(am), br2 = br - bf16_to_f32(bm);
+        h[i] = (uint32_t)ah | ((uint32_t)bh << 16);
+        m[i] = (uint32_t)am | ((uint32_t)bm << 16);
+        l[i] = pack_bf16x2(ar2, br2);
+    }
+    hi = make_uint4(h[0], h[1], h[2], h[3]);
+    mid = make_uint4(m[0], m[1], m[2], m[3]);
+    lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+// Two-part split (hi + lo) of 8 fp32 values; relative error about 2^-17.
+__device__ __forceinline__ void split2_bf16(const float v[8], uint4& hi, uint4& lo) {
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float a = v[2 * i], b = v[2 * i + 1];
+        uint16_t ah = f32_to_bf16(a), bh = f32_to_bf16(b);
+        h[i] = (uint32_t)ah | ((uint32_t)bh << 16);
+        l[i] = pack_bf16x2(a - bf16_to_f32(ah), b - bf16_to_f32(bh));
+    }
+    hi = make_uint4(h[0], h[1], h[2], h[3]);
+    lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
 
 #endif
 

@@ -139,7 +139,7 @@ size_t carve(const flint_moe_config& c, char* base, Workspace* w) {
     w->n_groups = static_cast<int*>(take(4));
     w->tiles = static_cast<int2*>(take(max_tiles * 8));
     w->n_tiles = static_cast<int*>(take(4));
-    w->counter = static_cast<int*>(take(4));
+    w->counter = static_cast<int*>(take((1 + (Tm + 15) / 16) * 4));
     w->h = take(slots * fmax * 4);
     w->y = take(slots * (size_t)c.d_model * 4);
     w->max_tiles = (int)max_tiles;
@@ -314,7 +314,10 @@ flint_status flint_moe_forward(flint_moe_t h, int32_t T, const void* hidden, con
     hipError_t e;
     {
         Timer tm(h, FLINT_KERNEL_ROUTE, stream);
-        e = launch_route_decode(a, h->ws, stream);
+        if (route_mfma_ok(a.dm))
+            e = launch_route_mfma(a, h->ws, true, stream);
+        else
+            e = launch_route_decode(a, h->ws, stream);
     }
     if (e != hipSuccess) return hip_fail(e, "route kernel");
     {

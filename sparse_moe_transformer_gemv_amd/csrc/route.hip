@@ -65,7 +65,7 @@ __device__ void router_row_logits(const ActT* __restrict__ x, const float* __res
 #pragma unroll
         for (int tt = 0; tt < TG; ++tt) {
             float v = wave_sum(acc[tt]);
-            if (lane == 0 && t0 + tt < t_end) logits[(size_t)(t0 + tt) * E + e] = v + b;
+            if (lane == 0 && t0 + tt < t_end) st_agent(logits + (size_t)(t0 + tt) * E + e, v + b);
         }
     }
 }
@@ -91,8 +91,8 @@ __device__ void wave_topk_token(const float* __restrict__ lrow, int E, int k, in
     float lv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        int e = lane + 64 * i;
-        lv[i] = (e < E) ? lrow[e] : 0.f;
+        const int e = lane + 64 * i;
+        lv[i] = ld_agent(lrow + (e < E ? e : 0));  // unconditional; lanes past E never compete
     }
     unsigned taken = 0;
     float my_v = 0.f;
@@ -123,8 +123,8 @@ __device__ void wave_topk_token(const float* __restrict__ lrow, int E, int k, in
     float p = (lane < k) ? expf(my_v - l0) : 0.f;
     float s = wave_sum(p);
     if (lane < k) {
-        sel_out[lane] = my_e;
-        w_out[lane] = p / s;
+        st_agent(sel_out + lane, my_e);
+        st_agent(w_out + lane, p / s);
     }
 }
 
@@ -146,7 +146,7 @@ __device__ void block_sort_and_groups(const int* __restrict__ keys, int P, int E
     __syncthreads();
     const int S = (((P + NW - 1) / NW) + 63) & ~63;
     const int b0 = min(P, w * S), b1 = min(P, b0 + S);
-    for (int i = b0 + lane; i < b1; i += 64) atomicAdd(&s_hist[w * E + keys[i]], 1);
+    for (int i = b0 + lane; i < b1; i += 64) atomicAdd(&s_hist[w * E + ld_agent(keys + i)], 1);
     __syncthreads();
 
     // per-expert totals and their exclusive scan (wave 0; 4 experts per lane)
@@ -198,7 +198,7 @@ __device__ void block_sort_and_groups(const int* __restrict__ keys, int P, int E
     for (int c0 = b0; c0 < b1; c0 += 64) {
         const int i = c0 + lane;
         const bool valid = i < b1;
-        const int key = valid ? keys[i] : 0;
+        const int key = valid ? ld_agent(keys + i) : 0;
         unsigned long long m = __ballot(valid);
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
@@ -216,10 +216,20 @@ __device__ void block_sort_and_groups(const int* __restrict__ keys, int P, int E
     }
     __syncthreads();
 
-    // active groups (experts with tokens, ascending), then the shared group;
+    // active groups: the shared expert first (its work items are the longest,
+    // so they start first), then the experts with tokens in ascending order;
     // with bm > 0 also the prefill tile list, ceil(rows / bm) tiles per group
     if (w == 0) {
         int n = 0, ntile = 0;
+        if (has_shared) {
+            if (lane == 0) ws.groups[0] = make_int4(E, 0, T, k * T);
+            if (bm > 0) {
+                const int nt = (T + bm - 1) / bm;
+                for (int t = lane; t < nt; t += 64) ws.tiles[t] = make_int2(0, t * bm);
+                ntile = nt;
+            }
+            n = 1;
+        }
         for (int e0 = 0; e0 < E; e0 += 64) {
             const int e = e0 + lane;
             const int c = (e < E) ? s_off[e + 1] - s_off[e] : 0;
@@ -239,15 +249,6 @@ __device__ void block_sort_and_groups(const int* __restrict__ keys, int P, int E
                 ntile += __shfl(inc, 63, 64);
             }
             n += __popcll(act);
-        }
-        if (has_shared) {
-            if (lane == 0) ws.groups[n] = make_int4(E, 0, T, k * T);
-            if (bm > 0) {
-                const int nt = (T + bm - 1) / bm;
-                for (int t = lane; t < nt; t += 64) ws.tiles[ntile + t] = make_int2(n, t * bm);
-                ntile += nt;
-            }
-            n += 1;
         }
         if (lane == 0) {
             *ws.n_groups = n;
@@ -279,18 +280,12 @@ __global__ __launch_bounds__(256) void route_decode_kernel(RouteDecodeParams p) 
     if (e < p.E)
         router_row_logits<ActT>(static_cast<const ActT*>(p.x), p.wr + (size_t)e * p.d,
                                 p.bias ? p.bias[e] : 0.f, 0, p.T, p.d, p.E, e, p.ws.logits, lane);
-    // publish this block's logits, then take a ticket
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) s_last = (atomicAdd(p.ws.counter, 1) == (int)gridDim.x - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();  // acquire: every other block's logits are visible
-    if (threadIdx.x == 0) atomicExch(p.ws.counter, 0);
+    // the last block to finish runs top-k for every token, then the sort
+    if (!last_arrival(p.ws.counter, (int)gridDim.x, &s_last)) return;
     for (int t = wave; t < p.T; t += 4)
         wave_topk_token(p.ws.logits + (size_t)t * p.E, p.E, p.k, lane, p.ws.sel + (size_t)t * p.k,
                         p.ws.wts + (size_t)t * p.k);
-    __threadfence();
+    wait_stores();
     __syncthreads();
     block_sort_and_groups<256>(p.ws.sel, p.k * p.T, p.E, p.T, p.k, p.has_shared != 0, 0, p.ws,
                                s_hist, s_off);
@@ -303,6 +298,112 @@ hipError_t launch_route_decode(const LayerArgs& a, const Workspace& w, hipStream
         hipLaunchKernelGGL(route_decode_kernel<float>, grid, dim3(256), 0, s, p);
     else
         hipLaunchKernelGGL(route_decode_kernel<uint16_t>, grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Router on the matrix cores (bf16 activations): logits of a 16-token x
+// 16-expert tile, K split over the 4 waves and summed in a fixed order.  The
+// fp32 router rows are split exactly into three bf16 parts, so the bf16 MFMA
+// reproduces the fp32 products (x is bf16); accumulation is fp32.  The last
+// expert block of each token tile then selects the top-k of its 16 tokens, and
+// (decode path) the last token tile sorts all pairs.
+// Tickets: counter[0] for the sort, counter[1 + token tile] per tile.
+// ---------------------------------------------------------------------------
+struct RouteMfmaParams {
+    const uint16_t* x;
+    const float* wr;
+    const float* bias;
+    int T, d, E, k;
+    int has_shared;
+    int do_sort;
+    Workspace ws;
+};
+
+// 8 waves per block; wave w covers k in [w*d/8, (w+1)*d/8) in NSTEP steps of
+// 32, with every load of its range issued before the first MFMA.
+template <int NSTEP>
+__global__ __launch_bounds__(512) void route_mfma_kernel(RouteMfmaParams p) {
+    constexpr int NW = 8;
+    __shared__ float s_part[NW][256];
+    __shared__ int s_hist[NW * 256];
+    __shared__ int s_off[257];
+    __shared__ int s_flag;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = lane & 15, q = lane >> 4;
+    const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
+    const int kbeg = wave * (32 * NSTEP);
+    const int tok = t0 + row, ex = e0 + row;
+    const bool tok_ok = tok < p.T, ex_ok = ex < p.E;
+    const uint16_t* xr = p.x + (size_t)(tok_ok ? tok : 0) * p.d + kbeg + 8 * q;
+    const float* wrow = p.wr + (size_t)(ex_ok ? ex : 0) * p.d + kbeg + 8 * q;
+    // unconditional loads from clamped rows, so they issue back to back;
+    // rows past T or E are zeroed afterwards
+    uint4 a[NSTEP];
+    float4 w0[NSTEP], w1[NSTEP];
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+        a[s] = *reinterpret_cast<const uint4*>(xr + 32 * s);
+        w0[s] = *reinterpret_cast<const float4*>(wrow + 32 * s);
+        w1[s] = *reinterpret_cast<const float4*>(wrow + 32 * s + 4);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the first MFMA
+    const uint32_t keep_a = tok_ok ? 0xFFFFFFFFu : 0u;
+    const float keep_w = ex_ok ? 1.f : 0.f;
+    floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+        a[s] = make_uint4(a[s].x & keep_a, a[s].y & keep_a, a[s].z & keep_a, a[s].w & keep_a);
+        const float wv[8] = {w0[s].x * keep_w, w0[s].y * keep_w, w0[s].z * keep_w, w0[s].w * keep_w,
+                             w1[s].x * keep_w, w1[s].y * keep_w, w1[s].z * keep_w, w1[s].w * keep_w};
+        uint4 hi, mid, lo;
+        split3_bf16(wv, hi, mid, lo);
+        acc = mfma16x16x32(a[s], hi, acc);
+        acc = mfma16x16x32(a[s], mid, acc);
+        acc = mfma16x16x32(a[s], lo, acc);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_part[wave][(4 * q + i) * 16 + row] = acc[i];
+    __syncthreads();
+    if (tid < 256) {
+        const int m = tid >> 4, n = tid & 15;
+        float v = s_part[0][tid];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) v += s_part[w][tid];
+        if (t0 + m < p.T && e0 + n < p.E)
+            st_agent(p.ws.logits + (size_t)(t0 + m) * p.E + e0 + n,
+                     v + (p.bias ? p.bias[e0 + n] : 0.f));
+    }
+    // top-k of this token tile by the last of its expert blocks
+    if (!last_arrival(&p.ws.counter[1 + blockIdx.x], (int)gridDim.y, &s_flag)) return;
+    for (int m = wave; m < 16; m += NW) {
+        const int t = t0 + m;
+        if (t < p.T)
+            wave_topk_token(p.ws.logits + (size_t)t * p.E, p.E, p.k, lane,
+                            p.ws.sel + (size_t)t * p.k, p.ws.wts + (size_t)t * p.k);
+    }
+    if (!p.do_sort) return;
+    // counting sort of every pair by the last token tile
+    if (!last_arrival(&p.ws.counter[0], (int)gridDim.x, &s_flag)) return;
+    block_sort_and_groups<512>(p.ws.sel, p.k * p.T, p.E, p.T, p.k, p.has_shared != 0, 0, p.ws,
+                               s_hist, s_off);
+}
+
+bool route_mfma_ok(const Dims& dm) {
+    const int ns = dm.d / 256;
+    return dm.act == DT_BF16 && dm.d % 256 == 0 && (ns == 1 || ns == 2 || ns == 4 || ns == 8);
+}
+
+hipError_t launch_route_mfma(const LayerArgs& a, const Workspace& w, bool do_sort, hipStream_t s) {
+    RouteMfmaParams p{static_cast<const uint16_t*>(a.x), a.wr, a.bias, a.dm.T, a.dm.d, a.dm.E,
+                      a.dm.k, a.dm.fs > 0, do_sort ? 1 : 0, w};
+    dim3 grid((a.dm.T + 15) / 16, (a.dm.E + 15) / 16);
+    switch (a.dm.d / 256) {
+    case 1: hipLaunchKernelGGL(route_mfma_kernel<1>, grid, dim3(512), 0, s, p); break;
+    case 2: hipLaunchKernelGGL(route_mfma_kernel<2>, grid, dim3(512), 0, s, p); break;
+    case 4: hipLaunchKernelGGL(route_mfma_kernel<4>, grid, dim3(512), 0, s, p); break;
+    default: hipLaunchKernelGGL(route_mfma_kernel<8>, grid, dim3(512), 0, s, p); break;
+    }
     return hipGetLastError();
 }
 

@@ -45,6 +45,21 @@ def test_small_nvfp4_decode(T):
     _case(4, T, d=256, E=32, k=4, f=64, fs=64)
 
 
+@pytest.mark.parametrize("T", [1, 7, 40, 64])
+def test_small_bf16_matrix_core_path(T):
+    # d % 128 == 0 and f, fs % 128 == 0 select the MFMA router and expert kernels
+    _case(1, T, d=256, E=64, f=128, fs=256)
+
+
+def test_matrix_core_path_d128_k2():
+    _case(1, 33, d=128, E=32, k=2, f=128, fs=128)
+
+
+def test_zipf_bias_many_tokens_decode_path():
+    # skewed routing (one expert takes most tokens), forced onto the decode path
+    _case(2, 300, flags=FLINT_FORCE_DECODE_PATH, d=256, E=64, f=128, fs=128)
+
+
 def test_f32_activations_bf16_weights():
     _case(1, 9, d=192, E=48, f=32, fs=64, act=synth.F32)
 
