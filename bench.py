@@ -153,6 +153,7 @@ def main():
         kms = moe.profile_end()
         f, fs, d, k = c["f"], c["fs"], c["d"], c["k"]
         act_b = 4 if c["act"] == 0 else 2
+        up_flops = 2.0 * (k * T * f + T * fs) * d * 2
         # whole-layer algorithmic bytes: active expert weights + router + x + out
         layer_bytes = [(n * expert_bytes(c, f) + expert_bytes(c, fs)) + c["E"] * d * 4 +
                        2 * T * d * act_b for n in nd]
@@ -163,10 +164,12 @@ def main():
             ms=ms, tok_s=T / (ms * 1e-3),
             hbm_frac=float(np.mean(layer_bytes)) / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
             distinct=float(np.mean(nd)), layer_bytes=float(np.mean(layer_bytes)),
-            up_us=float(np.mean(kms)) * 1e3, up_bytes=float(np.mean(up_bytes)))
-        log("T=%d: %.1f us/step, %.0f tok/s, %.1f%% HBM (layer), dominant kernel %.1f us" % (
+            up_us=float(np.mean(kms)) * 1e3, up_bytes=float(np.mean(up_bytes)),
+            layer_flops=2.0 * (k * T * f + T * fs) * d * 3, up_flops=up_flops)
+        results[T]["mfma_frac"] = results[T]["layer_flops"] / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)
+        log("T=%d: %.1f us/step, %.0f tok/s, %.1f%% HBM / %.1f%% MFMA (layer), dominant %.1f us" % (
             T, ms * 1e3, results[T]["tok_s"], 100 * results[T]["hbm_frac"],
-            results[T]["up_us"]))
+            100 * results[T]["mfma_frac"], results[T]["up_us"]))
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -176,8 +179,8 @@ def main():
         log("copy calibration: 1 GiB device-to-device copy done")
 
     H = results[Tmax]
-    achieved = H["up_bytes"] / (H["up_us"] * 1e-6) / 1e9
-    kname = "gateup_decode_kernel"
+    prefill = args.workload == "prefill"
+    kname = "gateup_prefill_kernel" if prefill else "gateup_decode_kernel"
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "%s_%s_T%d_traffic.json" % (kname, args.workload, Tmax))
     if os.path.exists(tpath):
@@ -185,30 +188,40 @@ def main():
             tr = json.load(fh)
         if tr.get("source_sha") == file_sha(KERNEL_SRC[kname]):
             traffic = tr.get("bytes_per_launch")
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": kname, "bytes_per_launch": int(H["up_bytes"]),
-                "us_per_launch": round(H["up_us"], 2)}
+    if prefill:
+        achieved = H["up_flops"] / (H["up_us"] * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                    "traffic": traffic, "kernel": kname, "flops_per_launch": H["up_flops"],
+                    "us_per_launch": round(H["up_us"], 2)}
+    else:
+        achieved = H["up_bytes"] / (H["up_us"] * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "kernel": kname, "bytes_per_launch": int(H["up_bytes"]),
+                    "us_per_launch": round(H["up_us"], 2)}
 
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
         x0 = synth.hidden(cfg_id, Tmax, c["d"], c["act"], draw=0)
+        # bounded sample: batches of up to 64 tokens of the same workload
+        sample = x0[:64]
         ntok = 0
         t1 = time.time()
         while True:
-            oracle.moe_forward(x0, host0["router_w"], host0["experts"], host0["shared"],
+            oracle.moe_forward(sample, host0["router_w"], host0["experts"], host0["shared"],
                                top_k=c["k"], router_bias=host0["router_bias"],
                                wdtype=c["wdtype"])
-            ntok += Tmax
+            ntok += sample.shape[0]
             if time.time() - t1 >= args.cpu_seconds:
                 break
         dt = time.time() - t1
         cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
         cpu = {"value": round(ntok / dt, 2), "unit": "tokens/s", "cores": cores,
                "kind": "oracle",
-               "sample": "%d forwards of T=%d tokens, layer 0 of the same workload, fp64" % (
-                   ntok // Tmax, Tmax)}
+               "sample": "%d forwards of the first %d tokens of the same batch, layer 0, fp64" % (
+                   ntok // sample.shape[0], sample.shape[0])}
 
     line = {
         "metric": "MoE-layer tokens/s",
@@ -226,11 +239,12 @@ def main():
         "config": {"workload": "%s T=%d (d=%d, E=%d, top-%d + shared, f=%d)" % (
             c["name"], Tmax, c["d"], c["E"], c["k"], c["f"]), "tokens": Tmax,
             "layers_rotated": n_layers, "hbm_frac_layer": round(H["hbm_frac"], 4),
-            "distinct_experts": H["distinct"]},
+            "mfma_frac_layer": round(H["mfma_frac"], 4), "distinct_experts": H["distinct"]},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "t_sweep": {str(T): {"tok_s": round(r["tok_s"], 1), "us": round(r["ms"] * 1e3, 2),
                              "hbm_frac_layer": round(r["hbm_frac"], 4),
+                             "mfma_frac_layer": round(r["mfma_frac"], 4),
                              "dominant_us": round(r["up_us"], 2),
                              "distinct_experts": r["distinct"]} for T, r in results.items()},
     }

@@ -64,6 +64,7 @@ struct LayerArgs {
 hipError_t launch_route_decode(const LayerArgs& a, const Workspace& w, hipStream_t s);
 hipError_t launch_route_mfma(const LayerArgs& a, const Workspace& w, bool do_sort, hipStream_t s);
 bool route_mfma_ok(const Dims& dm);
+bool prefill_ok(const Dims& dm);
 hipError_t launch_router_logits(const LayerArgs& a, const Workspace& w, hipStream_t s);
 hipError_t launch_topk(const LayerArgs& a, const Workspace& w, hipStream_t s);
 hipError_t launch_sort(const LayerArgs& a, const Workspace& w, int bm, hipStream_t s);

@@ -305,13 +305,52 @@ flint_status flint_moe_forward(flint_moe_t h, int32_t T, const void* hidden, con
     a.residual = residual;
     a.out = out;
 
-    const bool mfma_ok = c.act_dtype == FLINT_BF16 && c.weight_dtype == FLINT_BF16;
+    const bool mfma_ok = prefill_ok(a.dm);
     bool prefill = false;
-    if (c.flags & FLINT_FORCE_PREFILL_PATH) prefill = true;
-    else if (!(c.flags & FLINT_FORCE_DECODE_PATH)) prefill = mfma_ok && T > h->decode_max_t;
-    if (prefill) return fail(FLINT_ERR_UNSUPPORTED, "grouped-MFMA path not built yet");
+    if (c.flags & FLINT_FORCE_PREFILL_PATH) {
+        if (!mfma_ok)
+            return fail(FLINT_ERR_UNSUPPORTED,
+                        "grouped-MFMA path needs d %% 256 == 0 and f, f_s %% 128 == 0");
+        prefill = true;
+    } else if (!(c.flags & FLINT_FORCE_DECODE_PATH)) {
+        prefill = mfma_ok && T > h->decode_max_t;
+    }
 
     hipError_t e;
+    if (prefill) {
+        {
+            Timer tm(h, FLINT_KERNEL_ROUTE, stream);
+            if (route_mfma_ok(a.dm)) {
+                e = launch_route_mfma(a, h->ws, false, stream);
+            } else {
+                e = launch_router_logits(a, h->ws, stream);
+                if (e == hipSuccess) e = launch_topk(a, h->ws, stream);
+            }
+        }
+        if (e != hipSuccess) return hip_fail(e, "route kernel");
+        {
+            Timer tm(h, FLINT_KERNEL_SORT, stream);
+            e = launch_sort(a, h->ws, kPrefillBM, stream);
+        }
+        if (e != hipSuccess) return hip_fail(e, "sort kernel");
+        {
+            Timer tm(h, FLINT_KERNEL_EXPERT_UP, stream);
+            e = launch_gateup_prefill(a, h->ws, stream);
+        }
+        if (e != hipSuccess) return hip_fail(e, "gate/up kernel");
+        {
+            Timer tm(h, FLINT_KERNEL_EXPERT_DOWN, stream);
+            e = launch_down_prefill(a, h->ws, stream);
+        }
+        if (e != hipSuccess) return hip_fail(e, "down kernel");
+        {
+            Timer tm(h, FLINT_KERNEL_COMBINE, stream);
+            e = launch_combine(a, h->ws, true, stream);
+        }
+        if (e != hipSuccess) return hip_fail(e, "combine kernel");
+        h->last_T = T;
+        return ok();
+    }
     {
         Timer tm(h, FLINT_KERNEL_ROUTE, stream);
         if (route_mfma_ok(a.dm))

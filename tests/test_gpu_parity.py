@@ -12,7 +12,8 @@ import oracle
 import synth
 from gpu_helpers import (check_permutation, compare, dev_array, dev_layer, make_layer_obj,
                          out_host, run_gpu, run_oracle, x_device)
-from sparse_moe_transformer_gemv_amd import FLINT_FORCE_DECODE_PATH, FlintError
+from sparse_moe_transformer_gemv_amd import (FLINT_FORCE_DECODE_PATH, FLINT_FORCE_PREFILL_PATH,
+                                             FlintError)
 
 pytestmark = pytest.mark.gpu
 
@@ -58,6 +59,20 @@ def test_matrix_core_path_d128_k2():
 def test_zipf_bias_many_tokens_decode_path():
     # skewed routing (one expert takes most tokens), forced onto the decode path
     _case(2, 300, flags=FLINT_FORCE_DECODE_PATH, d=256, E=64, f=128, fs=128)
+
+
+@pytest.mark.parametrize("T", [1, 37, 200])
+def test_small_prefill_path_forced(T):
+    _case(1, T, flags=FLINT_FORCE_PREFILL_PATH, d=256, E=64, f=128, fs=256)
+
+
+def test_prefill_path_zipf_default_choice():
+    # T above the decode threshold picks the grouped-MFMA path by itself
+    _case(2, 700, d=512, E=64, f=256, fs=128)
+
+
+def test_prefill_path_k8_odd_experts():
+    _case(2, 333, flags=FLINT_FORCE_PREFILL_PATH, d=256, E=100, k=8, f=128, fs=128)
 
 
 def test_f32_activations_bf16_weights():
@@ -205,3 +220,33 @@ def test_full_decode_nvfp4(fp4_layer, T):
     out32, rout32 = run_gpu(layer, D, x, residual=zero)
     rep32 = compare(out32, rout32, ref, c["k"], c["wdtype"], out_bf16=False)
     print("decode nvfp4 T=%d: %s | fp32 out: %s" % (T, rep, rep32), flush=True)
+
+
+@pytest.fixture(scope="module")
+def prefill_layer():
+    L = synth.layer(2)
+    return L, dev_layer(L)
+
+
+def test_full_prefill_zipf_sampled(prefill_layer):
+    L, D = prefill_layer
+    c = L["cfg"]
+    T = 4096
+    x = synth.hidden(2, T, c["d"], c["act"])
+    layer = make_layer_obj(c, T)
+    out, rout = run_gpu(layer, D, x)
+    check_permutation(rout, T, c["k"], c["E"])
+    counts = rout["counts"]
+    # sample tokens: spread over the batch, plus tokens of the largest and of
+    # the smallest non-empty expert groups (ragged tiles)
+    rng = np.random.default_rng(7)
+    pick = set(rng.choice(T, 40, replace=False).tolist())
+    big, small = int(np.argmax(counts)), int(np.argmin(np.where(counts > 0, counts, 1 << 30)))
+    for e in (big, small):
+        pick.update(np.where((rout["idx"] == e).any(1))[0][:4].tolist())
+    pick = np.array(sorted(pick))
+    ref = run_oracle(L, x[pick])
+    sub = {"idx": rout["idx"][pick], "weights": rout["weights"][pick]}
+    rep = compare(out[pick], sub, ref, c["k"], c["wdtype"], out_bf16=True)
+    print("prefill T=4096 sampled %d tokens: %s, groups used %d, largest %d" % (
+        len(pick), rep, int((counts > 0).sum()), int(counts.max())), flush=True)
