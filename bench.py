@@ -102,7 +102,7 @@ def main():
     cfg_id, Ts, n_layers = WORKLOADS[args.workload]
     c = dict(synth.CONFIGS[cfg_id])
     if args.workload == "stack":
-        raise SystemExit("stack workload: see bench_stack (not built yet)")
+        return bench_stack(args, c, cfg_id, Ts[0], n_layers)
     Tmax = max(Ts)
 
     t0 = time.time()
@@ -247,6 +247,116 @@ def main():
                              "mfma_frac_layer": round(r["mfma_frac"], 4),
                              "dominant_us": round(r["up_us"], 2),
                              "distinct_experts": r["distinct"]} for T, r in results.items()},
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_stack(args, c, cfg_id, T, n_layers):
+    """47 resident layers, T tokens: h <- h + MoE_l(bf16(RMSNorm(h))) per layer.
+    One step = the whole pass (rmsnorm + layer for every layer), captured once
+    as a HIP graph and replayed."""
+    import numpy as np
+    import torch
+
+    import synth
+    from gpu_helpers import dev_array, dev_layer, make_layer_obj, stack_gpu
+    import sparse_moe_transformer_gemv_amd as fm
+
+    t0 = time.time()
+    layers, nd = [], []
+    host0 = None
+    for l in range(n_layers):
+        L = synth.layer(cfg_id, l)
+        layers.append(dev_layer(L))
+        if l == 0:
+            host0 = L
+        del L
+    log("generated %d layer(s) in %.1fs" % (n_layers, time.time() - t0))
+    h0 = dev_array(synth.hidden(cfg_id, T, c["d"], synth.F32))
+    h = h0.clone()
+    moe = make_layer_obj(c, T)
+    # distinct experts per layer for this batch (eager pass with routing read-back)
+    h.copy_(h0)
+    from sparse_moe_transformer_gemv_amd import flint_rmsnorm_forward
+    x = torch.empty((T, c["d"]), dtype=torch.bfloat16, device="cuda")
+    for D in layers:
+        flint_rmsnorm_forward(h, 1e-6, out=x)
+        moe.forward(x, D["router_w"], D["experts"], D["shared"], None, residual=h, out=h)
+        nd.append(int((moe.routing()["counts"] > 0).sum().item()))
+    # dominant kernel timing: one eager pass with the event hook
+    h.copy_(h0)
+    torch.cuda.synchronize()
+    moe.profile_begin(fm.KERNEL_EXPERT_UP, n_layers)
+    stack_gpu(moe, h, layers)
+    torch.cuda.synchronize()
+    kms = moe.profile_end()
+    # graph of one full pass
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            h.copy_(h0)
+            stack_gpu(moe, h, layers)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        h.copy_(h0)
+        stack_gpu(moe, h, layers)
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    f, fs, d, k = c["f"], c["fs"], c["d"], c["k"]
+    pass_bytes = sum(n * expert_bytes(c, f) + expert_bytes(c, fs) + c["E"] * d * 4 +
+                     T * d * (2 + 4 + 4) for n in nd)
+    up_bytes = float(np.mean([n * expert_bytes(c, f, ("gate_up",)) +
+                              expert_bytes(c, fs, ("gate_up",)) + T * d * 2 +
+                              (k * T * f + T * fs) * 4 for n in nd]))
+    up_us = float(np.mean(kms)) * 1e3
+    achieved = up_bytes / (up_us * 1e-6) / 1e9
+    log("stack: %.3f ms/pass, %.0f tok/s, %.1f%% HBM, gate/up %.1f us" % (
+        ms, T / (ms * 1e-3), 100 * pass_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), up_us))
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        # one layer's forward on the same T tokens stands for 1/47 of a pass
+        xs = synth.hidden(cfg_id, T, d, c["act"], draw=0)
+        t1 = time.time()
+        n = 0
+        while True:
+            oracle.moe_forward(xs, host0["router_w"], host0["experts"], host0["shared"],
+                               top_k=k, wdtype=c["wdtype"])
+            n += 1
+            if time.time() - t1 >= args.cpu_seconds:
+                break
+        per_layer = (time.time() - t1) / n
+        cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+        cpu = {"value": round(T / (per_layer * n_layers), 3), "unit": "tokens/s", "cores": cores,
+               "kind": "oracle",
+               "sample": "%d single-layer forwards of T=%d (layer 0), scaled to %d layers" % (
+                   n, T, n_layers)}
+    line = {
+        "metric": "MoE-layer tokens/s", "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s: %d layers x (RMSNorm + MoE + residual), T=%d" % (
+            c["name"], n_layers, T), "tokens": T, "layers": n_layers,
+            "hbm_frac_pass": round(pass_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+            "pass_bytes": int(pass_bytes), "graph": True},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gateup_decode_kernel", "bytes_per_launch": int(up_bytes),
+                     "us_per_launch": round(up_us, 2)},
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

@@ -227,5 +227,6 @@ def stack_forward(h0, layers, *, top_k=6, eps=1e-6, wdtype=BF16):
         r = moe_forward(xb, L["router_w"], L["experts"], L["shared"], top_k=top_k,
                         router_bias=L.get("router_bias"), wdtype=wdtype)
         h = h + r["out"]
-        trace.append({"idx": r["idx"], "w": r["w"], "logits": r["logits"], "x": xb})
+        trace.append({"idx": r["idx"], "w": r["w"], "logits": r["logits"], "x": xb,
+                      "out_rms": float(np.sqrt(np.mean(r["out"] ** 2)))})
     return h, trace

@@ -385,7 +385,8 @@ __global__ __launch_bounds__(256) void gateup_mfma_kernel(ExpertParams p) {
 
 // down: block = (group, NT tiles of 16 output rows); K = F split over the
 // waves, NSMAX >= F / 128 k steps per wave.  h is fp32; it enters the MFMA
-// as hi + lo bf16 parts (relative error about 2^-17), the weights exactly.
+// exactly as three bf16 parts (hi + mid + lo), the weights exactly, so the
+// only rounding is the fp32 accumulation.
 template <int NSMAX, int NT>
 __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertParams p) {
     __shared__ float s_part[4][NT][256];
@@ -437,11 +438,12 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertParams p) {
             if (s >= nsteps) break;
             const float v[8] = {hv0[s].x * keep, hv0[s].y * keep, hv0[s].z * keep, hv0[s].w * keep,
                                 hv1[s].x * keep, hv1[s].y * keep, hv1[s].z * keep, hv1[s].w * keep};
-            uint4 ahi, alo;
-            split2_bf16(v, ahi, alo);
+            uint4 ahi, amid, alo;
+            split3_bf16(v, ahi, amid, alo);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 acc[t] = mfma16x16x32(ahi, b[t][s], acc[t]);
+                acc[t] = mfma16x16x32(amid, b[t][s], acc[t]);
                 acc[t] = mfma16x16x32(alo, b[t][s], acc[t]);
             }
         }
