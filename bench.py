@@ -34,9 +34,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+# logical dominant kernel (gate/up + SwiGLU of the chosen path) -> its source
 KERNEL_SRC = {
-    "gateup_decode_kernel": "sparse_moe_transformer_gemv_amd/csrc/expert_decode.hip",
-    "gateup_prefill_kernel": "sparse_moe_transformer_gemv_amd/csrc/expert_prefill.hip",
+    "gateup_decode": "sparse_moe_transformer_gemv_amd/csrc/expert_decode.hip",
+    "gateup_prefill": "sparse_moe_transformer_gemv_amd/csrc/expert_prefill.hip",
 }
 
 WORKLOADS = {
@@ -180,7 +181,7 @@ def main():
 
     H = results[Tmax]
     prefill = args.workload == "prefill"
-    kname = "gateup_prefill_kernel" if prefill else "gateup_decode_kernel"
+    kname = "gateup_prefill" if prefill else "gateup_decode"
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "%s_%s_T%d_traffic.json" % (kname, args.workload, Tmax))
     if os.path.exists(tpath):
@@ -354,7 +355,7 @@ def bench_stack(args, c, cfg_id, T, n_layers):
             "pass_bytes": int(pass_bytes), "graph": True},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "gateup_decode_kernel", "bytes_per_launch": int(up_bytes),
+                     "kernel": "gateup_decode", "bytes_per_launch": int(up_bytes),
                      "us_per_launch": round(up_us, 2)},
         "cpu_baseline": cpu,
     }
