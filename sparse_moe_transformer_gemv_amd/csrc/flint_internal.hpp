@@ -70,13 +70,13 @@ hipError_t launch_topk(const LayerArgs& a, const Workspace& w, hipStream_t s);
 hipError_t launch_sort(const LayerArgs& a, const Workspace& w, int bm, hipStream_t s);
 hipError_t launch_gateup_decode(const LayerArgs& a, const Workspace& w, hipStream_t s);
 hipError_t launch_down_decode(const LayerArgs& a, const Workspace& w, hipStream_t s);
-hipError_t launch_gateup_prefill(const LayerArgs& a, const Workspace& w, hipStream_t s);
-hipError_t launch_down_prefill(const LayerArgs& a, const Workspace& w, hipStream_t s);
+hipError_t launch_gateup_prefill(const LayerArgs& a, const Workspace& w, int n_cu, hipStream_t s);
+hipError_t launch_down_prefill(const LayerArgs& a, const Workspace& w, int n_cu, hipStream_t s);
 hipError_t launch_combine(const LayerArgs& a, const Workspace& w, bool y_bf16, hipStream_t s);
 hipError_t launch_rmsnorm(int T, int d, const float* in, float eps, void* out, hipStream_t s);
 
 // Prefill tile height (rows of A per MFMA tile); the sort builds its tile list with it.
-constexpr int kPrefillBM = 64;
+constexpr int kPrefillBM = 256;
 
 // ---------------------------------------------------------------------------
 // Device helpers

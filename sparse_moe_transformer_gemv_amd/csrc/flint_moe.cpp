@@ -26,6 +26,7 @@ struct flint_moe {
     Workspace ws;
     int last_T;
     int decode_max_t;
+    int n_cu;
     // measurement hook
     int prof_kernel;
     int prof_cap;
@@ -95,7 +96,7 @@ flint_status check_config(const flint_moe_config* c) {
     return FLINT_OK;
 }
 
-flint_status check_device(int* dev_out) {
+flint_status check_device(int* dev_out, int* n_cu) {
     int n = 0;
     hipError_t e = hipGetDeviceCount(&n);
     if (e != hipSuccess || n < 1) {
@@ -111,6 +112,7 @@ flint_status check_device(int* dev_out) {
         return fail(FLINT_ERR_NO_DEVICE, "device %d is %s; this library is built for gfx950", dev,
                     prop.gcnArchName);
     *dev_out = dev;
+    *n_cu = prop.multiProcessorCount;
     return FLINT_OK;
 }
 
@@ -210,13 +212,14 @@ flint_status flint_moe_create(const flint_moe_config* cfg, flint_moe_t* out) {
     *out = nullptr;
     flint_status st = check_config(cfg);
     if (st != FLINT_OK) return st;
-    int dev = 0;
-    st = check_device(&dev);
+    int dev = 0, n_cu = 0;
+    st = check_device(&dev, &n_cu);
     if (st != FLINT_OK) return st;
     flint_moe* h = new (std::nothrow) flint_moe();
     if (!h) return fail(FLINT_ERR_OUT_OF_MEMORY, "host allocation failed");
     h->cfg = *cfg;
     h->device = dev;
+    h->n_cu = n_cu;
     h->last_T = 0;
     h->prof_kernel = -1;
     h->prof_cap = 0;
@@ -335,12 +338,12 @@ flint_status flint_moe_forward(flint_moe_t h, int32_t T, const void* hidden, con
         if (e != hipSuccess) return hip_fail(e, "sort kernel");
         {
             Timer tm(h, FLINT_KERNEL_EXPERT_UP, stream);
-            e = launch_gateup_prefill(a, h->ws, stream);
+            e = launch_gateup_prefill(a, h->ws, h->n_cu, stream);
         }
         if (e != hipSuccess) return hip_fail(e, "gate/up kernel");
         {
             Timer tm(h, FLINT_KERNEL_EXPERT_DOWN, stream);
-            e = launch_down_prefill(a, h->ws, stream);
+            e = launch_down_prefill(a, h->ws, h->n_cu, stream);
         }
         if (e != hipSuccess) return hip_fail(e, "down kernel");
         {
