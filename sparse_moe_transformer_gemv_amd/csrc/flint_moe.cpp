@@ -323,12 +323,11 @@ flint_status flint_moe_forward(flint_moe_t h, int32_t T, const void* hidden, con
     if (prefill) {
         {
             Timer tm(h, FLINT_KERNEL_ROUTE, stream);
-            if (route_mfma_ok(a.dm)) {
-                e = launch_route_mfma(a, h->ws, false, stream);
-            } else {
-                e = launch_router_logits(a, h->ws, stream);
-                if (e == hipSuccess) e = launch_topk(a, h->ws, stream);
-            }
+            // logits (matrix cores when the shape allows), then top-k with one
+            // wavefront per token
+            e = route_mfma_ok(a.dm) ? launch_route_mfma(a, h->ws, false, stream)
+                                    : launch_router_logits(a, h->ws, stream);
+            if (e == hipSuccess) e = launch_topk(a, h->ws, stream);
         }
         if (e != hipSuccess) return hip_fail(e, "route kernel");
         {

@@ -85,6 +85,7 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
     }
 }
 
+template <bool COHERENT = true>
 __device__ void wave_topk_token(const float* __restrict__ lrow, int E, int k, int lane,
                                 int* __restrict__ sel_out, float* __restrict__ w_out) {
     constexpr int NONE = 0x7FFFFFFF;
@@ -92,7 +93,8 @@ __device__ void wave_topk_token(const float* __restrict__ lrow, int E, int k, in
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e = lane + 64 * i;
-        lv[i] = ld_agent(lrow + (e < E ? e : 0));  // unconditional; lanes past E never compete
+        const int ec = e < E ? e : 0;  // unconditional; lanes past E never compete
+        lv[i] = COHERENT ? ld_agent(lrow + ec) : lrow[ec];
     }
     unsigned taken = 0;
     float my_v = 0.f;
@@ -134,10 +136,13 @@ __device__ void wave_topk_token(const float* __restrict__ lrow, int E, int k, in
 // group list and (if bm > 0) the prefill tile list.
 // s_hist: LDS [NW*E]; s_off: LDS [E+1].
 // ---------------------------------------------------------------------------
-template <int NT>
+template <int NT, bool COHERENT = true>
 __device__ void block_sort_and_groups(const int* __restrict__ keys, int P, int E, int T, int k,
                                       bool has_shared, int bm, const Workspace& ws, int* s_hist,
                                       int* s_off) {
+    // keys written earlier in the same kernel by other workgroups need
+    // device-coherent loads; keys from an earlier kernel are read plainly
+    auto key_at = [&](int i) { return COHERENT ? ld_agent(keys + i) : keys[i]; };
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const unsigned long long lt = (1ull << lane) - 1ull;
@@ -146,7 +151,19 @@ __device__ void block_sort_and_groups(const int* __restrict__ keys, int P, int E
     __syncthreads();
     const int S = (((P + NW - 1) / NW) + 63) & ~63;
     const int b0 = min(P, w * S), b1 = min(P, b0 + S);
-    for (int i = b0 + lane; i < b1; i += 64) atomicAdd(&s_hist[w * E + ld_agent(keys + i)], 1);
+    // keys are read KU chunks of 64 at a time so that their loads overlap
+    constexpr int KU = 8;
+    for (int c0 = b0; c0 < b1; c0 += 64 * KU) {
+        int kv[KU];
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+            const int i = c0 + 64 * u + lane;
+            kv[u] = i < b1 ? key_at(i) : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < KU; ++u)
+            if (kv[u] >= 0) atomicAdd(&s_hist[w * E + kv[u]], 1);
+    }
     __syncthreads();
 
     // per-expert totals and their exclusive scan (wave 0; 4 experts per lane)
@@ -195,24 +212,34 @@ __device__ void block_sort_and_groups(const int* __restrict__ keys, int P, int E
     }
     __syncthreads();
     // ordered scatter: rank inside each 64-pair chunk by ballot matching
-    for (int c0 = b0; c0 < b1; c0 += 64) {
-        const int i = c0 + lane;
-        const bool valid = i < b1;
-        const int key = valid ? ld_agent(keys + i) : 0;
-        unsigned long long m = __ballot(valid);
+    for (int c0 = b0; c0 < b1; c0 += 64 * KU) {
+        int kv[KU];
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            const bool bit = (key >> b) & 1;
-            const unsigned long long bb = __ballot(valid && bit);
-            m &= bit ? bb : ~bb;
+        for (int u = 0; u < KU; ++u) {
+            const int i = c0 + 64 * u + lane;
+            kv[u] = i < b1 ? key_at(i) : -1;
         }
-        if (valid) {
-            const int pos = s_hist[w * E + key] + __popcll(m & lt);
-            ws.sorted_pair[pos] = i;
-            ws.pair_pos[i] = pos;
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+            if (c0 + 64 * u >= b1) break;  // uniform
+            const int i = c0 + 64 * u + lane;
+            const bool valid = kv[u] >= 0;
+            const int key = valid ? kv[u] : 0;
+            unsigned long long m = __ballot(valid);
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                const bool bit = (key >> b) & 1;
+                const unsigned long long bb = __ballot(valid && bit);
+                m &= bit ? bb : ~bb;
+            }
+            if (valid) {
+                const int pos = s_hist[w * E + key] + __popcll(m & lt);
+                ws.sorted_pair[pos] = i;
+                ws.pair_pos[i] = pos;
+            }
+            // the highest lane of each key group advances that key's base
+            if (valid && (m >> lane) == 1ull) s_hist[w * E + key] += __popcll(m);
         }
-        // the highest lane of each key group advances that key's base
-        if (valid && (m >> lane) == 1ull) s_hist[w * E + key] += __popcll(m);
     }
     __syncthreads();
 
@@ -316,73 +343,93 @@ struct RouteMfmaParams {
     const float* bias;
     int T, d, E, k;
     int has_shared;
-    int do_sort;
+    int do_sort;  // 0: logits only (prefill: top-k and sort run as their own kernels)
     Workspace ws;
 };
 
 // 8 waves per block; wave w covers k in [w*d/8, (w+1)*d/8) in NSTEP steps of
-// 32, with every load of its range issued before the first MFMA.
-template <int NSTEP>
+// 32, with every load of its range issued before the first MFMA.  A block
+// covers TT 16-token row tiles (the router rows are loaded once for all of
+// them) and one 16-expert column tile.
+template <int NSTEP, int TT>
 __global__ __launch_bounds__(512) void route_mfma_kernel(RouteMfmaParams p) {
     constexpr int NW = 8;
-    __shared__ float s_part[NW][256];
+    constexpr int TOK = 16 * TT;
+    __shared__ float s_part[NW][TT * 256];
     __shared__ int s_hist[NW * 256];
     __shared__ int s_off[257];
     __shared__ int s_flag;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, q = lane >> 4;
-    const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
+    const int t0 = blockIdx.x * TOK, e0 = blockIdx.y * 16;
     const int kbeg = wave * (32 * NSTEP);
-    const int tok = t0 + row, ex = e0 + row;
-    const bool tok_ok = tok < p.T, ex_ok = ex < p.E;
-    const uint16_t* xr = p.x + (size_t)(tok_ok ? tok : 0) * p.d + kbeg + 8 * q;
+    const int ex = e0 + row;
+    const bool ex_ok = ex < p.E;
     const float* wrow = p.wr + (size_t)(ex_ok ? ex : 0) * p.d + kbeg + 8 * q;
     // unconditional loads from clamped rows, so they issue back to back;
     // rows past T or E are zeroed afterwards
-    uint4 a[NSTEP];
+    uint4 a[TT][NSTEP];
     float4 w0[NSTEP], w1[NSTEP];
 #pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+        const int tok = t0 + 16 * tt + row;
+        const uint16_t* xr = p.x + (size_t)(tok < p.T ? tok : 0) * p.d + kbeg + 8 * q;
+#pragma unroll
+        for (int s = 0; s < NSTEP; ++s) a[tt][s] = *reinterpret_cast<const uint4*>(xr + 32 * s);
+    }
+#pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
-        a[s] = *reinterpret_cast<const uint4*>(xr + 32 * s);
         w0[s] = *reinterpret_cast<const float4*>(wrow + 32 * s);
         w1[s] = *reinterpret_cast<const float4*>(wrow + 32 * s + 4);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the first MFMA
-    const uint32_t keep_a = tok_ok ? 0xFFFFFFFFu : 0u;
     const float keep_w = ex_ok ? 1.f : 0.f;
-    floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+    floatx4_t acc[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+        const uint32_t keep_a = (t0 + 16 * tt + row < p.T) ? 0xFFFFFFFFu : 0u;
+        acc[tt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NSTEP; ++s)
+            a[tt][s] = make_uint4(a[tt][s].x & keep_a, a[tt][s].y & keep_a, a[tt][s].z & keep_a,
+                                  a[tt][s].w & keep_a);
+    }
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
-        a[s] = make_uint4(a[s].x & keep_a, a[s].y & keep_a, a[s].z & keep_a, a[s].w & keep_a);
         const float wv[8] = {w0[s].x * keep_w, w0[s].y * keep_w, w0[s].z * keep_w, w0[s].w * keep_w,
                              w1[s].x * keep_w, w1[s].y * keep_w, w1[s].z * keep_w, w1[s].w * keep_w};
         uint4 hi, mid, lo;
         split3_bf16(wv, hi, mid, lo);
-        acc = mfma16x16x32(a[s], hi, acc);
-        acc = mfma16x16x32(a[s], mid, acc);
-        acc = mfma16x16x32(a[s], lo, acc);
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+            acc[tt] = mfma16x16x32(a[tt][s], hi, acc[tt]);
+            acc[tt] = mfma16x16x32(a[tt][s], mid, acc[tt]);
+            acc[tt] = mfma16x16x32(a[tt][s], lo, acc[tt]);
+        }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s_part[wave][(4 * q + i) * 16 + row] = acc[i];
-    __syncthreads();
-    if (tid < 256) {
-        const int m = tid >> 4, n = tid & 15;
-        float v = s_part[0][tid];
+    for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-        for (int w = 1; w < NW; ++w) v += s_part[w][tid];
+        for (int i = 0; i < 4; ++i) s_part[wave][tt * 256 + (4 * q + i) * 16 + row] = acc[tt][i];
+    __syncthreads();
+    for (int idx = tid; idx < TT * 256; idx += 512) {
+        const int m = idx >> 4, n = idx & 15;  // token m of the block, expert n
+        float v = s_part[0][idx];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) v += s_part[w][idx];
         if (t0 + m < p.T && e0 + n < p.E)
             st_agent(p.ws.logits + (size_t)(t0 + m) * p.E + e0 + n,
                      v + (p.bias ? p.bias[e0 + n] : 0.f));
     }
+    if (!p.do_sort) return;
     // top-k of this token tile by the last of its expert blocks
     if (!last_arrival(&p.ws.counter[1 + blockIdx.x], (int)gridDim.y, &s_flag)) return;
-    for (int m = wave; m < 16; m += NW) {
+    for (int m = wave; m < TOK; m += NW) {
         const int t = t0 + m;
         if (t < p.T)
             wave_topk_token(p.ws.logits + (size_t)t * p.E, p.E, p.k, lane,
                             p.ws.sel + (size_t)t * p.k, p.ws.wts + (size_t)t * p.k);
     }
-    if (!p.do_sort) return;
     // counting sort of every pair by the last token tile
     if (!last_arrival(&p.ws.counter[0], (int)gridDim.x, &s_flag)) return;
     block_sort_and_groups<512>(p.ws.sel, p.k * p.T, p.E, p.T, p.k, p.has_shared != 0, 0, p.ws,
@@ -397,13 +444,19 @@ bool route_mfma_ok(const Dims& dm) {
 hipError_t launch_route_mfma(const LayerArgs& a, const Workspace& w, bool do_sort, hipStream_t s) {
     RouteMfmaParams p{static_cast<const uint16_t*>(a.x), a.wr, a.bias, a.dm.T, a.dm.d, a.dm.E,
                       a.dm.k, a.dm.fs > 0, do_sort ? 1 : 0, w};
-    dim3 grid((a.dm.T + 15) / 16, (a.dm.E + 15) / 16);
+    const bool wide = a.dm.T > 64;  // prefill-sized: 64-token blocks share router loads
+    const int tok = wide ? 64 : 16;
+    dim3 grid((a.dm.T + tok - 1) / tok, (a.dm.E + 15) / 16);
+#define FLINT_ROUTE_LAUNCH(NS)                                                                \
+    if (wide) hipLaunchKernelGGL((route_mfma_kernel<NS, 4>), grid, dim3(512), 0, s, p);        \
+    else hipLaunchKernelGGL((route_mfma_kernel<NS, 1>), grid, dim3(512), 0, s, p);
     switch (a.dm.d / 256) {
-    case 1: hipLaunchKernelGGL(route_mfma_kernel<1>, grid, dim3(512), 0, s, p); break;
-    case 2: hipLaunchKernelGGL(route_mfma_kernel<2>, grid, dim3(512), 0, s, p); break;
-    case 4: hipLaunchKernelGGL(route_mfma_kernel<4>, grid, dim3(512), 0, s, p); break;
-    default: hipLaunchKernelGGL(route_mfma_kernel<8>, grid, dim3(512), 0, s, p); break;
+    case 1: FLINT_ROUTE_LAUNCH(1) break;
+    case 2: FLINT_ROUTE_LAUNCH(2) break;
+    case 4: FLINT_ROUTE_LAUNCH(4) break;
+    default: FLINT_ROUTE_LAUNCH(8) break;
     }
+#undef FLINT_ROUTE_LAUNCH
     return hipGetLastError();
 }
 
@@ -438,8 +491,8 @@ __global__ __launch_bounds__(256) void topk_kernel(RouteDecodeParams p) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t < p.T)
-        wave_topk_token(p.ws.logits + (size_t)t * p.E, p.E, p.k, lane, p.ws.sel + (size_t)t * p.k,
-                        p.ws.wts + (size_t)t * p.k);
+        wave_topk_token<false>(p.ws.logits + (size_t)t * p.E, p.E, p.k, lane,
+                               p.ws.sel + (size_t)t * p.k, p.ws.wts + (size_t)t * p.k);
 }
 
 hipError_t launch_topk(const LayerArgs& a, const Workspace& w, hipStream_t s) {
@@ -456,8 +509,8 @@ struct SortParams {
 __global__ __launch_bounds__(1024) void sort_kernel(SortParams p) {
     __shared__ int s_hist[16 * 256];
     __shared__ int s_off[257];
-    block_sort_and_groups<1024>(p.ws.sel, p.k * p.T, p.E, p.T, p.k, p.has_shared != 0, p.bm, p.ws,
-                                s_hist, s_off);
+    block_sort_and_groups<1024, false>(p.ws.sel, p.k * p.T, p.E, p.T, p.k, p.has_shared != 0,
+                                       p.bm, p.ws, s_hist, s_off);
 }
 
 hipError_t launch_sort(const LayerArgs& a, const Workspace& w, int bm, hipStream_t s) {
