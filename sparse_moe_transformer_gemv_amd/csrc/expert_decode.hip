@@ -270,7 +270,7 @@ __global__ __launch_bounds__(256) void down_decode_kernel(ExpertParams p) {
         for (int tt = 0; tt < kTG; ++tt) {
             const int r = r0 + tt;
             slot[tt] = (r < g.z) ? g.w + r : -1;
-            wslot[tt] = (r < g.z && !is_shared) ? p.ws.wts[p.ws.sorted_pair[g.y + r]] : 1.f;
+            wslot[tt] = (r < g.z && !is_shared) ? p.ws.sorted_wt[g.y + r] : 1.f;
         }
         float acc[kTG][kRPW];
 #pragma unroll
@@ -454,7 +454,7 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertParams p) {
         __syncthreads();
         const int mm = tid >> 4, n = tid & 15;
         if (r0 + mm < g.z) {
-            const float ws = is_shared ? 1.f : p.ws.wts[p.ws.sorted_pair[g.y + r0 + mm]];
+            const float ws = is_shared ? 1.f : p.ws.sorted_wt[g.y + r0 + mm];
             float* yr = y + (size_t)(g.w + r0 + mm) * d + n0 + n;
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
@@ -465,6 +465,286 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertParams p) {
         }
         __syncthreads();
     }
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 on the matrix cores.  Each lane loads 16 bytes of codes (32 elements)
+// of its weight row for a group of four 32-wide MFMA k steps, plus the two
+// E4M3 scales of those elements.  The k order inside a group is permuted the
+// same way for activations and weights (lane quarter q holds elements
+// 32 q .. 32 q + 31 of the group, 8 per step), which leaves every dot product
+// unchanged.  A weight is E2M1 x E4M3 (at most 6 significant bits, so exact
+// in bf16): the hardware converts a pair of codes to fp32, the block scale is
+// applied in fp32, and the pair is packed back to bf16 without rounding.  The
+// tensor scale multiplies the finished sums.
+// ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(2))) float floatx2_t;
+
+// Upper halves of two fp32 values as a bf16 pair: exact when both values are
+// representable in bf16, as every E2M1 x E4M3 product is.
+__device__ __forceinline__ uint32_t hi16_pair(float lo, float hi) {
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// Two codes of byte B of w, decoded and multiplied by the block scale, as bf16.
+#define FLINT_FP4_PAIR(w, B, sc)                                                   \
+    ({                                                                              \
+        const floatx2_t v_ = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((w), 1.0f, B); \
+        hi16_pair(v_.x * (sc), v_.y * (sc));                                        \
+    })
+
+// Eight E2M1 codes (one 32-bit word, even element in the low nibble) times
+// their block scale, as one MFMA operand of 8 bf16.
+__device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t w, float sc) {
+    return make_uint4(FLINT_FP4_PAIR(w, 0, sc), FLINT_FP4_PAIR(w, 1, sc), FLINT_FP4_PAIR(w, 2, sc),
+                      FLINT_FP4_PAIR(w, 3, sc));
+}
+#undef FLINT_FP4_PAIR
+
+// Raw buffer view of [base, base + bytes): a load whose offset lies at or past
+// the end returns zeros without touching memory, which is how the kernels
+// below skip the rows of a 16-row tile that hold no token.
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+constexpr uint32_t kOffNone = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t u4_word(const uint4& v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// One 16-token tile of an NVFP4 gate/up block (see gateup_fp4_kernel).  sp is
+// the sorted pair of this lane's token row.
+template <int NG>
+__device__ __forceinline__ void gateup_fp4_tile(const ExpertParams& p, const int4& g, bool is_shared, int r0,
+                                                int sp, __amdgpu_buffer_rsrc_t xv, int kl, uint4 (&cw)[2][NG],
+                                                uint16_t (&sw)[2][NG], float tsg, float tsu, int j0,
+                                                float (&s_part)[4][2][256]) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = lane & 15, q = lane >> 4;
+    const int d = p.dm.d;
+    const int m = r0 + row;
+    const int tok = is_shared ? m : sp / p.dm.k;
+    const uint32_t xo = m < g.z ? (uint32_t)(tok * d + kl) * 2 : kOffNone;
+    uint4 a[NG][4];
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg)
+#pragma unroll
+        for (int st = 0; st < 4; ++st) a[gg][st] = buffer_load16(xv, xo + (128 * gg + 8 * st) * 2);
+    __builtin_amdgcn_sched_barrier(0);
+    // Decode the weights here, after the activation loads are issued: an empty
+    // asm that claims to change the codes keeps the decode from being hoisted
+    // ahead of those loads or out of the token loop (where its bf16 operands
+    // would cost 32 NG more registers per lane than the packed codes).
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg)
+            asm volatile("" : "+v"(cw[t][gg].x), "+v"(cw[t][gg].y), "+v"(cw[t][gg].z), "+v"(cw[t][gg].w),
+                         "+v"(sw[t][gg]));
+    floatx4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) {
+        const float g0 = __builtin_amdgcn_cvt_f32_fp8(sw[0][gg], 0), g1 = __builtin_amdgcn_cvt_f32_fp8(sw[0][gg], 1);
+        const float u0 = __builtin_amdgcn_cvt_f32_fp8(sw[1][gg], 0), u1 = __builtin_amdgcn_cvt_f32_fp8(sw[1][gg], 1);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            acc0 = mfma16x16x32(a[gg][st], fp4x8_to_bf16(u4_word(cw[0][gg], st), st < 2 ? g0 : g1), acc0);
+            acc1 = mfma16x16x32(a[gg][st], fp4x8_to_bf16(u4_word(cw[1][gg], st), st < 2 ? u0 : u1), acc1);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        s_part[wave][0][(4 * q + i) * 16 + row] = acc0[i];
+        s_part[wave][1][(4 * q + i) * 16 + row] = acc1[i];
+    }
+    __syncthreads();
+    const int mm = tid >> 4, n = tid & 15;
+    if (r0 + mm < g.z) {
+        const float gv = tsg * (((s_part[0][0][tid] + s_part[1][0][tid]) + s_part[2][0][tid]) + s_part[3][0][tid]);
+        const float uv = tsu * (((s_part[0][1][tid] + s_part[1][1][tid]) + s_part[2][1][tid]) + s_part[3][1][tid]);
+        static_cast<float*>(p.ws.h)[(size_t)(g.w + r0 + mm) * p.hstride + j0 + n] = silu_f32(gv) * uv;
+    }
+    __syncthreads();
+}
+
+// gate/up + SwiGLU, NVFP4 weights, bf16 activations.  Block = (group, 16
+// features): MFMA tile 0 holds their gate rows and tile 1 their up rows, so
+// the two results of one feature land in the same lane.  K is split over the
+// 4 waves, NG groups of 128 per wave (d = 512 NG).  The first token tile is
+// peeled off the loop so that the weights and its activations are all in
+// flight before the first wait.
+template <int NG>
+__global__ __launch_bounds__(256) void gateup_fp4_kernel(ExpertParams p) {
+    __shared__ float s_part[4][2][256];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = lane & 15, q = lane >> 4;
+    const int d = p.dm.d;
+    const int fblocks = p.hstride / 16;
+    const int gi = blockIdx.x / fblocks, fb = blockIdx.x % fblocks;
+    if (gi >= *p.ws.n_groups) return;
+    const int4 g = p.ws.groups[gi];
+    const bool is_shared = g.x == p.dm.E;
+    const int F = is_shared ? p.dm.fs : p.dm.f;
+    const int j0 = fb * 16;
+    if (j0 >= F) return;
+    const size_t e = is_shared ? 0 : (size_t)g.x;
+    const WeightPtrs& wp = is_shared ? p.shared : p.routed;
+    const int kl = wave * (d / 4) + 32 * q;  // this lane's first element in each group
+    // The token index is requested before the weights: vector loads retire in
+    // order, so the activation loads that need it wait for it alone.
+    const int sp = p.ws.sorted_pair[g.y + (row < g.z ? row : g.z - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 cw[2][NG];
+    uint16_t sw[2][NG];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const size_t wr = e * 2 * F + (size_t)t * F + j0 + row;
+        const uint8_t* crow = static_cast<const uint8_t*>(wp.gu) + wr * (d / 2) + kl / 2;
+        const uint8_t* srow = wp.gus + wr * (d / 16) + kl / 16;
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) {
+            cw[t][gg] = *reinterpret_cast<const uint4*>(crow + 64 * gg);
+            sw[t][gg] = *reinterpret_cast<const uint16_t*>(srow + 8 * gg);
+        }
+    }
+    const float tsg = wp.ts[e * 3 + 0], tsu = wp.ts[e * 3 + 1];
+    const __amdgpu_buffer_rsrc_t xv = buffer_view(p.x, (uint32_t)p.dm.T * d * 2);
+    gateup_fp4_tile<NG>(p, g, is_shared, 0, sp, xv, kl, cw, sw, tsg, tsu, j0, s_part);
+    for (int r0 = 16; r0 < g.z; r0 += 16) {
+        const int m = r0 + row;
+        const int spn = p.ws.sorted_pair[g.y + (m < g.z ? m : g.z - 1)];
+        gateup_fp4_tile<NG>(p, g, is_shared, r0, spn, xv, kl, cw, sw, tsg, tsu, j0, s_part);
+    }
+}
+
+// One 16-token tile of an NVFP4 down block (see down_fp4_kernel); rw is the
+// routing weight of the token row this thread stores.
+template <int NT, int NGMAX>
+__device__ __forceinline__ void down_fp4_tile(const ExpertParams& p, const int4& g, int r0, int ng, int kl, int n0,
+                                              __amdgpu_buffer_rsrc_t hv, uint4 (&cw)[NT][NGMAX],
+                                              uint16_t (&sw)[NT][NGMAX], float ws, float (&s_part)[4][NT][256]) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = lane & 15, q = lane >> 4;
+    const int m = r0 + row;
+    const uint32_t ho = m < g.z ? (uint32_t)(m * p.hstride + kl) * 4 : kOffNone;
+    floatx4_t acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int gg = 0; gg < NGMAX; ++gg) {
+        if (gg >= ng) break;
+        uint4 hr[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hr[i] = buffer_load16(hv, ho + (128 * gg + 4 * i) * 4);
+        __builtin_amdgcn_sched_barrier(0);
+        // decode after the h loads are issued, and inside the token loop
+        // (see gateup_fp4_tile)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            asm volatile("" : "+v"(cw[t][gg].x), "+v"(cw[t][gg].y), "+v"(cw[t][gg].z), "+v"(cw[t][gg].w),
+                         "+v"(sw[t][gg]));
+        float sc[NT][2];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            sc[t][0] = __builtin_amdgcn_cvt_f32_fp8(sw[t][gg], 0);
+            sc[t][1] = __builtin_amdgcn_cvt_f32_fp8(sw[t][gg], 1);
+        }
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const uint4 h0 = hr[2 * st], h1 = hr[2 * st + 1];
+            const float v[8] = {__uint_as_float(h0.x), __uint_as_float(h0.y), __uint_as_float(h0.z),
+                                __uint_as_float(h0.w), __uint_as_float(h1.x), __uint_as_float(h1.y),
+                                __uint_as_float(h1.z), __uint_as_float(h1.w)};
+            uint4 ahi, amid, alo;
+            split3_bf16(v, ahi, amid, alo);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const uint4 bw = fp4x8_to_bf16(u4_word(cw[t][gg], st), sc[t][st >> 1]);
+                acc[t] = mfma16x16x32(ahi, bw, acc[t]);
+                acc[t] = mfma16x16x32(amid, bw, acc[t]);
+                acc[t] = mfma16x16x32(alo, bw, acc[t]);
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_part[wave][t][(4 * q + i) * 16 + row] = acc[t][i];
+    __syncthreads();
+    const int mm = tid >> 4, n = tid & 15;
+    if (r0 + mm < g.z) {
+        float* yr = static_cast<float*>(p.ws.y) + (size_t)(g.w + r0 + mm) * p.dm.d + n0 + n;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const float v = ((s_part[0][t][tid] + s_part[1][t][tid]) + s_part[2][t][tid]) + s_part[3][t][tid];
+            yr[16 * t] = ws * v;
+        }
+    }
+    __syncthreads();
+}
+
+// down, NVFP4 weights: block = (group, 16 NT output rows), K = F split over
+// the 4 waves in groups of 128; h enters as three exact bf16 parts.  First
+// token tile peeled as in gateup_fp4_kernel.
+constexpr int kDownFp4Tiles = 4;  // 64 output rows per block
+
+template <int NT, int NGMAX>
+__global__ __launch_bounds__(256) void down_fp4_kernel(ExpertParams p) {
+    __shared__ float s_part[4][NT][256];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = lane & 15, q = lane >> 4;
+    const int d = p.dm.d;
+    const int rblocks = d / (16 * NT);
+    const int gi = blockIdx.x / rblocks, rb = blockIdx.x % rblocks;
+    if (gi >= *p.ws.n_groups) return;
+    const int4 g = p.ws.groups[gi];
+    const bool is_shared = g.x == p.dm.E;
+    const int F = is_shared ? p.dm.fs : p.dm.f;
+    const int ng = F / 512;
+    const int kl = wave * (F / 4) + 32 * q;
+    const size_t e = is_shared ? 0 : (size_t)g.x;
+    const WeightPtrs& wp = is_shared ? p.shared : p.routed;
+    const int n0 = rb * 16 * NT;
+    // routing weight of the row this thread stores in the first token tile
+    const int mm = tid >> 4;
+    const float rw_load = p.ws.sorted_wt[g.y + (mm < g.z ? mm : g.z - 1)];
+    uint4 cw[NT][NGMAX];
+    uint16_t sw[NT][NGMAX];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const size_t wr = e * (size_t)d + (size_t)(n0 + 16 * t + row);
+        const uint8_t* crow = static_cast<const uint8_t*>(wp.dn) + wr * (F / 2) + kl / 2;
+        const uint8_t* srow = wp.dns + wr * (F / 16) + kl / 16;
+#pragma unroll
+        for (int gg = 0; gg < NGMAX; ++gg) {
+            const int gc = gg < ng ? gg : 0;  // clamped: groups past ng are loaded but unused
+            cw[t][gg] = *reinterpret_cast<const uint4*>(crow + 64 * gc);
+            sw[t][gg] = *reinterpret_cast<const uint16_t*>(srow + 8 * gc);
+        }
+    }
+    const float tsd = wp.ts[e * 3 + 2];
+    const float rw0 = is_shared ? 1.f : rw_load;
+    const __amdgpu_buffer_rsrc_t hv =
+        buffer_view(static_cast<const float*>(p.ws.h) + (size_t)g.w * p.hstride, (uint32_t)g.z * p.hstride * 4);
+    down_fp4_tile<NT, NGMAX>(p, g, 0, ng, kl, n0, hv, cw, sw, tsd * rw0, s_part);
+    for (int r0 = 16; r0 < g.z; r0 += 16) {
+        const int m = r0 + mm;
+        const float rw = is_shared ? 1.f : p.ws.sorted_wt[g.y + (m < g.z ? m : g.z - 1)];
+        down_fp4_tile<NT, NGMAX>(p, g, r0, ng, kl, n0, hv, cw, sw, tsd * rw, s_part);
+    }
+}
+
+bool decode_fp4_ok(const Dims& dm) {
+    const int fmax = dm.f > dm.fs ? dm.f : dm.fs;
+    const int ng = dm.d / 512;
+    return dm.act == DT_BF16 && dm.wdt == DT_NVFP4 && dm.d % 512 == 0 &&
+           (ng == 1 || ng == 2 || ng == 4) && dm.f % 512 == 0 && dm.fs % 512 == 0 && fmax <= 2048 &&
+           (size_t)dm.T * dm.d * 2 < kOffNone && (size_t)dm.T * fmax * 4 < kOffNone;
 }
 
 bool decode_mfma_ok(const Dims& dm) {
@@ -493,6 +773,15 @@ static ExpertParams make_params(const LayerArgs& a, const Workspace& w) {
 
 hipError_t launch_gateup_decode(const LayerArgs& a, const Workspace& w, hipStream_t s) {
     ExpertParams p = make_params(a, w);
+    if (decode_fp4_ok(a.dm)) {
+        dim3 grid(max_groups(a.dm) * (p.hstride / 16));
+        switch (a.dm.d / 512) {
+        case 1: hipLaunchKernelGGL(gateup_fp4_kernel<1>, grid, dim3(256), 0, s, p); break;
+        case 2: hipLaunchKernelGGL(gateup_fp4_kernel<2>, grid, dim3(256), 0, s, p); break;
+        default: hipLaunchKernelGGL(gateup_fp4_kernel<4>, grid, dim3(256), 0, s, p); break;
+        }
+        return hipGetLastError();
+    }
     if (decode_mfma_ok(a.dm)) {
         dim3 grid(max_groups(a.dm) * (p.hstride / 8));
         switch (a.dm.d / 128) {
@@ -526,6 +815,17 @@ hipError_t launch_gateup_decode(const LayerArgs& a, const Workspace& w, hipStrea
 
 hipError_t launch_down_decode(const LayerArgs& a, const Workspace& w, hipStream_t s) {
     ExpertParams p = make_params(a, w);
+    if (decode_fp4_ok(a.dm)) {
+        constexpr int NT = kDownFp4Tiles;
+        if (a.dm.d % (16 * NT) != 0) return hipErrorInvalidValue;
+        dim3 grid(max_groups(a.dm) * (a.dm.d / (16 * NT)));
+        switch (p.hstride / 512) {
+        case 1: hipLaunchKernelGGL((down_fp4_kernel<NT, 1>), grid, dim3(256), 0, s, p); break;
+        case 2: hipLaunchKernelGGL((down_fp4_kernel<NT, 2>), grid, dim3(256), 0, s, p); break;
+        default: hipLaunchKernelGGL((down_fp4_kernel<NT, 4>), grid, dim3(256), 0, s, p); break;
+        }
+        return hipGetLastError();
+    }
     if (decode_mfma_ok(a.dm)) {
         constexpr int NT = 2;
         dim3 grid(max_groups(a.dm) * (a.dm.d / (16 * NT)));

@@ -182,7 +182,7 @@ void prefill_gemm_kernel(PrefillParams p) {
             float* s_w = reinterpret_cast<float*>(smem);
             if (tid < PBM) {  // one row per thread
                 const int m = tid;
-                s_w[m] = (is_shared || m >= rows) ? 1.f : p.ws.wts[p.ws.sorted_pair[g.y + m0 + m]];
+                s_w[m] = (is_shared || m >= rows) ? 1.f : p.ws.sorted_wt[g.y + m0 + m];
             }
             __syncthreads();
 #pragma unroll

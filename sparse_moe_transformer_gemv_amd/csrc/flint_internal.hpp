@@ -26,6 +26,7 @@ struct Workspace {
     int* offsets;        // [E+1] exclusive scan of counts
     int* sorted_pair;    // [k*Tm] pair ids ordered by (expert, pair id)
     int* pair_pos;       // [k*Tm] inverse: slot of pair id
+    float* sorted_wt;    // [k*Tm] combine weight of each sorted pair (wts[sorted_pair[i]])
     int4* groups;        // [E+1] active groups {expert (E = shared), first sorted index, rows, first slot}
     int* n_groups;       // [1]
     int2* tiles;         // [max_tiles] prefill m-tiles {group, first row}

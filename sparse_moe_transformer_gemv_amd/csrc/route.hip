@@ -132,12 +132,14 @@ __device__ void wave_topk_token(const float* __restrict__ lrow, int E, int k, in
 
 // ---------------------------------------------------------------------------
 // Stable counting sort of P pair keys (expert ids < E <= 256) by one block.
-// Writes counts[E], offsets[E+1], sorted_pair[P], pair_pos[P], the active
-// group list and (if bm > 0) the prefill tile list.
+// Writes counts[E], offsets[E+1], sorted_pair[P], pair_pos[P], sorted_wt[P]
+// (from the pair weights wts), the active group list and (if bm > 0) the
+// prefill tile list.
 // s_hist: LDS [NW*E]; s_off: LDS [E+1].
 // ---------------------------------------------------------------------------
 template <int NT, bool COHERENT = true>
-__device__ void block_sort_and_groups(const int* __restrict__ keys, int P, int E, int T, int k,
+__device__ void block_sort_and_groups(const int* __restrict__ keys, const float* __restrict__ wts, int P, int E,
+                                      int T, int k,
                                       bool has_shared, int bm, const Workspace& ws, int* s_hist,
                                       int* s_off) {
     // keys written earlier in the same kernel by other workgroups need
@@ -214,10 +216,13 @@ __device__ void block_sort_and_groups(const int* __restrict__ keys, int P, int E
     // ordered scatter: rank inside each 64-pair chunk by ballot matching
     for (int c0 = b0; c0 < b1; c0 += 64 * KU) {
         int kv[KU];
+        float wv[KU];
 #pragma unroll
         for (int u = 0; u < KU; ++u) {
             const int i = c0 + 64 * u + lane;
-            kv[u] = i < b1 ? key_at(i) : -1;
+            const int ic = i < b1 ? i : b0;
+            kv[u] = i < b1 ? key_at(ic) : -1;
+            wv[u] = COHERENT ? ld_agent(wts + ic) : wts[ic];
         }
 #pragma unroll
         for (int u = 0; u < KU; ++u) {
@@ -236,6 +241,7 @@ __device__ void block_sort_and_groups(const int* __restrict__ keys, int P, int E
                 const int pos = s_hist[w * E + key] + __popcll(m & lt);
                 ws.sorted_pair[pos] = i;
                 ws.pair_pos[i] = pos;
+                ws.sorted_wt[pos] = wv[u];
             }
             // the highest lane of each key group advances that key's base
             if (valid && (m >> lane) == 1ull) s_hist[w * E + key] += __popcll(m);
@@ -314,7 +320,7 @@ __global__ __launch_bounds__(256) void route_decode_kernel(RouteDecodeParams p) 
                         p.ws.wts + (size_t)t * p.k);
     wait_stores();
     __syncthreads();
-    block_sort_and_groups<256>(p.ws.sel, p.k * p.T, p.E, p.T, p.k, p.has_shared != 0, 0, p.ws,
+    block_sort_and_groups<256>(p.ws.sel, p.ws.wts, p.k * p.T, p.E, p.T, p.k, p.has_shared != 0, 0, p.ws,
                                s_hist, s_off);
 }
 
@@ -432,7 +438,7 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(RouteMfmaParams p) {
     }
     // counting sort of every pair by the last token tile
     if (!last_arrival(&p.ws.counter[0], (int)gridDim.x, &s_flag)) return;
-    block_sort_and_groups<512>(p.ws.sel, p.k * p.T, p.E, p.T, p.k, p.has_shared != 0, 0, p.ws,
+    block_sort_and_groups<512>(p.ws.sel, p.ws.wts, p.k * p.T, p.E, p.T, p.k, p.has_shared != 0, 0, p.ws,
                                s_hist, s_off);
 }
 
@@ -509,7 +515,7 @@ struct SortParams {
 __global__ __launch_bounds__(1024) void sort_kernel(SortParams p) {
     __shared__ int s_hist[16 * 256];
     __shared__ int s_off[257];
-    block_sort_and_groups<1024, false>(p.ws.sel, p.k * p.T, p.E, p.T, p.k, p.has_shared != 0,
+    block_sort_and_groups<1024, false>(p.ws.sel, p.ws.wts, p.k * p.T, p.E, p.T, p.k, p.has_shared != 0,
                                        p.bm, p.ws, s_hist, s_off);
 }
 

@@ -46,6 +46,17 @@ def test_small_nvfp4_decode(T):
     _case(4, T, d=256, E=32, k=4, f=64, fs=64)
 
 
+@pytest.mark.parametrize("T", [1, 23, 64])
+def test_small_nvfp4_matrix_core_path(T):
+    # d, f, fs multiples of 512 select the NVFP4 matrix-core expert kernels
+    _case(4, T, d=512, E=32, k=4, f=512, fs=1024)
+
+
+def test_nvfp4_matrix_core_path_d1024_ragged_f():
+    # f = 1536: three 128-groups per wave in the down kernel
+    _case(4, 19, d=1024, E=16, k=3, f=1536, fs=512)
+
+
 @pytest.mark.parametrize("T", [1, 7, 40, 64])
 def test_small_bf16_matrix_core_path(T):
     # d % 128 == 0 and f, fs % 128 == 0 select the MFMA router and expert kernels
