@@ -501,18 +501,6 @@ __device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t w, float sc) {
 }
 #undef FLINT_FP4_PAIR
 
-// Raw buffer view of [base, base + bytes): a load whose offset lies at or past
-// the end returns zeros without touching memory, which is how the kernels
-// below skip the rows of a 16-row tile that hold no token.
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
-constexpr uint32_t kOffNone = 0x80000000u;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
 __device__ __forceinline__ uint32_t u4_word(const uint4& v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }

@@ -26,6 +26,8 @@ struct Workspace {
     int* offsets;        // [E+1] exclusive scan of counts
     int* sorted_pair;    // [k*Tm] pair ids ordered by (expert, pair id)
     int* pair_pos;       // [k*Tm] inverse: slot of pair id
+    float* rpart;        // [d/256][64][E] split-K router partial logits (decode, T <= 64)
+    int* rcount;         // [4 ceil(E/16) + 8] router tickets, zero between launches
     float* sorted_wt;    // [k*Tm] combine weight of each sorted pair (wts[sorted_pair[i]])
     int4* groups;        // [E+1] active groups {expert (E = shared), first sorted index, rows, first slot}
     int* n_groups;       // [1]
@@ -139,6 +141,19 @@ __device__ __forceinline__ bool last_arrival(int* counter, int n_arrivals, int* 
     return *s_flag != 0;
 }
 
+// Raw buffer view of [base, base + bytes): a load whose offset lies at or past
+// the end returns zeros without touching memory, which is how kernels skip the
+// rows of a 16-row MFMA tile that hold no token.  Offsets are 32-bit; kOffNone
+// is past the end of every view (views stay below 2 GiB).
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+constexpr uint32_t kOffNone = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 // MFMA operand types (gfx950 v_mfma_f32_16x16x32_bf16).  Lane l of a wave
 // supplies A row (l & 15) and B column (l & 15), each with the 8 consecutive
 // k values 8*(l >> 4) .. +7 of a 32-wide k step; the 16x16 fp32 result puts

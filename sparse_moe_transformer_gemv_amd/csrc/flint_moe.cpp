@@ -138,6 +138,8 @@ size_t carve(const flint_moe_config& c, char* base, Workspace* w) {
     w->sorted_pair = static_cast<int*>(take(Tm * k * 4));
     w->pair_pos = static_cast<int*>(take(Tm * k * 4));
     w->sorted_wt = static_cast<float*>(take(Tm * k * 4));
+    w->rpart = static_cast<float*>(take((size_t)(c.d_model / 256 > 0 ? c.d_model / 256 : 1) * 64 * E * 4));
+    w->rcount = static_cast<int*>(take((4 * ((E + 15) / 16) + 8) * 4));
     w->groups = static_cast<int4*>(take((E + 1) * 16));
     w->n_groups = static_cast<int*>(take(4));
     w->tiles = static_cast<int2*>(take(max_tiles * 8));

@@ -442,6 +442,201 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(RouteMfmaParams p) {
                                s_hist, s_off);
 }
 
+// ---------------------------------------------------------------------------
+// Decode router for T <= 64, in one launch of (d/256) x (E/16) x (T/16)
+// blocks and four stages handed on by tickets:
+//   1. block (kc, et, tt) computes the partial logits of the 16 tokens of
+//      tile tt and the 16 experts of tile et over k in [256 kc, 256 kc + 256)
+//      (8 waves, one 32-wide MFMA step each) into rpart[kc];
+//   2. the last k-chunk block of (et, tt) sums the d/256 partials in kc order
+//      (so the result does not depend on timing) and adds the bias;
+//   3. the last expert tile of token tile tt selects the top-k of its tokens
+//      (two per wave);
+//   4. the last token tile runs the counting sort.
+// Spreading the 2 MB of fp32 router rows over >= 128 blocks keeps enough loads
+// in flight (a block per 16 experts would be bound by one CU's miss queue),
+// and spreading the selection over token tiles keeps it off one CU.
+// ---------------------------------------------------------------------------
+// Maximum over the 64 lanes: quad swaps, half-row and row mirrors reduce
+// each row of 16 lanes, the row broadcasts carry the result to lane 63, and
+// it is read back as a wave-uniform value.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#define FLINT_DPP_MAX(ctrl, rmask) \
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, ctrl, rmask, 0xF, false))
+    FLINT_DPP_MAX(0xB1, 0xF);   // quad_perm [1,0,3,2]
+    FLINT_DPP_MAX(0x4E, 0xF);   // quad_perm [2,3,0,1]
+    FLINT_DPP_MAX(0x141, 0xF);  // row_half_mirror
+    FLINT_DPP_MAX(0x140, 0xF);  // row_mirror
+    FLINT_DPP_MAX(0x142, 0xA);  // row_bcast:15 into rows 1 and 3
+    FLINT_DPP_MAX(0x143, 0xC);  // row_bcast:31 into rows 2 and 3
+#undef FLINT_DPP_MAX
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Order-preserving map of a float to an unsigned key (-0 taken as +0); key 0
+// marks an expert that can no longer be chosen.
+__device__ __forceinline__ uint32_t order_key(float f) {
+    const uint32_t u = __float_as_uint(f + 0.0f);
+    return (u >> 31) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t key) {
+    return __uint_as_float((key >> 31) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// Top-k of U tokens by one wavefront (tokens t0 + wave + 8 u), rounds interleaved
+// across the tokens.  Lane l holds the keys of experts 4 l .. 4 l + 3.  Each
+// round takes the wave maximum key; the lowest lane holding it, and inside
+// that lane the lowest slot, give the lowest expert index among equal logits.
+// The chosen logits are wave-uniform, so their softmax is formed directly.
+// Results go to global memory (device-coherent) and to LDS copies indexed
+// from t0.
+template <int U>
+__device__ __forceinline__ void wave_topk_tokens(const float* __restrict__ logits, int t0, int T, int E, int k,
+                                                 int wave, int lane, int* __restrict__ sel, float* __restrict__ wts,
+                                                 int* s_sel, float* s_wt) {
+    uint32_t key[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int t = t0 + wave + 8 * u;
+        const float* row = logits + (size_t)(t < T ? t : 0) * E;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * lane + i;
+            const float v = ld_agent(row + (e < E ? e : 0));
+            key[u][i] = e < E ? order_key(v) : 0u;
+        }
+    }
+    uint32_t cm[U][8];
+    int ce[U][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (j >= k) break;  // uniform
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            uint32_t m = key[u][0];
+            int li = 0;
+#pragma unroll
+            for (int i = 1; i < 4; ++i)
+                if (key[u][i] > m) {
+                    m = key[u][i];
+                    li = i;
+                }
+            const uint32_t M = wave_max_u32(m);
+            const int L = __builtin_ctzll(__ballot(m == M));
+            const int lis = __builtin_amdgcn_readlane(li, L);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (lane == L && lis == i) key[u][i] = 0u;
+            cm[u][j] = M;
+            ce[u][j] = 4 * L + lis;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int t = t0 + wave + 8 * u;
+        if (t >= T) break;  // uniform
+        const float v0 = key_value(cm[u][0]);
+        float pj[8], sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            pj[j] = j < k ? expf(key_value(cm[u][j]) - v0) : 0.f;
+            sum += pj[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < k && lane == j) {
+                const float w = pj[j] / sum;
+                st_agent(sel + t * k + j, ce[u][j]);
+                st_agent(wts + t * k + j, w);
+                s_sel[(t - t0) * k + j] = ce[u][j];
+                s_wt[(t - t0) * k + j] = w;
+            }
+    }
+}
+
+constexpr int kRouteSplitMaxT = 64;
+
+template <int NS>  // NS = d / 256 k-chunks
+__global__ __launch_bounds__(512) void route_splitk_kernel(RouteMfmaParams p) {
+    constexpr int NW = 8;
+    __shared__ float s_part[NW][256];
+    __shared__ int s_hist[NW * 256];
+    __shared__ int s_off[257];
+    __shared__ int s_sel[16 * 8];
+    __shared__ float s_wt[16 * 8];
+    __shared__ int s_flag;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = lane & 15, q = lane >> 4;
+    const int E = p.E, d = p.d, T = p.T;
+    const int NE = (E + 15) / 16, ntt = (T + 15) / 16, npairs = NS * NE;
+    // block -> (k-chunk, expert tile) pair and token tile; when the pairs
+    // divide into the 8 XCDs, the token tiles of one pair get ids equal mod 8
+    // (one XCD, so its router rows are fetched into one L2)
+    int pair, tt;
+    if (npairs % 8 == 0) {
+        const int slot = blockIdx.x >> 3;
+        pair = (slot / ntt) * 8 + (blockIdx.x & 7);
+        tt = slot % ntt;
+    } else {
+        pair = blockIdx.x / ntt;
+        tt = blockIdx.x % ntt;
+    }
+    const int kc = pair % NS, et = pair / NS, e0 = et * 16, t0 = tt * 16;
+    const int kl = kc * 256 + wave * 32 + 8 * q;
+    // 1. partial logits; router rows past E and tokens past T read as zeros
+    const __amdgpu_buffer_rsrc_t wv = buffer_view(p.wr, (uint32_t)E * d * 4);
+    const uint32_t wo = e0 + row < E ? (uint32_t)((e0 + row) * d + kl) * 4 : kOffNone;
+    const uint4 w0 = buffer_load16(wv, wo), w1 = buffer_load16(wv, wo + 16);
+    const __amdgpu_buffer_rsrc_t xv = buffer_view(p.x, (uint32_t)T * d * 2);
+    const int tok = t0 + row;
+    const uint4 a = buffer_load16(xv, tok < T ? (uint32_t)(tok * d + kl) * 2 : kOffNone);
+    const float wf[8] = {__uint_as_float(w0.x), __uint_as_float(w0.y), __uint_as_float(w0.z),
+                         __uint_as_float(w0.w), __uint_as_float(w1.x), __uint_as_float(w1.y),
+                         __uint_as_float(w1.z), __uint_as_float(w1.w)};
+    uint4 hi, mid, lo;
+    split3_bf16(wf, hi, mid, lo);
+    floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+    acc = mfma16x16x32(a, hi, acc);
+    acc = mfma16x16x32(a, mid, acc);
+    acc = mfma16x16x32(a, lo, acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_part[wave][(4 * q + i) * 16 + row] = acc[i];
+    __syncthreads();
+    const int m = tid >> 4, n = tid & 15;  // token t0 + m, expert e0 + n (first 256 threads)
+    const bool mine = tid < 256 && t0 + m < T && e0 + n < E;
+    const size_t o = (size_t)(t0 + m) * E + e0 + n;
+    if (mine) {
+        float v = s_part[0][tid];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) v += s_part[w][tid];
+        st_agent(p.ws.rpart + (size_t)kc * kRouteSplitMaxT * E + o, v);
+    }
+    // 2. the last k-chunk block of (et, tt) finishes these logits
+    if (!last_arrival(&p.ws.rcount[tt * NE + et], NS, &s_flag)) return;
+    if (mine) {
+        float pv[NS];
+#pragma unroll
+        for (int c = 0; c < NS; ++c) pv[c] = ld_agent(p.ws.rpart + (size_t)c * kRouteSplitMaxT * E + o);
+        float v = pv[0];
+#pragma unroll
+        for (int c = 1; c < NS; ++c) v += pv[c];
+        st_agent(p.ws.logits + o, v + (p.bias ? p.bias[e0 + n] : 0.f));
+    }
+    // 3. the last expert tile of token tile tt selects its tokens' experts
+    if (!last_arrival(&p.ws.rcount[ntt * NE + tt], NE, &s_flag)) return;
+    wave_topk_tokens<2>(p.ws.logits, t0, T, E, p.k, wave, lane, p.ws.sel, p.ws.wts, s_sel, s_wt);
+    // 4. the last token tile sorts every pair (from LDS when it is the only one)
+    if (ntt == 1) {
+        __syncthreads();
+        block_sort_and_groups<512, false>(s_sel, s_wt, p.k * T, E, T, p.k, p.has_shared != 0, 0, p.ws, s_hist,
+                                          s_off);
+        return;
+    }
+    if (!last_arrival(&p.ws.rcount[ntt * NE + ntt], ntt, &s_flag)) return;
+    block_sort_and_groups<512, true>(p.ws.sel, p.ws.wts, p.k * T, E, T, p.k, p.has_shared != 0, 0, p.ws, s_hist,
+                                     s_off);
+}
+
 bool route_mfma_ok(const Dims& dm) {
     const int ns = dm.d / 256;
     return dm.act == DT_BF16 && dm.d % 256 == 0 && (ns == 1 || ns == 2 || ns == 4 || ns == 8);
@@ -450,6 +645,16 @@ bool route_mfma_ok(const Dims& dm) {
 hipError_t launch_route_mfma(const LayerArgs& a, const Workspace& w, bool do_sort, hipStream_t s) {
     RouteMfmaParams p{static_cast<const uint16_t*>(a.x), a.wr, a.bias, a.dm.T, a.dm.d, a.dm.E,
                       a.dm.k, a.dm.fs > 0, do_sort ? 1 : 0, w};
+    if (do_sort && a.dm.T <= kRouteSplitMaxT && a.dm.E <= 256 && a.dm.k <= 8) {
+        dim3 grid((a.dm.d / 256) * ((a.dm.E + 15) / 16) * ((a.dm.T + 15) / 16));
+        switch (a.dm.d / 256) {
+        case 1: hipLaunchKernelGGL((route_splitk_kernel<1>), grid, dim3(512), 0, s, p); break;
+        case 2: hipLaunchKernelGGL((route_splitk_kernel<2>), grid, dim3(512), 0, s, p); break;
+        case 4: hipLaunchKernelGGL((route_splitk_kernel<4>), grid, dim3(512), 0, s, p); break;
+        default: hipLaunchKernelGGL((route_splitk_kernel<8>), grid, dim3(512), 0, s, p); break;
+        }
+        return hipGetLastError();
+    }
     const bool wide = a.dm.T > 64;  // prefill-sized: 64-token blocks share router loads
     const int tok = wide ? 64 : 16;
     dim3 grid((a.dm.T + tok - 1) / tok, (a.dm.E + 15) / 16);
