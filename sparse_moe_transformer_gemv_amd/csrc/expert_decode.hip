@@ -325,8 +325,44 @@ __global__ __launch_bounds__(256) void down_decode_kernel(ExpertParams p) {
 // tiles are summed through LDS in a fixed order.
 // ---------------------------------------------------------------------------
 
+// One 16-token tile of a bf16 gate/up block; sp is the sorted pair of this
+// lane's token row.  Padding rows read as zeros (buffer view past T).
+template <int NSTEP>
+__device__ __forceinline__ void gateup_mfma_tile(const ExpertParams& p, const int4& g, bool is_shared, int r0,
+                                                 int sp, __amdgpu_buffer_rsrc_t xv, int kl, const uint4 (&b)[NSTEP],
+                                                 int j0, float (&s_part)[4][256]) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = lane & 15, q = lane >> 4;
+    const int d = p.dm.d;
+    const int m = r0 + row;
+    const int tok = is_shared ? m : sp / p.dm.k;
+    const uint32_t xo = m < g.z ? (uint32_t)(tok * d + kl) * 2 : kOffNone;
+    uint4 a[NSTEP];
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) a[s] = buffer_load16(xv, xo + 64 * s);
+    __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the first MFMA
+    floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) acc = mfma16x16x32(a[s], b[s], acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_part[wave][(4 * q + i) * 16 + row] = acc[i];
+    __syncthreads();
+    const int mm = tid >> 4, n = tid & 15;
+    if (n < 8 && r0 + mm < g.z) {
+        const int gi_ = mm * 16 + n, ui_ = gi_ + 8;
+        const float gv = ((s_part[0][gi_] + s_part[1][gi_]) + s_part[2][gi_]) + s_part[3][gi_];
+        const float uv = ((s_part[0][ui_] + s_part[1][ui_]) + s_part[2][ui_]) + s_part[3][ui_];
+        static_cast<float*>(p.ws.h)[(size_t)(g.w + r0 + mm) * p.hstride + j0 + n] = silu_f32(gv) * uv;
+    }
+    __syncthreads();
+}
+
 // gate/up: block = (group, 8 features): B columns 0..7 are gate rows j0..j0+7,
 // columns 8..15 the matching up rows.  NSTEP = k steps per wave = d / 128.
+// The token index is requested first (vector loads retire in order, so the
+// activation loads that need it wait for it alone), then the weights, then the
+// first token tile's activations, all before the first wait; that tile is
+// peeled off the loop so no loop-carried register forces an earlier wait.
 template <int NSTEP>
 __global__ __launch_bounds__(256) void gateup_mfma_kernel(ExpertParams p) {
     __shared__ float s_part[4][256];
@@ -341,52 +377,84 @@ __global__ __launch_bounds__(256) void gateup_mfma_kernel(ExpertParams p) {
     const int F = is_shared ? p.dm.fs : p.dm.f;
     const int j0 = fb * 8;
     if (j0 >= F) return;
+    const int sp = p.ws.sorted_pair[g.y + (row < g.z ? row : g.z - 1)];
+    __builtin_amdgcn_sched_barrier(0);
     const size_t e = is_shared ? 0 : (size_t)g.x;
     const uint16_t* gu = static_cast<const uint16_t*>(is_shared ? p.shared.gu : p.routed.gu);
     const size_t wr = e * 2 * F + (row < 8 ? (size_t)(j0 + row) : (size_t)(F + j0 + row - 8));
-    const int kbeg = wave * (d / 4);
-    const uint16_t* wrow = gu + wr * d + kbeg + 8 * q;
+    const int kl = wave * (d / 4) + 8 * q;
+    const uint16_t* wrow = gu + wr * d + kl;
     uint4 b[NSTEP];
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) b[s] = *reinterpret_cast<const uint4*>(wrow + 32 * s);
-    __builtin_amdgcn_sched_barrier(0);
-    const uint16_t* x = static_cast<const uint16_t*>(p.x);
-    float* h = static_cast<float*>(p.ws.h);
-    for (int r0 = 0; r0 < g.z; r0 += 16) {
+    const __amdgpu_buffer_rsrc_t xv = buffer_view(p.x, (uint32_t)p.dm.T * d * 2);
+    gateup_mfma_tile<NSTEP>(p, g, is_shared, 0, sp, xv, kl, b, j0, s_part);
+    for (int r0 = 16; r0 < g.z; r0 += 16) {
         const int m = r0 + row;
-        const int tok = (m < g.z) ? (is_shared ? m : p.ws.sorted_pair[g.y + m] / p.dm.k) : -1;
-        const uint16_t* xr = x + (size_t)(tok < 0 ? 0 : tok) * d + kbeg + 8 * q;
-        floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-        // loads are unconditional (row 0 stands in for padding rows) so they
-        // issue back to back; padding rows are zeroed afterwards
-        uint4 a[NSTEP];
-#pragma unroll
-        for (int s = 0; s < NSTEP; ++s) a[s] = *reinterpret_cast<const uint4*>(xr + 32 * s);
-        __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the first MFMA
-        const uint32_t keep = tok >= 0 ? 0xFFFFFFFFu : 0u;
-#pragma unroll
-        for (int s = 0; s < NSTEP; ++s) {
-            const uint4 av = make_uint4(a[s].x & keep, a[s].y & keep, a[s].z & keep, a[s].w & keep);
-            acc = mfma16x16x32(av, b[s], acc);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s_part[wave][(4 * q + i) * 16 + row] = acc[i];
-        __syncthreads();
-        const int mm = tid >> 4, n = tid & 15;
-        if (n < 8 && r0 + mm < g.z) {
-            const int gi_ = mm * 16 + n, ui_ = gi_ + 8;
-            const float gv = ((s_part[0][gi_] + s_part[1][gi_]) + s_part[2][gi_]) + s_part[3][gi_];
-            const float uv = ((s_part[0][ui_] + s_part[1][ui_]) + s_part[2][ui_]) + s_part[3][ui_];
-            h[(size_t)(g.w + r0 + mm) * p.hstride + j0 + n] = silu_f32(gv) * uv;
-        }
-        __syncthreads();
+        const int spn = p.ws.sorted_pair[g.y + (m < g.z ? m : g.z - 1)];
+        gateup_mfma_tile<NSTEP>(p, g, is_shared, r0, spn, xv, kl, b, j0, s_part);
     }
+}
+
+// One 16-token tile of a bf16 down block; ws is the routing weight of the
+// token row this thread stores.  Padding rows of h read as zeros.
+template <int NSMAX, int NT>
+__device__ __forceinline__ void down_mfma_tile(const ExpertParams& p, const int4& g, int r0, int nsteps, int kl,
+                                               int n0, __amdgpu_buffer_rsrc_t hv, const uint4 (&b)[NT][NSMAX],
+                                               float ws, float (&s_part)[4][NT][256]) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = lane & 15, q = lane >> 4;
+    const int m = r0 + row;
+    const uint32_t ho = m < g.z ? (uint32_t)(m * p.hstride + kl) * 4 : kOffNone;
+    uint4 hr0[NSMAX], hr1[NSMAX];
+#pragma unroll
+    for (int s = 0; s < NSMAX; ++s) {
+        hr0[s] = buffer_load16(hv, ho + 128 * s);
+        hr1[s] = buffer_load16(hv, ho + 128 * s + 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the first MFMA
+    floatx4_t acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NSMAX; ++s) {
+        if (s >= nsteps) break;
+        const float v[8] = {__uint_as_float(hr0[s].x), __uint_as_float(hr0[s].y), __uint_as_float(hr0[s].z),
+                            __uint_as_float(hr0[s].w), __uint_as_float(hr1[s].x), __uint_as_float(hr1[s].y),
+                            __uint_as_float(hr1[s].z), __uint_as_float(hr1[s].w)};
+        uint4 ahi, amid, alo;
+        split3_bf16(v, ahi, amid, alo);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            acc[t] = mfma16x16x32(ahi, b[t][s], acc[t]);
+            acc[t] = mfma16x16x32(amid, b[t][s], acc[t]);
+            acc[t] = mfma16x16x32(alo, b[t][s], acc[t]);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_part[wave][t][(4 * q + i) * 16 + row] = acc[t][i];
+    __syncthreads();
+    const int mm = tid >> 4, n = tid & 15;
+    if (r0 + mm < g.z) {
+        float* yr = static_cast<float*>(p.ws.y) + (size_t)(g.w + r0 + mm) * p.dm.d + n0 + n;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const float v = ((s_part[0][t][tid] + s_part[1][t][tid]) + s_part[2][t][tid]) + s_part[3][t][tid];
+            yr[16 * t] = ws * v;
+        }
+    }
+    __syncthreads();
 }
 
 // down: block = (group, NT tiles of 16 output rows); K = F split over the
 // waves, NSMAX >= F / 128 k steps per wave.  h is fp32; it enters the MFMA
 // exactly as three bf16 parts (hi + mid + lo), the weights exactly, so the
-// only rounding is the fp32 accumulation.
+// only rounding is the fp32 accumulation.  Load order and the peeled first
+// token tile as in gateup_mfma_kernel.
+constexpr int kDownMfmaTiles = 4;  // 64 output rows per block
+
 template <int NSMAX, int NT>
 __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertParams p) {
     __shared__ float s_part[4][NT][256];
@@ -398,72 +466,32 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertParams p) {
     if (gi >= *p.ws.n_groups) return;
     const int4 g = p.ws.groups[gi];
     const bool is_shared = g.x == p.dm.E;
+    const int mm = tid >> 4;
+    const float rw_load = p.ws.sorted_wt[g.y + (mm < g.z ? mm : g.z - 1)];
+    __builtin_amdgcn_sched_barrier(0);
     const int F = is_shared ? p.dm.fs : p.dm.f;
     const int nsteps = F / 128;
-    const int kbeg = wave * (F / 4);
+    const int kl = wave * (F / 4) + 8 * q;
     const size_t e = is_shared ? 0 : (size_t)g.x;
     const uint16_t* dn = static_cast<const uint16_t*>(is_shared ? p.shared.dn : p.routed.dn);
     const int n0 = rb * 16 * NT;
     uint4 b[NT][NSMAX];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        const uint16_t* drow = dn + (e * d + (size_t)(n0 + 16 * t + row)) * F + kbeg + 8 * q;
+        const uint16_t* drow = dn + (e * d + (size_t)(n0 + 16 * t + row)) * F + kl;
 #pragma unroll
-        for (int s = 0; s < NSMAX; ++s)
-            b[t][s] = s < nsteps ? *reinterpret_cast<const uint4*>(drow + 32 * s)
-                                 : make_uint4(0, 0, 0, 0);
+        for (int s = 0; s < NSMAX; ++s) {
+            const int sc = s < nsteps ? s : 0;  // clamped: steps past nsteps are loaded but unused
+            b[t][s] = *reinterpret_cast<const uint4*>(drow + 32 * sc);
+        }
     }
-    const float* h = static_cast<const float*>(p.ws.h);
-    float* y = static_cast<float*>(p.ws.y);
-    for (int r0 = 0; r0 < g.z; r0 += 16) {
-        const int m = r0 + row;
-        const bool ok = m < g.z;
-        const float* hr = h + (size_t)(g.w + (ok ? m : 0)) * p.hstride + kbeg + 8 * q;
-        floatx4_t acc[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-        // unconditional loads (slot row of token 0 stands in for padding rows)
-        float4 hv0[NSMAX], hv1[NSMAX];
-#pragma unroll
-        for (int s = 0; s < NSMAX; ++s) {
-            if (s < nsteps) {
-                hv0[s] = *reinterpret_cast<const float4*>(hr + 32 * s);
-                hv1[s] = *reinterpret_cast<const float4*>(hr + 32 * s + 4);
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the first MFMA
-        const float keep = ok ? 1.f : 0.f;
-#pragma unroll
-        for (int s = 0; s < NSMAX; ++s) {
-            if (s >= nsteps) break;
-            const float v[8] = {hv0[s].x * keep, hv0[s].y * keep, hv0[s].z * keep, hv0[s].w * keep,
-                                hv1[s].x * keep, hv1[s].y * keep, hv1[s].z * keep, hv1[s].w * keep};
-            uint4 ahi, amid, alo;
-            split3_bf16(v, ahi, amid, alo);
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                acc[t] = mfma16x16x32(ahi, b[t][s], acc[t]);
-                acc[t] = mfma16x16x32(amid, b[t][s], acc[t]);
-                acc[t] = mfma16x16x32(alo, b[t][s], acc[t]);
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s_part[wave][t][(4 * q + i) * 16 + row] = acc[t][i];
-        __syncthreads();
-        const int mm = tid >> 4, n = tid & 15;
-        if (r0 + mm < g.z) {
-            const float ws = is_shared ? 1.f : p.ws.sorted_wt[g.y + r0 + mm];
-            float* yr = y + (size_t)(g.w + r0 + mm) * d + n0 + n;
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const float v = ((s_part[0][t][tid] + s_part[1][t][tid]) + s_part[2][t][tid]) +
-                                s_part[3][t][tid];
-                yr[16 * t] = ws * v;
-            }
-        }
-        __syncthreads();
+    const __amdgpu_buffer_rsrc_t hv =
+        buffer_view(static_cast<const float*>(p.ws.h) + (size_t)g.w * p.hstride, (uint32_t)g.z * p.hstride * 4);
+    down_mfma_tile<NSMAX, NT>(p, g, 0, nsteps, kl, n0, hv, b, is_shared ? 1.f : rw_load, s_part);
+    for (int r0 = 16; r0 < g.z; r0 += 16) {
+        const int m = r0 + mm;
+        const float rw = is_shared ? 1.f : p.ws.sorted_wt[g.y + (m < g.z ? m : g.z - 1)];
+        down_mfma_tile<NSMAX, NT>(p, g, r0, nsteps, kl, n0, hv, b, rw, s_part);
     }
 }
 
@@ -740,7 +768,8 @@ bool decode_mfma_ok(const Dims& dm) {
     const int ns = dm.d / 128;
     return dm.act == DT_BF16 && dm.wdt == DT_BF16 && dm.d % 128 == 0 &&
            (ns == 1 || ns == 2 || ns == 4 || ns == 8 || ns == 16) && dm.f % 128 == 0 &&
-           dm.fs % 128 == 0 && fmax <= 1024 && dm.d % 32 == 0;
+           dm.fs % 128 == 0 && fmax <= 1024 && dm.d % 32 == 0 && (size_t)dm.T * dm.d * 2 < kOffNone &&
+           (size_t)dm.T * fmax * 4 < kOffNone;
 }
 
 static int max_groups(const Dims& dm) {
@@ -815,7 +844,7 @@ hipError_t launch_down_decode(const LayerArgs& a, const Workspace& w, hipStream_
         return hipGetLastError();
     }
     if (decode_mfma_ok(a.dm)) {
-        constexpr int NT = 2;
+        constexpr int NT = kDownMfmaTiles;
         dim3 grid(max_groups(a.dm) * (a.dm.d / (16 * NT)));
         switch ((p.hstride + 127) / 128) {
         case 1: hipLaunchKernelGGL((down_mfma_kernel<1, NT>), grid, dim3(256), 0, s, p); break;
