@@ -14,15 +14,20 @@
 //   gate/up:  H[r][j] = SiLU(X_r . G_j) * (X_r . U_j)   (bf16 out, fp32 math)
 //   down:     Y[r][n] = w_r * (H_r . D_n)                (bf16 out, fp32 math)
 //
-// Tile 256 rows x 256 B rows, K step 64, 8 waves as 2 (M) x 4 (N), each wave
-// 128 x 64 = 8 x 4 MFMA 16x16x32 tiles (128 fp32 accumulators per lane), two
-// waves per SIMD so that one wave's LDS reads overlap the other's MFMAs.  For
-// gate/up the 256 B rows of a tile are, per 64-row quarter q, 32 gate rows then
-// the matching 32 up rows of features 32q..32q+31, so each wave holds matching
-// gate and up columns and applies SwiGLU in registers.  Two LDS stages of 64 KiB are
-// filled straight from global memory (direct-to-LDS 16-byte loads, two K steps
-// in flight); 16-byte chunks of each 128-byte LDS row are XOR-swizzled by row
-// so fragment reads are free of bank conflicts.
+// Tile 256 rows x 256 B rows, 8 waves as 2 (M) x 4 (N), each wave 128 x 64 =
+// 8 x 4 MFMA 16x16x32 tiles (128 fp32 accumulators per lane), two waves per
+// SIMD.  For gate/up the 256 B rows of a tile are, per 64-row quarter q, 32
+// gate rows then the matching 32 up rows of features 32q..32q+31, so each wave
+// holds matching gate and up columns and applies SwiGLU in registers.
+//
+// K advances in stages of 32 through four 32 KiB LDS buffers, filled straight
+// from global memory (direct-to-LDS 16-byte loads) three stages ahead; 16-byte
+// chunks of each 64-byte LDS row are XOR-swizzled by row so fragment reads are
+// free of bank conflicts.  The two waves of a SIMD run a ping-pong schedule:
+// waves 0-3 and 4-7 are kept one phase apart by workgroup barriers, so while
+// one group issues its 32 MFMAs of a stage the other reads its fragments of
+// that stage from LDS and issues the loads of a later one, and the matrix
+// pipe never waits for LDS.
 //
 // Scheduling: a persistent grid (one workgroup per CU) walks the tiles; the
 // tile range is cut into 8 contiguous chunks, one per XCD (workgroups are
@@ -35,9 +40,10 @@ namespace flint {
 
 constexpr int PBM = 256;  // rows per tile (the sort's tile height)
 constexpr int PBN = 256;  // B rows per tile
-constexpr int PBK = 64;   // k per stage
-constexpr int kStageBytes = (PBM + PBN) * PBK * 2;  // 64 KiB
-constexpr int kLdsBytes = 2 * kStageBytes;           // 128 KiB
+constexpr int PBK = 32;   // k per stage
+constexpr int kNStage = 4;
+constexpr int kStageBytes = (PBM + PBN) * PBK * 2;  // 32 KiB
+constexpr int kLdsBytes = kNStage * kStageBytes;     // 128 KiB
 static_assert(PBM == kPrefillBM, "tile height must match the sort's tile list");
 
 struct PrefillParams {
@@ -51,23 +57,78 @@ struct PrefillParams {
 
 enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+// byte offset of 16-byte chunk `chunk` (k = 8 chunk .. +7) of LDS row `row`
+__device__ __forceinline__ uint32_t swz(int row, int chunk) {
+    return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4);
+}
 
 constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / 64;
+
+// Fragments of one stage: 8 A and 4 B 16-byte LDS reads, 16 rows (1 KiB)
+// apart, from two per-lane base addresses, issued together and waited for
+// inside the same asm block.  Written as asm because the compiler cannot tell
+// these reads from the direct-to-LDS loads still in flight into other stages
+// and would otherwise wait for all of them (vmcnt 0) first.
+typedef __attribute__((ext_vector_type(4))) uint32_t frag_t;
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void read_frags(uint32_t a_base, uint32_t b_base, uint4 (&fa)[8], uint4 (&fb)[4]) {
+    frag_t a0, a1, a2, a3, a4, a5, a6, a7, b0, b1, b2, b3;
+    asm volatile(
+        "ds_read_b128 %0, %12 offset:0\n\t"
+        "ds_read_b128 %1, %12 offset:1024\n\t"
+        "ds_read_b128 %2, %12 offset:2048\n\t"
+        "ds_read_b128 %3, %12 offset:3072\n\t"
+        "ds_read_b128 %4, %12 offset:4096\n\t"
+        "ds_read_b128 %5, %12 offset:5120\n\t"
+        "ds_read_b128 %6, %12 offset:6144\n\t"
+        "ds_read_b128 %7, %12 offset:7168\n\t"
+        "ds_read_b128 %8, %13 offset:0\n\t"
+        "ds_read_b128 %9, %13 offset:1024\n\t"
+        "ds_read_b128 %10, %13 offset:2048\n\t"
+        "ds_read_b128 %11, %13 offset:3072\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(a4), "=&v"(a5), "=&v"(a6), "=&v"(a7), "=&v"(b0),
+          "=&v"(b1), "=&v"(b2), "=&v"(b3)
+        : "v"(a_base), "v"(b_base));
+    fa[0] = make_uint4(a0.x, a0.y, a0.z, a0.w);
+    fa[1] = make_uint4(a1.x, a1.y, a1.z, a1.w);
+    fa[2] = make_uint4(a2.x, a2.y, a2.z, a2.w);
+    fa[3] = make_uint4(a3.x, a3.y, a3.z, a3.w);
+    fa[4] = make_uint4(a4.x, a4.y, a4.z, a4.w);
+    fa[5] = make_uint4(a5.x, a5.y, a5.z, a5.w);
+    fa[6] = make_uint4(a6.x, a6.y, a6.z, a6.w);
+    fa[7] = make_uint4(a7.x, a7.y, a7.z, a7.w);
+    fb[0] = make_uint4(b0.x, b0.y, b0.z, b0.w);
+    fb[1] = make_uint4(b1.x, b1.y, b1.z, b1.w);
+    fb[2] = make_uint4(b2.x, b2.y, b2.z, b2.w);
+    fb[3] = make_uint4(b3.x, b3.y, b3.z, b3.w);
+}
+
+// A barrier that no instruction is scheduled across (the MFMAs of a compute
+// phase must stay between its two barriers for the ping-pong to hold).
+__device__ __forceinline__ void phase_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    barrier_keep_loads();
+    __builtin_amdgcn_sched_barrier(0);
+}
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_gemm_kernel(PrefillParams p) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = wave >> 2, wn = wave & 3;  // wm is also the ping-pong group
     const int row16 = lane & 15, q = lane >> 4;
     const int d = p.dm.d;
-    // load-slot geometry: instruction i of this wave fills LDS rows 64 i + 8 wave .. +7;
-    // lane l fills row (l >> 3) of those with global chunk (l & 7) ^ (l >> 3)
-    const int lrow = 8 * wave + (lane >> 3);
-    const int lchunk = (lane & 7) ^ (lane >> 3);
+    // load-slot geometry: load j (0, 1) of this wave fills LDS rows 32 wave + 16 j .. +15 of
+    // the A and of the B half of a stage; lane l fills row (l >> 2) of those, physical chunk l & 3
+    const int lrow = 32 * wave + (lane >> 2);
+    const uint32_t lds0 = lds_addr(lds);
+    // this lane's fragment base addresses within a stage
+    const uint32_t a_rd = swz(128 * wm + row16, q);
+    const uint32_t b_rd = PBM * PBK * 2 + swz(64 * wn + row16, q);
 
     const int total = *p.ws.n_tiles * p.nblk;
     const int per_xcd = (total + 7) / 8;
@@ -93,25 +154,24 @@ void prefill_gemm_kernel(PrefillParams p) {
             nb0 = jb * PBN;  // first output row
         }
 
-        // per-lane global pointers of the 4 A and 4 B load instructions
-        const uint16_t* asrc[4];
-        const uint16_t* bsrc[4];
+        // per-lane global sources of this wave's 2 A and 2 B loads (logical chunk of the lane's slot)
+        const uint16_t* asrc[2];
+        const uint16_t* bsrc[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 64 * i + lrow;
+        for (int j = 0; j < 2; ++j) {
+            const int r = lrow + 16 * j;
+            const int c = (lane & 3) ^ ((r >> 1) & 3);
             const int m = r < rows ? r : 0;  // padding rows repeat row 0; never stored
             if (MODE == MODE_GATEUP) {
                 const int mm = m0 + m;
                 const int tok = is_shared ? mm : p.ws.sorted_pair[g.y + mm] / p.dm.k;
-                asrc[i] = p.x + (size_t)tok * d + 8 * lchunk;
+                asrc[j] = p.x + (size_t)tok * d + 8 * c;
                 const int seg = r >> 5, rr = r & 31;  // per 64 rows: 32 gate, then 32 up
                 const size_t wrow = e * 2 * F + (size_t)((seg & 1) ? F : 0) + nb0 + 32 * (seg >> 1) + rr;
-                bsrc[i] = static_cast<const uint16_t*>(wp.gu) + wrow * K + 8 * lchunk;
+                bsrc[j] = static_cast<const uint16_t*>(wp.gu) + wrow * K + 8 * c;
             } else {
-                asrc[i] = static_cast<const uint16_t*>(p.ws.h) + (size_t)(g.w + m0 + m) * p.hstride +
-                          8 * lchunk;
-                bsrc[i] = static_cast<const uint16_t*>(wp.dn) + (e * (size_t)d + nb0 + r) * K +
-                          8 * lchunk;
+                asrc[j] = static_cast<const uint16_t*>(p.ws.h) + (size_t)(g.w + m0 + m) * p.hstride + 8 * c;
+                bsrc[j] = static_cast<const uint16_t*>(wp.dn) + (e * (size_t)d + nb0 + r) * K + 8 * c;
             }
         }
 
@@ -121,65 +181,58 @@ void prefill_gemm_kernel(PrefillParams p) {
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-#define FLINT_ISSUE(kt_, stage_)                                                        \
-    do {                                                                                \
-        unsigned char* sa_ = smem + (stage_) * kStageBytes;                             \
-        unsigned char* sb_ = sa_ + PBM * PBK * 2;                                       \
-        const int k0_ = (kt_) * PBK;                                                    \
-        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                \
-            __builtin_amdgcn_global_load_lds(asrc[i_] + k0_, sa_ + (64 * i_ + 8 * wave) * 128, \
-                                             16, 0, 0);                                 \
-        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                \
-            __builtin_amdgcn_global_load_lds(bsrc[i_] + k0_, sb_ + (64 * i_ + 8 * wave) * 128, \
-                                             16, 0, 0);                                 \
+#define FLINT_ISSUE(s_)                                                                               \
+    do {                                                                                              \
+        unsigned char* st_ = lds + ((s_) & (kNStage - 1)) * kStageBytes;                              \
+        const int k0_ = (s_) * PBK;                                                                   \
+        _Pragma("unroll") for (int j_ = 0; j_ < 2; ++j_) {                                            \
+            __builtin_amdgcn_global_load_lds(asrc[j_] + k0_, st_ + (32 * wave + 16 * j_) * 64, 16, 0, 0); \
+            __builtin_amdgcn_global_load_lds(bsrc[j_] + k0_, st_ + PBM * PBK * 2 + (32 * wave + 16 * j_) * 64, \
+                                             16, 0, 0);                                               \
+        }                                                                                             \
     } while (0)
 
         const int nk = K / PBK;
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // previous tile's stores retired (vmcnt 0)
-        __syncthreads();  // the previous tile's readers are done with both stages
-        FLINT_ISSUE(0, 0);
-        if (nk > 1) FLINT_ISSUE(1, 1);
-        for (int kt = 0; kt < nk; ++kt) {
-            // stage kt % 2 has landed once at most the next stage's 8 loads are pending
-            // (gfx9 s_waitcnt: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8])
-            if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(0x0F78 /* vmcnt(8) */);
-            else __builtin_amdgcn_s_waitcnt(0x0F70 /* vmcnt(0) */);
-            __syncthreads();
-            const unsigned char* sa = smem + (kt & 1) * kStageBytes;
-            const unsigned char* sb = sa + PBM * PBK * 2;
-            // fragments of both k steps first, then 128 MFMAs (rows past the
-            // tile's end hold a copy of its first row and are never stored)
-            uint4 fa[2][8], fb[2][4];
+        __syncthreads();  // the previous tile's epilogue is done with LDS (and its stores retired)
+        // prologue: stages 0..2 in flight, then every wave's stage 0 landed
+        FLINT_ISSUE(0);
+        if (nk > 1) FLINT_ISSUE(1);
+        if (nk > 2) FLINT_ISSUE(2);
+        if (nk > 2) __builtin_amdgcn_s_waitcnt(0x0F78);       // vmcnt(8)
+        else if (nk > 1) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+        else __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
+        phase_barrier();
+        if (wm == 1) phase_barrier();  // group 1 runs one phase behind
+        for (int s = 0; s < nk; ++s) {
+            // ---- memory phase of stage s: refill the buffer of stage s - 1 (read by both
+            // groups by now) with stage s + 3, make sure this wave's part of stage s + 1
+            // has landed (the other group reads it right after the next barrier), read
+            // this stage's fragments ----
+            if (s + 3 < nk) FLINT_ISSUE(s + 3);
+            const int ahead = min(s + 3, nk - 1) - s;  // own stages in flight after s
+            if (ahead >= 3) __builtin_amdgcn_s_waitcnt(0x0F78);       // vmcnt(8)
+            else if (ahead == 2) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+            else __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0)
+            const uint32_t st = lds0 + (s & (kNStage - 1)) * kStageBytes;
+            uint4 fa[8], fb[4];
+            read_frags(st + a_rd, st + b_rd, fa, fb);
+            phase_barrier();
+            // ---- compute phase of stage s ----
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const int c = ks * 4 + q;
+            for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    fb[ks][i] = *reinterpret_cast<const uint4*>(sb + swz(64 * wn + 16 * i + row16, c));
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    fa[ks][i] = *reinterpret_cast<const uint4*>(sa + swz(128 * wm + 16 * i + row16, c));
-            }
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int mi = 0; mi < 8; ++mi)
-#pragma unroll
-                    for (int ni = 0; ni < 4; ++ni)
-                        acc[mi][ni] = mfma16x16x32(fa[ks][mi], fb[ks][ni], acc[mi][ni]);
-            if (kt + 2 < nk) {
-                __syncthreads();  // everyone has read stage kt % 2
-                FLINT_ISSUE(kt + 2, kt & 1);
-            }
+                for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma16x16x32(fa[mi], fb[ni], acc[mi][ni]);
+            phase_barrier();
         }
+        if (wm == 0) phase_barrier();  // matches group 1's extra barrier
 #undef FLINT_ISSUE
 
         // ---- epilogue: results go through LDS (free after the K loop) so that
         // global stores are whole 16-byte chunks of output rows ----
-        __syncthreads();  // all waves are done reading the last stage
+        __syncthreads();  // all waves are done with the stages
         float wrow[8][4];  // routing weight of each of this lane's output rows (down)
         if (MODE == MODE_DOWN) {
-            float* s_w = reinterpret_cast<float*>(smem);
+            float* s_w = reinterpret_cast<float*>(lds);
             if (tid < PBM) {  // one row per thread
                 const int m = tid;
                 s_w[m] = (is_shared || m >= rows) ? 1.f : p.ws.sorted_wt[g.y + m0 + m];
@@ -193,7 +246,8 @@ void prefill_gemm_kernel(PrefillParams p) {
         }
         // this wave's output sub-tile in LDS: 128 rows x OC bf16, row stride OC*2 bytes
         constexpr int OC = (MODE == MODE_GATEUP) ? 32 : 64;
-        uint16_t* so = reinterpret_cast<uint16_t*>(smem + wave * (128 * OC * 2));
+        static_assert(8 * 128 * OC * 2 <= kLdsBytes, "epilogue staging fits the stages");
+        uint16_t* so = reinterpret_cast<uint16_t*>(lds + wave * (128 * OC * 2));
 #pragma unroll
         for (int mi = 0; mi < 8; ++mi) {
 #pragma unroll
@@ -257,15 +311,8 @@ bool prefill_ok(const Dims& dm) {
 
 template <int MODE>
 static hipError_t launch_prefill(const PrefillParams& p, int n_cu, hipStream_t s) {
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_gemm_kernel<MODE>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
     const int grid = ((n_cu > 0 ? n_cu : 256) + 7) / 8 * 8;
-    hipLaunchKernelGGL(prefill_gemm_kernel<MODE>, dim3(grid), dim3(kThreads), kLdsBytes, s, p);
+    hipLaunchKernelGGL(prefill_gemm_kernel<MODE>, dim3(grid), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

@@ -126,6 +126,14 @@ __device__ __forceinline__ int ld_agent(const int* p) {
 }
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
 
+// Workgroup barrier that leaves pending global loads in flight.  A
+// __syncthreads() carries a workgroup fence, for which the compiler waits for
+// every outstanding vector-memory load (vmcnt 0) before the barrier, which
+// would drain a prefetch pipeline at each step.  Callers wait explicitly
+// (s_waitcnt) for the data they hand over; the memory clobber keeps the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void barrier_keep_loads() { asm volatile("s_barrier" ::: "memory"); }
+
 // All threads: finish this workgroup's hand-off stores, then thread 0 takes a
 // ticket; returns true (in every thread) for the workgroup that arrives last.
 __device__ __forceinline__ bool last_arrival(int* counter, int n_arrivals, int* s_flag) {

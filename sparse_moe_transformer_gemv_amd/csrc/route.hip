@@ -488,8 +488,8 @@ __device__ __forceinline__ float key_value(uint32_t key) {
 // round takes the wave maximum key; the lowest lane holding it, and inside
 // that lane the lowest slot, give the lowest expert index among equal logits.
 // The chosen logits are wave-uniform, so their softmax is formed directly.
-// Results go to global memory (device-coherent) and to LDS copies indexed
-// from t0.
+// Results go to global memory (device-coherent) and, when s_sel is not null,
+// to LDS copies indexed from t0.
 template <int U>
 __device__ __forceinline__ void wave_topk_tokens(const float* __restrict__ logits, int t0, int T, int E, int k,
                                                  int wave, int lane, int* __restrict__ sel, float* __restrict__ wts,
@@ -548,8 +548,10 @@ __device__ __forceinline__ void wave_topk_tokens(const float* __restrict__ logit
                 const float w = pj[j] / sum;
                 st_agent(sel + t * k + j, ce[u][j]);
                 st_agent(wts + t * k + j, w);
-                s_sel[(t - t0) * k + j] = ce[u][j];
-                s_wt[(t - t0) * k + j] = w;
+                if (s_sel != nullptr) {
+                    s_sel[(t - t0) * k + j] = ce[u][j];
+                    s_wt[(t - t0) * k + j] = w;
+                }
             }
     }
 }
@@ -698,17 +700,16 @@ hipError_t launch_router_logits(const LayerArgs& a, const Workspace& w, hipStrea
     return hipGetLastError();
 }
 
-__global__ __launch_bounds__(256) void topk_kernel(RouteDecodeParams p) {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t < p.T)
-        wave_topk_token<false>(p.ws.logits + (size_t)t * p.E, p.E, p.k, lane,
-                               p.ws.sel + (size_t)t * p.k, p.ws.wts + (size_t)t * p.k);
+// Prefill top-k: 8 waves per block, two tokens per wave (16 per block).
+__global__ __launch_bounds__(512) void topk_kernel(RouteDecodeParams p) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    wave_topk_tokens<2>(p.ws.logits, blockIdx.x * 16, p.T, p.E, p.k, wave, lane, p.ws.sel, p.ws.wts, nullptr,
+                        nullptr);
 }
 
 hipError_t launch_topk(const LayerArgs& a, const Workspace& w, hipStream_t s) {
     RouteDecodeParams p{a.x, a.wr, a.bias, a.dm.T, a.dm.d, a.dm.E, a.dm.k, a.dm.fs > 0, w};
-    hipLaunchKernelGGL(topk_kernel, dim3((a.dm.T + 3) / 4), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(topk_kernel, dim3((a.dm.T + 15) / 16), dim3(512), 0, s, p);
     return hipGetLastError();
 }
 
