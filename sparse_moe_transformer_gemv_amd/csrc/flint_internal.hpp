@@ -28,6 +28,7 @@ struct Workspace {
     int* pair_pos;       // [k*Tm] inverse: slot of pair id
     float* rpart;        // [d/256][64][E] split-K router partial logits (decode, T <= 64)
     int* rcount;         // [4 ceil(E/16) + 8] router tickets, zero between launches
+    uint16_t* w3;        // [3][E][d] router split into exact hi, mid, lo bf16 planes (prefill)
     float* sorted_wt;    // [k*Tm] combine weight of each sorted pair (wts[sorted_pair[i]])
     int4* groups;        // [E+1] active groups {expert (E = shared), first sorted index, rows, first slot}
     int* n_groups;       // [1]
@@ -70,6 +71,8 @@ bool route_mfma_ok(const Dims& dm);
 bool prefill_ok(const Dims& dm);
 hipError_t launch_router_logits(const LayerArgs& a, const Workspace& w, hipStream_t s);
 hipError_t launch_topk(const LayerArgs& a, const Workspace& w, hipStream_t s);
+bool router_gemm_ok(const Dims& dm);
+hipError_t launch_router_gemm(const LayerArgs& a, const Workspace& w, hipStream_t s);
 hipError_t launch_sort(const LayerArgs& a, const Workspace& w, int bm, hipStream_t s);
 hipError_t launch_gateup_decode(const LayerArgs& a, const Workspace& w, hipStream_t s);
 hipError_t launch_down_decode(const LayerArgs& a, const Workspace& w, hipStream_t s);

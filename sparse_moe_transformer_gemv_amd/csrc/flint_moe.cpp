@@ -140,6 +140,7 @@ size_t carve(const flint_moe_config& c, char* base, Workspace* w) {
     w->sorted_wt = static_cast<float*>(take(Tm * k * 4));
     w->rpart = static_cast<float*>(take((size_t)(c.d_model / 256 > 0 ? c.d_model / 256 : 1) * 64 * E * 4));
     w->rcount = static_cast<int*>(take((4 * ((E + 15) / 16) + 8) * 4));
+    w->w3 = static_cast<uint16_t*>(take(3 * E * (size_t)c.d_model * 2));
     w->groups = static_cast<int4*>(take((E + 1) * 16));
     w->n_groups = static_cast<int*>(take(4));
     w->tiles = static_cast<int2*>(take(max_tiles * 8));
@@ -328,8 +329,9 @@ flint_status flint_moe_forward(flint_moe_t h, int32_t T, const void* hidden, con
             Timer tm(h, FLINT_KERNEL_ROUTE, stream);
             // logits (matrix cores when the shape allows), then top-k with one
             // wavefront per token
-            e = route_mfma_ok(a.dm) ? launch_route_mfma(a, h->ws, false, stream)
-                                    : launch_router_logits(a, h->ws, stream);
+            e = router_gemm_ok(a.dm)  ? launch_router_gemm(a, h->ws, stream)
+                : route_mfma_ok(a.dm) ? launch_route_mfma(a, h->ws, false, stream)
+                                      : launch_router_logits(a, h->ws, stream);
             if (e == hipSuccess) e = launch_topk(a, h->ws, stream);
         }
         if (e != hipSuccess) return hip_fail(e, "route kernel");

@@ -700,6 +700,174 @@ hipError_t launch_router_logits(const LayerArgs& a, const Workspace& w, hipStrea
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Prefill router logits as a tiled GEMM.  The fp32 router is first split
+// exactly into three bf16 planes (hi + mid + lo, once per forward), so bf16
+// MFMAs against the bf16 activations reproduce the fp32 products; the three
+// planes are accumulated in fp32 in the same k order.  Tiles of 64 tokens x
+// 64 experts are staged through LDS with coalesced row loads (an MFMA operand
+// loaded straight from global memory would put 16 different rows in each
+// load instruction, which the vector L1 serves one lane at a time).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ wr, uint16_t* __restrict__ w3,
+                                                           size_t n) {
+    const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (i >= n) return;
+    const float4 a = *reinterpret_cast<const float4*>(wr + i);
+    const float4 b = *reinterpret_cast<const float4*>(wr + i + 4);
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint4 hi, mid, lo;
+    split3_bf16(v, hi, mid, lo);
+    *reinterpret_cast<uint4*>(w3 + i) = hi;
+    *reinterpret_cast<uint4*>(w3 + n + i) = mid;
+    *reinterpret_cast<uint4*>(w3 + 2 * n + i) = lo;
+}
+
+struct RouterGemmParams {
+    const uint16_t* x;
+    const uint16_t* w3;
+    const float* bias;
+    float* logits;
+    int T, d, E;
+};
+
+constexpr int kRgBN = 64, kRgBK = 64;
+constexpr int kRgPlaneBytes = kRgBN * kRgBK * 2;  // 8 KiB per router plane per stage
+template <int BM>
+struct RgTile {
+    static constexpr int ABytes = BM * kRgBK * 2;
+    static constexpr int StageBytes = ABytes + 3 * kRgPlaneBytes;
+    static constexpr int AChunks = BM / 32;  // 16-byte A chunks per thread per stage (256 threads)
+    static constexpr int Chunks = AChunks + 6;
+    static constexpr int MI = BM / 32;       // 16-row A fragments per wave (2 waves along M)
+};
+
+// byte offset of 16-byte chunk c of 128-byte LDS row r (chunks XOR-swizzled by row)
+__device__ __forceinline__ int rg_swz(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+
+// One K step: refill rega with stage s + 2 (clamped: unconditional loads keep
+// the staging registers in registers), multiply LDS stage s, move regb (stage
+// s + 1) into the other LDS buffer, which nobody reads until after the barrier.
+template <int BM>
+__device__ __forceinline__ void router_gemm_step(int s, int nk, const uint16_t* const (&src)[RgTile<BM>::Chunks],
+                                                 const int (&dst)[RgTile<BM>::Chunks], unsigned char* lds, int wm,
+                                                 int wn, int row16, int q, u32x4_t (&rega)[RgTile<BM>::Chunks],
+                                                 const u32x4_t (&regb)[RgTile<BM>::Chunks],
+                                                 floatx4_t (&acc)[RgTile<BM>::MI][2]) {
+    using TL = RgTile<BM>;
+    const int s2 = s + 2 < nk ? s + 2 : nk - 1;
+#pragma unroll
+    for (int i = 0; i < TL::Chunks; ++i) rega[i] = *reinterpret_cast<const u32x4_t*>(src[i] + s2 * kRgBK);
+    __builtin_amdgcn_sched_barrier(0);  // these loads go out before anything else in the step
+    const unsigned char* buf = lds + (s & 1) * TL::StageBytes;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const int c = 4 * ks + q;
+        uint4 a[TL::MI], b[3][2];
+#pragma unroll
+        for (int i = 0; i < TL::MI; ++i)
+            a[i] = *reinterpret_cast<const uint4*>(buf + rg_swz((BM / 2) * wm + 16 * i + row16, c));
+#pragma unroll
+        for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                b[pl][j] = *reinterpret_cast<const uint4*>(buf + TL::ABytes + pl * kRgPlaneBytes +
+                                                           rg_swz(32 * wn + 16 * j + row16, c));
+#pragma unroll
+        for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int pl = 0; pl < 3; ++pl) acc[i][j] = mfma16x16x32(a[i], b[pl][j], acc[i][j]);
+    }
+    unsigned char* nbuf = lds + ((s + 1) & 1) * TL::StageBytes;
+#pragma unroll
+    for (int i = 0; i < TL::Chunks; ++i) *reinterpret_cast<u32x4_t*>(nbuf + dst[i]) = regb[i];
+    __syncthreads();
+}
+
+// Block = BM tokens x 64 experts, 4 waves as 2 (tokens) x 2 (32 experts).
+template <int BM>
+__global__ __launch_bounds__(256) void router_gemm_kernel(RouterGemmParams p) {
+    using TL = RgTile<BM>;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * TL::StageBytes];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int row16 = lane & 15, q = lane >> 4;
+    const int t0 = blockIdx.x * BM, e0 = blockIdx.y * kRgBN;
+    const int d = p.d;
+    const size_t plane = (size_t)p.E * d;
+    // this thread's chunks of a stage: AChunks of A (x rows), 2 of each router plane;
+    // chunk id c = tid + 256 i -> row c >> 3, 16-byte column c & 7 (8 threads per row)
+    const uint16_t* src[TL::Chunks];
+    int dst[TL::Chunks];
+#pragma unroll
+    for (int i = 0; i < TL::Chunks; ++i) {
+        if (i < TL::AChunks) {
+            const int c = tid + 256 * i;
+            const int r = c >> 3, col = c & 7;
+            const int t = t0 + r < p.T ? t0 + r : p.T - 1;  // rows past T repeat a valid row; never stored
+            src[i] = p.x + (size_t)t * d + 8 * col;
+            dst[i] = rg_swz(r, col);
+        } else {
+            const int ib = i - TL::AChunks;
+            const int c = tid + 256 * (ib & 1);
+            const int r = c >> 3, col = c & 7;
+            const int pl = ib >> 1;
+            const int e = e0 + r < p.E ? e0 + r : p.E - 1;
+            src[i] = p.w3 + pl * plane + (size_t)e * d + 8 * col;
+            dst[i] = TL::ABytes + pl * kRgPlaneBytes + rg_swz(r, col);
+        }
+    }
+    // two register stages in flight ahead of the LDS stage being multiplied
+    const int nk = d / kRgBK;
+    u32x4_t st0[TL::Chunks], st1[TL::Chunks];
+#pragma unroll
+    for (int i = 0; i < TL::Chunks; ++i) st0[i] = *reinterpret_cast<const u32x4_t*>(src[i]);
+#pragma unroll
+    for (int i = 0; i < TL::Chunks; ++i) st1[i] = *reinterpret_cast<const u32x4_t*>(src[i] + (nk > 1 ? kRgBK : 0));
+#pragma unroll
+    for (int i = 0; i < TL::Chunks; ++i) *reinterpret_cast<u32x4_t*>(lds + dst[i]) = st0[i];
+    __syncthreads();
+    floatx4_t acc[TL::MI][2];
+#pragma unroll
+    for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < nk; s += 2) {  // nk is even
+        router_gemm_step<BM>(s, nk, src, dst, lds, wm, wn, row16, q, st0, st1, acc);
+        router_gemm_step<BM>(s + 1, nk, src, dst, lds, wm, wn, row16, q, st1, st0, acc);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int e = e0 + 32 * wn + 16 * j + row16;
+        if (e >= p.E) continue;
+        const float b = p.bias ? p.bias[e] : 0.f;
+#pragma unroll
+        for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = t0 + (BM / 2) * wm + 16 * i + 4 * q + r;
+                if (t < p.T) p.logits[(size_t)t * p.E + e] = acc[i][j][r] + b;
+            }
+    }
+}
+
+constexpr int kRgBM = 64;  // tokens per block (32 doubles the router bytes per token and is slower)
+
+bool router_gemm_ok(const Dims& dm) {
+    return dm.act == DT_BF16 && dm.d % (2 * kRgBK) == 0 && (size_t)3 * dm.E * dm.d < ((size_t)1 << 31);
+}
+
+hipError_t launch_router_gemm(const LayerArgs& a, const Workspace& w, hipStream_t s) {
+    const size_t n = (size_t)a.dm.E * a.dm.d;  // d % 64 == 0, so n % 8 == 0
+    hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)((n / 8 + 255) / 256)), dim3(256), 0, s, a.wr, w.w3, n);
+    RouterGemmParams p{static_cast<const uint16_t*>(a.x), w.w3, a.bias, w.logits, a.dm.T, a.dm.d, a.dm.E};
+    dim3 grid((a.dm.T + kRgBM - 1) / kRgBM, (a.dm.E + kRgBN - 1) / kRgBN);
+    hipLaunchKernelGGL(router_gemm_kernel<kRgBM>, grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
 // Prefill top-k: 8 waves per block, two tokens per wave (16 per block).
 __global__ __launch_bounds__(512) void topk_kernel(RouteDecodeParams p) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
