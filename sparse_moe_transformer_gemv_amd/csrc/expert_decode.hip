@@ -496,41 +496,102 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// NVFP4 on the matrix cores.  Each lane loads 16 bytes of codes (32 elements)
-// of its weight row for a group of four 32-wide MFMA k steps, plus the two
-// E4M3 scales of those elements.  The k order inside a group is permuted the
-// same way for activations and weights (lane quarter q holds elements
-// 32 q .. 32 q + 31 of the group, 8 per step), which leaves every dot product
-// unchanged.  A weight is E2M1 x E4M3 (at most 6 significant bits, so exact
-// in bf16): the hardware converts a pair of codes to fp32, the block scale is
-// applied in fp32, and the pair is packed back to bf16 without rounding.  The
-// tensor scale multiplies the finished sums.
+// NVFP4 on the matrix cores, in f16.  A weight is E2M1 x E4M3 (at most 6
+// significant bits, within 2^-10 .. 2688 in magnitude), so it is exact in f16:
+// the hardware convert of a pair of codes applies the power-of-two part of the
+// block scale exactly, and one packed f16 multiply applies its 3-bit mantissa
+// (1 VALU per weight).  Activations enter as f16 scaled by a per-token power of
+// two (exact for every value above the f16 normal range's floor), the
+// hidden state h as two f16 parts (hi + lo, 22 significant bits).  The tensor
+// scale and the power-of-two factors multiply the finished fp32 sums.
+//
+// Lane quarter q of a 128-wide k group holds elements 32 q .. 32 q + 31, eight
+// per MFMA step: the same permutation of k for activations and weights, which
+// leaves every dot product unchanged.
 // ---------------------------------------------------------------------------
-typedef __attribute__((ext_vector_type(2))) float floatx2_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 half8_t;
 
-// Upper halves of two fp32 values as a bf16 pair: exact when both values are
-// representable in bf16, as every E2M1 x E4M3 product is.
-__device__ __forceinline__ uint32_t hi16_pair(float lo, float hi) {
-    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+__device__ __forceinline__ floatx4_t mfma16x16x32_f16(uint4 a, uint4 b, floatx4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c,
+                                                  0, 0, 0);
 }
-
-// Two codes of byte B of w, decoded and multiplied by the block scale, as bf16.
-#define FLINT_FP4_PAIR(w, B, sc)                                                   \
-    ({                                                                              \
-        const floatx2_t v_ = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((w), 1.0f, B); \
-        hi16_pair(v_.x * (sc), v_.y * (sc));                                        \
-    })
-
-// Eight E2M1 codes (one 32-bit word, even element in the low nibble) times
-// their block scale, as one MFMA operand of 8 bf16.
-__device__ __forceinline__ uint4 fp4x8_to_bf16(uint32_t w, float sc) {
-    return make_uint4(FLINT_FP4_PAIR(w, 0, sc), FLINT_FP4_PAIR(w, 1, sc), FLINT_FP4_PAIR(w, 2, sc),
-                      FLINT_FP4_PAIR(w, 3, sc));
-}
-#undef FLINT_FP4_PAIR
-
 __device__ __forceinline__ uint32_t u4_word(const uint4& v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// An E4M3 block scale split into its power-of-two part (fp32, for the
+// convert's scale operand) and its mantissa in [1, 2) (f16 pair).
+struct Fp4Scale {
+    float p2;
+    half2_t m;
+};
+__device__ __forceinline__ Fp4Scale fp4_scale(float s) {
+    const uint32_t b = __float_as_uint(s);
+    const float m = __uint_as_float((b & 0x007FFFFFu) | 0x3F800000u);
+    const _Float16 mh = (_Float16)m;  // exact: at most 3 fraction bits
+    return Fp4Scale{__uint_as_float(b & 0xFF800000u), half2_t{mh, mh}};
+}
+
+#define FLINT_FP4_F16_PAIR(w, B, sc)                                                               \
+    ({                                                                                              \
+        const half2_t v_ = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4((w), (sc).p2, B) * (sc).m;      \
+        __builtin_bit_cast(uint32_t, v_);                                                           \
+    })
+// Eight E2M1 codes (one word, even element in the low nibble) times their
+// block scale, as one f16 MFMA operand.
+__device__ __forceinline__ uint4 fp4x8_to_f16(uint32_t w, Fp4Scale sc) {
+    return make_uint4(FLINT_FP4_F16_PAIR(w, 0, sc), FLINT_FP4_F16_PAIR(w, 1, sc), FLINT_FP4_F16_PAIR(w, 2, sc),
+                      FLINT_FP4_F16_PAIR(w, 3, sc));
+}
+#undef FLINT_FP4_F16_PAIR
+
+// h of the NVFP4 path: two f16 planes (hi, lo) of (k+1) T rows each, holding
+// h * 2^-8 (headroom above the f16 range for large activations).
+constexpr float kHScale = 1.0f / 256.0f;
+
+// Activations to f16 for the NVFP4 kernels: per token, x * 2^-e with e chosen
+// so that the largest magnitude lands in [2^14, 2^15); xscale = 2^e.
+__global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ x16,
+                                                       float* __restrict__ xscale, int d) {
+    __shared__ float s_max[4];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    const uint16_t* xr = x + (size_t)t * d;
+    float m = 0.f;
+    for (int k = tid * 8; k < d; k += 256 * 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(xr + k);
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x))), fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y)))));
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))), fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w)))));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if ((tid & 63) == 0) s_max[tid >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+    // exponent of m (m > 0 and finite); e = exp - 14 puts m in [2^14, 2^15)
+    int e = 0;
+    if (m > 0.f && m <= 3.4e38f) e = (int)((__float_as_uint(m) >> 23) & 0xFF) - 127 - 14;
+    e = e < -100 ? -100 : (e > 100 ? 100 : e);
+    const float inv = ldexpf(1.f, -e);
+    if (tid == 0) xscale[t] = ldexpf(1.f, e);
+    uint16_t* yr = x16 + (size_t)t * d;
+    for (int k = tid * 8; k < d; k += 256 * 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(xr + k);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const half2_t hv = {(_Float16)(bf16_lo(w[i]) * inv), (_Float16)(bf16_hi(w[i]) * inv)};
+            o[i] = __builtin_bit_cast(uint32_t, hv);
+        }
+        *reinterpret_cast<uint4*>(yr + k) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+hipError_t launch_x_to_f16(const LayerArgs& a, const Workspace& w, hipStream_t s) {
+    hipLaunchKernelGGL(x_to_f16_kernel, dim3(a.dm.T), dim3(256), 0, s, static_cast<const uint16_t*>(a.x), w.x16,
+                       w.xscale, a.dm.d);
+    return hipGetLastError();
 }
 
 // One 16-token tile of an NVFP4 gate/up block (see gateup_fp4_kernel).  sp is
@@ -539,7 +600,7 @@ template <int NG>
 __device__ __forceinline__ void gateup_fp4_tile(const ExpertParams& p, const int4& g, bool is_shared, int r0,
                                                 int sp, __amdgpu_buffer_rsrc_t xv, int kl, uint4 (&cw)[2][NG],
                                                 uint16_t (&sw)[2][NG], float tsg, float tsu, int j0,
-                                                float (&s_part)[4][2][256]) {
+                                                float (&s_part)[4][2][256], float (&s_xs)[16]) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, q = lane >> 4;
     const int d = p.dm.d;
@@ -551,10 +612,11 @@ __device__ __forceinline__ void gateup_fp4_tile(const ExpertParams& p, const int
     for (int gg = 0; gg < NG; ++gg)
 #pragma unroll
         for (int st = 0; st < 4; ++st) a[gg][st] = buffer_load16(xv, xo + (128 * gg + 8 * st) * 2);
+    const float xs = p.ws.xscale[m < g.z ? tok : 0];
     __builtin_amdgcn_sched_barrier(0);
     // Decode the weights here, after the activation loads are issued: an empty
     // asm that claims to change the codes keeps the decode from being hoisted
-    // ahead of those loads or out of the token loop (where its bf16 operands
+    // ahead of those loads or out of the token loop (where its f16 operands
     // would cost 32 NG more registers per lane than the packed codes).
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -562,15 +624,18 @@ __device__ __forceinline__ void gateup_fp4_tile(const ExpertParams& p, const int
         for (int gg = 0; gg < NG; ++gg)
             asm volatile("" : "+v"(cw[t][gg].x), "+v"(cw[t][gg].y), "+v"(cw[t][gg].z), "+v"(cw[t][gg].w),
                          "+v"(sw[t][gg]));
+    if (wave == 0 && q == 0) s_xs[row] = xs;
     floatx4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) {
-        const float g0 = __builtin_amdgcn_cvt_f32_fp8(sw[0][gg], 0), g1 = __builtin_amdgcn_cvt_f32_fp8(sw[0][gg], 1);
-        const float u0 = __builtin_amdgcn_cvt_f32_fp8(sw[1][gg], 0), u1 = __builtin_amdgcn_cvt_f32_fp8(sw[1][gg], 1);
+        const Fp4Scale g0 = fp4_scale(__builtin_amdgcn_cvt_f32_fp8(sw[0][gg], 0));
+        const Fp4Scale g1 = fp4_scale(__builtin_amdgcn_cvt_f32_fp8(sw[0][gg], 1));
+        const Fp4Scale u0 = fp4_scale(__builtin_amdgcn_cvt_f32_fp8(sw[1][gg], 0));
+        const Fp4Scale u1 = fp4_scale(__builtin_amdgcn_cvt_f32_fp8(sw[1][gg], 1));
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-            acc0 = mfma16x16x32(a[gg][st], fp4x8_to_bf16(u4_word(cw[0][gg], st), st < 2 ? g0 : g1), acc0);
-            acc1 = mfma16x16x32(a[gg][st], fp4x8_to_bf16(u4_word(cw[1][gg], st), st < 2 ? u0 : u1), acc1);
+            acc0 = mfma16x16x32_f16(a[gg][st], fp4x8_to_f16(u4_word(cw[0][gg], st), st < 2 ? g0 : g1), acc0);
+            acc1 = mfma16x16x32_f16(a[gg][st], fp4x8_to_f16(u4_word(cw[1][gg], st), st < 2 ? u0 : u1), acc1);
         }
     }
 #pragma unroll
@@ -581,22 +646,31 @@ __device__ __forceinline__ void gateup_fp4_tile(const ExpertParams& p, const int
     __syncthreads();
     const int mm = tid >> 4, n = tid & 15;
     if (r0 + mm < g.z) {
-        const float gv = tsg * (((s_part[0][0][tid] + s_part[1][0][tid]) + s_part[2][0][tid]) + s_part[3][0][tid]);
-        const float uv = tsu * (((s_part[0][1][tid] + s_part[1][1][tid]) + s_part[2][1][tid]) + s_part[3][1][tid]);
-        static_cast<float*>(p.ws.h)[(size_t)(g.w + r0 + mm) * p.hstride + j0 + n] = silu_f32(gv) * uv;
+        const float xsm = s_xs[mm];
+        const float gv = tsg * xsm * (((s_part[0][0][tid] + s_part[1][0][tid]) + s_part[2][0][tid]) + s_part[3][0][tid]);
+        const float uv = tsu * xsm * (((s_part[0][1][tid] + s_part[1][1][tid]) + s_part[2][1][tid]) + s_part[3][1][tid]);
+        const float hv = silu_f32(gv) * uv * kHScale;
+        const _Float16 hi = (_Float16)hv;
+        const _Float16 lo = (_Float16)(hv - (float)hi);
+        uint16_t* h16 = static_cast<uint16_t*>(p.ws.h);
+        const size_t plane = (size_t)(p.dm.k + 1) * p.dm.T * p.hstride;
+        const size_t o = (size_t)(g.w + r0 + mm) * p.hstride + j0 + n;
+        h16[o] = __builtin_bit_cast(uint16_t, hi);
+        h16[plane + o] = __builtin_bit_cast(uint16_t, lo);
     }
     __syncthreads();
 }
 
-// gate/up + SwiGLU, NVFP4 weights, bf16 activations.  Block = (group, 16
-// features): MFMA tile 0 holds their gate rows and tile 1 their up rows, so
-// the two results of one feature land in the same lane.  K is split over the
-// 4 waves, NG groups of 128 per wave (d = 512 NG).  The first token tile is
-// peeled off the loop so that the weights and its activations are all in
-// flight before the first wait.
+// gate/up + SwiGLU, NVFP4 weights: block = (group, 16 features): MFMA tile 0
+// holds their gate rows and tile 1 their up rows, so the two results of one
+// feature land in the same lane.  K is split over the 4 waves, NG groups of
+// 128 per wave (d = 512 NG).  The first token tile is peeled off the loop so
+// that the weights and its activations are all in flight before the first
+// wait.
 template <int NG>
 __global__ __launch_bounds__(256) void gateup_fp4_kernel(ExpertParams p) {
     __shared__ float s_part[4][2][256];
+    __shared__ float s_xs[16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, q = lane >> 4;
     const int d = p.dm.d;
@@ -629,34 +703,39 @@ __global__ __launch_bounds__(256) void gateup_fp4_kernel(ExpertParams p) {
         }
     }
     const float tsg = wp.ts[e * 3 + 0], tsu = wp.ts[e * 3 + 1];
-    const __amdgpu_buffer_rsrc_t xv = buffer_view(p.x, (uint32_t)p.dm.T * d * 2);
-    gateup_fp4_tile<NG>(p, g, is_shared, 0, sp, xv, kl, cw, sw, tsg, tsu, j0, s_part);
+    const __amdgpu_buffer_rsrc_t xv = buffer_view(p.ws.x16, (uint32_t)p.dm.T * d * 2);
+    gateup_fp4_tile<NG>(p, g, is_shared, 0, sp, xv, kl, cw, sw, tsg, tsu, j0, s_part, s_xs);
     for (int r0 = 16; r0 < g.z; r0 += 16) {
         const int m = r0 + row;
         const int spn = p.ws.sorted_pair[g.y + (m < g.z ? m : g.z - 1)];
-        gateup_fp4_tile<NG>(p, g, is_shared, r0, spn, xv, kl, cw, sw, tsg, tsu, j0, s_part);
+        gateup_fp4_tile<NG>(p, g, is_shared, r0, spn, xv, kl, cw, sw, tsg, tsu, j0, s_part, s_xs);
     }
 }
 
-// One 16-token tile of an NVFP4 down block (see down_fp4_kernel); rw is the
-// routing weight of the token row this thread stores.
+// One 16-token tile of an NVFP4 down block (see down_fp4_kernel); ws is the
+// routing weight of the token row this thread stores, times the tensor scale
+// and the inverse of the h scale.
 template <int NT, int NGMAX>
 __device__ __forceinline__ void down_fp4_tile(const ExpertParams& p, const int4& g, int r0, int ng, int kl, int n0,
-                                              __amdgpu_buffer_rsrc_t hv, uint4 (&cw)[NT][NGMAX],
-                                              uint16_t (&sw)[NT][NGMAX], float ws, float (&s_part)[4][NT][256]) {
+                                              __amdgpu_buffer_rsrc_t hv_hi, __amdgpu_buffer_rsrc_t hv_lo,
+                                              uint4 (&cw)[NT][NGMAX], uint16_t (&sw)[NT][NGMAX], float ws,
+                                              float (&s_part)[4][NT][256]) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, q = lane >> 4;
     const int m = r0 + row;
-    const uint32_t ho = m < g.z ? (uint32_t)(m * p.hstride + kl) * 4 : kOffNone;
+    const uint32_t ho = m < g.z ? (uint32_t)(m * p.hstride + kl) * 2 : kOffNone;
     floatx4_t acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int gg = 0; gg < NGMAX; ++gg) {
         if (gg >= ng) break;
-        uint4 hr[8];
+        uint4 hhi[4], hlo[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) hr[i] = buffer_load16(hv, ho + (128 * gg + 4 * i) * 4);
+        for (int st = 0; st < 4; ++st) {
+            hhi[st] = buffer_load16(hv_hi, ho + (128 * gg + 8 * st) * 2);
+            hlo[st] = buffer_load16(hv_lo, ho + (128 * gg + 8 * st) * 2);
+        }
         __builtin_amdgcn_sched_barrier(0);
         // decode after the h loads are issued, and inside the token loop
         // (see gateup_fp4_tile)
@@ -664,26 +743,19 @@ __device__ __forceinline__ void down_fp4_tile(const ExpertParams& p, const int4&
         for (int t = 0; t < NT; ++t)
             asm volatile("" : "+v"(cw[t][gg].x), "+v"(cw[t][gg].y), "+v"(cw[t][gg].z), "+v"(cw[t][gg].w),
                          "+v"(sw[t][gg]));
-        float sc[NT][2];
+        Fp4Scale sc[NT][2];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            sc[t][0] = __builtin_amdgcn_cvt_f32_fp8(sw[t][gg], 0);
-            sc[t][1] = __builtin_amdgcn_cvt_f32_fp8(sw[t][gg], 1);
+            sc[t][0] = fp4_scale(__builtin_amdgcn_cvt_f32_fp8(sw[t][gg], 0));
+            sc[t][1] = fp4_scale(__builtin_amdgcn_cvt_f32_fp8(sw[t][gg], 1));
         }
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-            const uint4 h0 = hr[2 * st], h1 = hr[2 * st + 1];
-            const float v[8] = {__uint_as_float(h0.x), __uint_as_float(h0.y), __uint_as_float(h0.z),
-                                __uint_as_float(h0.w), __uint_as_float(h1.x), __uint_as_float(h1.y),
-                                __uint_as_float(h1.z), __uint_as_float(h1.w)};
-            uint4 ahi, amid, alo;
-            split3_bf16(v, ahi, amid, alo);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                const uint4 bw = fp4x8_to_bf16(u4_word(cw[t][gg], st), sc[t][st >> 1]);
-                acc[t] = mfma16x16x32(ahi, bw, acc[t]);
-                acc[t] = mfma16x16x32(amid, bw, acc[t]);
-                acc[t] = mfma16x16x32(alo, bw, acc[t]);
+                const uint4 bw = fp4x8_to_f16(u4_word(cw[t][gg], st), sc[t][st >> 1]);
+                acc[t] = mfma16x16x32_f16(hhi[st], bw, acc[t]);
+                acc[t] = mfma16x16x32_f16(hlo[st], bw, acc[t]);
             }
         }
     }
@@ -705,8 +777,8 @@ __device__ __forceinline__ void down_fp4_tile(const ExpertParams& p, const int4&
 }
 
 // down, NVFP4 weights: block = (group, 16 NT output rows), K = F split over
-// the 4 waves in groups of 128; h enters as three exact bf16 parts.  First
-// token tile peeled as in gateup_fp4_kernel.
+// the 4 waves in groups of 128; h enters as its two f16 parts (two MFMAs per
+// step).  First token tile peeled as in gateup_fp4_kernel.
 constexpr int kDownFp4Tiles = 4;  // 64 output rows per block
 
 template <int NT, int NGMAX>
@@ -720,15 +792,15 @@ __global__ __launch_bounds__(256) void down_fp4_kernel(ExpertParams p) {
     if (gi >= *p.ws.n_groups) return;
     const int4 g = p.ws.groups[gi];
     const bool is_shared = g.x == p.dm.E;
+    // routing weight of the row this thread stores in the first token tile
+    const int mm = tid >> 4;
+    const float rw_load = p.ws.sorted_wt[g.y + (mm < g.z ? mm : g.z - 1)];
     const int F = is_shared ? p.dm.fs : p.dm.f;
     const int ng = F / 512;
     const int kl = wave * (F / 4) + 32 * q;
     const size_t e = is_shared ? 0 : (size_t)g.x;
     const WeightPtrs& wp = is_shared ? p.shared : p.routed;
     const int n0 = rb * 16 * NT;
-    // routing weight of the row this thread stores in the first token tile
-    const int mm = tid >> 4;
-    const float rw_load = p.ws.sorted_wt[g.y + (mm < g.z ? mm : g.z - 1)];
     uint4 cw[NT][NGMAX];
     uint16_t sw[NT][NGMAX];
 #pragma unroll
@@ -743,15 +815,18 @@ __global__ __launch_bounds__(256) void down_fp4_kernel(ExpertParams p) {
             sw[t][gg] = *reinterpret_cast<const uint16_t*>(srow + 8 * gc);
         }
     }
-    const float tsd = wp.ts[e * 3 + 2];
+    const float tsd = wp.ts[e * 3 + 2] / kHScale;
     const float rw0 = is_shared ? 1.f : rw_load;
-    const __amdgpu_buffer_rsrc_t hv =
-        buffer_view(static_cast<const float*>(p.ws.h) + (size_t)g.w * p.hstride, (uint32_t)g.z * p.hstride * 4);
-    down_fp4_tile<NT, NGMAX>(p, g, 0, ng, kl, n0, hv, cw, sw, tsd * rw0, s_part);
+    const uint16_t* h16 = static_cast<const uint16_t*>(p.ws.h);
+    const size_t plane = (size_t)(p.dm.k + 1) * p.dm.T * p.hstride;
+    const uint32_t vbytes = (uint32_t)g.z * p.hstride * 2;
+    const __amdgpu_buffer_rsrc_t hv_hi = buffer_view(h16 + (size_t)g.w * p.hstride, vbytes);
+    const __amdgpu_buffer_rsrc_t hv_lo = buffer_view(h16 + plane + (size_t)g.w * p.hstride, vbytes);
+    down_fp4_tile<NT, NGMAX>(p, g, 0, ng, kl, n0, hv_hi, hv_lo, cw, sw, tsd * rw0, s_part);
     for (int r0 = 16; r0 < g.z; r0 += 16) {
         const int m = r0 + mm;
         const float rw = is_shared ? 1.f : p.ws.sorted_wt[g.y + (m < g.z ? m : g.z - 1)];
-        down_fp4_tile<NT, NGMAX>(p, g, r0, ng, kl, n0, hv, cw, sw, tsd * rw, s_part);
+        down_fp4_tile<NT, NGMAX>(p, g, r0, ng, kl, n0, hv_hi, hv_lo, cw, sw, tsd * rw, s_part);
     }
 }
 
