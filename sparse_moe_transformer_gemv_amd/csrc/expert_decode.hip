@@ -546,6 +546,8 @@ __device__ __forceinline__ uint4 fp4x8_to_f16(uint32_t w, Fp4Scale sc) {
 }
 #undef FLINT_FP4_F16_PAIR
 
+constexpr int kGateupFp4FeatureTiles = 2;  // 16-feature tile pairs per gate/up block
+
 // h of the NVFP4 path: two f16 planes (hi, lo) of (k+1) T rows each, holding
 // h * 2^-8 (headroom above the f16 range for large activations).
 constexpr float kHScale = 1.0f / 256.0f;
@@ -596,11 +598,11 @@ hipError_t launch_x_to_f16(const LayerArgs& a, const Workspace& w, hipStream_t s
 
 // One 16-token tile of an NVFP4 gate/up block (see gateup_fp4_kernel).  sp is
 // the sorted pair of this lane's token row.
-template <int NG>
+template <int NG, int NW, int FT>
 __device__ __forceinline__ void gateup_fp4_tile(const ExpertParams& p, const int4& g, bool is_shared, int r0,
-                                                int sp, __amdgpu_buffer_rsrc_t xv, int kl, uint4 (&cw)[2][NG],
-                                                uint16_t (&sw)[2][NG], float tsg, float tsu, int j0,
-                                                float (&s_part)[4][2][256], float (&s_xs)[16]) {
+                                                int sp, __amdgpu_buffer_rsrc_t xv, int kl, uint4 (&cw)[2 * FT][NG],
+                                                uint16_t (&sw)[2 * FT][NG], float tsg, float tsu, int j0,
+                                                float (&s_part)[NW][2 * FT][256], float (&s_xs)[16]) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, q = lane >> 4;
     const int d = p.dm.d;
@@ -617,83 +619,89 @@ __device__ __forceinline__ void gateup_fp4_tile(const ExpertParams& p, const int
     // Decode the weights here, after the activation loads are issued: an empty
     // asm that claims to change the codes keeps the decode from being hoisted
     // ahead of those loads or out of the token loop (where its f16 operands
-    // would cost 32 NG more registers per lane than the packed codes).
+    // would cost 32 NG more registers per tile than the packed codes).
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2 * FT; ++t)
 #pragma unroll
         for (int gg = 0; gg < NG; ++gg)
             asm volatile("" : "+v"(cw[t][gg].x), "+v"(cw[t][gg].y), "+v"(cw[t][gg].z), "+v"(cw[t][gg].w),
                          "+v"(sw[t][gg]));
     if (wave == 0 && q == 0) s_xs[row] = xs;
-    floatx4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    floatx4_t acc[2 * FT];
+#pragma unroll
+    for (int t = 0; t < 2 * FT; ++t) acc[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) {
-        const Fp4Scale g0 = fp4_scale(__builtin_amdgcn_cvt_f32_fp8(sw[0][gg], 0));
-        const Fp4Scale g1 = fp4_scale(__builtin_amdgcn_cvt_f32_fp8(sw[0][gg], 1));
-        const Fp4Scale u0 = fp4_scale(__builtin_amdgcn_cvt_f32_fp8(sw[1][gg], 0));
-        const Fp4Scale u1 = fp4_scale(__builtin_amdgcn_cvt_f32_fp8(sw[1][gg], 1));
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            acc0 = mfma16x16x32_f16(a[gg][st], fp4x8_to_f16(u4_word(cw[0][gg], st), st < 2 ? g0 : g1), acc0);
-            acc1 = mfma16x16x32_f16(a[gg][st], fp4x8_to_f16(u4_word(cw[1][gg], st), st < 2 ? u0 : u1), acc1);
+        for (int t = 0; t < 2 * FT; ++t) {
+            const Fp4Scale s0 = fp4_scale(__builtin_amdgcn_cvt_f32_fp8(sw[t][gg], 0));
+            const Fp4Scale s1 = fp4_scale(__builtin_amdgcn_cvt_f32_fp8(sw[t][gg], 1));
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+                acc[t] = mfma16x16x32_f16(a[gg][st], fp4x8_to_f16(u4_word(cw[t][gg], st), st < 2 ? s0 : s1), acc[t]);
         }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        s_part[wave][0][(4 * q + i) * 16 + row] = acc0[i];
-        s_part[wave][1][(4 * q + i) * 16 + row] = acc1[i];
-    }
+    for (int t = 0; t < 2 * FT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_part[wave][t][(4 * q + i) * 16 + row] = acc[t][i];
     __syncthreads();
-    const int mm = tid >> 4, n = tid & 15;
-    if (r0 + mm < g.z) {
+    // thread -> (feature tile ft, token row mm, feature n); tiles ft (gate) and FT + ft (up)
+    for (int idx = tid; idx < 256 * FT; idx += 64 * NW) {
+        const int ft = idx >> 8, mm = (idx >> 4) & 15, n = idx & 15, o = idx & 255;
+        if (r0 + mm >= g.z) continue;
+        float gs = s_part[0][ft][o], us = s_part[0][FT + ft][o];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) {  // fixed order
+            gs += s_part[w][ft][o];
+            us += s_part[w][FT + ft][o];
+        }
         const float xsm = s_xs[mm];
-        const float gv = tsg * xsm * (((s_part[0][0][tid] + s_part[1][0][tid]) + s_part[2][0][tid]) + s_part[3][0][tid]);
-        const float uv = tsu * xsm * (((s_part[0][1][tid] + s_part[1][1][tid]) + s_part[2][1][tid]) + s_part[3][1][tid]);
-        const float hv = silu_f32(gv) * uv * kHScale;
+        const float hv = silu_f32(tsg * xsm * gs) * (tsu * xsm * us) * kHScale;
         const _Float16 hi = (_Float16)hv;
         const _Float16 lo = (_Float16)(hv - (float)hi);
         uint16_t* h16 = static_cast<uint16_t*>(p.ws.h);
         const size_t plane = (size_t)(p.dm.k + 1) * p.dm.T * p.hstride;
-        const size_t o = (size_t)(g.w + r0 + mm) * p.hstride + j0 + n;
-        h16[o] = __builtin_bit_cast(uint16_t, hi);
-        h16[plane + o] = __builtin_bit_cast(uint16_t, lo);
+        const size_t off = (size_t)(g.w + r0 + mm) * p.hstride + j0 + 16 * ft + n;
+        h16[off] = __builtin_bit_cast(uint16_t, hi);
+        h16[plane + off] = __builtin_bit_cast(uint16_t, lo);
     }
     __syncthreads();
 }
 
-// gate/up + SwiGLU, NVFP4 weights: block = (group, 16 features): MFMA tile 0
-// holds their gate rows and tile 1 their up rows, so the two results of one
-// feature land in the same lane.  K is split over the 4 waves, NG groups of
-// 128 per wave (d = 512 NG).  The first token tile is peeled off the loop so
-// that the weights and its activations are all in flight before the first
-// wait.
-template <int NG>
-__global__ __launch_bounds__(256) void gateup_fp4_kernel(ExpertParams p) {
-    __shared__ float s_part[4][2][256];
+// gate/up + SwiGLU, NVFP4 weights: block = (group, 16 FT features): MFMA tiles
+// 0..FT-1 hold their gate rows and tiles FT..2FT-1 their up rows, so the two
+// results of one feature land in the same lane.  K is split over the NW waves,
+// NG groups of 128 per wave (d = 128 NG NW).  The first token tile is peeled
+// off the loop so that the weights and its activations are all in flight
+// before the first wait.
+template <int NG, int NW, int FT>
+__global__ __launch_bounds__(64 * NW) void gateup_fp4_kernel(ExpertParams p) {
+    __shared__ float s_part[NW][2 * FT][256];
     __shared__ float s_xs[16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, q = lane >> 4;
     const int d = p.dm.d;
-    const int fblocks = p.hstride / 16;
+    const int fblocks = p.hstride / (16 * FT);
     const int gi = blockIdx.x / fblocks, fb = blockIdx.x % fblocks;
     if (gi >= *p.ws.n_groups) return;
     const int4 g = p.ws.groups[gi];
     const bool is_shared = g.x == p.dm.E;
     const int F = is_shared ? p.dm.fs : p.dm.f;
-    const int j0 = fb * 16;
+    const int j0 = fb * 16 * FT;
     if (j0 >= F) return;
     const size_t e = is_shared ? 0 : (size_t)g.x;
     const WeightPtrs& wp = is_shared ? p.shared : p.routed;
-    const int kl = wave * (d / 4) + 32 * q;  // this lane's first element in each group
+    const int kl = wave * (d / NW) + 32 * q;  // this lane's first element in each group
     // The token index is requested before the weights: vector loads retire in
     // order, so the activation loads that need it wait for it alone.
     const int sp = p.ws.sorted_pair[g.y + (row < g.z ? row : g.z - 1)];
     __builtin_amdgcn_sched_barrier(0);
-    uint4 cw[2][NG];
-    uint16_t sw[2][NG];
+    uint4 cw[2 * FT][NG];
+    uint16_t sw[2 * FT][NG];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const size_t wr = e * 2 * F + (size_t)t * F + j0 + row;
+    for (int t = 0; t < 2 * FT; ++t) {
+        const size_t wr = e * 2 * F + (size_t)(t >= FT ? F : 0) + j0 + 16 * (t % FT) + row;
         const uint8_t* crow = static_cast<const uint8_t*>(wp.gu) + wr * (d / 2) + kl / 2;
         const uint8_t* srow = wp.gus + wr * (d / 16) + kl / 16;
 #pragma unroll
@@ -704,11 +712,11 @@ __global__ __launch_bounds__(256) void gateup_fp4_kernel(ExpertParams p) {
     }
     const float tsg = wp.ts[e * 3 + 0], tsu = wp.ts[e * 3 + 1];
     const __amdgpu_buffer_rsrc_t xv = buffer_view(p.ws.x16, (uint32_t)p.dm.T * d * 2);
-    gateup_fp4_tile<NG>(p, g, is_shared, 0, sp, xv, kl, cw, sw, tsg, tsu, j0, s_part, s_xs);
+    gateup_fp4_tile<NG, NW, FT>(p, g, is_shared, 0, sp, xv, kl, cw, sw, tsg, tsu, j0, s_part, s_xs);
     for (int r0 = 16; r0 < g.z; r0 += 16) {
         const int m = r0 + row;
         const int spn = p.ws.sorted_pair[g.y + (m < g.z ? m : g.z - 1)];
-        gateup_fp4_tile<NG>(p, g, is_shared, r0, spn, xv, kl, cw, sw, tsg, tsu, j0, s_part, s_xs);
+        gateup_fp4_tile<NG, NW, FT>(p, g, is_shared, r0, spn, xv, kl, cw, sw, tsg, tsu, j0, s_part, s_xs);
     }
 }
 
@@ -866,11 +874,13 @@ static ExpertParams make_params(const LayerArgs& a, const Workspace& w) {
 hipError_t launch_gateup_decode(const LayerArgs& a, const Workspace& w, hipStream_t s) {
     ExpertParams p = make_params(a, w);
     if (decode_fp4_ok(a.dm)) {
-        dim3 grid(max_groups(a.dm) * (p.hstride / 16));
-        switch (a.dm.d / 512) {
-        case 1: hipLaunchKernelGGL(gateup_fp4_kernel<1>, grid, dim3(256), 0, s, p); break;
-        case 2: hipLaunchKernelGGL(gateup_fp4_kernel<2>, grid, dim3(256), 0, s, p); break;
-        default: hipLaunchKernelGGL(gateup_fp4_kernel<4>, grid, dim3(256), 0, s, p); break;
+        // 8 waves split K; 32 features (64 weight rows) per block
+        constexpr int FT = kGateupFp4FeatureTiles;
+        dim3 grid(max_groups(a.dm) * (p.hstride / (16 * FT)));
+        switch (a.dm.d / 1024) {
+        case 0: hipLaunchKernelGGL((gateup_fp4_kernel<1, 4, FT>), grid, dim3(256), 0, s, p); break;  // d = 512
+        case 1: hipLaunchKernelGGL((gateup_fp4_kernel<1, 8, FT>), grid, dim3(512), 0, s, p); break;
+        default: hipLaunchKernelGGL((gateup_fp4_kernel<2, 8, FT>), grid, dim3(512), 0, s, p); break;
         }
         return hipGetLastError();
     }
