@@ -330,7 +330,7 @@ __global__ __launch_bounds__(256) void down_decode_kernel(ExpertParams p) {
 template <int NSTEP>
 __device__ __forceinline__ void gateup_mfma_tile(const ExpertParams& p, const int4& g, bool is_shared, int r0,
                                                  int sp, __amdgpu_buffer_rsrc_t xv, int kl, const uint4 (&b)[NSTEP],
-                                                 int j0, float (&s_part)[4][256]) {
+                                                 int j0, float (&s_part)[4][256], uint16_t (&s_h)[16][3][8]) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, q = lane >> 4;
     const int d = p.dm.d;
@@ -352,9 +352,24 @@ __device__ __forceinline__ void gateup_mfma_tile(const ExpertParams& p, const in
         const int gi_ = mm * 16 + n, ui_ = gi_ + 8;
         const float gv = ((s_part[0][gi_] + s_part[1][gi_]) + s_part[2][gi_]) + s_part[3][gi_];
         const float uv = ((s_part[0][ui_] + s_part[1][ui_]) + s_part[2][ui_]) + s_part[3][ui_];
-        static_cast<float*>(p.ws.h)[(size_t)(g.w + r0 + mm) * p.hstride + j0 + n] = silu_f32(gv) * uv;
+        // h goes out as its exact three-part bf16 split (hi + mid + lo), once,
+        // instead of being split again by every down block that reads it
+        const float hv = silu_f32(gv) * uv;
+        const uint16_t hi = f32_to_bf16(hv);
+        const float r1 = hv - bf16_to_f32(hi);
+        const uint16_t mid = f32_to_bf16(r1);
+        s_h[mm][0][n] = hi;
+        s_h[mm][1][n] = mid;
+        s_h[mm][2][n] = f32_to_bf16(r1 - bf16_to_f32(mid));
     }
     __syncthreads();
+    // one 16-byte store per (token row, plane): the 8 features of this block
+    if (tid < 48 && r0 + tid / 3 < g.z) {
+        const int r = tid / 3, pl = tid % 3;
+        const size_t plane = (size_t)(p.dm.k + 1) * p.dm.T * p.hstride;
+        uint16_t* dst = static_cast<uint16_t*>(p.ws.h) + pl * plane + (size_t)(g.w + r0 + r) * p.hstride + j0;
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(&s_h[r][pl][0]);
+    }
 }
 
 // gate/up: block = (group, 8 features): B columns 0..7 are gate rows j0..j0+7,
@@ -366,6 +381,7 @@ __device__ __forceinline__ void gateup_mfma_tile(const ExpertParams& p, const in
 template <int NSTEP>
 __global__ __launch_bounds__(256) void gateup_mfma_kernel(ExpertParams p) {
     __shared__ float s_part[4][256];
+    __shared__ __attribute__((aligned(16))) uint16_t s_h[16][3][8];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, q = lane >> 4;
     const int d = p.dm.d;
@@ -388,30 +404,30 @@ __global__ __launch_bounds__(256) void gateup_mfma_kernel(ExpertParams p) {
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) b[s] = *reinterpret_cast<const uint4*>(wrow + 32 * s);
     const __amdgpu_buffer_rsrc_t xv = buffer_view(p.x, (uint32_t)p.dm.T * d * 2);
-    gateup_mfma_tile<NSTEP>(p, g, is_shared, 0, sp, xv, kl, b, j0, s_part);
+    gateup_mfma_tile<NSTEP>(p, g, is_shared, 0, sp, xv, kl, b, j0, s_part, s_h);
     for (int r0 = 16; r0 < g.z; r0 += 16) {
         const int m = r0 + row;
         const int spn = p.ws.sorted_pair[g.y + (m < g.z ? m : g.z - 1)];
-        gateup_mfma_tile<NSTEP>(p, g, is_shared, r0, spn, xv, kl, b, j0, s_part);
+        gateup_mfma_tile<NSTEP>(p, g, is_shared, r0, spn, xv, kl, b, j0, s_part, s_h);
     }
 }
 
 // One 16-token tile of a bf16 down block; ws is the routing weight of the
-// token row this thread stores.  Padding rows of h read as zeros.
+// token row this thread stores.  h arrives as its three bf16 planes; padding
+// rows read as zeros.
 template <int NSMAX, int NT>
 __device__ __forceinline__ void down_mfma_tile(const ExpertParams& p, const int4& g, int r0, int nsteps, int kl,
-                                               int n0, __amdgpu_buffer_rsrc_t hv, const uint4 (&b)[NT][NSMAX],
-                                               float ws, float (&s_part)[4][NT][256]) {
+                                               int n0, const __amdgpu_buffer_rsrc_t (&hv)[3],
+                                               const uint4 (&b)[NT][NSMAX], float ws, float (&s_part)[4][NT][256]) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, q = lane >> 4;
     const int m = r0 + row;
-    const uint32_t ho = m < g.z ? (uint32_t)(m * p.hstride + kl) * 4 : kOffNone;
-    uint4 hr0[NSMAX], hr1[NSMAX];
+    const uint32_t ho = m < g.z ? (uint32_t)(m * p.hstride + kl) * 2 : kOffNone;
+    uint4 ah[3][NSMAX];
 #pragma unroll
-    for (int s = 0; s < NSMAX; ++s) {
-        hr0[s] = buffer_load16(hv, ho + 128 * s);
-        hr1[s] = buffer_load16(hv, ho + 128 * s + 16);
-    }
+    for (int s = 0; s < NSMAX; ++s)
+#pragma unroll
+        for (int pl = 0; pl < 3; ++pl) ah[pl][s] = buffer_load16(hv[pl], ho + 64 * s);
     __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the first MFMA
     floatx4_t acc[NT];
 #pragma unroll
@@ -419,16 +435,11 @@ __device__ __forceinline__ void down_mfma_tile(const ExpertParams& p, const int4
 #pragma unroll
     for (int s = 0; s < NSMAX; ++s) {
         if (s >= nsteps) break;
-        const float v[8] = {__uint_as_float(hr0[s].x), __uint_as_float(hr0[s].y), __uint_as_float(hr0[s].z),
-                            __uint_as_float(hr0[s].w), __uint_as_float(hr1[s].x), __uint_as_float(hr1[s].y),
-                            __uint_as_float(hr1[s].z), __uint_as_float(hr1[s].w)};
-        uint4 ahi, amid, alo;
-        split3_bf16(v, ahi, amid, alo);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            acc[t] = mfma16x16x32(ahi, b[t][s], acc[t]);
-            acc[t] = mfma16x16x32(amid, b[t][s], acc[t]);
-            acc[t] = mfma16x16x32(alo, b[t][s], acc[t]);
+            acc[t] = mfma16x16x32(ah[0][s], b[t][s], acc[t]);
+            acc[t] = mfma16x16x32(ah[1][s], b[t][s], acc[t]);
+            acc[t] = mfma16x16x32(ah[2][s], b[t][s], acc[t]);
         }
     }
 #pragma unroll
@@ -449,9 +460,9 @@ __device__ __forceinline__ void down_mfma_tile(const ExpertParams& p, const int4
 }
 
 // down: block = (group, NT tiles of 16 output rows); K = F split over the
-// waves, NSMAX >= F / 128 k steps per wave.  h is fp32; it enters the MFMA
-// exactly as three bf16 parts (hi + mid + lo), the weights exactly, so the
-// only rounding is the fp32 accumulation.  Load order and the peeled first
+// waves, NSMAX >= F / 128 k steps per wave.  h enters the MFMA exactly as the
+// three bf16 planes (hi + mid + lo of the fp32 value) written by the gate/up
+// kernel, the weights exactly, so the only rounding is the fp32 accumulation.  Load order and the peeled first
 // token tile as in gateup_mfma_kernel.
 constexpr int kDownMfmaTiles = 4;  // 64 output rows per block
 
@@ -485,8 +496,12 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertParams p) {
             b[t][s] = *reinterpret_cast<const uint4*>(drow + 32 * sc);
         }
     }
-    const __amdgpu_buffer_rsrc_t hv =
-        buffer_view(static_cast<const float*>(p.ws.h) + (size_t)g.w * p.hstride, (uint32_t)g.z * p.hstride * 4);
+    const uint16_t* h16 = static_cast<const uint16_t*>(p.ws.h);
+    const size_t plane = (size_t)(p.dm.k + 1) * p.dm.T * p.hstride;
+    const uint32_t vbytes = (uint32_t)g.z * p.hstride * 2;
+    __amdgpu_buffer_rsrc_t hv[3];
+#pragma unroll
+    for (int pl = 0; pl < 3; ++pl) hv[pl] = buffer_view(h16 + pl * plane + (size_t)g.w * p.hstride, vbytes);
     down_mfma_tile<NSMAX, NT>(p, g, 0, nsteps, kl, n0, hv, b, is_shared ? 1.f : rw_load, s_part);
     for (int r0 = 16; r0 < g.z; r0 += 16) {
         const int m = r0 + mm;

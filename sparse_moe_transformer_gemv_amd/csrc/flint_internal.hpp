@@ -37,7 +37,8 @@ struct Workspace {
     int2* tiles;         // [max_tiles] prefill m-tiles {group, first row}
     int* n_tiles;        // [1]
     int* counter;        // [1 + ceil(Tm/16)] last-block tickets, zero between launches
-    void* h;             // [(k+1)*Tm][fmax]: fp32 (decode) or bf16 (prefill)
+    void* h;             // [(k+1)*Tm][fmax] x 8 B: fp32 (decode VALU), three exact bf16 planes (decode
+                         // MFMA), two f16 planes (NVFP4), or bf16 (prefill)
     void* y;             // [(k+1)*Tm][d]:    fp32 (decode) or bf16 (prefill)
     int max_tiles;
 };

@@ -148,7 +148,7 @@ size_t carve(const flint_moe_config& c, char* base, Workspace* w) {
     w->tiles = static_cast<int2*>(take(max_tiles * 8));
     w->n_tiles = static_cast<int*>(take(4));
     w->counter = static_cast<int*>(take((1 + (Tm + 15) / 16) * 4));
-    w->h = take(slots * fmax * 4);
+    w->h = take(slots * fmax * 8);
     w->y = take(slots * (size_t)c.d_model * 4);
     w->max_tiles = (int)max_tiles;
     return off;
