@@ -6,7 +6,8 @@
 // Feature Overview, "Sparse architecture"; swarmz.net, "Recursive Flint: 40B
 // Open Model, 2.5B Active", section "The architecture, in plain terms"]:
 //     out[t] = (residual[t]) + y[shared slot t] + sum_j y[slot of pair (t, j)]
-// where the routed rows of y already carry their combine weight.  The sum runs
+// where the routed rows of y already carry their combine weight (a layer built
+// without a shared expert skips that term).  The sum runs
 // in a fixed order (residual, shared, slot 0..k-1), so results are
 // deterministic; no atomics.
 #include "flint_internal.hpp"
@@ -19,7 +20,8 @@ struct CombineParams {
     const int* pair_pos;  // [T][k]
     const float* residual;
     void* out;
-    int out_f32;  // 1: fp32 out (act fp32, or residual given); 0: bf16 out
+    int out_f32;     // 1: fp32 out (act fp32, or residual given); 0: bf16 out
+    int has_shared;  // 0: no shared expert (f_s = 0); its slots are never written
 };
 
 template <bool YBF16>
@@ -45,9 +47,11 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     }
     float v[4];
     const size_t kT = (size_t)p.k * p.T;
-    load_y4<YBF16>(p.y, kT + t, p.d, c, v);
+    if (p.has_shared) {
+        load_y4<YBF16>(p.y, kT + t, p.d, c, v);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] += v[i];
+        for (int i = 0; i < 4; ++i) acc[i] += v[i];
+    }
     for (int j = 0; j < p.k; ++j) {
         const int slot = p.pair_pos[(size_t)t * p.k + j];
         load_y4<YBF16>(p.y, (size_t)slot, p.d, c, v);
@@ -75,6 +79,7 @@ hipError_t launch_combine(const LayerArgs& a, const Workspace& w, bool y_bf16, h
     p.residual = a.residual;
     p.out = a.out;
     p.out_f32 = (a.residual != nullptr || a.dm.act == DT_F32) ? 1 : 0;
+    p.has_shared = a.dm.fs > 0 ? 1 : 0;
     dim3 grid((a.dm.d + 1023) / 1024, a.dm.T);
     if (y_bf16) hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s, p);
     else hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, s, p);

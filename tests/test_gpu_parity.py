@@ -103,6 +103,25 @@ def test_no_shared_expert():
     compare(out, rout, ref, c["k"], synth.BF16, out_bf16=True)
 
 
+def test_no_shared_expert_decode_then_prefill_same_handle():
+    # the prefill forward must not pick up rows an earlier decode forward left in
+    # the shared slots' place (there is no shared expert to write them)
+    L = synth.layer(1, d=256, E=32, f=128, fs=128)
+    L["shared"] = None
+    c = dict(L["cfg"], fs=0)
+    L["cfg"] = c
+    layer = make_layer_obj(c, 256)
+    D = dev_layer(L)
+    # decode at T=64 writes fp32 rows over the bytes where the T=100 prefill
+    # forward's (bf16) shared-slot rows would sit
+    for T in (64, 100):
+        x = synth.hidden(1, T, 256, synth.BF16, draw=T)
+        out, rout = run_gpu(layer, D, x)
+        ref = oracle.moe_forward(x, L["router_w"], L["experts"], None, top_k=c["k"], wdtype=synth.BF16)
+        rep = compare(out, rout, ref, c["k"], synth.BF16, out_bf16=True)
+        print("no shared expert T=%d: %s" % (T, rep), flush=True)
+
+
 def test_odd_expert_count_and_k8():
     _case(1, 20, d=128, E=100, k=8, f=32, fs=32)
 
