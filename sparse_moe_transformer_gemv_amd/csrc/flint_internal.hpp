@@ -76,6 +76,7 @@ hipError_t launch_router_logits(const LayerArgs& a, const Workspace& w, hipStrea
 hipError_t launch_topk(const LayerArgs& a, const Workspace& w, hipStream_t s);
 bool router_gemm_ok(const Dims& dm);
 hipError_t launch_router_gemm(const LayerArgs& a, const Workspace& w, hipStream_t s);
+constexpr int kSortBlock = 1024;  // pairs per block of the prefill sort
 hipError_t launch_sort(const LayerArgs& a, const Workspace& w, int bm, hipStream_t s);
 hipError_t launch_gateup_decode(const LayerArgs& a, const Workspace& w, hipStream_t s);
 hipError_t launch_down_decode(const LayerArgs& a, const Workspace& w, hipStream_t s);

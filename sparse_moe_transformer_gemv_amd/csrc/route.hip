@@ -130,6 +130,49 @@ __device__ void wave_topk_token(const float* __restrict__ lrow, int E, int k, in
     }
 }
 
+// Active groups from the expert offsets s_off[0..E] (LDS), written by one
+// wavefront: the shared expert first (its work items are the longest, so they
+// start first), then the experts with tokens in ascending order; with bm > 0
+// also the prefill tile list, ceil(rows / bm) tiles per group.
+__device__ void write_groups(const int* s_off, int E, int T, int k, bool has_shared, int bm, const Workspace& ws,
+                             int lane) {
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    int n = 0, ntile = 0;
+    if (has_shared) {
+        if (lane == 0) ws.groups[0] = make_int4(E, 0, T, k * T);
+        if (bm > 0) {
+            const int nt = (T + bm - 1) / bm;
+            for (int t = lane; t < nt; t += 64) ws.tiles[t] = make_int2(0, t * bm);
+            ntile = nt;
+        }
+        n = 1;
+    }
+    for (int e0 = 0; e0 < E; e0 += 64) {
+        const int e = e0 + lane;
+        const int c = (e < E) ? s_off[e + 1] - s_off[e] : 0;
+        const unsigned long long act = __ballot(c > 0);
+        const int gidx = n + __popcll(act & lt);
+        if (c > 0) ws.groups[gidx] = make_int4(e, s_off[e], c, s_off[e]);
+        if (bm > 0) {
+            const int nt = (c + bm - 1) / bm;
+            int inc = nt;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int v = __shfl_up(inc, off, 64);
+                if (lane >= off) inc += v;
+            }
+            const int pos = ntile + inc - nt;
+            for (int t = 0; t < nt; ++t) ws.tiles[pos + t] = make_int2(gidx, t * bm);
+            ntile += __shfl(inc, 63, 64);
+        }
+        n += __popcll(act);
+    }
+    if (lane == 0) {
+        *ws.n_groups = n;
+        if (bm > 0) *ws.n_tiles = ntile;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Stable counting sort of P pair keys (expert ids < E <= 256) by one block.
 // Writes counts[E], offsets[E+1], sorted_pair[P], pair_pos[P], sorted_wt[P]
@@ -249,45 +292,7 @@ __device__ void block_sort_and_groups(const int* __restrict__ keys, const float*
     }
     __syncthreads();
 
-    // active groups: the shared expert first (its work items are the longest,
-    // so they start first), then the experts with tokens in ascending order;
-    // with bm > 0 also the prefill tile list, ceil(rows / bm) tiles per group
-    if (w == 0) {
-        int n = 0, ntile = 0;
-        if (has_shared) {
-            if (lane == 0) ws.groups[0] = make_int4(E, 0, T, k * T);
-            if (bm > 0) {
-                const int nt = (T + bm - 1) / bm;
-                for (int t = lane; t < nt; t += 64) ws.tiles[t] = make_int2(0, t * bm);
-                ntile = nt;
-            }
-            n = 1;
-        }
-        for (int e0 = 0; e0 < E; e0 += 64) {
-            const int e = e0 + lane;
-            const int c = (e < E) ? s_off[e + 1] - s_off[e] : 0;
-            const unsigned long long act = __ballot(c > 0);
-            const int gidx = n + __popcll(act & lt);
-            if (c > 0) ws.groups[gidx] = make_int4(e, s_off[e], c, s_off[e]);
-            if (bm > 0) {
-                const int nt = (c + bm - 1) / bm;
-                int inc = nt;
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const int v = __shfl_up(inc, off, 64);
-                    if (lane >= off) inc += v;
-                }
-                const int pos = ntile + inc - nt;
-                for (int t = 0; t < nt; ++t) ws.tiles[pos + t] = make_int2(gidx, t * bm);
-                ntile += __shfl(inc, 63, 64);
-            }
-            n += __popcll(act);
-        }
-        if (lane == 0) {
-            *ws.n_groups = n;
-            if (bm > 0) *ws.n_tiles = ntile;
-        }
-    }
+    if (w == 0) write_groups(s_off, E, T, k, has_shared, bm, ws, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -886,16 +891,134 @@ struct SortParams {
     Workspace ws;
 };
 
-__global__ __launch_bounds__(1024) void sort_kernel(SortParams p) {
-    __shared__ int s_hist[16 * 256];
+// ---------------------------------------------------------------------------
+// Prefill counting sort, one launch of ceil(P / kSortBlock) blocks.  Block b
+// places the pairs [kSortBlock b, kSortBlock (b + 1)); pair i is read by
+// thread i mod kSortBlock of every block, so each block counts all P keys
+// itself (per expert: the pairs in earlier blocks and in later ones) with no
+// hand-off between blocks.  Counting uses a histogram per wavefront in LDS, so
+// atomics collide only inside a wavefront.  The block's own pairs are ranked
+// among equal keys by ballots over the 8 key bits.  The order is stable (pairs
+// of one expert keep pair order), so the result does not depend on timing.
+// Block 0 also writes the counts, offsets, group list and tile list.  The
+// scattered writes of the permutation are spread over the blocks: from one
+// block they cost a cache line per distinct expert per 64 pairs, one
+// instruction after another.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kSortBlock) void sort_kernel(SortParams p) {
+    constexpr int NW = kSortBlock / 64, KU = 32;
+    __shared__ int s_pre[NW][256];   // per wave: pairs per expert in blocks before b
+    __shared__ int s_post[NW][256];  // per wave: pairs per expert in blocks after b
+    __shared__ int s_base[NW][256];  // per wave: this block's pairs per expert, then their first positions
+    __shared__ int s_tot[256];
+    __shared__ int s_before[256];
     __shared__ int s_off[257];
-    block_sort_and_groups<1024, false>(p.ws.sel, p.ws.wts, p.k * p.T, p.E, p.T, p.k, p.has_shared != 0,
-                                       p.bm, p.ws, s_hist, s_off);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int E = p.E, P = p.k * p.T, nb = (int)gridDim.x, b = (int)blockIdx.x;
+    for (int j = tid; j < NW * 256; j += kSortBlock) {
+        (&s_pre[0][0])[j] = 0;
+        (&s_post[0][0])[j] = 0;
+        (&s_base[0][0])[j] = 0;
+    }
+    // this block's own pair, requested with the first batch of keys
+    const int i = b * kSortBlock + tid;
+    const bool valid = i < P;
+    const int key = valid ? p.ws.sel[i] : 0;
+    const float wt = valid ? p.ws.wts[i] : 0.f;
+    __syncthreads();
+    for (int j0 = 0; j0 < nb; j0 += KU) {
+        int kv[KU];
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+            const int ii = (j0 + u) * kSortBlock + tid;
+            kv[u] = (j0 + u < nb && ii < P) ? p.ws.sel[ii] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+            const int j = j0 + u;
+            if (j >= nb) break;  // uniform
+            if (kv[u] >= 0 && j != b) atomicAdd(j < b ? &s_pre[w][kv[u]] : &s_post[w][kv[u]], 1);
+        }
+    }
+    // lanes of this wave holding the same expert as this lane
+    unsigned long long m = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+        const bool set = (key >> bit) & 1;
+        const unsigned long long bb = __ballot(valid && set);
+        m &= set ? bb : ~bb;
+    }
+    const int rank = __popcll(m & ((1ull << lane) - 1ull));
+    // the highest lane of each group of equal keys records its size
+    if (valid && (m >> lane) == 1ull) s_base[w][key] = __popcll(m);
+    __syncthreads();
+    if (tid < E) {
+        int before = 0, rest = 0;
+        for (int ww = 0; ww < NW; ++ww) {
+            before += s_pre[ww][tid];
+            rest += s_post[ww][tid] + s_base[ww][tid];
+        }
+        s_before[tid] = before;
+        s_tot[tid] = before + rest;
+    }
+    __syncthreads();
+    // exclusive scan of the totals (wave 0, 4 experts per lane)
+    if (w == 0) {
+        int c[4], local = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = 4 * lane + q;
+            c[q] = e < E ? s_tot[e] : 0;
+            local += c[q];
+        }
+        int inc = local;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int v = __shfl_up(inc, off, 64);
+            if (lane >= off) inc += v;
+        }
+        int run = inc - local;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = 4 * lane + q;
+            if (e < E) {
+                s_off[e] = run;
+                if (b == 0) {
+                    p.ws.offsets[e] = run;
+                    p.ws.counts[e] = c[q];
+                }
+            }
+            run += c[q];
+        }
+        if (lane == 63) {
+            s_off[E] = inc;
+            if (b == 0) p.ws.offsets[E] = inc;
+        }
+    }
+    __syncthreads();
+    // first position of each (wave, expert) of this block, in wave order
+    if (tid < E) {
+        int run = s_off[tid] + s_before[tid];
+        for (int ww = 0; ww < NW; ++ww) {
+            const int c = s_base[ww][tid];
+            s_base[ww][tid] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    if (valid) {
+        const int pos = s_base[w][key] + rank;
+        p.ws.sorted_pair[pos] = i;
+        p.ws.pair_pos[i] = pos;
+        p.ws.sorted_wt[pos] = wt;
+    }
+    if (b == 0 && w == 0) write_groups(s_off, E, p.T, p.k, p.has_shared != 0, p.bm, p.ws, lane);
 }
 
 hipError_t launch_sort(const LayerArgs& a, const Workspace& w, int bm, hipStream_t s) {
     SortParams p{a.dm.T, a.dm.E, a.dm.k, a.dm.fs > 0, bm, w};
-    hipLaunchKernelGGL(sort_kernel, dim3(1), dim3(1024), 0, s, p);
+    const dim3 grid((a.dm.k * a.dm.T + kSortBlock - 1) / kSortBlock);
+    hipLaunchKernelGGL(sort_kernel, grid, dim3(kSortBlock), 0, s, p);
     return hipGetLastError();
 }
 
