@@ -562,6 +562,14 @@ __device__ __forceinline__ uint4 fp4x8_to_f16(uint32_t w, Fp4Scale sc) {
 #undef FLINT_FP4_F16_PAIR
 
 constexpr int kGateupFp4FeatureTiles = 2;  // 16-feature tile pairs per gate/up block
+// LDS row stride of a gate/up block's staged E4M3 scales: d / 16 bytes, plus
+// 16 so that the 16 rows read by one instruction fall in different banks.
+template <int NG, int NW>
+constexpr int kFp4ScRow = 8 * NG * NW + 16;
+// LDS row stride of a down block's staged scales: at most F / 16 = 32 NGMAX
+// bytes, plus 16 (banks, as for gate/up)
+template <int NGMAX>
+constexpr int kFp4DownScRow = 32 * NGMAX + 16;
 
 // h of the NVFP4 path: two f16 planes (hi, lo) of (k+1) T rows each, holding
 // h * 2^-8 (headroom above the f16 range for large activations).
@@ -616,8 +624,9 @@ hipError_t launch_x_to_f16(const LayerArgs& a, const Workspace& w, hipStream_t s
 template <int NG, int NW, int FT>
 __device__ __forceinline__ void gateup_fp4_tile(const ExpertParams& p, const int4& g, bool is_shared, int r0,
                                                 int sp, __amdgpu_buffer_rsrc_t xv, int kl, uint4 (&cw)[2 * FT][NG],
-                                                uint16_t (&sw)[2 * FT][NG], float tsg, float tsu, int j0,
-                                                float (&s_part)[NW][2 * FT][256], float (&s_xs)[16]) {
+                                                const uint8_t* s_sc, bool first, uint4* sc_dst, const uint4& sc_val,
+                                                float tsg, float tsu, int j0, float (&s_part)[NW][2 * FT][256],
+                                                float (&s_xs)[16]) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, q = lane >> 4;
     const int d = p.dm.d;
@@ -631,6 +640,13 @@ __device__ __forceinline__ void gateup_fp4_tile(const ExpertParams& p, const int
         for (int st = 0; st < 4; ++st) a[gg][st] = buffer_load16(xv, xo + (128 * gg + 8 * st) * 2);
     const float xs = p.ws.xscale[m < g.z ? tok : 0];
     __builtin_amdgcn_sched_barrier(0);
+    // first tile (uniform): the block's scales, loaded before the codes, go to
+    // LDS once every load of the tile is in flight (sc_dst is null for threads
+    // past the last chunk)
+    if (first) {
+        if (sc_dst != nullptr) *sc_dst = sc_val;
+        __syncthreads();
+    }
     // Decode the weights here, after the activation loads are issued: an empty
     // asm that claims to change the codes keeps the decode from being hoisted
     // ahead of those loads or out of the token loop (where its f16 operands
@@ -639,8 +655,15 @@ __device__ __forceinline__ void gateup_fp4_tile(const ExpertParams& p, const int
     for (int t = 0; t < 2 * FT; ++t)
 #pragma unroll
         for (int gg = 0; gg < NG; ++gg)
-            asm volatile("" : "+v"(cw[t][gg].x), "+v"(cw[t][gg].y), "+v"(cw[t][gg].z), "+v"(cw[t][gg].w),
-                         "+v"(sw[t][gg]));
+            asm volatile("" : "+v"(cw[t][gg].x), "+v"(cw[t][gg].y), "+v"(cw[t][gg].z), "+v"(cw[t][gg].w));
+    // this lane's two block scales per k group: row (16 t + row), k = kl + 128 gg
+    uint16_t sw[2 * FT][NG];
+#pragma unroll
+    for (int t = 0; t < 2 * FT; ++t)
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg)
+            sw[t][gg] = *reinterpret_cast<const uint16_t*>(s_sc + (16 * t + row) * kFp4ScRow<NG, NW> +
+                                                          kl / 16 + 8 * gg);
     if (wave == 0 && q == 0) s_xs[row] = xs;
     floatx4_t acc[2 * FT];
 #pragma unroll
@@ -694,6 +717,7 @@ template <int NG, int NW, int FT>
 __global__ __launch_bounds__(64 * NW) void gateup_fp4_kernel(ExpertParams p) {
     __shared__ float s_part[NW][2 * FT][256];
     __shared__ float s_xs[16];
+    __shared__ __attribute__((aligned(16))) uint8_t s_sc[2 * FT * 16 * kFp4ScRow<NG, NW>];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, q = lane >> 4;
     const int d = p.dm.d;
@@ -712,26 +736,33 @@ __global__ __launch_bounds__(64 * NW) void gateup_fp4_kernel(ExpertParams p) {
     // order, so the activation loads that need it wait for it alone.
     const int sp = p.ws.sorted_pair[g.y + (row < g.z ? row : g.z - 1)];
     __builtin_amdgcn_sched_barrier(0);
+    // The block's scales (2 FT x 16 rows of d / 16 bytes) in 16-byte chunks,
+    // one per thread, coalesced; threads past the last chunk repeat it.
+    constexpr int kCpr = NG * NW / 2;  // chunks per row
+    constexpr int kChunks = 2 * FT * 16 * kCpr;
+    static_assert(kChunks <= 64 * NW, "one scale chunk per thread");
+    const int sc_c = tid < kChunks ? tid : kChunks - 1;
+    const int sc_r = sc_c / kCpr, sc_cc = sc_c % kCpr, sc_t = sc_r >> 4;
+    const size_t sc_wr = e * 2 * F + (size_t)(sc_t >= FT ? F : 0) + j0 + 16 * (sc_t % FT) + (sc_r & 15);
+    const uint4 sc_val = *reinterpret_cast<const uint4*>(wp.gus + sc_wr * (d / 16) + 16 * sc_cc);
+    uint4* sc_dst = reinterpret_cast<uint4*>(s_sc + sc_r * kFp4ScRow<NG, NW> + 16 * sc_cc);
     uint4 cw[2 * FT][NG];
-    uint16_t sw[2 * FT][NG];
 #pragma unroll
     for (int t = 0; t < 2 * FT; ++t) {
         const size_t wr = e * 2 * F + (size_t)(t >= FT ? F : 0) + j0 + 16 * (t % FT) + row;
         const uint8_t* crow = static_cast<const uint8_t*>(wp.gu) + wr * (d / 2) + kl / 2;
-        const uint8_t* srow = wp.gus + wr * (d / 16) + kl / 16;
 #pragma unroll
-        for (int gg = 0; gg < NG; ++gg) {
-            cw[t][gg] = *reinterpret_cast<const uint4*>(crow + 64 * gg);
-            sw[t][gg] = *reinterpret_cast<const uint16_t*>(srow + 8 * gg);
-        }
+        for (int gg = 0; gg < NG; ++gg) cw[t][gg] = *reinterpret_cast<const uint4*>(crow + 64 * gg);
     }
     const float tsg = wp.ts[e * 3 + 0], tsu = wp.ts[e * 3 + 1];
     const __amdgpu_buffer_rsrc_t xv = buffer_view(p.ws.x16, (uint32_t)p.dm.T * d * 2);
-    gateup_fp4_tile<NG, NW, FT>(p, g, is_shared, 0, sp, xv, kl, cw, sw, tsg, tsu, j0, s_part, s_xs);
+    gateup_fp4_tile<NG, NW, FT>(p, g, is_shared, 0, sp, xv, kl, cw, s_sc, true, tid < kChunks ? sc_dst : nullptr,
+                                sc_val, tsg, tsu, j0, s_part, s_xs);
     for (int r0 = 16; r0 < g.z; r0 += 16) {
         const int m = r0 + row;
         const int spn = p.ws.sorted_pair[g.y + (m < g.z ? m : g.z - 1)];
-        gateup_fp4_tile<NG, NW, FT>(p, g, is_shared, r0, spn, xv, kl, cw, sw, tsg, tsu, j0, s_part, s_xs);
+        gateup_fp4_tile<NG, NW, FT>(p, g, is_shared, r0, spn, xv, kl, cw, s_sc, false, nullptr, sc_val, tsg, tsu, j0,
+                                    s_part, s_xs);
     }
 }
 
@@ -741,7 +772,8 @@ __global__ __launch_bounds__(64 * NW) void gateup_fp4_kernel(ExpertParams p) {
 template <int NT, int NGMAX>
 __device__ __forceinline__ void down_fp4_tile(const ExpertParams& p, const int4& g, int r0, int ng, int kl, int n0,
                                               __amdgpu_buffer_rsrc_t hv_hi, __amdgpu_buffer_rsrc_t hv_lo,
-                                              uint4 (&cw)[NT][NGMAX], uint16_t (&sw)[NT][NGMAX], float ws,
+                                              uint4 (&cw)[NT][NGMAX], uint8_t* s_sc, bool first, int sc_o0,
+                                              int sc_o1, u32x4_t sc_v0, u32x4_t sc_v1, float ws,
                                               float (&s_part)[4][NT][256]) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, q = lane >> 4;
@@ -760,17 +792,25 @@ __device__ __forceinline__ void down_fp4_tile(const ExpertParams& p, const int4&
             hlo[st] = buffer_load16(hv_lo, ho + (128 * gg + 8 * st) * 2);
         }
         __builtin_amdgcn_sched_barrier(0);
+        // first tile (uniform): the block's scales go to LDS once the first h
+        // loads are in flight (see gateup_fp4_tile)
+        if (first && gg == 0) {
+            if (sc_o0 >= 0) *reinterpret_cast<u32x4_t*>(s_sc + sc_o0) = sc_v0;
+            if (sc_o1 >= 0) *reinterpret_cast<u32x4_t*>(s_sc + sc_o1) = sc_v1;
+            __syncthreads();
+        }
         // decode after the h loads are issued, and inside the token loop
         // (see gateup_fp4_tile)
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-            asm volatile("" : "+v"(cw[t][gg].x), "+v"(cw[t][gg].y), "+v"(cw[t][gg].z), "+v"(cw[t][gg].w),
-                         "+v"(sw[t][gg]));
+            asm volatile("" : "+v"(cw[t][gg].x), "+v"(cw[t][gg].y), "+v"(cw[t][gg].z), "+v"(cw[t][gg].w));
         Fp4Scale sc[NT][2];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            sc[t][0] = fp4_scale(__builtin_amdgcn_cvt_f32_fp8(sw[t][gg], 0));
-            sc[t][1] = fp4_scale(__builtin_amdgcn_cvt_f32_fp8(sw[t][gg], 1));
+            const uint16_t sw = *reinterpret_cast<const uint16_t*>(s_sc + (16 * t + row) * kFp4DownScRow<NGMAX> +
+                                                                  kl / 16 + 8 * gg);
+            sc[t][0] = fp4_scale(__builtin_amdgcn_cvt_f32_fp8(sw, 0));
+            sc[t][1] = fp4_scale(__builtin_amdgcn_cvt_f32_fp8(sw, 1));
         }
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
@@ -807,6 +847,7 @@ constexpr int kDownFp4Tiles = 4;  // 64 output rows per block
 template <int NT, int NGMAX>
 __global__ __launch_bounds__(256) void down_fp4_kernel(ExpertParams p) {
     __shared__ float s_part[4][NT][256];
+    __shared__ __attribute__((aligned(16))) uint8_t s_sc[16 * NT * kFp4DownScRow<NGMAX>];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, q = lane >> 4;
     const int d = p.dm.d;
@@ -824,18 +865,28 @@ __global__ __launch_bounds__(256) void down_fp4_kernel(ExpertParams p) {
     const size_t e = is_shared ? 0 : (size_t)g.x;
     const WeightPtrs& wp = is_shared ? p.shared : p.routed;
     const int n0 = rb * 16 * NT;
+    // The block's scales (16 NT rows of F / 16 bytes) in 16-byte chunks, at
+    // most two per thread, coalesced; chunks past the last repeat it.
+    static_assert(16 * NT * 2 * NGMAX <= 2 * 256, "two scale chunks per thread");
+    const int cpr = F / 256, nchunks = 16 * NT * cpr;
+    auto sc_chunk = [&](int ci, u32x4_t& v) {  // LDS offset of chunk ci, or -1 past the last
+        const int cc = ci < nchunks ? ci : nchunks - 1;
+        const int r = cc / cpr, col = cc % cpr;
+        const size_t wr = e * (size_t)d + (size_t)(n0 + r);
+        v = *reinterpret_cast<const u32x4_t*>(wp.dns + wr * (F / 16) + 16 * col);
+        return ci < nchunks ? r * kFp4DownScRow<NGMAX> + 16 * col : -1;
+    };
+    u32x4_t sc_v0, sc_v1;
+    const int sc_o0 = sc_chunk(tid, sc_v0), sc_o1 = sc_chunk(tid + 256, sc_v1);
     uint4 cw[NT][NGMAX];
-    uint16_t sw[NT][NGMAX];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         const size_t wr = e * (size_t)d + (size_t)(n0 + 16 * t + row);
         const uint8_t* crow = static_cast<const uint8_t*>(wp.dn) + wr * (F / 2) + kl / 2;
-        const uint8_t* srow = wp.dns + wr * (F / 16) + kl / 16;
 #pragma unroll
         for (int gg = 0; gg < NGMAX; ++gg) {
             const int gc = gg < ng ? gg : 0;  // clamped: groups past ng are loaded but unused
             cw[t][gg] = *reinterpret_cast<const uint4*>(crow + 64 * gc);
-            sw[t][gg] = *reinterpret_cast<const uint16_t*>(srow + 8 * gc);
         }
     }
     const float tsd = wp.ts[e * 3 + 2] / kHScale;
@@ -845,11 +896,13 @@ __global__ __launch_bounds__(256) void down_fp4_kernel(ExpertParams p) {
     const uint32_t vbytes = (uint32_t)g.z * p.hstride * 2;
     const __amdgpu_buffer_rsrc_t hv_hi = buffer_view(h16 + (size_t)g.w * p.hstride, vbytes);
     const __amdgpu_buffer_rsrc_t hv_lo = buffer_view(h16 + plane + (size_t)g.w * p.hstride, vbytes);
-    down_fp4_tile<NT, NGMAX>(p, g, 0, ng, kl, n0, hv_hi, hv_lo, cw, sw, tsd * rw0, s_part);
+    down_fp4_tile<NT, NGMAX>(p, g, 0, ng, kl, n0, hv_hi, hv_lo, cw, s_sc, true, sc_o0, sc_o1, sc_v0, sc_v1,
+                             tsd * rw0, s_part);
     for (int r0 = 16; r0 < g.z; r0 += 16) {
         const int m = r0 + mm;
         const float rw = is_shared ? 1.f : p.ws.sorted_wt[g.y + (m < g.z ? m : g.z - 1)];
-        down_fp4_tile<NT, NGMAX>(p, g, r0, ng, kl, n0, hv_hi, hv_lo, cw, sw, tsd * rw, s_part);
+        down_fp4_tile<NT, NGMAX>(p, g, r0, ng, kl, n0, hv_hi, hv_lo, cw, s_sc, false, -1, -1, sc_v0, sc_v1,
+                                 tsd * rw, s_part);
     }
 }
 
