@@ -46,15 +46,17 @@ def test_small_nvfp4_decode(T):
     _case(4, T, d=256, E=32, k=4, f=64, fs=64)
 
 
-@pytest.mark.parametrize("T", [1, 23, 64])
+@pytest.mark.parametrize("T", [1, 9, 16, 23, 64])
 def test_small_nvfp4_matrix_core_path(T):
-    # d, f, fs multiples of 512 select the NVFP4 matrix-core expert kernels
+    # d, f, fs multiples of 512 select the NVFP4 matrix-core expert kernels;
+    # the shared expert has more features than a routed one
     _case(4, T, d=512, E=32, k=4, f=512, fs=1024)
 
 
-def test_nvfp4_matrix_core_path_d1024_ragged_f():
+@pytest.mark.parametrize("T", [5, 19])
+def test_nvfp4_matrix_core_path_d1024_ragged_f(T):
     # f = 1536: three 128-groups per wave in the down kernel
-    _case(4, 19, d=1024, E=16, k=3, f=1536, fs=512)
+    _case(4, T, d=1024, E=16, k=3, f=1536, fs=512)
 
 
 @pytest.mark.parametrize("T", [1, 7, 40, 64])
