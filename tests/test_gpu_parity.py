@@ -124,8 +124,35 @@ def test_no_shared_expert_decode_then_prefill_same_handle():
         print("no shared expert T=%d: %s" % (T, rep), flush=True)
 
 
+@pytest.mark.parametrize("T,flags", [(48, 0), (700, FLINT_FORCE_PREFILL_PATH), (300, FLINT_FORCE_DECODE_PATH)])
+def test_every_token_picks_the_same_experts(T, flags):
+    # degenerate routing: a router bias makes every token choose the same k
+    # experts (in a fixed order), so k groups hold all T tokens and every
+    # other expert is empty; one prefill group spans several 256-row tiles
+    L = synth.layer(1, d=256, E=64, f=128, fs=128)
+    b = np.zeros(64, np.float32)
+    chosen = [63, 3, 40, 9, 33, 17]
+    b[chosen] = [60.0, 50.0, 40.0, 30.0, 20.0, 10.0]
+    L["router_bias"] = b
+    c = L["cfg"]
+    x = synth.hidden(1, T, 256, synth.BF16, draw=5)
+    layer = make_layer_obj(c, T, flags)
+    out, rout = run_gpu(layer, dev_layer(L), x)
+    assert np.array_equal(rout["idx"], np.tile(np.array(chosen), (T, 1)))
+    ref = run_oracle(L, x)
+    rep = compare(out, rout, ref, c["k"], c["wdtype"], out_bf16=True)
+    check_permutation(rout, T, c["k"], c["E"])
+    print("same experts T=%d flags=%d: %s" % (T, flags, rep), flush=True)
+
+
 def test_odd_expert_count_and_k8():
     _case(1, 20, d=128, E=100, k=8, f=32, fs=32)
+
+
+@pytest.mark.parametrize("flags", [0, FLINT_FORCE_PREFILL_PATH])
+def test_every_expert_chosen(flags):
+    # k = E: each token takes every expert (a dense softmax mixture)
+    _case(1, 13, flags=flags, d=256, E=8, k=8, f=128, fs=128)
 
 
 def test_top1():
