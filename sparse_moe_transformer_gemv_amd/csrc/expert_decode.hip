@@ -515,10 +515,11 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertParams p) {
 // significant bits, within 2^-10 .. 2688 in magnitude), so it is exact in f16:
 // the hardware convert of a pair of codes applies the power-of-two part of the
 // block scale exactly, and one packed f16 multiply applies its 3-bit mantissa
-// (1 VALU per weight).  Activations enter as f16 scaled by a per-token power of
-// two (exact for every value above the f16 normal range's floor), the
-// hidden state h as two f16 parts (hi + lo, 22 significant bits).  The tensor
-// scale and the power-of-two factors multiply the finished fp32 sums.
+// (1 VALU per weight).  Activations enter as f16 scaled by a power of two per
+// token and wave k range (see x_tile_to_f16; exact for every value above the
+// f16 normal range's floor), the hidden state h as two f16 parts (hi + lo, 22
+// significant bits).  The tensor scale and the power-of-two factors multiply
+// the fp32 sums.
 //
 // Lane quarter q of a 128-wide k group holds elements 32 q .. 32 q + 31, eight
 // per MFMA step: the same permutation of k for activations and weights, which
@@ -575,48 +576,49 @@ constexpr int kFp4DownScRow = 32 * NGMAX + 16;
 // h * 2^-8 (headroom above the f16 range for large activations).
 constexpr float kHScale = 1.0f / 256.0f;
 
-// Activations to f16 for the NVFP4 kernels: per token, x * 2^-e with e chosen
-// so that the largest magnitude lands in [2^14, 2^15); xscale = 2^e.
-__global__ __launch_bounds__(256) void x_to_f16_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ x16,
-                                                       float* __restrict__ xscale, int d) {
-    __shared__ float s_max[4];
-    const int t = blockIdx.x, tid = threadIdx.x;
-    const uint16_t* xr = x + (size_t)t * d;
-    float m = 0.f;
-    for (int k = tid * 8; k < d; k += 256 * 8) {
-        const uint4 v = *reinterpret_cast<const uint4*>(xr + k);
-        m = fmaxf(m, fmaxf(fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x))), fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y)))));
-        m = fmaxf(m, fmaxf(fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))), fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w)))));
-    }
+// Activations to f16 inside the NVFP4 gate/up kernel.  The four lanes of a
+// token row in one wave (lanes row + 16 q) hold that token's whole k range of
+// the wave (its d / NW activations); their largest magnitude sets a power of
+// two 2^-e that brings it into [2^14, 2^15), the bf16 values are scaled by it
+// (exact) and rounded to f16, and the wave's fp32 partial sums for that token
+// are multiplied back by 2^e (exact) before the waves' sums are added.
+template <int NG>
+__device__ __forceinline__ float x_tile_to_f16(uint4 (&a)[NG][4]) {
+    // largest |x| of this lane's values, as bf16 bits (two 16-bit lanes at a time)
+    typedef __attribute__((ext_vector_type(2))) unsigned short u16x2_t;
+    u16x2_t m2 = {0, 0};
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-    if ((tid & 63) == 0) s_max[tid >> 6] = m;
-    __syncthreads();
-    m = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
-    // exponent of m (m > 0 and finite); e = exp - 14 puts m in [2^14, 2^15)
-    int e = 0;
-    if (m > 0.f && m <= 3.4e38f) e = (int)((__float_as_uint(m) >> 23) & 0xFF) - 127 - 14;
-    e = e < -100 ? -100 : (e > 100 ? 100 : e);
-    const float inv = ldexpf(1.f, -e);
-    if (tid == 0) xscale[t] = ldexpf(1.f, e);
-    uint16_t* yr = x16 + (size_t)t * d;
-    for (int k = tid * 8; k < d; k += 256 * 8) {
-        const uint4 v = *reinterpret_cast<const uint4*>(xr + k);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        uint32_t o[4];
+    for (int gg = 0; gg < NG; ++gg)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const half2_t hv = {(_Float16)(bf16_lo(w[i]) * inv), (_Float16)(bf16_hi(w[i]) * inv)};
-            o[i] = __builtin_bit_cast(uint32_t, hv);
+        for (int st = 0; st < 4; ++st) {
+            const uint32_t w[4] = {a[gg][st].x, a[gg][st].y, a[gg][st].z, a[gg][st].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, w[i] & 0x7FFF7FFFu));
         }
-        *reinterpret_cast<uint4*>(yr + k) = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-}
-
-hipError_t launch_x_to_f16(const LayerArgs& a, const Workspace& w, hipStream_t s) {
-    hipLaunchKernelGGL(x_to_f16_kernel, dim3(a.dm.T), dim3(256), 0, s, static_cast<const uint16_t*>(a.x), w.x16,
-                       w.xscale, a.dm.d);
-    return hipGetLastError();
+    uint32_t mx = m2.x > m2.y ? m2.x : m2.y;
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16, 64));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32, 64));
+    // biased exponent E of the maximum: scale 2^(141 - E) puts it in [2^14, 2^15),
+    // limited to 2^127 for tiny rows and to 1 for rows of zeros or past the group
+    const int E = (int)(mx >> 7);
+    int sb = mx == 0 ? 127 : 268 - E;  // biased exponent of the scale
+    sb = sb < 1 ? 1 : (sb > 254 ? 254 : sb);
+    const float sc = __uint_as_float((uint32_t)sb << 23);
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg)
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            uint32_t w[4] = {a[gg][st].x, a[gg][st].y, a[gg][st].z, a[gg][st].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const half2_t h = {(_Float16)(__uint_as_float(w[i] << 16) * sc),
+                                   (_Float16)(__uint_as_float(w[i] & 0xFFFF0000u) * sc)};
+                w[i] = __builtin_bit_cast(uint32_t, h);
+            }
+            a[gg][st] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    return __uint_as_float((uint32_t)(254 - sb) << 23);  // 1 / sc, exact
 }
 
 // One 16-token tile of an NVFP4 gate/up block (see gateup_fp4_kernel).  sp is
@@ -625,8 +627,7 @@ template <int NG, int NW, int FT>
 __device__ __forceinline__ void gateup_fp4_tile(const ExpertParams& p, const int4& g, bool is_shared, int r0,
                                                 int sp, __amdgpu_buffer_rsrc_t xv, int kl, uint4 (&cw)[2 * FT][NG],
                                                 const uint8_t* s_sc, bool first, uint4* sc_dst, const uint4& sc_val,
-                                                float tsg, float tsu, int j0, float (&s_part)[NW][2 * FT][256],
-                                                float (&s_xs)[16]) {
+                                                float tsg, float tsu, int j0, float (&s_part)[NW][2 * FT][256]) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, q = lane >> 4;
     const int d = p.dm.d;
@@ -638,7 +639,6 @@ __device__ __forceinline__ void gateup_fp4_tile(const ExpertParams& p, const int
     for (int gg = 0; gg < NG; ++gg)
 #pragma unroll
         for (int st = 0; st < 4; ++st) a[gg][st] = buffer_load16(xv, xo + (128 * gg + 8 * st) * 2);
-    const float xs = p.ws.xscale[m < g.z ? tok : 0];
     __builtin_amdgcn_sched_barrier(0);
     // first tile (uniform): the block's scales, loaded before the codes, go to
     // LDS once every load of the tile is in flight (sc_dst is null for threads
@@ -664,7 +664,7 @@ __device__ __forceinline__ void gateup_fp4_tile(const ExpertParams& p, const int
         for (int gg = 0; gg < NG; ++gg)
             sw[t][gg] = *reinterpret_cast<const uint16_t*>(s_sc + (16 * t + row) * kFp4ScRow<NG, NW> +
                                                           kl / 16 + 8 * gg);
-    if (wave == 0 && q == 0) s_xs[row] = xs;
+    const float xinv = x_tile_to_f16<NG>(a);  // 2^e of this lane's token row
     floatx4_t acc[2 * FT];
 #pragma unroll
     for (int t = 0; t < 2 * FT; ++t) acc[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
@@ -679,10 +679,14 @@ __device__ __forceinline__ void gateup_fp4_tile(const ExpertParams& p, const int
                 acc[t] = mfma16x16x32_f16(a[gg][st], fp4x8_to_f16(u4_word(cw[t][gg], st), st < 2 ? s0 : s1), acc[t]);
         }
     }
+    // acc[t][i] belongs to token row 4 q + i, whose scale lane 4 q + i holds
+    float xr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xr[i] = __shfl(xinv, 4 * q + i, 64);
 #pragma unroll
     for (int t = 0; t < 2 * FT; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s_part[wave][t][(4 * q + i) * 16 + row] = acc[t][i];
+        for (int i = 0; i < 4; ++i) s_part[wave][t][(4 * q + i) * 16 + row] = acc[t][i] * xr[i];
     __syncthreads();
     // thread -> (feature tile ft, token row mm, feature n); tiles ft (gate) and FT + ft (up)
     for (int idx = tid; idx < 256 * FT; idx += 64 * NW) {
@@ -694,8 +698,7 @@ __device__ __forceinline__ void gateup_fp4_tile(const ExpertParams& p, const int
             gs += s_part[w][ft][o];
             us += s_part[w][FT + ft][o];
         }
-        const float xsm = s_xs[mm];
-        const float hv = silu_f32(tsg * xsm * gs) * (tsu * xsm * us) * kHScale;
+        const float hv = silu_f32(tsg * gs) * (tsu * us) * kHScale;
         const _Float16 hi = (_Float16)hv;
         const _Float16 lo = (_Float16)(hv - (float)hi);
         uint16_t* h16 = static_cast<uint16_t*>(p.ws.h);
@@ -716,7 +719,6 @@ __device__ __forceinline__ void gateup_fp4_tile(const ExpertParams& p, const int
 template <int NG, int NW, int FT>
 __global__ __launch_bounds__(64 * NW) void gateup_fp4_kernel(ExpertParams p) {
     __shared__ float s_part[NW][2 * FT][256];
-    __shared__ float s_xs[16];
     __shared__ __attribute__((aligned(16))) uint8_t s_sc[2 * FT * 16 * kFp4ScRow<NG, NW>];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, q = lane >> 4;
@@ -755,14 +757,14 @@ __global__ __launch_bounds__(64 * NW) void gateup_fp4_kernel(ExpertParams p) {
         for (int gg = 0; gg < NG; ++gg) cw[t][gg] = *reinterpret_cast<const uint4*>(crow + 64 * gg);
     }
     const float tsg = wp.ts[e * 3 + 0], tsu = wp.ts[e * 3 + 1];
-    const __amdgpu_buffer_rsrc_t xv = buffer_view(p.ws.x16, (uint32_t)p.dm.T * d * 2);
+    const __amdgpu_buffer_rsrc_t xv = buffer_view(p.x, (uint32_t)p.dm.T * d * 2);
     gateup_fp4_tile<NG, NW, FT>(p, g, is_shared, 0, sp, xv, kl, cw, s_sc, true, tid < kChunks ? sc_dst : nullptr,
-                                sc_val, tsg, tsu, j0, s_part, s_xs);
+                                sc_val, tsg, tsu, j0, s_part);
     for (int r0 = 16; r0 < g.z; r0 += 16) {
         const int m = r0 + row;
         const int spn = p.ws.sorted_pair[g.y + (m < g.z ? m : g.z - 1)];
         gateup_fp4_tile<NG, NW, FT>(p, g, is_shared, r0, spn, xv, kl, cw, s_sc, false, nullptr, sc_val, tsg, tsu, j0,
-                                    s_part, s_xs);
+                                    s_part);
     }
 }
 

@@ -29,8 +29,6 @@ struct Workspace {
     float* rpart;        // [d/256][64][E] split-K router partial logits (decode, T <= 64)
     int* rcount;         // [4 ceil(E/16) + 8] router tickets, zero between launches
     uint16_t* w3;        // [3][E][d] router split into exact hi, mid, lo bf16 planes (prefill)
-    uint16_t* x16;       // [Tm][d] f16 activations scaled by 2^-xexp (NVFP4 decode)
-    float* xscale;       // [Tm] 2^xexp per token (NVFP4 decode)
     float* sorted_wt;    // [k*Tm] combine weight of each sorted pair (wts[sorted_pair[i]])
     int4* groups;        // [E+1] active groups {expert (E = shared), first sorted index, rows, first slot}
     int* n_groups;       // [1]
@@ -81,7 +79,6 @@ hipError_t launch_sort(const LayerArgs& a, const Workspace& w, int bm, hipStream
 hipError_t launch_gateup_decode(const LayerArgs& a, const Workspace& w, hipStream_t s);
 hipError_t launch_down_decode(const LayerArgs& a, const Workspace& w, hipStream_t s);
 bool decode_fp4_ok(const Dims& dm);
-hipError_t launch_x_to_f16(const LayerArgs& a, const Workspace& w, hipStream_t s);
 hipError_t launch_gateup_prefill(const LayerArgs& a, const Workspace& w, int n_cu, hipStream_t s);
 hipError_t launch_down_prefill(const LayerArgs& a, const Workspace& w, int n_cu, hipStream_t s);
 hipError_t launch_combine(const LayerArgs& a, const Workspace& w, bool y_bf16, hipStream_t s);

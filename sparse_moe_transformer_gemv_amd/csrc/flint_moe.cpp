@@ -141,8 +141,6 @@ size_t carve(const flint_moe_config& c, char* base, Workspace* w) {
     w->rpart = static_cast<float*>(take((size_t)(c.d_model / 256 > 0 ? c.d_model / 256 : 1) * 64 * E * 4));
     w->rcount = static_cast<int*>(take((4 * ((E + 15) / 16) + 8) * 4));
     w->w3 = static_cast<uint16_t*>(take(3 * E * (size_t)c.d_model * 2));
-    w->x16 = static_cast<uint16_t*>(take(Tm * (size_t)c.d_model * 2));
-    w->xscale = static_cast<float*>(take(Tm * 4));
     w->groups = static_cast<int4*>(take((E + 1) * 16));
     w->n_groups = static_cast<int*>(take(4));
     w->tiles = static_cast<int2*>(take(max_tiles * 8));
@@ -368,10 +366,6 @@ flint_status flint_moe_forward(flint_moe_t h, int32_t T, const void* hidden, con
             e = launch_route_decode(a, h->ws, stream);
     }
     if (e != hipSuccess) return hip_fail(e, "route kernel");
-    if (decode_fp4_ok(a.dm)) {
-        e = launch_x_to_f16(a, h->ws, stream);
-        if (e != hipSuccess) return hip_fail(e, "activation convert kernel");
-    }
     {
         Timer tm(h, FLINT_KERNEL_EXPERT_UP, stream);
         e = launch_gateup_decode(a, h->ws, stream);
