@@ -46,10 +46,11 @@ def test_small_nvfp4_decode(T):
     _case(4, T, d=256, E=32, k=4, f=64, fs=64)
 
 
-@pytest.mark.parametrize("T", [1, 9, 16, 23, 64])
+@pytest.mark.parametrize("T", [1, 9, 16, 23, 64, 150])
 def test_small_nvfp4_matrix_core_path(T):
     # d, f, fs multiples of 512 select the NVFP4 matrix-core expert kernels;
-    # the shared expert has more features than a routed one
+    # the shared expert has more features than a routed one; NVFP4 layers
+    # always take the decode path, so T = 150 runs it above 64 tokens
     _case(4, T, d=512, E=32, k=4, f=512, fs=1024)
 
 
