@@ -156,6 +156,12 @@ def test_every_expert_chosen(flags):
     _case(1, 13, flags=flags, d=256, E=8, k=8, f=128, fs=128)
 
 
+@pytest.mark.parametrize("flags", [0, FLINT_FORCE_PREFILL_PATH])
+def test_single_expert(flags):
+    # E = 1, k = 1: one routed expert (weight 1) plus the shared one
+    _case(1, 21, flags=flags, d=256, E=1, k=1, f=128, fs=128)
+
+
 def test_top1():
     _case(1, 11, d=128, E=64, k=1, f=32, fs=32)
 
