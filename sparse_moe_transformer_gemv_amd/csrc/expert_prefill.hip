@@ -20,14 +20,20 @@
 // gate rows then the matching 32 up rows of features 32q..32q+31, so each wave
 // holds matching gate and up columns and applies SwiGLU in registers.
 //
-// K advances in stages of 32 through four 32 KiB LDS buffers, filled straight
-// from global memory (direct-to-LDS 16-byte loads) three stages ahead; 16-byte
-// chunks of each 64-byte LDS row are XOR-swizzled by row so fragment reads are
-// free of bank conflicts.  The two waves of a SIMD run a ping-pong schedule:
-// waves 0-3 and 4-7 are kept one phase apart by workgroup barriers, so while
-// one group issues its 32 MFMAs of a stage the other reads its fragments of
-// that stage from LDS and issues the loads of a later one, and the matrix
-// pipe never waits for LDS.
+// K advances in pairs of 32-wide sub-stages through two 64 KiB LDS buffers,
+// filled straight from global memory with direct-to-LDS 16-byte loads of whole
+// 128-byte lines (8 rows x 128 bytes per load: on this part that moves about a
+// third more bytes per clock than 16 rows x 64 bytes); 16-byte chunks of each
+// 128-byte LDS row are XOR-swizzled by row so fragment reads are free of bank
+// conflicts.  One barrier per pair: after it a pair's data is visible to every
+// wave and the other buffer is free for the next pair, whose loads fly while
+// the two sub-stages run.  The two waves of a SIMD interleave on their own
+// (one issues MFMAs while the other reads fragments); keeping them one phase
+// apart with a barrier per phase measured slower.
+//
+// Rows of a tile past its group's end are neither loaded (their lanes get
+// out-of-range buffer offsets) nor multiplied (their 16-row MFMA blocks are
+// skipped); they are not stored.
 //
 // Scheduling: a persistent grid (one workgroup per CU) walks the tiles; the
 // tile range is cut into 8 contiguous chunks, one per XCD (workgroups are
@@ -40,10 +46,10 @@ namespace flint {
 
 constexpr int PBM = 256;  // rows per tile (the sort's tile height)
 constexpr int PBN = 256;  // B rows per tile
-constexpr int PBK = 32;   // k per stage
-constexpr int kNStage = 4;
-constexpr int kStageBytes = (PBM + PBN) * PBK * 2;  // 32 KiB
-constexpr int kLdsBytes = kNStage * kStageBytes;     // 128 KiB
+constexpr int PBK = 32;   // k per MFMA step (one sub-stage)
+constexpr int kRowBytes = 128;                    // an LDS row holds k = 64 (two sub-stages)
+constexpr int kPairBytes = (PBM + PBN) * kRowBytes;  // 64 KiB: A rows, then B rows
+constexpr int kLdsBytes = 2 * kPairBytes;            // 128 KiB
 static_assert(PBM == kPrefillBM, "tile height must match the sort's tile list");
 
 struct PrefillParams {
@@ -57,17 +63,20 @@ struct PrefillParams {
 
 enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
 
-// byte offset of 16-byte chunk `chunk` (k = 8 chunk .. +7) of LDS row `row`
+// Byte offset of 16-byte chunk `chunk` (k = 8 chunk .. +7 of the pair's 64) of
+// LDS row `row`: the 8 chunks of a 128-byte row are XOR-swizzled by row & 7, so
+// the fragment reads (one chunk column of 16 consecutive rows per 16 lanes)
+// are free of LDS bank conflicts (measured).
 __device__ __forceinline__ uint32_t swz(int row, int chunk) {
-    return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4);
+    return row * kRowBytes + ((chunk ^ (row & 7)) << 4);
 }
 
 constexpr int kThreads = 512;
 
-// Fragments of one stage: 8 A and NI B 16-byte LDS reads, 16 rows (1 KiB)
+// Fragments of one sub-stage: 8 A and NI B 16-byte LDS reads, 16 rows (2 KiB)
 // apart, from two per-lane base addresses, issued together and waited for
 // inside the same asm block.  Written as asm because the compiler cannot tell
-// these reads from the direct-to-LDS loads still in flight into other stages
+// these reads from the direct-to-LDS loads still in flight into the other buffer
 // and would otherwise wait for all of them (vmcnt 0) first.
 typedef __attribute__((ext_vector_type(4))) uint32_t frag_t;
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -80,17 +89,17 @@ __device__ __forceinline__ void read_frags<4>(uint32_t a_base, uint32_t b_base, 
     frag_t a0, a1, a2, a3, a4, a5, a6, a7, b0, b1, b2, b3;
     asm volatile(
         "ds_read_b128 %0, %12 offset:0\n\t"
-        "ds_read_b128 %1, %12 offset:1024\n\t"
-        "ds_read_b128 %2, %12 offset:2048\n\t"
-        "ds_read_b128 %3, %12 offset:3072\n\t"
-        "ds_read_b128 %4, %12 offset:4096\n\t"
-        "ds_read_b128 %5, %12 offset:5120\n\t"
-        "ds_read_b128 %6, %12 offset:6144\n\t"
-        "ds_read_b128 %7, %12 offset:7168\n\t"
+        "ds_read_b128 %1, %12 offset:2048\n\t"
+        "ds_read_b128 %2, %12 offset:4096\n\t"
+        "ds_read_b128 %3, %12 offset:6144\n\t"
+        "ds_read_b128 %4, %12 offset:8192\n\t"
+        "ds_read_b128 %5, %12 offset:10240\n\t"
+        "ds_read_b128 %6, %12 offset:12288\n\t"
+        "ds_read_b128 %7, %12 offset:14336\n\t"
         "ds_read_b128 %8, %13 offset:0\n\t"
-        "ds_read_b128 %9, %13 offset:1024\n\t"
-        "ds_read_b128 %10, %13 offset:2048\n\t"
-        "ds_read_b128 %11, %13 offset:3072\n\t"
+        "ds_read_b128 %9, %13 offset:2048\n\t"
+        "ds_read_b128 %10, %13 offset:4096\n\t"
+        "ds_read_b128 %11, %13 offset:6144\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(a4), "=&v"(a5), "=&v"(a6), "=&v"(a7), "=&v"(b0),
           "=&v"(b1), "=&v"(b2), "=&v"(b3)
@@ -113,15 +122,15 @@ __device__ __forceinline__ void read_frags<2>(uint32_t a_base, uint32_t b_base, 
     frag_t a0, a1, a2, a3, a4, a5, a6, a7, b0, b1;
     asm volatile(
         "ds_read_b128 %0, %10 offset:0\n\t"
-        "ds_read_b128 %1, %10 offset:1024\n\t"
-        "ds_read_b128 %2, %10 offset:2048\n\t"
-        "ds_read_b128 %3, %10 offset:3072\n\t"
-        "ds_read_b128 %4, %10 offset:4096\n\t"
-        "ds_read_b128 %5, %10 offset:5120\n\t"
-        "ds_read_b128 %6, %10 offset:6144\n\t"
-        "ds_read_b128 %7, %10 offset:7168\n\t"
+        "ds_read_b128 %1, %10 offset:2048\n\t"
+        "ds_read_b128 %2, %10 offset:4096\n\t"
+        "ds_read_b128 %3, %10 offset:6144\n\t"
+        "ds_read_b128 %4, %10 offset:8192\n\t"
+        "ds_read_b128 %5, %10 offset:10240\n\t"
+        "ds_read_b128 %6, %10 offset:12288\n\t"
+        "ds_read_b128 %7, %10 offset:14336\n\t"
         "ds_read_b128 %8, %11 offset:0\n\t"
-        "ds_read_b128 %9, %11 offset:1024\n\t"
+        "ds_read_b128 %9, %11 offset:2048\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(a4), "=&v"(a5), "=&v"(a6), "=&v"(a7), "=&v"(b0),
           "=&v"(b1)
@@ -138,8 +147,8 @@ __device__ __forceinline__ void read_frags<2>(uint32_t a_base, uint32_t b_base, 
     fb[1] = make_uint4(b1.x, b1.y, b1.z, b1.w);
 }
 
-// A barrier that no instruction is scheduled across (the MFMAs of a compute
-// phase must stay between its two barriers for the ping-pong to hold).
+// A workgroup barrier that keeps this wave's loads in flight (no vmcnt wait)
+// and that no instruction is scheduled across.
 __device__ __forceinline__ void phase_barrier() {
     __builtin_amdgcn_sched_barrier(0);
     barrier_keep_loads();
@@ -158,49 +167,66 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
     constexpr int BN = 64 * NI;  // B rows of the tile
     constexpr int HS = 8 * NI;   // gate/up: features per wave (gate rows, then as many up rows)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 2, wn = wave & 3;  // wm is also the ping-pong group
+    const int wm = wave >> 2, wn = wave & 3;
     const int row16 = lane & 15, q = lane >> 4;
     const int d = p.dm.d;
     const uint32_t lds0 = lds_addr(lds);
-    // this lane's fragment base addresses within a stage
+    // this lane's fragment base addresses within a pair buffer, sub-stage 0
+    // (sub-stage 1 reads logical chunk q + 4: address bit 6 flipped)
     const uint32_t a_rd = swz(128 * wm + row16, q);
-    const uint32_t b_rd = PBM * PBK * 2 + swz(BN / 4 * wn + row16, q);
+    const uint32_t b_rd = PBM * kRowBytes + swz(BN / 4 * wn + row16, q);
     const bool is_shared = g.x == p.dm.E;
     const int F = is_shared ? p.dm.fs : p.dm.f;
     const int rows = min(PBM, g.z - m0);
     const size_t e = is_shared ? 0 : (size_t)g.x;
     const WeightPtrs& wp = is_shared ? p.shared : p.routed;
     const int K = MODE == MODE_GATEUP ? d : F;
+    // 16-row MFMA blocks of this wave's 128 rows that hold rows of the group
+    const int nmi = (min(max(rows - 128 * wm, 0), 128) + 15) >> 4;
 
-    // Load slots: A slot j (0, 1) of this wave fills LDS rows 32 wave + 16 j ..
-    // +15 of the A half of a stage, B slot j (< NI / 2) rows BN / 8 wave + 16 j
-    // .. +15 of the B half; lane l fills row (l >> 2) of a slot, physical chunk
-    // l & 3.  Per-lane global sources (logical chunk of the lane's slot):
-    const uint16_t* asrc[2];
-    const uint16_t* bsrc[NI / 2];
+    // Load slots: A slot j (< 4) of this wave fills LDS rows 32 wave + 8 j .. +7
+    // of the A part of a pair buffer, B slot j (< NI) rows BN / 8 wave + 8 j ..
+    // +7 of the B part; lane l fills row (l >> 3) of a slot, physical chunk l & 7,
+    // so each load moves whole 128-byte lines of 8 rows.  Both operands go through
+    // buffer views: the lanes of A padding rows (past the group's end) fetch
+    // nothing, and every offset fits 32 bits.
+    __amdgpu_buffer_rsrc_t aview, bview;
+    uint32_t aoff[4];   // byte offset of the lane's A chunk at k = 0 (kOffNone: padding)
+    uint32_t boff[NI];  // byte offset of the lane's B chunk at k = 0
+    if (MODE == MODE_GATEUP) {
+        aview = buffer_view(p.x, (uint32_t)((size_t)p.dm.T * d * 2));
+        bview = buffer_view(static_cast<const uint16_t*>(wp.gu) + e * 2 * F * (size_t)K,
+                            (uint32_t)((size_t)2 * F * K * 2));
+    } else {
+        // the tile's rows of h are contiguous: view exactly those
+        aview = buffer_view(static_cast<const uint16_t*>(p.ws.h) + (size_t)(g.w + m0) * p.hstride,
+                            (uint32_t)((size_t)rows * p.hstride * 2));
+        bview = buffer_view(static_cast<const uint16_t*>(wp.dn) + e * (size_t)d * K, (uint32_t)((size_t)d * K * 2));
+    }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int r = 32 * wave + 16 * j + (lane >> 2);
-        const int c = (lane & 3) ^ ((r >> 1) & 3);
-        const int m = r < rows ? r : 0;  // padding rows repeat row 0; never stored
-        if (MODE == MODE_GATEUP) {
-            const int mm = m0 + m;
+    for (int j = 0; j < 4; ++j) {
+        const int r = 32 * wave + 8 * j + (lane >> 3);
+        const int c = (lane & 7) ^ (r & 7);  // logical chunk landing in physical chunk lane & 7
+        if (r >= rows) {
+            aoff[j] = kOffNone;
+        } else if (MODE == MODE_GATEUP) {
+            const int mm = m0 + r;
             const int tok = is_shared ? mm : p.ws.sorted_pair[g.y + mm] / p.dm.k;
-            asrc[j] = p.x + (size_t)tok * d + 8 * c;
+            aoff[j] = (uint32_t)(((size_t)tok * d + 8 * c) * 2);
         } else {
-            asrc[j] = static_cast<const uint16_t*>(p.ws.h) + (size_t)(g.w + m0 + m) * p.hstride + 8 * c;
+            aoff[j] = (uint32_t)(((size_t)r * p.hstride + 8 * c) * 2);
         }
     }
 #pragma unroll
-    for (int j = 0; j < NI / 2; ++j) {
-        const int r = BN / 8 * wave + 16 * j + (lane >> 2);
-        const int c = (lane & 3) ^ ((r >> 1) & 3);
+    for (int j = 0; j < NI; ++j) {
+        const int r = BN / 8 * wave + 8 * j + (lane >> 3);
+        const int c = (lane & 7) ^ (r & 7);
         if (MODE == MODE_GATEUP) {
             const int seg = r / HS, rr = r % HS;  // even: gate rows, odd: the matching up rows
-            const size_t wrow = e * 2 * F + (size_t)((seg & 1) ? F : 0) + nb0 + HS * (seg >> 1) + rr;
-            bsrc[j] = static_cast<const uint16_t*>(wp.gu) + wrow * K + 8 * c;
+            const int wrow = ((seg & 1) ? F : 0) + nb0 + HS * (seg >> 1) + rr;
+            boff[j] = (uint32_t)(((size_t)wrow * K + 8 * c) * 2);
         } else {
-            bsrc[j] = static_cast<const uint16_t*>(wp.dn) + (e * (size_t)d + nb0 + r) * K + 8 * c;
+            boff[j] = (uint32_t)(((size_t)(nb0 + r) * K + 8 * c) * 2);
         }
     }
 
@@ -210,60 +236,53 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-    // loads per wave and stage: 2 A + NI / 2 B
-    constexpr int LPS = 2 + NI / 2;
-    auto issue = [&](int s_) {
-        unsigned char* st_ = lds + (s_ & (kNStage - 1)) * kStageBytes;
-        const int k0_ = s_ * PBK;
+    // k advances in pairs of sub-stages (k = 64 per pair); pair pp lands in buffer pp & 1
+    auto issue = [&](int pp) {
+        unsigned char* st_ = lds + (pp & 1) * kPairBytes;
+        const uint32_t kb = (uint32_t)pp * kRowBytes;  // byte offset of k = 64 pp in a row
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            __builtin_amdgcn_global_load_lds(asrc[j] + k0_, st_ + (32 * wave + 16 * j) * 64, 16, 0, 0);
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(aview, st_ + (32 * wave + 8 * j) * kRowBytes, 16, aoff[j] + kb,
+                                                     0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < NI / 2; ++j)
-            __builtin_amdgcn_global_load_lds(bsrc[j] + k0_, st_ + PBM * PBK * 2 + (BN / 8 * wave + 16 * j) * 64,
-                                             16, 0, 0);
-    };
-    // s_waitcnt vmcnt(n) for n own loads still in flight (n = 0, LPS, 2 LPS)
-    auto wait_loads = [&](int stages_ahead) {
-        if (stages_ahead >= 2) {
-            if (LPS == 4) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
-            else __builtin_amdgcn_s_waitcnt(0x0F76);           // vmcnt(6)
-        } else if (stages_ahead == 1) {
-            if (LPS == 4) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
-            else __builtin_amdgcn_s_waitcnt(0x0F73);           // vmcnt(3)
-        } else {
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-        }
+        for (int j = 0; j < NI; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(bview, st_ + PBM * kRowBytes + (BN / 8 * wave + 8 * j) * kRowBytes,
+                                                     16, boff[j] + kb, 0, 0, 0);
     };
 
-    const int nk = K / PBK;
+    const int np = K / (2 * PBK);  // pairs (K is a multiple of 64)
     __syncthreads();  // the previous tile's epilogue is done with LDS (and its stores retired)
-    // prologue: stages 0..2 in flight, then every wave's stage 0 landed
     issue(0);
-    if (nk > 1) issue(1);
-    if (nk > 2) issue(2);
-    wait_loads(min(nk, 3) - 1);
-    phase_barrier();
-    if (wm == 1) phase_barrier();  // group 1 runs one phase behind
-    for (int s = 0; s < nk; ++s) {
-        // ---- memory phase of stage s: refill the buffer of stage s - 1 (read by both
-        // groups by now) with stage s + 3, make sure this wave's part of stage s + 1
-        // has landed (the other group reads it right after the next barrier), read
-        // this stage's fragments ----
-        if (s + 3 < nk) issue(s + 3);
-        wait_loads(min(s + 3, nk - 1) - s - 1);
-        const uint32_t st = lds0 + (s & (kNStage - 1)) * kStageBytes;
-        uint4 fa[8], fb[NI];
-        read_frags<NI>(st + a_rd, st + b_rd, fa, fb);
+    for (int pp = 0; pp < np; ++pp) {
+        // this wave's part of pair pp has landed; after the barrier every wave's has,
+        // and every wave is done reading pair pp - 1, whose buffer pair pp + 1 refills
+        // while the two sub-stages of pair pp run
+        __builtin_amdgcn_s_waitcnt(0x0F70);
         phase_barrier();
-        // ---- compute phase of stage s ----
+        if (pp + 1 < np) issue(pp + 1);
+        const uint32_t st = lds0 + (pp & 1) * kPairBytes;
 #pragma unroll
-        for (int mi = 0; mi < 8; ++mi)
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t hx = (uint32_t)h << 6;
+            uint4 fa[8], fb[NI];
+            if (nmi > 0) read_frags<NI>(st + (a_rd ^ hx), st + (b_rd ^ hx), fa, fb);
+            // 16-row blocks past the group's end are skipped
+            if (nmi == 8) {
 #pragma unroll
-            for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma16x16x32(fa[mi], fb[ni], acc[mi][ni]);
-        phase_barrier();
+                for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma16x16x32(fa[mi], fb[ni], acc[mi][ni]);
+            } else {
+#pragma unroll
+                for (int mi = 0; mi < 8; ++mi)
+                    if (mi < nmi) {
+#pragma unroll
+                        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma16x16x32(fa[mi], fb[ni], acc[mi][ni]);
+                    }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
-    if (wm == 0) phase_barrier();  // matches group 1's extra barrier
 
     // ---- epilogue: results go through LDS (free after the K loop) so that
     // global stores are whole 16-byte chunks of output rows ----
@@ -295,12 +314,12 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
 #pragma unroll
                 for (int ni = 0; ni < NI / 2; ++ni) {
                     const float gv = acc[mi][ni][i], uv = acc[mi][ni + NI / 2][i];
-                    so[ml * OC + 16 * ni + row16] = f32_to_bf16(silu_f32(gv) * uv);
+                    so[ml * OC + 16 * ni + row16] = f32_to_bf16_hw(silu_f32(gv) * uv);
                 }
             } else {
                 const float ws = wrow[mi][i];
 #pragma unroll
-                for (int ni = 0; ni < NI; ++ni) so[ml * OC + 16 * ni + row16] = f32_to_bf16(ws * acc[mi][ni][i]);
+                for (int ni = 0; ni < NI; ++ni) so[ml * OC + 16 * ni + row16] = f32_to_bf16_hw(ws * acc[mi][ni][i]);
             }
         }
     }
@@ -391,8 +410,11 @@ static PrefillParams make_prefill_params(const LayerArgs& a, const Workspace& w,
 }
 
 bool prefill_ok(const Dims& dm) {
+    // the activation rows are read through one buffer view, whose offsets are 32-bit
+    // and must stay below kOffNone
     return dm.act == DT_BF16 && dm.wdt == DT_BF16 && dm.d % PBN == 0 && dm.f % (PBN / 2) == 0 &&
-           dm.fs % (PBN / 2) == 0 && dm.d % PBK == 0 && dm.f % PBK == 0;
+           dm.fs % (PBN / 2) == 0 && dm.d % PBK == 0 && dm.f % PBK == 0 &&
+           (size_t)dm.T * dm.d * 2 < (size_t)kOffNone;
 }
 
 template <int MODE>

@@ -110,7 +110,17 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+// SiLU z * sigmoid(z) = z / (1 + e^-z) from the hardware base-2 exponential and
+// reciprocal (v_exp_f32, v_rcp_f32; about 1 ulp each): four instructions in
+// place of the expf expansion and the IEEE divide sequence.  Every caller rounds
+// the product to bf16 or scales it into an fp32 sum, far coarser than this error.
+__device__ __forceinline__ float silu_f32(float z) {
+    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+}
+
+// fp32 -> bf16 with the hardware convert (v_cvt_pk_bf16_f32: round to nearest
+// even, the result f32_to_bf16 gives for every non-NaN input).
+__device__ __forceinline__ uint16_t f32_to_bf16_hw(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
 
 // Cross-workgroup hand-off inside one kernel without full device fences.
 // Data that another workgroup reads later in the same kernel is written and
@@ -179,6 +189,14 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_ca
 
 __device__ __forceinline__ floatx4_t mfma16x16x32(uint4 a, uint4 b, floatx4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+// gfx950 v_mfma_f32_32x32x16_bf16: lane l supplies A row (l & 31) and B column
+// (l & 31), each with the 8 consecutive k values 8*(l >> 5) .. +7 of a 16-wide
+// k step; result value v of lane l is row 8*(v >> 2) + 4*(l >> 5) + (v & 3),
+// column l & 31.
+typedef __attribute__((ext_vector_type(16))) float floatx16_t;
+__device__ __forceinline__ floatx16_t mfma32x32x16(uint4 a, uint4 b, floatx16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
