@@ -155,6 +155,17 @@ __device__ __forceinline__ void phase_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// Output column (within a wave's block of 16 NT columns) produced by row jr of
+// MFMA column tile tn.  The MFMA result puts rows 4 q .. 4 q + 3 of a tile in
+// lane group q, so tiles 2 t and 2 t + 1 are interleaved in steps of 4: lane
+// group q then holds 8 consecutive output columns 32 t + 8 q .. +7 of the two
+// tiles, written with one 16-byte store.  A single tile (NT = 1) keeps its order.
+template <int NT>
+__device__ __forceinline__ int out_col(int tn, int jr) {
+    if (NT == 1) return jr;
+    return 32 * (tn >> 1) + 8 * (jr >> 2) + 4 * (tn & 1) + (jr & 3);
+}
+
 // One tile: 256 rows of one group (from m0) times 64 NI B rows (NI = 4: a
 // full tile; NI = 2: a half tile, see prefill_gemm_kernel) from B row nb0 of
 // the weights (gate/up: feature nb0 / 1 ... see below; down: output row nb0).
@@ -221,12 +232,16 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
     for (int j = 0; j < NI; ++j) {
         const int r = BN / 8 * wave + 8 * j + (lane >> 3);
         const int c = (lane & 7) ^ (r & 7);
+        // B row r is row jr of column tile tn of the wave block wb that reads it;
+        // out_col() gives the output column (gate/up: feature) it produces
+        const int wb = r / (16 * NI), tn = (r >> 4) % NI, jr = r & 15;
         if (MODE == MODE_GATEUP) {
-            const int seg = r / HS, rr = r % HS;  // even: gate rows, odd: the matching up rows
-            const int wrow = ((seg & 1) ? F : 0) + nb0 + HS * (seg >> 1) + rr;
+            // tiles < NI / 2 gate, the rest the matching up rows
+            const bool up = tn >= NI / 2;
+            const int wrow = (up ? F : 0) + nb0 + HS * wb + out_col<NI / 2>(tn % (NI / 2), jr);
             boff[j] = (uint32_t)(((size_t)wrow * K + 8 * c) * 2);
         } else {
-            boff[j] = (uint32_t)(((size_t)(nb0 + r) * K + 8 * c) * 2);
+            boff[j] = (uint32_t)(((size_t)(nb0 + 16 * NI * wb + out_col<NI>(tn, jr)) * K + 8 * c) * 2);
         }
     }
 
@@ -251,7 +266,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
     };
 
     const int np = K / (2 * PBK);  // pairs (K is a multiple of 64)
-    __syncthreads();  // the previous tile's epilogue is done with LDS (and its stores retired)
+    // Buffer 0 is free: the previous tile's last pair (np is even) was in buffer 1,
+    // and every wave read its pair np - 2 before that pair's barrier.
     issue(0);
     for (int pp = 0; pp < np; ++pp) {
         // this wave's part of pair pp has landed; after the barrier every wave's has,
@@ -271,77 +287,80 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
 #pragma unroll
                 for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
-                    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma16x16x32(fa[mi], fb[ni], acc[mi][ni]);
+                    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma16x16x32(fb[ni], fa[mi], acc[mi][ni]);
             } else {
 #pragma unroll
                 for (int mi = 0; mi < 8; ++mi)
                     if (mi < nmi) {
 #pragma unroll
-                        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma16x16x32(fa[mi], fb[ni], acc[mi][ni]);
+                        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma16x16x32(fb[ni], fa[mi], acc[mi][ni]);
                     }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 
-    // ---- epilogue: results go through LDS (free after the K loop) so that
-    // global stores are whole 16-byte chunks of output rows ----
-    __syncthreads();  // all waves are done with the stages
-    float wrow[8][4];  // routing weight of each of this lane's output rows (down)
-    if (MODE == MODE_DOWN) {
-        float* s_w = reinterpret_cast<float*>(lds);
-        if (tid < PBM) {  // one row per thread
-            const int m = tid;
-            s_w[m] = (is_shared || m >= rows) ? 1.f : p.ws.sorted_wt[g.y + m0 + m];
-        }
-        __syncthreads();
+    // ---- epilogue, straight from registers.  The MFMAs take the B rows (weights)
+    // as their first operand, so lane (row16, q) holds, for each (mi, ni), rows
+    // 4 q .. 4 q + 3 of B tile ni for output row 16 mi + row16, which out_col()
+    // made consecutive output columns: 16-byte stores (8 bytes for a lone tile),
+    // 64 contiguous bytes per row and instruction. ----
+    const int wrows = min(max(rows - 128 * wm, 0), 128);
+    if (MODE == MODE_GATEUP) {
+        // gate tile t and up tile t + NI / 2 hold the same features
+        uint16_t* dst = static_cast<uint16_t*>(p.ws.h) + (size_t)(g.w + m0 + 128 * wm + row16) * p.hstride + nb0 +
+                        HS * wn + (NI == 4 ? 8 : 4) * q;
 #pragma unroll
-        for (int mi = 0; mi < 8; ++mi)
+        for (int mi = 0; mi < 8; ++mi) {
+            if (16 * mi + row16 < wrows) {
+                uint16_t* o = dst + (size_t)16 * mi * p.hstride;
+                if (NI == 4) {
+                    float hv[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) wrow[mi][i] = s_w[128 * wm + 16 * mi + 4 * q + i];
-        __syncthreads();  // s_w is overwritten below
-    }
-    // this wave's output sub-tile in LDS: 128 rows x OC bf16, row stride OC*2 bytes
-    constexpr int OC = (MODE == MODE_GATEUP) ? HS : 16 * NI;
-    static_assert(8 * 128 * OC * 2 <= kLdsBytes, "epilogue staging fits the stages");
-    uint16_t* so = reinterpret_cast<uint16_t*>(lds + wave * (128 * OC * 2));
+                    for (int i = 0; i < 4; ++i) {
+                        hv[i] = silu_f32(acc[mi][0][i]) * acc[mi][2][i];
+                        hv[4 + i] = silu_f32(acc[mi][1][i]) * acc[mi][3][i];
+                    }
+                    *reinterpret_cast<uint4*>(o) = make_uint4(pack_bf16x2_hw(hv[0], hv[1]), pack_bf16x2_hw(hv[2], hv[3]),
+                                                              pack_bf16x2_hw(hv[4], hv[5]), pack_bf16x2_hw(hv[6], hv[7]));
+                } else {
+                    float hv[4];
 #pragma unroll
-    for (int mi = 0; mi < 8; ++mi) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int ml = 16 * mi + 4 * q + i;  // row within the wave's 128
-            if (MODE == MODE_GATEUP) {
-#pragma unroll
-                for (int ni = 0; ni < NI / 2; ++ni) {
-                    const float gv = acc[mi][ni][i], uv = acc[mi][ni + NI / 2][i];
-                    so[ml * OC + 16 * ni + row16] = f32_to_bf16_hw(silu_f32(gv) * uv);
+                    for (int i = 0; i < 4; ++i) hv[i] = silu_f32(acc[mi][0][i]) * acc[mi][1][i];
+                    *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2_hw(hv[0], hv[1]), pack_bf16x2_hw(hv[2], hv[3]));
                 }
-            } else {
-                const float ws = wrow[mi][i];
-#pragma unroll
-                for (int ni = 0; ni < NI; ++ni) so[ml * OC + 16 * ni + row16] = f32_to_bf16_hw(ws * acc[mi][ni][i]);
             }
         }
-    }
-    __syncthreads();
-    // copy out: each lane moves 16-byte chunks of the wave's rows
-    {
-        constexpr int CPR = OC * 2 / 16;  // chunks per row
-        uint16_t* dst_base;
-        size_t dst_stride;
-        if (MODE == MODE_GATEUP) {
-            dst_base = static_cast<uint16_t*>(p.ws.h) + (size_t)(g.w + m0 + 128 * wm) * p.hstride + nb0 + OC * wn;
-            dst_stride = p.hstride;
-        } else {
-            dst_base = static_cast<uint16_t*>(p.ws.y) + (size_t)(g.w + m0 + 128 * wm) * d + nb0 + OC * wn;
-            dst_stride = d;
+    } else {
+        uint16_t* dst = static_cast<uint16_t*>(p.ws.y) + (size_t)(g.w + m0 + 128 * wm + row16) * d + nb0 +
+                        16 * NI * wn + 8 * q;
+        // routing weights of the lane's 8 rows, loaded before any store (loads and
+        // stores share one in-order counter, so a load after a store waits for it)
+        // (unconditional buffer loads: a load behind a branch makes every later use
+        // wait for all of this wave's memory operations)
+        const __amdgpu_buffer_rsrc_t wview = buffer_view(p.ws.sorted_wt + g.y + m0, (uint32_t)(rows * 4));
+        float wv[8];
+#pragma unroll
+        for (int mi = 0; mi < 8; ++mi) {
+            const int m = 128 * wm + 16 * mi + row16;
+            const uint32_t off = (is_shared || m >= rows) ? kOffNone : (uint32_t)(m * 4);
+            const float w = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(wview, (int)off, 0, 0));
+            wv[mi] = is_shared ? 1.f : w;
         }
-        const int wrows = min(128, rows - 128 * wm);
-        for (int idx = lane; idx < 128 * CPR; idx += 64) {
-            const int r = idx / CPR, cc = idx % CPR;
-            if (r < wrows)
-                *reinterpret_cast<uint4*>(dst_base + (size_t)r * dst_stride + cc * 8) =
-                    *reinterpret_cast<const uint4*>(so + r * OC + cc * 8);
+#pragma unroll
+        for (int mi = 0; mi < 8; ++mi) {
+            if (16 * mi + row16 < wrows) {
+                const float ws = wv[mi];
+                uint16_t* o = dst + (size_t)16 * mi * d;
+#pragma unroll
+                for (int t = 0; t < NI / 2; ++t) {
+                    const floatx4_t& a0 = acc[mi][2 * t];
+                    const floatx4_t& a1 = acc[mi][2 * t + 1];
+                    *reinterpret_cast<uint4*>(o + 32 * t) =
+                        make_uint4(pack_bf16x2_hw(ws * a0[0], ws * a0[1]), pack_bf16x2_hw(ws * a0[2], ws * a0[3]),
+                                   pack_bf16x2_hw(ws * a1[0], ws * a1[1]), pack_bf16x2_hw(ws * a1[2], ws * a1[3]));
+                }
+            }
         }
     }
 }

@@ -121,6 +121,12 @@ __device__ __forceinline__ float silu_f32(float z) {
 // fp32 -> bf16 with the hardware convert (v_cvt_pk_bf16_f32: round to nearest
 // even, the result f32_to_bf16 gives for every non-NaN input).
 __device__ __forceinline__ uint16_t f32_to_bf16_hw(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
+// Two fp32 values to a packed bf16 pair (lo in bits 0-15) with one v_cvt_pk_bf16_f32.
+typedef __attribute__((ext_vector_type(2))) float floatx2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+__device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2_t){lo, hi}, bf16x2_t));
+}
 
 // Cross-workgroup hand-off inside one kernel without full device fences.
 // Data that another workgroup reads later in the same kernel is written and
