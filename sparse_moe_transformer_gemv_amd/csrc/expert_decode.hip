@@ -327,19 +327,25 @@ __global__ __launch_bounds__(256) void down_decode_kernel(ExpertParams p) {
 
 // One 16-token tile of a bf16 gate/up block; sp is the sorted pair of this
 // lane's token row.  Padding rows read as zeros (buffer view past T).
+// The lane's activation fragments of one 16-token tile (token row r0 + row).
 template <int NSTEP>
-__device__ __forceinline__ void gateup_mfma_tile(const ExpertParams& p, const int4& g, bool is_shared, int r0,
-                                                 int sp, __amdgpu_buffer_rsrc_t xv, int kl, const uint4 (&b)[NSTEP],
-                                                 int j0, float (&s_part)[4][256], uint16_t (&s_h)[16][3][8]) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int row = lane & 15, q = lane >> 4;
-    const int d = p.dm.d;
+__device__ __forceinline__ void gateup_load_x(const ExpertParams& p, const int4& g, bool is_shared, int r0, int sp,
+                                              __amdgpu_buffer_rsrc_t xv, int kl, uint4 (&a)[NSTEP]) {
+    const int row = threadIdx.x & 15;
     const int m = r0 + row;
     const int tok = is_shared ? m : sp / p.dm.k;
-    const uint32_t xo = m < g.z ? (uint32_t)(tok * d + kl) * 2 : kOffNone;
-    uint4 a[NSTEP];
+    const uint32_t xo = m < g.z ? (uint32_t)(tok * p.dm.d + kl) * 2 : kOffNone;
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) a[s] = buffer_load16(xv, xo + 64 * s);
+}
+
+// a: the tile's activation fragments (gateup_load_x)
+template <int NSTEP>
+__device__ __forceinline__ void gateup_mfma_tile(const ExpertParams& p, const int4& g, int r0,
+                                                 const uint4 (&a)[NSTEP], const uint4 (&b)[NSTEP], int j0,
+                                                 float (&s_part)[4][256], uint16_t (&s_h)[16][3][8]) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = lane & 15, q = lane >> 4;
     __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the first MFMA
     floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -378,10 +384,25 @@ __device__ __forceinline__ void gateup_mfma_tile(const ExpertParams& p, const in
 // activation loads that need it wait for it alone), then the weights, then the
 // first token tile's activations, all before the first wait; that tile is
 // peeled off the loop so no loop-carried register forces an earlier wait.
+// With NSTEP >= 2 the weights travel through LDS: each wave fetches its 16
+// rows x d / 4 k with direct-to-LDS loads of whole 128-byte lines (8 rows per
+// load) carrying the non-temporal hint, then reads them back in the MFMA
+// layout.  Loads of 64 bytes per row (the MFMA layout straight from memory)
+// split every line over two instructions, and the hint then makes the second
+// half fetch the line again; whole lines with the hint stream about 6% faster
+// than the split form without it.  Each wave reads only what it loaded, so no
+// barrier is needed; 16-byte chunks are XOR-swizzled by row so the reads are
+// free of bank conflicts.
+template <int NSTEP>
+struct GateupWeightLds {
+    static constexpr int kBytes = NSTEP >= 2 ? 4 * 16 * 64 * NSTEP : 16;  // 4 waves x 16 rows x d / 2 bytes
+};
+
 template <int NSTEP>
 __global__ __launch_bounds__(256) void gateup_mfma_kernel(ExpertParams p) {
     __shared__ float s_part[4][256];
     __shared__ __attribute__((aligned(16))) uint16_t s_h[16][3][8];
+    __shared__ __attribute__((aligned(16))) unsigned char s_w[GateupWeightLds<NSTEP>::kBytes];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, q = lane >> 4;
     const int d = p.dm.d;
@@ -399,16 +420,45 @@ __global__ __launch_bounds__(256) void gateup_mfma_kernel(ExpertParams p) {
     const uint16_t* gu = static_cast<const uint16_t*>(is_shared ? p.shared.gu : p.routed.gu);
     const size_t wr = e * 2 * F + (row < 8 ? (size_t)(j0 + row) : (size_t)(F + j0 + row - 8));
     const int kl = wave * (d / 4) + 8 * q;
-    const uint16_t* wrow = gu + wr * d + kl;
-    uint4 b[NSTEP];
-#pragma unroll
-    for (int s = 0; s < NSTEP; ++s) b[s] = *reinterpret_cast<const uint4*>(wrow + 32 * s);
     const __amdgpu_buffer_rsrc_t xv = buffer_view(p.x, (uint32_t)p.dm.T * d * 2);
-    gateup_mfma_tile<NSTEP>(p, g, is_shared, 0, sp, xv, kl, b, j0, s_part, s_h);
+    uint4 b[NSTEP];
+    if constexpr (NSTEP >= 2) {
+        // load i: rows 8 (i & 1) + (lane >> 3) of this block, 128-byte segment i >> 1 of
+        // the wave's k range; the lane fetches logical chunk (lane & 7) ^ (row & 7)
+        unsigned char* sw = s_w + wave * (16 * 64 * NSTEP);
+        const int kw = wave * (d / 4);
+#pragma unroll
+        for (int i = 0; i < NSTEP; ++i) {
+            const int r = 8 * (i & 1) + (lane >> 3);
+            const size_t wrr = e * 2 * F + (r < 8 ? (size_t)(j0 + r) : (size_t)(F + j0 + r - 8));
+            const int c = (lane & 7) ^ (r & 7);
+            __builtin_amdgcn_global_load_lds(gu + wrr * d + kw + 64 * (i >> 1) + 8 * c, sw + i * 1024, 16, 0, 2);
+        }
+        uint4 a0[NSTEP];
+        gateup_load_x<NSTEP>(p, g, is_shared, 0, sp, xv, kl, a0);
+        // every load above has landed before the reads below (the compiler waits for
+        // the direct-to-LDS loads before any LDS read)
+        const uint32_t rbase = (uint32_t)((row >> 3) * 1024 + (row & 7) * 128);
+#pragma unroll
+        for (int s = 0; s < NSTEP; ++s) {
+            const uint32_t off = (s >> 1) * 2048 + rbase + ((((4 * (s & 1)) + q) ^ (row & 7)) << 4);
+            b[s] = *reinterpret_cast<const uint4*>(sw + off);
+        }
+        gateup_mfma_tile<NSTEP>(p, g, 0, a0, b, j0, s_part, s_h);
+    } else {
+        const uint16_t* wrow = gu + wr * d + kl;
+#pragma unroll
+        for (int s = 0; s < NSTEP; ++s) b[s] = *reinterpret_cast<const uint4*>(wrow + 32 * s);
+        uint4 a0[NSTEP];
+        gateup_load_x<NSTEP>(p, g, is_shared, 0, sp, xv, kl, a0);
+        gateup_mfma_tile<NSTEP>(p, g, 0, a0, b, j0, s_part, s_h);
+    }
     for (int r0 = 16; r0 < g.z; r0 += 16) {
         const int m = r0 + row;
         const int spn = p.ws.sorted_pair[g.y + (m < g.z ? m : g.z - 1)];
-        gateup_mfma_tile<NSTEP>(p, g, is_shared, r0, spn, xv, kl, b, j0, s_part, s_h);
+        uint4 a[NSTEP];
+        gateup_load_x<NSTEP>(p, g, is_shared, r0, spn, xv, kl, a);
+        gateup_mfma_tile<NSTEP>(p, g, r0, a, b, j0, s_part, s_h);
     }
 }
 
