@@ -18,7 +18,11 @@
 // 8 x 4 MFMA 16x16x32 tiles (128 fp32 accumulators per lane), two waves per
 // SIMD.  For gate/up the 256 B rows of a tile are, per 64-row quarter q, 32
 // gate rows then the matching 32 up rows of features 32q..32q+31, so each wave
-// holds matching gate and up columns and applies SwiGLU in registers.
+// holds matching gate and up columns and applies SwiGLU in registers.  The
+// MFMAs take the weights as their first operand, which leaves 4 consecutive
+// output columns of one row in each lane; the weight rows of each pair of
+// column tiles are interleaved so that a lane holds 8, and the results leave
+// as 16-byte stores straight from registers.
 //
 // K advances in pairs of 32-wide sub-stages through two 64 KiB LDS buffers,
 // filled straight from global memory with direct-to-LDS 16-byte loads of whole
@@ -168,10 +172,10 @@ __device__ __forceinline__ int out_col(int tn, int jr) {
 
 // One tile: 256 rows of one group (from m0) times 64 NI B rows (NI = 4: a
 // full tile; NI = 2: a half tile, see prefill_gemm_kernel) from B row nb0 of
-// the weights (gate/up: feature nb0 / 1 ... see below; down: output row nb0).
-// For gate/up the B rows are taken in quarters of 16 NI rows: 8 NI gate rows,
-// then the 8 NI up rows of the same features, so wave wn's NI column tiles
-// hold matching gate (ni < NI / 2) and up (ni >= NI / 2) columns.
+// the weights (gate/up: first feature nb0; down: first output row nb0).  For
+// gate/up the B rows are taken in quarters of 16 NI rows: 8 NI gate rows, then
+// the 8 NI up rows of the same features (in out_col order), so wave wn's NI
+// column tiles hold matching gate (ni < NI / 2) and up (ni >= NI / 2) columns.
 template <int MODE, int NI>
 __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned char* lds, const int4& g, int m0,
                                              int nb0) {
