@@ -173,6 +173,81 @@ __device__ void write_groups(const int* s_off, int E, int T, int k, bool has_sha
     }
 }
 
+// The same results as block_sort_and_groups (decode lists, no tiles) for at
+// most 64 pairs, by one wavefront.  Each pair's rank comes from ballots over
+// the 8 key bits (the pairs with a smaller expert id, then those with the same
+// id and a lower index: a stable order); the keys are put in sorted order
+// through LDS, group starts come from one neighbour exchange, and the counts
+// are built in LDS and scanned once.  Chains of cross-lane exchanges (a
+// bitonic network, binary searches) measured several microseconds here:
+// each exchange waits for the previous one.  keys/wts: the block's pairs in
+// LDS; s_tmp: LDS scratch of 64 + 256 ints.
+__device__ void wave_sort_small(const int* keys, const float* wts, int P, int E, int T, int k, bool has_shared,
+                                const Workspace& ws, int* s_tmp, int lane) {
+    int* s_key = s_tmp;       // [64] expert ids in sorted order
+    int* s_cnt = s_tmp + 64;  // [256] pairs per expert
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    const bool valid = lane < P;
+    const int key = valid ? keys[lane] : 0;
+    const float w = valid ? wts[lane] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_cnt[4 * lane + i] = 0;
+    unsigned long long eq = __ballot(valid);  // lanes equal to this one on the bits seen so far
+    int below = 0;
+#pragma unroll
+    for (int b = 7; b >= 0; --b) {
+        const bool bit = (key >> b) & 1;
+        const unsigned long long ones = __ballot(valid && bit);
+        if (bit) below += __popcll(eq & ~ones);
+        eq &= bit ? ones : ~ones;
+    }
+    const int rank = below + __popcll(eq & lt);
+    if (valid) {
+        ws.sorted_pair[rank] = lane;
+        ws.pair_pos[lane] = rank;
+        ws.sorted_wt[rank] = w;
+        s_key[rank] = key;
+    }
+    // (LDS operations of one wavefront take effect in program order)
+    const int skey = valid ? s_key[lane] : E;  // lane p: the expert of the p-th sorted pair
+    const int prev = __shfl_up(skey, 1, 64);
+    const bool start = valid && (lane == 0 || skey != prev);
+    const unsigned long long sm = __ballot(start);
+    const int base = has_shared ? 1 : 0;
+    if (start) {
+        const unsigned long long later = lane < 63 ? sm >> (lane + 1) : 0ull;
+        const int end = later ? lane + 1 + __builtin_ctzll(later) : P;
+        ws.groups[base + __popcll(sm & lt)] = make_int4(skey, lane, end - lane, lane);
+        s_cnt[skey] = end - lane;
+    }
+    if (has_shared && lane == 0) ws.groups[0] = make_int4(E, 0, T, k * T);
+    if (lane == 0) *ws.n_groups = base + __popcll(sm);
+    // counts and their exclusive scan, experts 4 lane .. 4 lane + 3 per lane
+    int c[4], local = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        c[i] = s_cnt[4 * lane + i];
+        local += c[i];
+    }
+    int inc = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(inc, off, 64);
+        if (lane >= off) inc += v;
+    }
+    int run = inc - local;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = 4 * lane + i;
+        if (e < E) {
+            ws.offsets[e] = run;
+            ws.counts[e] = c[i];
+        }
+        run += c[i];
+    }
+    if (lane == 63) ws.offsets[E] = inc;
+}
+
 // ---------------------------------------------------------------------------
 // Stable counting sort of P pair keys (expert ids < E <= 256) by one block.
 // Writes counts[E], offsets[E+1], sorted_pair[P], pair_pos[P], sorted_wt[P]
@@ -635,8 +710,12 @@ __global__ __launch_bounds__(512) void route_splitk_kernel(RouteMfmaParams p) {
     // 4. the last token tile sorts every pair (from LDS when it is the only one)
     if (ntt == 1) {
         __syncthreads();
-        block_sort_and_groups<512, false>(s_sel, s_wt, p.k * T, E, T, p.k, p.has_shared != 0, 0, p.ws, s_hist,
-                                          s_off);
+        if (p.k * T <= 64) {
+            if (wave == 0) wave_sort_small(s_sel, s_wt, p.k * T, E, T, p.k, p.has_shared != 0, p.ws, s_hist, lane);
+        } else {
+            block_sort_and_groups<512, false>(s_sel, s_wt, p.k * T, E, T, p.k, p.has_shared != 0, 0, p.ws, s_hist,
+                                              s_off);
+        }
         return;
     }
     if (!last_arrival(&p.ws.rcount[ntt * NE + ntt], ntt, &s_flag)) return;
