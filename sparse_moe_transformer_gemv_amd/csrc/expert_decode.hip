@@ -135,6 +135,11 @@ struct ExpertParams {
     WeightPtrs routed, shared;
     Workspace ws;
     int hstride;  // row stride of h (max(f, fs))
+    // down kernels that fold the combine in (see down_mfma_kernel)
+    int combine;            // 1: this launch also writes out
+    const float* residual;  // added first when not null
+    void* out;              // [T][d] fp32 (out_f32) or bf16
+    int out_f32;
 };
 
 // ---------------------------------------------------------------------------
@@ -503,10 +508,60 @@ __device__ __forceinline__ void down_mfma_tile(const ExpertParams& p, const int4
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const float v = ((s_part[0][t][tid] + s_part[1][t][tid]) + s_part[2][t][tid]) + s_part[3][t][tid];
-            yr[16 * t] = ws * v;
+            if (p.combine)
+                st_agent(yr + 16 * t, ws * v);  // read by another workgroup of this launch
+            else
+                yr[16 * t] = ws * v;
         }
     }
     __syncthreads();
+}
+
+// The combine of output columns n0 .. n0 + 16 NT - 1 for every token, by the
+// last down workgroup of those columns (the y rows of every group are written
+// through at agent scope and read the same way): out = residual + shared row +
+// routed rows in pair order, the order of combine_kernel.  Every load of a
+// thread is issued before the first add (addresses clamped to valid rows, the
+// unused terms selected away), so the tail costs two memory round trips.
+constexpr int kDownCombineMaxT = 16;
+constexpr int kCombineMaxK = 8;
+template <int NT>
+__device__ __forceinline__ void combine_columns(const ExpertParams& p, int n0) {
+    constexpr int nc = 16 * NT;
+    constexpr int kPer = (kDownCombineMaxT * nc + 255) / 256;
+    __shared__ int s_pos[kDownCombineMaxT * kCombineMaxK];
+    const int T = p.dm.T, d = p.dm.d, k = p.dm.k;
+    const float* y = static_cast<const float*>(p.ws.y);
+    const size_t kT = (size_t)k * T;
+    const bool has_shared = p.dm.fs > 0;
+    for (int i = threadIdx.x; i < T * k; i += blockDim.x) s_pos[i] = p.ws.pair_pos[i];
+    __syncthreads();
+    float v[kPer][kCombineMaxK + 2];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+        const int i = threadIdx.x + 256 * r;
+        const int t = min(i / nc, T - 1), c = n0 + i % nc;
+        v[r][0] = p.residual ? p.residual[(size_t)t * d + c] : 0.f;
+        v[r][1] = has_shared ? ld_agent(y + (kT + t) * d + c) : 0.f;
+#pragma unroll
+        for (int j = 0; j < kCombineMaxK; ++j)
+            v[r][2 + j] = ld_agent(y + (size_t)s_pos[t * k + (j < k ? j : 0)] * d + c);
+    }
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+        const int i = threadIdx.x + 256 * r;
+        const int t = i / nc, c = n0 + i % nc;
+        if (t >= T) continue;
+        float acc = v[r][0];
+        if (has_shared) acc += v[r][1];
+#pragma unroll
+        for (int j = 0; j < kCombineMaxK; ++j)
+            if (j < k) acc += v[r][2 + j];
+        if (p.out_f32)
+            static_cast<float*>(p.out)[(size_t)t * d + c] = acc;
+        else
+            static_cast<uint16_t*>(p.out)[(size_t)t * d + c] = f32_to_bf16(acc);
+    }
 }
 
 // down: block = (group, NT tiles of 16 output rows); K = F split over the
@@ -557,6 +612,11 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertParams p) {
         const int m = r0 + mm;
         const float rw = is_shared ? 1.f : p.ws.sorted_wt[g.y + (m < g.z ? m : g.z - 1)];
         down_mfma_tile<NSMAX, NT>(p, g, r0, nsteps, kl, n0, hv, b, rw, s_part);
+    }
+    if (p.combine) {  // uniform
+        // one workgroup per active group arrives for these columns; the last one combines
+        __shared__ int s_flag;
+        if (last_arrival(&p.ws.dcount[rb], *p.ws.n_groups, &s_flag)) combine_columns<NT>(p, n0);
     }
 }
 
@@ -988,6 +1048,10 @@ static ExpertParams make_params(const LayerArgs& a, const Workspace& w) {
     p.shared = a.shared;
     p.ws = w;
     p.hstride = a.dm.f > a.dm.fs ? a.dm.f : a.dm.fs;
+    p.combine = 0;
+    p.residual = a.residual;
+    p.out = a.out;
+    p.out_f32 = (a.residual != nullptr || a.dm.act == DT_F32) ? 1 : 0;
     return p;
 }
 
@@ -1035,6 +1099,14 @@ hipError_t launch_gateup_decode(const LayerArgs& a, const Workspace& w, hipStrea
     return hipGetLastError();
 }
 
+// The bf16 matrix-core down kernel folds the combine in up to 16 tokens: the
+// last workgroup of each block of output columns sums those columns, which saves
+// the combine launch.  Above that the combine kernel, which spreads the rows
+// over the whole chip, is as fast.
+bool down_decode_combines(const Dims& dm) {
+    return !decode_fp4_ok(dm) && decode_mfma_ok(dm) && dm.T <= kDownCombineMaxT && dm.k <= kCombineMaxK;
+}
+
 hipError_t launch_down_decode(const LayerArgs& a, const Workspace& w, hipStream_t s) {
     ExpertParams p = make_params(a, w);
     if (decode_fp4_ok(a.dm)) {
@@ -1050,6 +1122,7 @@ hipError_t launch_down_decode(const LayerArgs& a, const Workspace& w, hipStream_
     }
     if (decode_mfma_ok(a.dm)) {
         constexpr int NT = kDownMfmaTiles;
+        p.combine = down_decode_combines(a.dm) ? 1 : 0;
         dim3 grid(max_groups(a.dm) * (a.dm.d / (16 * NT)));
         switch ((p.hstride + 127) / 128) {
         case 1: hipLaunchKernelGGL((down_mfma_kernel<1, NT>), grid, dim3(256), 0, s, p); break;

@@ -35,6 +35,7 @@ struct Workspace {
     int2* tiles;         // [max_tiles] prefill m-tiles {group, first row}
     int* n_tiles;        // [1]
     int* counter;        // [1 + ceil(Tm/16)] last-block tickets, zero between launches
+    int* dcount;         // [ceil(d/16)] decode down tickets (combine folded in), zero between launches
     void* h;             // [(k+1)*Tm][fmax] x 8 B: fp32 (decode VALU), three exact bf16 planes (decode
                          // MFMA), two f16 planes (NVFP4), or bf16 (prefill)
     void* y;             // [(k+1)*Tm][d]:    fp32 (decode) or bf16 (prefill)
@@ -78,6 +79,8 @@ constexpr int kSortBlock = 1024;  // pairs per block of the prefill sort
 hipError_t launch_sort(const LayerArgs& a, const Workspace& w, int bm, hipStream_t s);
 hipError_t launch_gateup_decode(const LayerArgs& a, const Workspace& w, hipStream_t s);
 hipError_t launch_down_decode(const LayerArgs& a, const Workspace& w, hipStream_t s);
+// true when launch_down_decode also performs the combine (no launch_combine then)
+bool down_decode_combines(const Dims& dm);
 bool decode_fp4_ok(const Dims& dm);
 hipError_t launch_gateup_prefill(const LayerArgs& a, const Workspace& w, int n_cu, hipStream_t s);
 hipError_t launch_down_prefill(const LayerArgs& a, const Workspace& w, int n_cu, hipStream_t s);

@@ -146,6 +146,7 @@ size_t carve(const flint_moe_config& c, char* base, Workspace* w) {
     w->tiles = static_cast<int2*>(take(max_tiles * 8));
     w->n_tiles = static_cast<int*>(take(4));
     w->counter = static_cast<int*>(take((1 + (Tm + 15) / 16) * 4));
+    w->dcount = static_cast<int*>(take((size_t)((c.d_model + 15) / 16) * 4));
     w->h = take(slots * fmax * 8);
     w->y = take(slots * (size_t)c.d_model * 4);
     w->max_tiles = (int)max_tiles;
@@ -376,7 +377,7 @@ flint_status flint_moe_forward(flint_moe_t h, int32_t T, const void* hidden, con
         e = launch_down_decode(a, h->ws, stream);
     }
     if (e != hipSuccess) return hip_fail(e, "down kernel");
-    {
+    if (!down_decode_combines(a.dm)) {
         Timer tm(h, FLINT_KERNEL_COMBINE, stream);
         e = launch_combine(a, h->ws, false, stream);
     }
