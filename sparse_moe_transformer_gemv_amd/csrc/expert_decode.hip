@@ -945,7 +945,10 @@ __device__ __forceinline__ void down_fp4_tile(const ExpertParams& p, const int4&
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const float v = ((s_part[0][t][tid] + s_part[1][t][tid]) + s_part[2][t][tid]) + s_part[3][t][tid];
-            yr[16 * t] = ws * v;
+            if (p.combine)
+                st_agent(yr + 16 * t, ws * v);  // read by another workgroup of this launch
+            else
+                yr[16 * t] = ws * v;
         }
     }
     __syncthreads();
@@ -1015,6 +1018,10 @@ __global__ __launch_bounds__(256) void down_fp4_kernel(ExpertParams p) {
         const float rw = is_shared ? 1.f : p.ws.sorted_wt[g.y + (m < g.z ? m : g.z - 1)];
         down_fp4_tile<NT, NGMAX>(p, g, r0, ng, kl, n0, hv_hi, hv_lo, cw, s_sc, false, -1, -1, sc_v0, sc_v1,
                                  tsd * rw, s_part);
+    }
+    if (p.combine) {  // uniform; as in down_mfma_kernel
+        __shared__ int s_flag;
+        if (last_arrival(&p.ws.dcount[rb], *p.ws.n_groups, &s_flag)) combine_columns<NT>(p, n0);
     }
 }
 
@@ -1099,12 +1106,18 @@ hipError_t launch_gateup_decode(const LayerArgs& a, const Workspace& w, hipStrea
     return hipGetLastError();
 }
 
-// The bf16 matrix-core down kernel folds the combine in up to 16 tokens: the
-// last workgroup of each block of output columns sums those columns, which saves
-// the combine launch.  Above that the combine kernel, which spreads the rows
-// over the whole chip, is as fast.
+// The matrix-core down kernels fold the combine in (bf16 weights up to 16
+// tokens, NVFP4 up to 4): the last workgroup of each block of output columns
+// sums those columns, which saves the combine launch.  Every workgroup then
+// waits for its write-through stores and takes a ticket; the short NVFP4
+// workgroups pay more for that at 16 tokens than the combine launch costs.
+// Above these sizes the combine kernel, which spreads the rows over the whole
+// chip, is as fast.
+constexpr int kDownCombineMaxTFp4 = 4;
 bool down_decode_combines(const Dims& dm) {
-    return !decode_fp4_ok(dm) && decode_mfma_ok(dm) && dm.T <= kDownCombineMaxT && dm.k <= kCombineMaxK;
+    const bool fp4 = decode_fp4_ok(dm);
+    return (fp4 || decode_mfma_ok(dm)) && dm.T <= (fp4 ? kDownCombineMaxTFp4 : kDownCombineMaxT) &&
+           dm.k <= kCombineMaxK;
 }
 
 hipError_t launch_down_decode(const LayerArgs& a, const Workspace& w, hipStream_t s) {
@@ -1112,6 +1125,7 @@ hipError_t launch_down_decode(const LayerArgs& a, const Workspace& w, hipStream_
     if (decode_fp4_ok(a.dm)) {
         constexpr int NT = kDownFp4Tiles;
         if (a.dm.d % (16 * NT) != 0) return hipErrorInvalidValue;
+        p.combine = down_decode_combines(a.dm) ? 1 : 0;
         dim3 grid(max_groups(a.dm) * (a.dm.d / (16 * NT)));
         switch (p.hstride / 512) {
         case 1: hipLaunchKernelGGL((down_fp4_kernel<NT, 1>), grid, dim3(256), 0, s, p); break;

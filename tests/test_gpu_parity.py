@@ -288,6 +288,27 @@ def test_full_decode_nvfp4(fp4_layer, T):
     print("decode nvfp4 T=%d: %s | fp32 out: %s" % (T, rep, rep32), flush=True)
 
 
+@pytest.mark.parametrize("which,T", [("bf16", 4), ("nvfp4", 1)])
+def test_decode_combine_in_down_with_residual(decode_layer, fp4_layer, which, T):
+    # small batches fold the combine into the down kernel; a nonzero residual
+    # is added there, also when the output aliases it
+    L, D = decode_layer if which == "bf16" else fp4_layer
+    c = L["cfg"]
+    cfg_id = 1 if which == "bf16" else 4
+    x = synth.hidden(cfg_id, T, c["d"], c["act"])
+    res = np.random.default_rng(11).standard_normal((T, c["d"])).astype(np.float32)
+    layer = make_layer_obj(c, 16)
+    rd = dev_array(res)
+    out, rout = run_gpu(layer, D, x, residual=rd)
+    ref = run_oracle(L, x)
+    ref = dict(ref, out=ref["out"] + res.astype(np.float64))
+    rep = compare(out, rout, ref, c["k"], c["wdtype"], out_bf16=False)
+    layer.forward(x_device(x), D["router_w"], D["experts"], D["shared"], residual=rd, out=rd)
+    torch.cuda.synchronize()
+    assert np.abs(out_host(rd) - out).max() <= 1e-6 * np.abs(out).max()
+    print("combine in down %s T=%d: %s" % (which, T, rep), flush=True)
+
+
 @pytest.fixture(scope="module")
 def prefill_layer():
     L = synth.layer(2)
