@@ -523,19 +523,16 @@ __device__ __forceinline__ void down_mfma_tile(const ExpertParams& p, const int4
 // routed rows in pair order, the order of combine_kernel.  Every load of a
 // thread is issued before the first add (addresses clamped to valid rows, the
 // unused terms selected away), so the tail costs two memory round trips.
+// kPer elements per thread cover T x 16 NT outputs.
 constexpr int kDownCombineMaxT = 16;
 constexpr int kCombineMaxK = 8;
-template <int NT>
-__device__ __forceinline__ void combine_columns(const ExpertParams& p, int n0) {
+template <int NT, int kPer>
+__device__ __forceinline__ void combine_columns_n(const ExpertParams& p, int n0, const int* s_pos) {
     constexpr int nc = 16 * NT;
-    constexpr int kPer = (kDownCombineMaxT * nc + 255) / 256;
-    __shared__ int s_pos[kDownCombineMaxT * kCombineMaxK];
     const int T = p.dm.T, d = p.dm.d, k = p.dm.k;
     const float* y = static_cast<const float*>(p.ws.y);
     const size_t kT = (size_t)k * T;
     const bool has_shared = p.dm.fs > 0;
-    for (int i = threadIdx.x; i < T * k; i += blockDim.x) s_pos[i] = p.ws.pair_pos[i];
-    __syncthreads();
     float v[kPer][kCombineMaxK + 2];
 #pragma unroll
     for (int r = 0; r < kPer; ++r) {
@@ -562,6 +559,17 @@ __device__ __forceinline__ void combine_columns(const ExpertParams& p, int n0) {
         else
             static_cast<uint16_t*>(p.out)[(size_t)t * d + c] = f32_to_bf16(acc);
     }
+}
+template <int NT>
+__device__ __forceinline__ void combine_columns(const ExpertParams& p, int n0) {
+    static_assert(kDownCombineMaxT * 16 * NT <= 4 * 256, "at most four elements per thread");
+    __shared__ int s_pos[kDownCombineMaxT * kCombineMaxK];
+    for (int i = threadIdx.x; i < p.dm.T * p.dm.k; i += blockDim.x) s_pos[i] = p.ws.pair_pos[i];
+    __syncthreads();
+    const int n = p.dm.T * 16 * NT;  // uniform
+    if (n <= 256) combine_columns_n<NT, 1>(p, n0, s_pos);
+    else if (n <= 512) combine_columns_n<NT, 2>(p, n0, s_pos);
+    else combine_columns_n<NT, 4>(p, n0, s_pos);
 }
 
 // down: block = (group, NT tiles of 16 output rows); K = F split over the
