@@ -152,7 +152,9 @@ flint_status flint_moe_get_routing(flint_moe_t h, int32_t* idx, float* weights,
 #define FLINT_KERNEL_ROUTE        0  /* router + top-k (+ sort on the decode path) */
 #define FLINT_KERNEL_SORT         1  /* prefill counting sort */
 #define FLINT_KERNEL_EXPERT_UP    2  /* gate/up + SwiGLU (decode GEMV or prefill MFMA) */
-#define FLINT_KERNEL_EXPERT_DOWN  3  /* down projection */
+#define FLINT_KERNEL_EXPERT_DOWN  3  /* down projection (with the combine folded in for small
+                                        decode batches: bf16 weights up to 16 tokens, NVFP4
+                                        up to 4; no combine launch is then recorded) */
 #define FLINT_KERNEL_COMBINE      4  /* weighted unpermute + shared + residual */
 #define FLINT_KERNEL_COUNT        5
 flint_status flint_moe_profile_begin(flint_moe_t h, int32_t kernel_id, int32_t n_launches);
