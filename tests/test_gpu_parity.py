@@ -309,6 +309,45 @@ def test_decode_combine_in_down_with_residual(decode_layer, fp4_layer, which, T)
     print("combine in down %s T=%d: %s" % (which, T, rep), flush=True)
 
 
+@pytest.mark.parametrize("which,T,flags", [("bf16", 4, 0), ("bf16", 64, 0), ("nvfp4", 1, 0),
+                                           ("bf16", 700, FLINT_FORCE_PREFILL_PATH)])
+def test_forward_replayed_from_hip_graph(decode_layer, fp4_layer, which, T, flags):
+    # a forward captured in a HIP graph and replayed, with eager forwards and new
+    # inputs between the replays, gives the eager result bit for bit every time
+    # (the hand-off tickets reset themselves; nothing is allocated or cleared
+    # with a memset inside the forward)
+    L, D = decode_layer if which == "bf16" else fp4_layer
+    c = L["cfg"]
+    cfg_id = 1 if which == "bf16" else 4
+    layer = make_layer_obj(c, max(T, 64), flags)
+    xs = [x_device(synth.hidden(cfg_id, T, c["d"], c["act"], draw=i)) for i in range(2)]
+    fwd = lambda x, out=None: layer.forward(x, D["router_w"], D["experts"], D["shared"], out=out)
+    ref = []
+    for x in xs:
+        o = fwd(x)
+        torch.cuda.synchronize()
+        ref.append(out_host(o))
+    x_static = xs[0].clone()
+    out_static = torch.empty_like(fwd(x_static))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fwd(x_static, out_static)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fwd(x_static, out_static)
+    for rep in range(4):
+        i = rep % 2
+        x_static.copy_(xs[i])
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out_host(out_static), ref[i]), "replay %d differs from the eager forward" % rep
+        fwd(xs[1 - i])  # eager work between the replays
+        torch.cuda.synchronize()
+
+
 @pytest.fixture(scope="module")
 def prefill_layer():
     L = synth.layer(2)
