@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the Flint routed-expert MoE layer on one MI355X.
 
-    python bench.py [--workload decode|fp4|prefill|stack|tiny] [--steps K] [--warmup W]
+    python bench.py [--workload decode|fp4|prefill|stack|tiny|dense] [--steps K] [--warmup W]
 
 Prints ONE JSON line.  A step is one forward of the whole layer (router +
 top-k + permutation + experts + combine) over one batch of seeded synthetic
@@ -47,7 +47,10 @@ WORKLOADS = {
     "prefill": (2, (4096,), 2),
     "stack": (3, (32,), 47),
     "tiny": (0, (64,), 1),
+    # dense SwiGLU FFN (the model's first layers), width DENSE_F, on the same engine
+    "dense": (1, (32, 4096), 2),
 }
+DENSE_F = 16384  # about 0.1B parameters per dense layer at d = 2048
 
 
 def parse():
@@ -104,6 +107,8 @@ def main():
     c = dict(synth.CONFIGS[cfg_id])
     if args.workload == "stack":
         return bench_stack(args, c, cfg_id, Ts[0], n_layers)
+    if args.workload == "dense":
+        return bench_dense(args, c, cfg_id, Ts, n_layers)
     Tmax = max(Ts)
 
     t0 = time.time()
@@ -248,6 +253,99 @@ def main():
                              "mfma_frac_layer": round(r["mfma_frac"], 4),
                              "dominant_us": round(r["up_us"], 2),
                              "distinct_experts": r["distinct"]} for T, r in results.items()},
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_dense(args, c, cfg_id, Ts, n_layers):
+    """Dense SwiGLU FFN of width DENSE_F: out = D (SiLU(G x) * (U x)) for T tokens."""
+    import numpy as np
+    import torch
+
+    import synth
+    from gpu_helpers import dev_weights, x_device
+    import sparse_moe_transformer_gemv_amd as fm
+
+    d, F, wd = c["d"], DENSE_F, c["wdtype"]
+    t0 = time.time()
+    hosts = [synth.expert_set(cfg_id, l, 1, d, F, wd) for l in range(n_layers)]
+    ws = [dev_weights(h, wd) for h in hosts]
+    log("generated %d dense layer(s) of width %d in %.1fs" % (n_layers, F, time.time() - t0))
+    Tmax = max(Ts)
+    ffn = fm.DenseFFN(d, F, c["act"], wd, max_tokens=Tmax)
+    stream = torch.cuda.current_stream()
+    n_x = 4
+    results = {}
+    for T in Ts:
+        xs = [x_device(synth.hidden(cfg_id, T, d, c["act"], draw=i)) for i in range(n_x)]
+        for i in range(args.warmup):
+            ffn.forward(xs[i % n_x], ws[i % n_layers])
+        torch.cuda.synchronize()
+        ffn.layer.profile_begin(fm.KERNEL_EXPERT_UP, args.steps)
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for i in range(args.steps):
+            ffn.forward(xs[i % n_x], ws[i % n_layers])
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / args.steps
+        up_us = float(np.mean(ffn.layer.profile_end())) * 1e3
+        w_bytes = 3.0 * F * d * 2
+        up_flops = 2.0 * T * 2 * F * d
+        results[T] = dict(ms=ms, tok_s=T / (ms * 1e-3), up_us=up_us, up_flops=up_flops,
+                          up_bytes=2.0 * F * d * 2 + T * d * 2 + T * F * 4,
+                          hbm_frac=(w_bytes + 2 * T * d * 2) / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                          mfma_frac=3 * up_flops / 2 / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12))
+        log("T=%d: %.1f us/step, %.0f tok/s, %.1f%% HBM / %.1f%% MFMA (layer), gate/up %.1f us" % (
+            T, ms * 1e3, results[T]["tok_s"], 100 * results[T]["hbm_frac"],
+            100 * results[T]["mfma_frac"], up_us))
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy calibration: 1 GiB device-to-device copy done")
+    H = results[Tmax]
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "gateup_prefill_dense_T%d_traffic.json" % Tmax)
+    if os.path.exists(tpath):
+        with open(tpath) as fh:
+            tr = json.load(fh)
+        if tr.get("source_sha") == file_sha(KERNEL_SRC["gateup_prefill"]):
+            traffic = tr.get("bytes_per_launch")
+    achieved = H["up_flops"] / (H["up_us"] * 1e-6) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                "kernel": "gateup_prefill", "flops_per_launch": H["up_flops"],
+                "us_per_launch": round(H["up_us"], 2)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        sample = synth.hidden(cfg_id, 2, d, c["act"], draw=0)
+        ntok = 0
+        t1 = time.time()
+        while True:
+            oracle.ffn_forward(sample, hosts[0], wdtype=wd)
+            ntok += sample.shape[0]
+            if time.time() - t1 >= args.cpu_seconds:
+                break
+        dt = time.time() - t1
+        cpu = {"value": round(ntok / dt, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": "%d forwards of 2 tokens, layer 0, fp64" % (ntok // 2)}
+    line = {
+        "metric": "dense-FFN tokens/s", "value": round(H["tok_s"], 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(H["ms"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {0: "f32", 1: "bf16", 2: "nvfp4"}[wd], "data": "synthetic",
+        "config": {"workload": "dense SwiGLU FFN T=%d (d=%d, f=%d)" % (Tmax, d, F), "tokens": Tmax,
+                   "layers_rotated": n_layers, "hbm_frac_layer": round(H["hbm_frac"], 4),
+                   "mfma_frac_layer": round(H["mfma_frac"], 4)},
+        "roofline": roofline, "cpu_baseline": cpu,
+        "t_sweep": {str(T): {"tok_s": round(r["tok_s"], 1), "us": round(r["ms"] * 1e3, 2),
+                             "hbm_frac_layer": round(r["hbm_frac"], 4),
+                             "mfma_frac_layer": round(r["mfma_frac"], 4),
+                             "dominant_us": round(r["up_us"], 2)} for T, r in results.items()},
     }
     print(json.dumps(line), flush=True)
 

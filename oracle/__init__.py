@@ -24,7 +24,7 @@ import numpy as np
 
 __all__ = [
     "build", "lib", "F32", "BF16", "NVFP4",
-    "moe_forward", "expert_forward", "rmsnorm", "round_to_bf16",
+    "moe_forward", "expert_forward", "ffn_forward", "rmsnorm", "round_to_bf16",
     "bf16_value", "e2m1_value", "e4m3_value", "silu", "stack_forward",
 ]
 
@@ -176,6 +176,22 @@ def expert_forward(x, ws, e, *, wdtype=BF16, f=None):
     if rc != 0:
         raise ValueError("oracle_expert_forward rejected its arguments")
     return y
+
+
+def ffn_forward(x, ws, *, wdtype=BF16):
+    """fp64 output of a dense SwiGLU feed-forward layer for the tokens in ``x``.
+
+    The model's first layers are dense, the rest mixture-of-experts
+    [evermx.com, "Recursive Flint: Open-Weight MoE Coding Model, 2.5B Active",
+    Feature Overview, "Sparse architecture"].  A dense layer applies the one
+    SwiGLU feed-forward map that every expert is (width a parameter) to every
+    token, so this is ``expert_forward`` of expert 0 of the weight set ``ws``
+    (gate_up [1][2F][d], down [1][d][F], NVFP4 scales of one expert) per token.
+    x [T, d] float32, or bf16 bits as uint16.  Returns [T, d] fp64.
+    """
+    x = np.ascontiguousarray(x)
+    xv = bf16_value(x) if x.dtype == np.uint16 else x.astype(np.float64)
+    return np.stack([expert_forward(xv[t], ws, 0, wdtype=wdtype) for t in range(xv.shape[0])])
 
 
 def rmsnorm(h, eps=1e-6):

@@ -6,6 +6,6 @@ this package holds its kernels (csrc/), the build step and the ctypes binding.
 from .flint_moe import (  # noqa: F401
     EXPORTED, FLINT_BF16, FLINT_F32, FLINT_FORCE_DECODE_PATH, FLINT_FORCE_PREFILL_PATH,
     FLINT_NVFP4, KERNEL_COMBINE, KERNEL_EXPERT_DOWN, KERNEL_EXPERT_UP, KERNEL_ROUTE, KERNEL_SORT,
-    ExpertWeights, FlintError, MoELayer, flint_expert_weights, flint_moe_config,
+    DenseFFN, ExpertWeights, FlintError, MoELayer, flint_expert_weights, flint_moe_config,
     flint_moe_create, flint_moe_destroy, flint_rmsnorm_forward, load_library,
 )

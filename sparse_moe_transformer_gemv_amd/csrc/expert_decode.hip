@@ -145,13 +145,16 @@ struct ExpertParams {
 // ---------------------------------------------------------------------------
 // gate/up + SwiGLU.  Block = 4 waves, each wave owns FPW features (FPW gate
 // rows and the matching FPW up rows); work item = (group, block of 4*FPW
-// features).  Tokens of the group are processed TG at a time.
+// features).  Tokens of the group are processed kTG at a time, each pass
+// streaming the block's weight rows once: 4 for small batches, 16 from 16
+// tokens on (fewer passes over the weights, more accumulators).
 // ---------------------------------------------------------------------------
 constexpr int kFPW = 2;
 constexpr int kFPB = 4 * kFPW;
-constexpr int kTG = 4;
+constexpr int kTGWide = 16;  // tokens per pass from this batch size on
+__host__ __device__ constexpr int tokens_per_pass(int T) { return T >= kTGWide ? kTGWide : 4; }
 
-template <typename ActT, int WT>
+template <typename ActT, int WT, int kTG>
 __global__ __launch_bounds__(256) void gateup_decode_kernel(ExpertParams p) {
     using W = WChunk<WT>;
     constexpr int VEC = W::VEC;
@@ -241,7 +244,7 @@ __global__ __launch_bounds__(256) void gateup_decode_kernel(ExpertParams p) {
 constexpr int kRPW = 4;
 constexpr int kRPB = 4 * kRPW;
 
-template <int WT>
+template <int WT, int kTG>
 __global__ __launch_bounds__(256) void down_decode_kernel(ExpertParams p) {
     using W = WChunk<WT>;
     constexpr int VEC = W::VEC;
@@ -1070,6 +1073,25 @@ static ExpertParams make_params(const LayerArgs& a, const Workspace& w) {
     return p;
 }
 
+template <int TG>
+static void launch_gateup_generic(const LayerArgs& a, const ExpertParams& p, dim3 grid, hipStream_t s) {
+    const bool f32 = a.dm.act == DT_F32;
+    switch (a.dm.wdt) {
+    case DT_F32:
+        if (f32) hipLaunchKernelGGL((gateup_decode_kernel<float, DT_F32, TG>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((gateup_decode_kernel<uint16_t, DT_F32, TG>), grid, dim3(256), 0, s, p);
+        break;
+    case DT_BF16:
+        if (f32) hipLaunchKernelGGL((gateup_decode_kernel<float, DT_BF16, TG>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((gateup_decode_kernel<uint16_t, DT_BF16, TG>), grid, dim3(256), 0, s, p);
+        break;
+    default:
+        if (f32) hipLaunchKernelGGL((gateup_decode_kernel<float, DT_NVFP4, TG>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((gateup_decode_kernel<uint16_t, DT_NVFP4, TG>), grid, dim3(256), 0, s, p);
+        break;
+    }
+}
+
 hipError_t launch_gateup_decode(const LayerArgs& a, const Workspace& w, hipStream_t s) {
     ExpertParams p = make_params(a, w);
     if (decode_fp4_ok(a.dm)) {
@@ -1096,21 +1118,8 @@ hipError_t launch_gateup_decode(const LayerArgs& a, const Workspace& w, hipStrea
     }
     const int fblocks = (p.hstride + kFPB - 1) / kFPB;
     dim3 grid(max_groups(a.dm) * fblocks);
-    const bool f32 = a.dm.act == DT_F32;
-    switch (a.dm.wdt) {
-    case DT_F32:
-        if (f32) hipLaunchKernelGGL((gateup_decode_kernel<float, DT_F32>), grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((gateup_decode_kernel<uint16_t, DT_F32>), grid, dim3(256), 0, s, p);
-        break;
-    case DT_BF16:
-        if (f32) hipLaunchKernelGGL((gateup_decode_kernel<float, DT_BF16>), grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((gateup_decode_kernel<uint16_t, DT_BF16>), grid, dim3(256), 0, s, p);
-        break;
-    default:
-        if (f32) hipLaunchKernelGGL((gateup_decode_kernel<float, DT_NVFP4>), grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((gateup_decode_kernel<uint16_t, DT_NVFP4>), grid, dim3(256), 0, s, p);
-        break;
-    }
+    if (tokens_per_pass(a.dm.T) == kTGWide) launch_gateup_generic<kTGWide>(a, p, grid, s);
+    else launch_gateup_generic<4>(a, p, grid, s);
     return hipGetLastError();
 }
 
@@ -1157,10 +1166,20 @@ hipError_t launch_down_decode(const LayerArgs& a, const Workspace& w, hipStream_
     }
     const int rblocks = (a.dm.d + kRPB - 1) / kRPB;
     dim3 grid(max_groups(a.dm) * rblocks);
+    const bool wide = tokens_per_pass(a.dm.T) == kTGWide;
     switch (a.dm.wdt) {
-    case DT_F32: hipLaunchKernelGGL(down_decode_kernel<DT_F32>, grid, dim3(256), 0, s, p); break;
-    case DT_BF16: hipLaunchKernelGGL(down_decode_kernel<DT_BF16>, grid, dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL(down_decode_kernel<DT_NVFP4>, grid, dim3(256), 0, s, p); break;
+    case DT_F32:
+        if (wide) hipLaunchKernelGGL((down_decode_kernel<DT_F32, kTGWide>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((down_decode_kernel<DT_F32, 4>), grid, dim3(256), 0, s, p);
+        break;
+    case DT_BF16:
+        if (wide) hipLaunchKernelGGL((down_decode_kernel<DT_BF16, kTGWide>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((down_decode_kernel<DT_BF16, 4>), grid, dim3(256), 0, s, p);
+        break;
+    default:
+        if (wide) hipLaunchKernelGGL((down_decode_kernel<DT_NVFP4, kTGWide>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((down_decode_kernel<DT_NVFP4, 4>), grid, dim3(256), 0, s, p);
+        break;
     }
     return hipGetLastError();
 }

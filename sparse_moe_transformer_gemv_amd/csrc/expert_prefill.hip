@@ -369,6 +369,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
     }
 }
 
+constexpr int kNMajorBlocks = 64;  // B-row blocks per m-tile from which items run B-block-major
+
 // Persistent grid: the work items (m-tile, B-row block) are cut into 8
 // contiguous chunks, one per XCD, walked by that XCD's workgroups in rounds.
 // When the last round of a chunk would leave at least half of the XCD's
@@ -386,9 +388,15 @@ void prefill_gemm_kernel(PrefillParams p) {
     const int rem = cnt % nper;
     const bool split = rem > 0 && 2 * rem <= nper;
     const int nfull = split ? cnt - rem : cnt;
+    // Items run m-tile-major (the B-row blocks of one m-tile in a row, sharing its
+    // A rows), except with many B-row blocks per tile (a wide dense layer): then
+    // B-row-block-major, so each XCD's chunk reads its own slice of the weights
+    // once, rather than every XCD reading all of them.
+    const int ntl = *p.ws.n_tiles;
+    const bool nmajor = p.nblk >= kNMajorBlocks;
     auto coords = [&](int t, int4& g, int& m0, int& jb) {
-        const int2 tile = p.ws.tiles[t / p.nblk];
-        jb = t % p.nblk;
+        const int2 tile = p.ws.tiles[nmajor ? t % ntl : t / p.nblk];
+        jb = nmajor ? t / ntl : t % p.nblk;
         g = p.ws.groups[tile.x];
         m0 = tile.y;
     };

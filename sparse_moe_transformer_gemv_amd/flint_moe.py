@@ -237,3 +237,33 @@ class MoELayer:
         n = ctypes.c_int32(0)
         _check(load_library().flint_moe_profile_end(self.handle, buf, cap, ctypes.byref(n)))
         return [buf[i] for i in range(n.value)]
+
+
+class DenseFFN:
+    """A dense SwiGLU feed-forward layer, out = [residual +] D (SiLU(G x) * (U x)).
+
+    The first layers of the model are dense rather than mixture-of-experts
+    [evermx.com, "Recursive Flint: Open-Weight MoE Coding Model, 2.5B Active",
+    Feature Overview, "Sparse architecture"]; their width is a parameter.  The
+    MoE engine runs it unchanged, configured with one routed expert, top-1 and no
+    shared expert: the router is all zeros, the renormalised softmax over the one
+    chosen logit is exactly 1, and the layer output is that expert's output.
+    Weights use the layout of one expert: gate_up [1][2F][d] (gate rows first),
+    down [1][d][F]; NVFP4 adds the scales of one expert.
+    """
+
+    def __init__(self, d_model: int, d_ff: int, act_dtype: int = FLINT_BF16,
+                 weight_dtype: int = FLINT_BF16, max_tokens: int = 64, flags: int = 0):
+        self.layer = MoELayer(d_model, 1, 1, d_ff, 0, act_dtype, weight_dtype, max_tokens, flags)
+        self.router_w = torch.zeros((1, d_model), dtype=torch.float32,
+                                    device=torch.device("cuda", torch.cuda.current_device()))
+
+    def close(self):
+        self.layer.close()
+
+    def forward(self, x: torch.Tensor, weights: ExpertWeights,
+                residual: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        return self.layer.forward(x, self.router_w, weights, None, None, residual, out)
+
+    __call__ = forward

@@ -420,3 +420,40 @@ def test_stack_layer_alone_full_size(layer_idx):
     out, rout = run_gpu(layer, D, x, residual=zero)
     rep = compare(out, rout, run_oracle(L, x), c["k"], c["wdtype"], out_bf16=False)
     print("stack layer %d alone: %s" % (layer_idx, rep), flush=True)
+
+
+# ------------------------------------------------------------- dense FFN layer
+
+@pytest.mark.parametrize("cfg_id,d,F,T,flags", [
+    (1, 256, 512, 3, 0),                           # decode, matrix-core kernels
+    (1, 256, 512, 300, FLINT_FORCE_PREFILL_PATH),  # grouped GEMM, one group
+    (1, 2048, 16384, 4, 0),                        # full width: decode kernels for wide f
+    (1, 2048, 16384, 4096, 0),                     # full width prefill, sampled rows
+    (4, 2048, 2048, 16, 0),                        # NVFP4 matrix-core decode
+    (4, 2048, 16384, 2, 0),                        # NVFP4, wide f
+])
+def test_dense_ffn(cfg_id, d, F, T, flags):
+    from sparse_moe_transformer_gemv_amd import DenseFFN
+    from gpu_helpers import TOL, dev_weights, half_ulp_bf16
+    wd = synth.CONFIGS[cfg_id]["wdtype"]
+    act = synth.CONFIGS[cfg_id]["act"]
+    ws = synth.expert_set(cfg_id, 0, 1, d, F, wd)
+    x = synth.hidden(cfg_id, T, d, act)
+    ffn = DenseFFN(d, F, act, wd, max_tokens=max(T, 64), flags=flags)
+    out = out_host(ffn.forward(x_device(x), dev_weights(ws, wd)))
+    torch.cuda.synchronize()
+    rows = np.arange(T) if T <= 64 else np.random.default_rng(5).choice(T, 24, replace=False)
+    ref = oracle.ffn_forward(x[rows], ws, wdtype=wd)
+    err = np.abs(out[rows] - ref)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    assert np.all(err <= TOL[wd] * rms + half_ulp_bf16(ref)), "max|err| %.3e vs %.1e * RMS %.3e" % (
+        err.max(), TOL[wd], rms)
+    # the fp32-output form (zero residual) meets the plain bound
+    zero = torch.zeros((T, d), dtype=torch.float32, device="cuda")
+    out32 = out_host(ffn.forward(x_device(x), dev_weights(ws, wd), residual=zero))
+    torch.cuda.synchronize()
+    err32 = np.abs(out32[rows] - ref)
+    assert err32.max() <= TOL[wd] * rms, "fp32 out: max|err| %.3e vs %.1e * RMS %.3e" % (
+        err32.max(), TOL[wd], rms)
+    print("dense FFN cfg %d d=%d F=%d T=%d: max|err| %.2e (bf16 out), %.2e (fp32 out), RMS %.3e" % (
+        cfg_id, d, F, T, err.max(), err32.max(), rms), flush=True)

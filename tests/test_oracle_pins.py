@@ -434,3 +434,37 @@ def test_stack_with_zero_layers_is_identity_and_rounds_input():
     h, trace = oracle.stack_forward(h0, [zero, zero], top_k=2)
     assert np.array_equal(h, h0)
     assert np.array_equal(trace[0]["x"], oracle.round_to_bf16(oracle.rmsnorm(h0)))
+
+
+# ---------------------------------------------------------- dense FFN layer
+
+def test_dense_ffn_closed_form_permutation_weights():
+    # every token of a dense layer goes through the same SwiGLU map, written out
+    # term by term for permutation weights; bf16 activations read as their values
+    rng = np.random.default_rng(21)
+    d, f, T = 7, 3, 4
+    gu, dn, apply = _perm_expert(rng, d, f)
+    ws = {"gate_up": gu[None], "down": dn[None]}
+    x = (rng.integers(-6, 7, size=(T, d)) / 2.0).astype(np.float32)
+    y = oracle.ffn_forward(x, ws, wdtype=oracle.F32)
+    assert y.shape == (T, d)
+    for t in range(T):
+        assert np.allclose(y[t], apply(x[t].astype(np.float64)), rtol=1e-14, atol=1e-15)
+    yb = oracle.ffn_forward(synth.bf16_bits(x), ws, wdtype=oracle.F32)  # these x are exact in bf16
+    assert np.array_equal(yb, y)
+
+
+def test_dense_ffn_is_the_top1_layer_of_one_expert():
+    # one routed expert, top-1, no shared expert: the renormalised weight of the
+    # single chosen logit is exactly 1, whatever the router, so the layer is the FFN
+    rng = np.random.default_rng(22)
+    d, f, T = 16, 8, 5
+    gu = synth.bf16_bits(rng.standard_normal((1, 2 * f, d)) / math.sqrt(d))
+    dn = synth.bf16_bits(rng.standard_normal((1, d, f)) / math.sqrt(f))
+    ws = {"gate_up": gu, "down": dn}
+    x = synth.bf16_bits(rng.standard_normal((T, d)))
+    ref = oracle.ffn_forward(x, ws)
+    for wr in (np.zeros((1, d), np.float32), rng.standard_normal((1, d)).astype(np.float32)):
+        r = oracle.moe_forward(x, wr, ws, None, top_k=1)
+        assert (r["idx"] == 0).all() and (r["w"] == 1.0).all()
+        assert np.array_equal(r["out"], ref)
