@@ -140,6 +140,7 @@ struct ExpertParams {
     const float* residual;  // added first when not null
     void* out;              // [T][d] fp32 (out_f32) or bf16
     int out_f32;
+    int kchunks;            // down_mfma_kernel: K chunks of the widest group (1: no split)
 };
 
 // ---------------------------------------------------------------------------
@@ -476,7 +477,8 @@ __global__ __launch_bounds__(256) void gateup_mfma_kernel(ExpertParams p) {
 template <int NSMAX, int NT>
 __device__ __forceinline__ void down_mfma_tile(const ExpertParams& p, const int4& g, int r0, int nsteps, int kl,
                                                int n0, const __amdgpu_buffer_rsrc_t (&hv)[3],
-                                               const uint4 (&b)[NT][NSMAX], float ws, float (&s_part)[4][NT][256]) {
+                                               const uint4 (&b)[NT][NSMAX], float ws, float (&s_part)[4][NT][256],
+                                               float* ybase, bool handoff) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, q = lane >> 4;
     const int m = r0 + row;
@@ -507,11 +509,11 @@ __device__ __forceinline__ void down_mfma_tile(const ExpertParams& p, const int4
     __syncthreads();
     const int mm = tid >> 4, n = tid & 15;
     if (r0 + mm < g.z) {
-        float* yr = static_cast<float*>(p.ws.y) + (size_t)(g.w + r0 + mm) * p.dm.d + n0 + n;
+        float* yr = ybase + (size_t)(g.w + r0 + mm) * p.dm.d + n0 + n;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const float v = ((s_part[0][t][tid] + s_part[1][t][tid]) + s_part[2][t][tid]) + s_part[3][t][tid];
-            if (p.combine)
+            if (handoff)
                 st_agent(yr + 16 * t, ws * v);  // read by another workgroup of this launch
             else
                 yr[16 * t] = ws * v;
@@ -575,8 +577,11 @@ __device__ __forceinline__ void combine_columns(const ExpertParams& p, int n0) {
     else combine_columns_n<NT, 4>(p, n0, s_pos);
 }
 
-// down: block = (group, NT tiles of 16 output rows); K = F split over the
-// waves, NSMAX >= F / 128 k steps per wave.  h enters the MFMA exactly as the
+// down: block = (group, NT tiles of 16 output rows, K chunk); K = F (or its
+// chunk) split over the waves, NSMAX >= chunk / 128 k steps per wave.  Groups
+// wider than kDownKChunk split K into chunks of that width: each chunk writes
+// its weighted partial rows to Workspace::part, and the last chunk of the
+// (group, rows) pair to arrive sums them in chunk order into y.  h enters the MFMA exactly as the
 // three bf16 planes (hi + mid + lo of the fp32 value) written by the gate/up
 // kernel, the weights exactly, so the only rounding is the fp32 accumulation.  Load order and the peeled first
 // token tile as in gateup_mfma_kernel.
@@ -589,16 +594,23 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertParams p) {
     const int row = lane & 15, q = lane >> 4;
     const int d = p.dm.d;
     const int rblocks = d / (16 * NT);
-    const int gi = blockIdx.x / rblocks, rb = blockIdx.x % rblocks;
+    const int per_g = rblocks * p.kchunks;
+    const int gi = blockIdx.x / per_g, rb = blockIdx.x % rblocks, kc = (blockIdx.x % per_g) / rblocks;
     if (gi >= *p.ws.n_groups) return;
     const int4 g = p.ws.groups[gi];
     const bool is_shared = g.x == p.dm.E;
+    const int F = is_shared ? p.dm.fs : p.dm.f;
+    const int kcg = F > kDownKChunk ? F / kDownKChunk : 1;  // this group's K chunks
+    if (kc >= kcg) return;
     const int mm = tid >> 4;
     const float rw_load = p.ws.sorted_wt[g.y + (mm < g.z ? mm : g.z - 1)];
     __builtin_amdgcn_sched_barrier(0);
-    const int F = is_shared ? p.dm.fs : p.dm.f;
-    const int nsteps = F / 128;
-    const int kl = wave * (F / 4) + 8 * q;
+    const int Fc = F / kcg;
+    const int nsteps = Fc / 128;
+    const int kl = kc * Fc + wave * (Fc / 4) + 8 * q;
+    const bool split = kcg > 1;
+    float* ybase = split ? p.ws.part + (size_t)kc * kSplitRowsMax * d : static_cast<float*>(p.ws.y);
+    const bool handoff = split || p.combine;
     const size_t e = is_shared ? 0 : (size_t)g.x;
     const uint16_t* dn = static_cast<const uint16_t*>(is_shared ? p.shared.dn : p.routed.dn);
     const int n0 = rb * 16 * NT;
@@ -618,11 +630,25 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertParams p) {
     __amdgpu_buffer_rsrc_t hv[3];
 #pragma unroll
     for (int pl = 0; pl < 3; ++pl) hv[pl] = buffer_view(h16 + pl * plane + (size_t)g.w * p.hstride, vbytes);
-    down_mfma_tile<NSMAX, NT>(p, g, 0, nsteps, kl, n0, hv, b, is_shared ? 1.f : rw_load, s_part);
+    down_mfma_tile<NSMAX, NT>(p, g, 0, nsteps, kl, n0, hv, b, is_shared ? 1.f : rw_load, s_part, ybase, handoff);
     for (int r0 = 16; r0 < g.z; r0 += 16) {
         const int m = r0 + mm;
         const float rw = is_shared ? 1.f : p.ws.sorted_wt[g.y + (m < g.z ? m : g.z - 1)];
-        down_mfma_tile<NSMAX, NT>(p, g, r0, nsteps, kl, n0, hv, b, rw, s_part);
+        down_mfma_tile<NSMAX, NT>(p, g, r0, nsteps, kl, n0, hv, b, rw, s_part, ybase, handoff);
+    }
+    if (split) {  // uniform: the last chunk of (group, rows) sums the partials in chunk order
+        __shared__ int s_kflag;
+        if (!last_arrival(&p.ws.kcount[gi * rblocks + rb], kcg, &s_kflag)) return;
+        float* y = static_cast<float*>(p.ws.y);
+        for (int i = tid; i < g.z * 16 * NT; i += blockDim.x) {
+            const size_t o = (size_t)(g.w + i / (16 * NT)) * d + n0 + i % (16 * NT);
+            float v = ld_agent(p.ws.part + o);
+            for (int c = 1; c < kcg; ++c) v += ld_agent(p.ws.part + (size_t)c * kSplitRowsMax * d + o);
+            if (p.combine)
+                st_agent(y + o, v);
+            else
+                y[o] = v;
+        }
     }
     if (p.combine) {  // uniform
         // one workgroup per active group arrives for these columns; the last one combines
@@ -1047,10 +1073,14 @@ bool decode_fp4_ok(const Dims& dm) {
 bool decode_mfma_ok(const Dims& dm) {
     const int fmax = dm.f > dm.fs ? dm.f : dm.fs;
     const int ns = dm.d / 128;
+    // widths above kDownKChunk split K in the down kernel: whole chunks, and a
+    // partial-sum buffer that holds every (token, slot) row
+    auto width_ok = [&](int w) { return w <= kDownKChunk || w % kDownKChunk == 0; };
+    const bool split_ok = fmax <= kDownKChunk || (size_t)(dm.k + 1) * dm.T <= (size_t)kSplitRowsMax;
     return dm.act == DT_BF16 && dm.wdt == DT_BF16 && dm.d % 128 == 0 &&
            (ns == 1 || ns == 2 || ns == 4 || ns == 8 || ns == 16) && dm.f % 128 == 0 &&
-           dm.fs % 128 == 0 && fmax <= 1024 && dm.d % 32 == 0 && (size_t)dm.T * dm.d * 2 < kOffNone &&
-           (size_t)dm.T * fmax * 4 < kOffNone;
+           dm.fs % 128 == 0 && width_ok(dm.f) && width_ok(dm.fs) && split_ok && dm.d % 32 == 0 &&
+           (size_t)dm.T * dm.d * 2 < kOffNone && (size_t)dm.T * fmax * 4 < kOffNone;
 }
 
 static int max_groups(const Dims& dm) {
@@ -1070,6 +1100,7 @@ static ExpertParams make_params(const LayerArgs& a, const Workspace& w) {
     p.residual = a.residual;
     p.out = a.out;
     p.out_f32 = (a.residual != nullptr || a.dm.act == DT_F32) ? 1 : 0;
+    p.kchunks = 1;
     return p;
 }
 
@@ -1154,7 +1185,8 @@ hipError_t launch_down_decode(const LayerArgs& a, const Workspace& w, hipStream_
     if (decode_mfma_ok(a.dm)) {
         constexpr int NT = kDownMfmaTiles;
         p.combine = down_decode_combines(a.dm) ? 1 : 0;
-        dim3 grid(max_groups(a.dm) * (a.dm.d / (16 * NT)));
+        p.kchunks = p.hstride > kDownKChunk ? p.hstride / kDownKChunk : 1;
+        dim3 grid(max_groups(a.dm) * (a.dm.d / (16 * NT)) * p.kchunks);
         switch ((p.hstride + 127) / 128) {
         case 1: hipLaunchKernelGGL((down_mfma_kernel<1, NT>), grid, dim3(256), 0, s, p); break;
         case 2: hipLaunchKernelGGL((down_mfma_kernel<2, NT>), grid, dim3(256), 0, s, p); break;

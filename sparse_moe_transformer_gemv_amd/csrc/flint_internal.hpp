@@ -36,11 +36,19 @@ struct Workspace {
     int* n_tiles;        // [1]
     int* counter;        // [1 + ceil(Tm/16)] last-block tickets, zero between launches
     int* dcount;         // [ceil(d/16)] decode down tickets (combine folded in), zero between launches
+    float* part;         // [kchunks][kSplitRowsMax][d] split-K partial sums of the decode down (f > 1024)
+    int* kcount;         // [(E+1) ceil(d/16)] split-K tickets, zero between launches
     void* h;             // [(k+1)*Tm][fmax] x 8 B: fp32 (decode VALU), three exact bf16 planes (decode
                          // MFMA), two f16 planes (NVFP4), or bf16 (prefill)
     void* y;             // [(k+1)*Tm][d]:    fp32 (decode) or bf16 (prefill)
     int max_tiles;
 };
+
+// The matrix-core decode down kernel holds at most 1024 of K in registers;
+// wider experts split K into 1024-wide chunks whose partial sums meet in
+// Workspace::part, which holds up to kSplitRowsMax (token, slot) rows.
+constexpr int kDownKChunk = 1024;
+constexpr int kSplitRowsMax = 576;
 
 struct Dims {
     int T, d, E, k, f, fs;

@@ -147,6 +147,10 @@ size_t carve(const flint_moe_config& c, char* base, Workspace* w) {
     w->n_tiles = static_cast<int*>(take(4));
     w->counter = static_cast<int*>(take((1 + (Tm + 15) / 16) * 4));
     w->dcount = static_cast<int*>(take((size_t)((c.d_model + 15) / 16) * 4));
+    const size_t kchunks = fmax > (size_t)kDownKChunk ? (fmax + kDownKChunk - 1) / kDownKChunk : 0;
+    // the down kernel strides its chunks by kSplitRowsMax rows
+    w->part = static_cast<float*>(take(kchunks * (size_t)kSplitRowsMax * c.d_model * 4));
+    w->kcount = static_cast<int*>(take((E + 1) * (size_t)((c.d_model + 15) / 16) * 4));
     w->h = take(slots * fmax * 8);
     w->y = take(slots * (size_t)c.d_model * 4);
     w->max_tiles = (int)max_tiles;

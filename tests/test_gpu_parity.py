@@ -427,7 +427,8 @@ def test_stack_layer_alone_full_size(layer_idx):
 @pytest.mark.parametrize("cfg_id,d,F,T,flags", [
     (1, 256, 512, 3, 0),                           # decode, matrix-core kernels
     (1, 256, 512, 300, FLINT_FORCE_PREFILL_PATH),  # grouped GEMM, one group
-    (1, 2048, 16384, 4, 0),                        # full width: decode kernels for wide f
+    (1, 2048, 16384, 4, 0),                        # full width decode: K split in 16 chunks, combine folded
+    (1, 2048, 16384, 32, 0),                       # the same without the folded combine
     (1, 2048, 16384, 4096, 0),                     # full width prefill, sampled rows
     (4, 2048, 2048, 16, 0),                        # NVFP4 matrix-core decode
     (4, 2048, 16384, 2, 0),                        # NVFP4, wide f
@@ -457,3 +458,10 @@ def test_dense_ffn(cfg_id, d, F, T, flags):
         err32.max(), TOL[wd], rms)
     print("dense FFN cfg %d d=%d F=%d T=%d: max|err| %.2e (bf16 out), %.2e (fp32 out), RMS %.3e" % (
         cfg_id, d, F, T, err.max(), err32.max(), rms), flush=True)
+
+
+@pytest.mark.parametrize("T", [3, 40])
+def test_wide_shared_expert_splits_k(T):
+    # a shared expert wider than one K chunk of the decode down kernel: only its
+    # group is split (two chunks), the routed groups are not
+    _case(1, T, d=256, E=64, f=128, fs=2048)
