@@ -718,6 +718,7 @@ constexpr int kFp4ScRow = 8 * NG * NW + 16;
 // bytes, plus 16 (banks, as for gate/up)
 template <int NGMAX>
 constexpr int kFp4DownScRow = 32 * NGMAX + 16;
+constexpr int kFp4DownKChunk = 2048;  // K held by one NVFP4 down block (NGMAX = 4)
 
 // h of the NVFP4 path: two f16 planes (hi, lo) of (k+1) T rows each, holding
 // h * 2^-8 (headroom above the f16 range for large activations).
@@ -919,11 +920,12 @@ __global__ __launch_bounds__(64 * NW) void gateup_fp4_kernel(ExpertParams p) {
 // routing weight of the token row this thread stores, times the tensor scale
 // and the inverse of the h scale.
 template <int NT, int NGMAX>
-__device__ __forceinline__ void down_fp4_tile(const ExpertParams& p, const int4& g, int r0, int ng, int kl, int n0,
+__device__ __forceinline__ void down_fp4_tile(const ExpertParams& p, const int4& g, int r0, int ng, int kl, int kls,
+                                              int n0,
                                               __amdgpu_buffer_rsrc_t hv_hi, __amdgpu_buffer_rsrc_t hv_lo,
                                               uint4 (&cw)[NT][NGMAX], uint8_t* s_sc, bool first, int sc_o0,
                                               int sc_o1, u32x4_t sc_v0, u32x4_t sc_v1, float ws,
-                                              float (&s_part)[4][NT][256]) {
+                                              float (&s_part)[4][NT][256], float* ybase, bool handoff) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, q = lane >> 4;
     const int m = r0 + row;
@@ -957,7 +959,7 @@ __device__ __forceinline__ void down_fp4_tile(const ExpertParams& p, const int4&
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const uint16_t sw = *reinterpret_cast<const uint16_t*>(s_sc + (16 * t + row) * kFp4DownScRow<NGMAX> +
-                                                                  kl / 16 + 8 * gg);
+                                                                  kls / 16 + 8 * gg);
             sc[t][0] = fp4_scale(__builtin_amdgcn_cvt_f32_fp8(sw, 0));
             sc[t][1] = fp4_scale(__builtin_amdgcn_cvt_f32_fp8(sw, 1));
         }
@@ -978,11 +980,11 @@ __device__ __forceinline__ void down_fp4_tile(const ExpertParams& p, const int4&
     __syncthreads();
     const int mm = tid >> 4, n = tid & 15;
     if (r0 + mm < g.z) {
-        float* yr = static_cast<float*>(p.ws.y) + (size_t)(g.w + r0 + mm) * p.dm.d + n0 + n;
+        float* yr = ybase + (size_t)(g.w + r0 + mm) * p.dm.d + n0 + n;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const float v = ((s_part[0][t][tid] + s_part[1][t][tid]) + s_part[2][t][tid]) + s_part[3][t][tid];
-            if (p.combine)
+            if (handoff)
                 st_agent(yr + 16 * t, ws * v);  // read by another workgroup of this launch
             else
                 yr[16 * t] = ws * v;
@@ -1004,28 +1006,37 @@ __global__ __launch_bounds__(256) void down_fp4_kernel(ExpertParams p) {
     const int row = lane & 15, q = lane >> 4;
     const int d = p.dm.d;
     const int rblocks = d / (16 * NT);
-    const int gi = blockIdx.x / rblocks, rb = blockIdx.x % rblocks;
+    const int per_g = rblocks * p.kchunks;
+    const int gi = blockIdx.x / per_g, rb = blockIdx.x % rblocks, kc = (blockIdx.x % per_g) / rblocks;
     if (gi >= *p.ws.n_groups) return;
     const int4 g = p.ws.groups[gi];
     const bool is_shared = g.x == p.dm.E;
+    const int F = is_shared ? p.dm.fs : p.dm.f;
+    // groups wider than kFp4DownKChunk split K as down_mfma_kernel does
+    const int kcg = F > kFp4DownKChunk ? F / kFp4DownKChunk : 1;
+    if (kc >= kcg) return;
     // routing weight of the row this thread stores in the first token tile
     const int mm = tid >> 4;
     const float rw_load = p.ws.sorted_wt[g.y + (mm < g.z ? mm : g.z - 1)];
-    const int F = is_shared ? p.dm.fs : p.dm.f;
-    const int ng = F / 512;
-    const int kl = wave * (F / 4) + 32 * q;
+    const int Fc = F / kcg;                            // this chunk's K
+    const int ng = Fc / 512;
+    const int kls = wave * (Fc / 4) + 32 * q;          // within the chunk (scales in LDS)
+    const int kl = kc * Fc + kls;                      // within the row (codes, h)
+    const bool split = kcg > 1;
+    float* ybase = split ? p.ws.part + (size_t)kc * kSplitRowsMax * d : static_cast<float*>(p.ws.y);
+    const bool handoff = split || p.combine;
     const size_t e = is_shared ? 0 : (size_t)g.x;
     const WeightPtrs& wp = is_shared ? p.shared : p.routed;
     const int n0 = rb * 16 * NT;
     // The block's scales (16 NT rows of F / 16 bytes) in 16-byte chunks, at
     // most two per thread, coalesced; chunks past the last repeat it.
     static_assert(16 * NT * 2 * NGMAX <= 2 * 256, "two scale chunks per thread");
-    const int cpr = F / 256, nchunks = 16 * NT * cpr;
+    const int cpr = Fc / 256, nchunks = 16 * NT * cpr;
     auto sc_chunk = [&](int ci, u32x4_t& v) {  // LDS offset of chunk ci, or -1 past the last
         const int cc = ci < nchunks ? ci : nchunks - 1;
         const int r = cc / cpr, col = cc % cpr;
         const size_t wr = e * (size_t)d + (size_t)(n0 + r);
-        v = *reinterpret_cast<const u32x4_t*>(wp.dns + wr * (F / 16) + 16 * col);
+        v = *reinterpret_cast<const u32x4_t*>(wp.dns + wr * (F / 16) + kc * (Fc / 16) + 16 * col);
         return ci < nchunks ? r * kFp4DownScRow<NGMAX> + 16 * col : -1;
     };
     u32x4_t sc_v0, sc_v1;
@@ -1048,13 +1059,27 @@ __global__ __launch_bounds__(256) void down_fp4_kernel(ExpertParams p) {
     const uint32_t vbytes = (uint32_t)g.z * p.hstride * 2;
     const __amdgpu_buffer_rsrc_t hv_hi = buffer_view(h16 + (size_t)g.w * p.hstride, vbytes);
     const __amdgpu_buffer_rsrc_t hv_lo = buffer_view(h16 + plane + (size_t)g.w * p.hstride, vbytes);
-    down_fp4_tile<NT, NGMAX>(p, g, 0, ng, kl, n0, hv_hi, hv_lo, cw, s_sc, true, sc_o0, sc_o1, sc_v0, sc_v1,
-                             tsd * rw0, s_part);
+    down_fp4_tile<NT, NGMAX>(p, g, 0, ng, kl, kls, n0, hv_hi, hv_lo, cw, s_sc, true, sc_o0, sc_o1, sc_v0, sc_v1,
+                             tsd * rw0, s_part, ybase, handoff);
     for (int r0 = 16; r0 < g.z; r0 += 16) {
         const int m = r0 + mm;
         const float rw = is_shared ? 1.f : p.ws.sorted_wt[g.y + (m < g.z ? m : g.z - 1)];
-        down_fp4_tile<NT, NGMAX>(p, g, r0, ng, kl, n0, hv_hi, hv_lo, cw, s_sc, false, -1, -1, sc_v0, sc_v1,
-                                 tsd * rw, s_part);
+        down_fp4_tile<NT, NGMAX>(p, g, r0, ng, kl, kls, n0, hv_hi, hv_lo, cw, s_sc, false, -1, -1, sc_v0,
+                                 sc_v1, tsd * rw, s_part, ybase, handoff);
+    }
+    if (split) {  // uniform: the last chunk of (group, rows) sums the partials in chunk order
+        __shared__ int s_kflag;
+        if (!last_arrival(&p.ws.kcount[gi * rblocks + rb], kcg, &s_kflag)) return;
+        float* y = static_cast<float*>(p.ws.y);
+        for (int i = tid; i < g.z * 16 * NT; i += blockDim.x) {
+            const size_t o = (size_t)(g.w + i / (16 * NT)) * d + n0 + i % (16 * NT);
+            float v = ld_agent(p.ws.part + o);
+            for (int c = 1; c < kcg; ++c) v += ld_agent(p.ws.part + (size_t)c * kSplitRowsMax * d + o);
+            if (p.combine)
+                st_agent(y + o, v);
+            else
+                y[o] = v;
+        }
     }
     if (p.combine) {  // uniform; as in down_mfma_kernel
         __shared__ int s_flag;
@@ -1065,8 +1090,11 @@ __global__ __launch_bounds__(256) void down_fp4_kernel(ExpertParams p) {
 bool decode_fp4_ok(const Dims& dm) {
     const int fmax = dm.f > dm.fs ? dm.f : dm.fs;
     const int ng = dm.d / 512;
+    auto width_ok = [&](int w) { return w <= kFp4DownKChunk || w % kFp4DownKChunk == 0; };
+    const bool split_ok = fmax <= kFp4DownKChunk || (size_t)(dm.k + 1) * dm.T <= (size_t)kSplitRowsMax;
     return dm.act == DT_BF16 && dm.wdt == DT_NVFP4 && dm.d % 512 == 0 &&
-           (ng == 1 || ng == 2 || ng == 4) && dm.f % 512 == 0 && dm.fs % 512 == 0 && fmax <= 2048 &&
+           (ng == 1 || ng == 2 || ng == 4) && dm.f % 512 == 0 && dm.fs % 512 == 0 && width_ok(dm.f) &&
+           width_ok(dm.fs) && split_ok &&
            (size_t)dm.T * dm.d * 2 < kOffNone && (size_t)dm.T * fmax * 4 < kOffNone;
 }
 
@@ -1174,7 +1202,8 @@ hipError_t launch_down_decode(const LayerArgs& a, const Workspace& w, hipStream_
         constexpr int NT = kDownFp4Tiles;
         if (a.dm.d % (16 * NT) != 0) return hipErrorInvalidValue;
         p.combine = down_decode_combines(a.dm) ? 1 : 0;
-        dim3 grid(max_groups(a.dm) * (a.dm.d / (16 * NT)));
+        p.kchunks = p.hstride > kFp4DownKChunk ? p.hstride / kFp4DownKChunk : 1;
+        dim3 grid(max_groups(a.dm) * (a.dm.d / (16 * NT)) * p.kchunks);
         switch (p.hstride / 512) {
         case 1: hipLaunchKernelGGL((down_fp4_kernel<NT, 1>), grid, dim3(256), 0, s, p); break;
         case 2: hipLaunchKernelGGL((down_fp4_kernel<NT, 2>), grid, dim3(256), 0, s, p); break;

@@ -431,7 +431,8 @@ def test_stack_layer_alone_full_size(layer_idx):
     (1, 2048, 16384, 32, 0),                       # the same without the folded combine
     (1, 2048, 16384, 4096, 0),                     # full width prefill, sampled rows
     (4, 2048, 2048, 16, 0),                        # NVFP4 matrix-core decode
-    (4, 2048, 16384, 2, 0),                        # NVFP4, wide f
+    (4, 2048, 16384, 2, 0),                        # NVFP4, K split in 8 chunks
+    (4, 2048, 16384, 32, 0),                       # the same at a larger batch
 ])
 def test_dense_ffn(cfg_id, d, F, T, flags):
     from sparse_moe_transformer_gemv_amd import DenseFFN
@@ -465,3 +466,9 @@ def test_wide_shared_expert_splits_k(T):
     # a shared expert wider than one K chunk of the decode down kernel: only its
     # group is split (two chunks), the routed groups are not
     _case(1, T, d=256, E=64, f=128, fs=2048)
+
+
+@pytest.mark.parametrize("T", [3, 20])
+def test_wide_nvfp4_shared_expert_splits_k(T):
+    # an NVFP4 shared expert twice as wide as one K chunk of the NVFP4 down kernel
+    _case(4, T, d=512, E=64, f=512, fs=4096)
