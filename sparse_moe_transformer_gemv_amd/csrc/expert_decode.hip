@@ -140,7 +140,7 @@ struct ExpertParams {
     const float* residual;  // added first when not null
     void* out;              // [T][d] fp32 (out_f32) or bf16
     int out_f32;
-    int kchunks;            // down_mfma_kernel: K chunks of the widest group (1: no split)
+    int kchunks;            // down kernels: K chunks of the widest group (1: no split)
 };
 
 // ---------------------------------------------------------------------------
