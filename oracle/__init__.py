@@ -24,7 +24,7 @@ import numpy as np
 
 __all__ = [
     "build", "lib", "F32", "BF16", "NVFP4",
-    "moe_forward", "expert_forward", "ffn_forward", "rmsnorm", "round_to_bf16",
+    "moe_forward", "route", "expert_forward", "ffn_forward", "rmsnorm", "round_to_bf16",
     "bf16_value", "e2m1_value", "e4m3_value", "silu", "stack_forward",
 ]
 
@@ -75,6 +75,8 @@ def load_library(path):
     vp, ip, dp = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
     L.oracle_moe_forward.restype = ip
     L.oracle_moe_forward.argtypes = [ip] * 8 + [vp] * 17
+    L.oracle_route.restype = ip
+    L.oracle_route.argtypes = [ip] * 5 + [vp] * 6
     L.oracle_expert_forward.restype = ip
     L.oracle_expert_forward.argtypes = [ip, ip, ip, ctypes.c_long] + [vp] * 7
     L.oracle_rmsnorm.restype = None
@@ -161,6 +163,25 @@ def moe_forward(x, router_w, experts, shared, *, top_k=6, router_bias=None, wdty
     if rc != 0:
         raise ValueError("oracle_moe_forward rejected its arguments")
     return {"out": out, "idx": idx, "w": w, "logits": logits}
+
+
+def route(x, router_w, *, top_k=6, router_bias=None):
+    """The router alone for the tokens in ``x`` (the same steps as moe_forward):
+    returns idx [T, k] int32, w [T, k] fp64 and logits [T, E] fp64."""
+    x = np.ascontiguousarray(x)
+    act = _act_dtype(x)
+    T, d = x.shape
+    router_w = _c(router_w, np.float32)
+    E = router_w.shape[0]
+    router_bias = _c(router_bias, np.float32)
+    idx = np.zeros((T, top_k), np.int32)
+    w = np.zeros((T, top_k), np.float64)
+    logits = np.zeros((T, E), np.float64)
+    rc = lib().oracle_route(T, d, E, top_k, act, _p(x), _p(router_w), _p(router_bias), _p(idx),
+                            _p(w), _p(logits))
+    if rc != 0:
+        raise ValueError("oracle_route rejected its arguments")
+    return {"idx": idx, "w": w, "logits": logits}
 
 
 def expert_forward(x, ws, e, *, wdtype=BF16, f=None):

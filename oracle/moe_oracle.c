@@ -312,6 +312,35 @@ int oracle_moe_forward(int T, int d, int E, int k, int f, int fs, int act_dtype,
     return fail ? -1 : 0;
 }
 
+/*
+ * The router alone on T tokens: logits, the chosen k experts and their
+ * weights, exactly as oracle_moe_forward computes them (route_token), without
+ * the experts.  Arguments as in oracle_moe_forward.  Returns 0, or -1.
+ */
+int oracle_route(int T, int d, int E, int k, int act_dtype, const void* x,
+                 const float* router_w, const float* router_bias, int32_t* sel,
+                 double* w, double* logits) {
+    if (T < 0 || d <= 0 || E <= 0 || k <= 0 || k > E) return -1;
+    int fail = 0;
+#pragma omp parallel for schedule(dynamic, 16) reduction(| : fail)
+    for (int t = 0; t < T; ++t) {
+        double* xr = malloc(sizeof(double) * d);
+        double* lg = malloc(sizeof(double) * E);
+        double* p = malloc(sizeof(double) * E);
+        unsigned char* taken = malloc((size_t)E);
+        if (!xr || !lg || !p || !taken) {
+            fail = 1;
+        } else {
+            load_row(act_dtype, x, t, d, xr);
+            route_token(d, E, k, xr, router_w, router_bias, sel + (long)t * k,
+                        w + (long)t * k, lg, taken, p);
+            if (logits) memcpy(logits + (long)t * E, lg, sizeof(double) * E);
+        }
+        free(xr); free(lg); free(p); free(taken);
+    }
+    return fail ? -1 : 0;
+}
+
 /* One expert applied to one fp64 vector (weights as above, expert e). */
 int oracle_expert_forward(int d, int f, int wdtype, long e, const void* gate_up,
                           const void* down, const uint8_t* gu_scales,

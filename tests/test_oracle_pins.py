@@ -468,3 +468,98 @@ def test_dense_ffn_is_the_top1_layer_of_one_expert():
         r = oracle.moe_forward(x, wr, ws, None, top_k=1)
         assert (r["idx"] == 0).all() and (r["w"] == 1.0).all()
         assert np.array_equal(r["out"], ref)
+
+
+# ------------------------------------------------ dense brute force (pure Python)
+
+def _dense_case(wdtype, k, bias, shared, seed):
+    """Random dense tiny layer in stored formats, plus its fp64 decoding done
+    here (bf16 bits through their binary32 bit layout, NVFP4 through the OCP
+    golden tables and the documented packing: even element in the low nibble,
+    one E4M3 scale per 16 elements, a tensor scale per matrix)."""
+    from oracle import brute
+    rng = np.random.default_rng(seed)
+    T, d, E, f = 3, 32, 8, 16
+    x = synth.bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    router = (rng.standard_normal((E, d)) / math.sqrt(d)).astype(np.float32)
+    b = (rng.standard_normal(E) * 0.3).astype(np.float32) if bias else None
+    e2m1 = dict(_read_table("e2m1_ocp_mx.txt"))
+    e4m3 = dict(_read_table("e4m3_ocp_fp8.txt"))
+
+    def mk(n):
+        if wdtype == synth.NVFP4:
+            gu = rng.integers(0, 256, (n, 2 * f, d // 2), dtype=np.uint8)
+            dn = rng.integers(0, 256, (n, d, f // 2), dtype=np.uint8)
+            gs = rng.integers(0x28, 0x41, (n, 2 * f, d // 16), dtype=np.uint8)
+            ds = rng.integers(0x28, 0x41, (n, d, f // 16), dtype=np.uint8)
+            ts = rng.uniform(0.05, 0.5, (n, 3)).astype(np.float32)
+            ws = dict(gate_up=gu, down=dn, gate_up_scales=gs, down_scales=ds, tensor_scales=ts)
+
+            def dq(codes, scales, tsc, K):
+                out = []
+                for r in range(codes.shape[0]):
+                    row = []
+                    for c in range(K):
+                        byte = int(codes[r][c // 2])
+                        code = byte & 0xF if c % 2 == 0 else byte >> 4
+                        row.append(e2m1[code] * e4m3[int(scales[r][c // 16])] * float(tsc))
+                    out.append(row)
+                return out
+            dense_gu = [dq(gu[e][:f], gs[e][:f], ts[e][0], d) + dq(gu[e][f:], gs[e][f:], ts[e][1], d)
+                        for e in range(n)]
+            dense_dn = [dq(dn[e], ds[e], ts[e][2], f) for e in range(n)]
+            return ws, dense_gu, dense_dn
+        gu = rng.standard_normal((n, 2 * f, d)).astype(np.float32) / np.float32(math.sqrt(d))
+        dn = rng.standard_normal((n, d, f)).astype(np.float32) / np.float32(math.sqrt(f))
+        if wdtype == synth.BF16:
+            gu, dn = synth.bf16_bits(gu), synth.bf16_bits(dn)
+            conv = brute.bf16_to_float
+        else:
+            conv = brute.f32_to_float
+        dense_gu = [[[conv(v) for v in row] for row in gu[e]] for e in range(n)]
+        dense_dn = [[[conv(v) for v in row] for row in dn[e]] for e in range(n)]
+        return dict(gate_up=gu, down=dn), dense_gu, dense_dn
+
+    ex, egu, edn = mk(E)
+    sh, sgu, sdn = mk(1) if shared else (None, [None], [None])
+    xs = [[brute.bf16_to_float(v) for v in row] for row in x]
+    want = brute.layer(xs, [[float(v) for v in row] for row in router],
+                       None if b is None else [float(v) for v in b], egu, edn, sgu[0], sdn[0], k)
+    got = oracle.moe_forward(x, router, ex, sh, top_k=k, router_bias=b, wdtype=wdtype)
+    return got, want
+
+
+def test_dense_layer_matches_brute_force():
+    # (not parametrized: the planted-mistake test calls every pin without arguments)
+    for wdtype in (synth.F32, synth.BF16, synth.NVFP4):
+        for k, bias, shared in ((1, False, True), (2, True, True), (6, False, False), (6, True, True)):
+            got, (out, sel, w, logits) = _dense_case(wdtype, k, bias, shared, seed=17 + k)
+            assert np.array_equal(got["idx"], np.array(sel, np.int32))
+            assert np.allclose(got["logits"], np.array(logits), rtol=0, atol=1e-13)
+            assert np.allclose(got["w"], np.array(w), rtol=0, atol=1e-14)
+            out = np.array(out)
+            scale = np.abs(out).max()
+            assert scale > 0
+            err = np.abs(got["out"] - out).max()
+            assert err <= 1e-12 * scale, (wdtype, k, bias, shared, err / scale)
+
+
+def test_dense_brute_force_with_ties():
+    # duplicate router rows (equal logits): the brute force's stable sort and
+    # the oracle's selection keep the lower index
+    from oracle import brute
+    rng = np.random.default_rng(3)
+    d, E = 32, 8
+    router = (rng.standard_normal((E, d)) / math.sqrt(d)).astype(np.float32)
+    router[5] = router[2]
+    router[7] = router[2]
+    b = np.zeros(E, np.float32)
+    b[[2, 5, 7]] = 20.0  # the three equal rows lead every token
+    x = synth.bf16_bits(rng.standard_normal((4, d)).astype(np.float32))
+    got = oracle.route(x, router, top_k=2, router_bias=b)
+    for t in range(4):
+        xs = [brute.bf16_to_float(v) for v in x[t]]
+        _, chosen, w = brute.route(xs, [[float(v) for v in r] for r in router], [float(v) for v in b], 2)
+        assert chosen == [2, 5]
+        assert list(got["idx"][t]) == chosen
+        assert np.allclose(got["w"][t], w, rtol=0, atol=1e-15)
