@@ -98,8 +98,7 @@ def main():
     import torch
 
     import synth
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from gpu_helpers import dev_layer, make_layer_obj, x_device
+    from synth.device import dev_layer, make_layer_obj, x_device
     import sparse_moe_transformer_gemv_amd as fm
 
     torch.cuda.set_device(0)
@@ -263,7 +262,7 @@ def bench_dense(args, c, cfg_id, Ts, n_layers):
     import torch
 
     import synth
-    from gpu_helpers import dev_weights, x_device
+    from synth.device import dev_weights, x_device
     import sparse_moe_transformer_gemv_amd as fm
 
     d, F, wd = c["d"], DENSE_F, c["wdtype"]
@@ -358,8 +357,15 @@ def bench_stack(args, c, cfg_id, T, n_layers):
     import torch
 
     import synth
-    from gpu_helpers import dev_array, dev_layer, make_layer_obj, stack_gpu
+    from synth.device import dev_array, dev_layer, make_layer_obj
     import sparse_moe_transformer_gemv_amd as fm
+
+    xbuf = torch.empty((T, c["d"]), dtype=torch.bfloat16, device="cuda")
+
+    def stack_gpu(moe, h, layers):
+        for D in layers:
+            fm.flint_rmsnorm_forward(h, 1e-6, out=xbuf)
+            moe.forward(xbuf, D["router_w"], D["experts"], D["shared"], None, residual=h, out=h)
 
     t0 = time.time()
     layers, nd = [], []

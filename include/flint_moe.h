@@ -65,6 +65,12 @@ typedef enum {
 /* flags of flint_moe_config */
 #define FLINT_FORCE_DECODE_PATH  0x1u  /* always use the expert-GEMV path */
 #define FLINT_FORCE_PREFILL_PATH 0x2u  /* always use the grouped-MFMA path (bf16 only) */
+/* Debug: at create and before every forward, fill the floating-point part of
+ * the workspace (logits, weights, partial sums, h, y) with NaN bit patterns,
+ * so that a kernel reading a value that no kernel of the same forward wrote
+ * makes the output NaN.  The hand-off tickets and the integer routing tables
+ * keep their contents.  Adds one fill launch per forward; for tests only. */
+#define FLINT_DEBUG_POISON_WORKSPACE 0x4u
 
 typedef struct {
     uint32_t struct_size;   /* = sizeof(flint_moe_config) */
@@ -76,7 +82,7 @@ typedef struct {
     int32_t act_dtype;      /* flint_dtype of hidden/out: FLINT_F32 or FLINT_BF16 */
     int32_t weight_dtype;   /* flint_dtype of expert and shared weights */
     int32_t max_tokens;     /* largest T a forward may pass; sizes the workspace; 1..65536 */
-    uint32_t flags;         /* FLINT_FORCE_* */
+    uint32_t flags;         /* FLINT_FORCE_*, FLINT_DEBUG_POISON_WORKSPACE */
 } flint_moe_config;
 
 /*

@@ -16,7 +16,7 @@ namespace flint {
 
 struct CombineParams {
     int T, d, k;
-    const void* y;        // fp32 or bf16 rows, see y_bf16
+    const float* y;       // [(k+1)T][d] fp32 rows
     const int* pair_pos;  // [T][k]
     const float* residual;
     void* out;
@@ -24,18 +24,6 @@ struct CombineParams {
     int has_shared;  // 0: no shared expert (f_s = 0); its slots are never written
 };
 
-template <bool YBF16>
-__device__ __forceinline__ void load_y4(const void* y, size_t row, int d, int c, float v[4]) {
-    if constexpr (YBF16) {
-        uint2 a = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(y) + row * d + c);
-        v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x); v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
-    } else {
-        float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(y) + row * d + c);
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    }
-}
-
-template <bool YBF16>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     const int t = blockIdx.y;
     const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
@@ -45,18 +33,15 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
         float4 r = *reinterpret_cast<const float4*>(p.residual + (size_t)t * p.d + c);
         acc[0] = r.x; acc[1] = r.y; acc[2] = r.z; acc[3] = r.w;
     }
-    float v[4];
     const size_t kT = (size_t)p.k * p.T;
     if (p.has_shared) {
-        load_y4<YBF16>(p.y, kT + t, p.d, c, v);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += v[i];
+        const float4 v = *reinterpret_cast<const float4*>(p.y + (kT + t) * p.d + c);
+        acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
     }
     for (int j = 0; j < p.k; ++j) {
         const int slot = p.pair_pos[(size_t)t * p.k + j];
-        load_y4<YBF16>(p.y, (size_t)slot, p.d, c, v);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += v[i];
+        const float4 v = *reinterpret_cast<const float4*>(p.y + (size_t)slot * p.d + c);
+        acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
     }
     if (p.out_f32) {
         *reinterpret_cast<float4*>(static_cast<float*>(p.out) + (size_t)t * p.d + c) =
@@ -69,20 +54,19 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     }
 }
 
-hipError_t launch_combine(const LayerArgs& a, const Workspace& w, bool y_bf16, hipStream_t s) {
+hipError_t launch_combine(const LayerArgs& a, const Workspace& w, hipStream_t s) {
     CombineParams p;
     p.T = a.dm.T;
     p.d = a.dm.d;
     p.k = a.dm.k;
-    p.y = w.y;
+    p.y = static_cast<const float*>(w.y);
     p.pair_pos = w.pair_pos;
     p.residual = a.residual;
     p.out = a.out;
     p.out_f32 = (a.residual != nullptr || a.dm.act == DT_F32) ? 1 : 0;
     p.has_shared = a.dm.fs > 0 ? 1 : 0;
     dim3 grid((a.dm.d + 1023) / 1024, a.dm.T);
-    if (y_bf16) hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
@@ -119,6 +103,21 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(int d, const float* __rest
 hipError_t launch_rmsnorm(int T, int d, const float* in, float eps, void* out, hipStream_t s) {
     hipLaunchKernelGGL(rmsnorm_kernel, dim3(T), dim3(256), 0, s, d, in, eps,
                        static_cast<uint16_t*>(out));
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fill of n 32-bit words (workspace clearing and the debug poison).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p, size_t n, uint32_t v) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = v;
+}
+
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    const size_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s, p, n,
+                       v);
     return hipGetLastError();
 }
 

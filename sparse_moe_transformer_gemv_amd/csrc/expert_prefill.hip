@@ -12,7 +12,7 @@
 // design for CDNA4 matrix cores, not a port of those.
 //
 //   gate/up:  H[r][j] = SiLU(X_r . G_j) * (X_r . U_j)   (bf16 out, fp32 math)
-//   down:     Y[r][n] = w_r * (H_r . D_n)                (bf16 out, fp32 math)
+//   down:     Y[r][n] = w_r * (H_r . D_n)                (fp32 out, fp32 math)
 //
 // Tile 256 rows x 256 B rows, 8 waves as 2 (M) x 4 (N), each wave 128 x 64 =
 // 8 x 4 MFMA 16x16x32 tiles (128 fp32 accumulators per lane), two waves per
@@ -336,8 +336,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
             }
         }
     } else {
-        uint16_t* dst = static_cast<uint16_t*>(p.ws.y) + (size_t)(g.w + m0 + 128 * wm + row16) * d + nb0 +
-                        16 * NI * wn + 8 * q;
+        float* dst = static_cast<float*>(p.ws.y) + (size_t)(g.w + m0 + 128 * wm + row16) * d + nb0 +
+                     16 * NI * wn + 8 * q;
         // routing weights of the lane's 8 rows, loaded before any store (loads and
         // stores share one in-order counter, so a load after a store waits for it)
         // (unconditional buffer loads: a load behind a branch makes every later use
@@ -355,14 +355,13 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
         for (int mi = 0; mi < 8; ++mi) {
             if (16 * mi + row16 < wrows) {
                 const float ws = wv[mi];
-                uint16_t* o = dst + (size_t)16 * mi * d;
+                float* o = dst + (size_t)16 * mi * d;
 #pragma unroll
                 for (int t = 0; t < NI / 2; ++t) {
                     const floatx4_t& a0 = acc[mi][2 * t];
                     const floatx4_t& a1 = acc[mi][2 * t + 1];
-                    *reinterpret_cast<uint4*>(o + 32 * t) =
-                        make_uint4(pack_bf16x2_hw(ws * a0[0], ws * a0[1]), pack_bf16x2_hw(ws * a0[2], ws * a0[3]),
-                                   pack_bf16x2_hw(ws * a1[0], ws * a1[1]), pack_bf16x2_hw(ws * a1[2], ws * a1[3]));
+                    *reinterpret_cast<float4*>(o + 32 * t) = make_float4(ws * a0[0], ws * a0[1], ws * a0[2], ws * a0[3]);
+                    *reinterpret_cast<float4*>(o + 32 * t + 4) = make_float4(ws * a1[0], ws * a1[1], ws * a1[2], ws * a1[3]);
                 }
             }
         }

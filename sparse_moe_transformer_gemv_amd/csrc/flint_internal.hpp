@@ -40,8 +40,10 @@ struct Workspace {
     int* kcount;         // [(E+1) ceil(d/16)] split-K tickets, zero between launches
     void* h;             // [(k+1)*Tm][fmax] x 8 B: fp32 (decode VALU), three exact bf16 planes (decode
                          // MFMA), two f16 planes (NVFP4), or bf16 (prefill)
-    void* y;             // [(k+1)*Tm][d]:    fp32 (decode) or bf16 (prefill)
+    void* y;             // [(k+1)*Tm][d] fp32 rows (weighted expert outputs; split-K sums)
     int max_tiles;
+    size_t ticket_bytes;  // the tickets occupy [0, ticket_bytes) of the allocation
+    size_t float_off;     // floating-point data from here to the end
 };
 
 // The matrix-core decode down kernel holds at most 1024 of K in registers;
@@ -92,8 +94,10 @@ bool down_decode_combines(const Dims& dm);
 bool decode_fp4_ok(const Dims& dm);
 hipError_t launch_gateup_prefill(const LayerArgs& a, const Workspace& w, int n_cu, hipStream_t s);
 hipError_t launch_down_prefill(const LayerArgs& a, const Workspace& w, int n_cu, hipStream_t s);
-hipError_t launch_combine(const LayerArgs& a, const Workspace& w, bool y_bf16, hipStream_t s);
+hipError_t launch_combine(const LayerArgs& a, const Workspace& w, hipStream_t s);
 hipError_t launch_rmsnorm(int T, int d, const float* in, float eps, void* out, hipStream_t s);
+// p[0 .. n) = v (a plain kernel, no memset node, so it is safe under graph capture)
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 
 // Prefill tile height (rows of A per MFMA tile); the sort builds its tile list with it.
 constexpr int kPrefillBM = 256;

@@ -86,7 +86,7 @@ flint_status check_config(const flint_moe_config* c) {
         return fail(FLINT_ERR_INVALID_ARG, "weight_dtype %d unknown", c->weight_dtype);
     if (c->max_tokens < 1 || c->max_tokens > 65536)
         return fail(FLINT_ERR_INVALID_ARG, "max_tokens %d: need 1..65536", c->max_tokens);
-    if (c->flags & ~(FLINT_FORCE_DECODE_PATH | FLINT_FORCE_PREFILL_PATH))
+    if (c->flags & ~(FLINT_FORCE_DECODE_PATH | FLINT_FORCE_PREFILL_PATH | FLINT_DEBUG_POISON_WORKSPACE))
         return fail(FLINT_ERR_INVALID_ARG, "unknown flags 0x%x", c->flags);
     if ((c->flags & FLINT_FORCE_DECODE_PATH) && (c->flags & FLINT_FORCE_PREFILL_PATH))
         return fail(FLINT_ERR_INVALID_ARG, "both path-forcing flags set");
@@ -118,7 +118,10 @@ flint_status check_device(int* dev_out, int* n_cu) {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Lay the workspace out in `base` (nullptr: just measure).
+// Lay the workspace out in `base` (nullptr: just measure).  Three regions, in
+// this order: the hand-off tickets (zero between launches), the integer
+// routing tables, and the floating-point data (w->float_off onwards: the only
+// region the debug poison fills).
 size_t carve(const flint_moe_config& c, char* base, Workspace* w) {
     const size_t Tm = (size_t)c.max_tokens, E = (size_t)c.n_experts, k = (size_t)c.top_k;
     const size_t fmax = (size_t)(c.d_ff > c.d_ff_shared ? c.d_ff : c.d_ff_shared);
@@ -130,27 +133,32 @@ size_t carve(const flint_moe_config& c, char* base, Workspace* w) {
         off = align_up(off + bytes, 256);
         return base ? static_cast<void*>(base + o) : nullptr;
     };
-    w->logits = static_cast<float*>(take(Tm * E * 4));
+    // tickets
+    w->rcount = static_cast<int*>(take((4 * ((E + 15) / 16) + 8) * 4));
+    w->counter = static_cast<int*>(take((1 + (Tm + 15) / 16) * 4));
+    w->dcount = static_cast<int*>(take((size_t)((c.d_model + 15) / 16) * 4));
+    w->kcount = static_cast<int*>(take((E + 1) * (size_t)((c.d_model + 15) / 16) * 4));
+    w->ticket_bytes = off;
+    // integer routing tables
     w->sel = static_cast<int*>(take(Tm * k * 4));
-    w->wts = static_cast<float*>(take(Tm * k * 4));
     w->counts = static_cast<int*>(take(E * 4));
     w->offsets = static_cast<int*>(take((E + 1) * 4));
     w->sorted_pair = static_cast<int*>(take(Tm * k * 4));
     w->pair_pos = static_cast<int*>(take(Tm * k * 4));
-    w->sorted_wt = static_cast<float*>(take(Tm * k * 4));
-    w->rpart = static_cast<float*>(take((size_t)(c.d_model / 256 > 0 ? c.d_model / 256 : 1) * 64 * E * 4));
-    w->rcount = static_cast<int*>(take((4 * ((E + 15) / 16) + 8) * 4));
-    w->w3 = static_cast<uint16_t*>(take(3 * E * (size_t)c.d_model * 2));
     w->groups = static_cast<int4*>(take((E + 1) * 16));
     w->n_groups = static_cast<int*>(take(4));
     w->tiles = static_cast<int2*>(take(max_tiles * 8));
     w->n_tiles = static_cast<int*>(take(4));
-    w->counter = static_cast<int*>(take((1 + (Tm + 15) / 16) * 4));
-    w->dcount = static_cast<int*>(take((size_t)((c.d_model + 15) / 16) * 4));
+    w->float_off = off;
+    // floating-point data
+    w->logits = static_cast<float*>(take(Tm * E * 4));
+    w->wts = static_cast<float*>(take(Tm * k * 4));
+    w->sorted_wt = static_cast<float*>(take(Tm * k * 4));
+    w->rpart = static_cast<float*>(take((size_t)(c.d_model / 256 > 0 ? c.d_model / 256 : 1) * 64 * E * 4));
+    w->w3 = static_cast<uint16_t*>(take(3 * E * (size_t)c.d_model * 2));
     const size_t kchunks = fmax > (size_t)kDownKChunk ? (fmax + kDownKChunk - 1) / kDownKChunk : 0;
     // the down kernel strides its chunks by kSplitRowsMax rows
     w->part = static_cast<float*>(take(kchunks * (size_t)kSplitRowsMax * c.d_model * 4));
-    w->kcount = static_cast<int*>(take((E + 1) * (size_t)((c.d_model + 15) / 16) * 4));
     w->h = take(slots * fmax * 8);
     w->y = take(slots * (size_t)c.d_model * 4);
     w->max_tiles = (int)max_tiles;
@@ -179,6 +187,17 @@ flint_status check_weights(const flint_moe_config& c, const flint_expert_weights
     return FLINT_OK;
 }
 
+// Debug mode: fill the floating-point region of the workspace with all-ones
+// words (NaN as fp32, and as each bf16 / f16 half), so a kernel that reads a
+// value no kernel of the same forward wrote makes the output NaN.  The
+// tickets and the integer tables keep their contents: a stale index read as
+// -1 could address memory outside every buffer.
+hipError_t poison(const flint_moe* h, hipStream_t s) {
+    const size_t off = h->ws.float_off;
+    return launch_fill_u32(reinterpret_cast<uint32_t*>(static_cast<char*>(h->mem) + off),
+                           (h->mem_bytes - off) / 4, 0xFFFFFFFFu, s);
+}
+
 struct Timer {
     flint_moe* h;
     int id;
@@ -203,7 +222,11 @@ struct Timer {
 extern "C" {
 
 const char* flint_status_string(flint_status s) {
-    switch (s) {
+    // A C caller may pass any int; reading it through the C++ enum type would
+    // be undefined for values outside the enumerators' range, so take the bits.
+    int v;
+    std::memcpy(&v, &s, sizeof v);
+    switch (v) {
     case FLINT_OK: return "FLINT_OK";
     case FLINT_ERR_INVALID_ARG: return "FLINT_ERR_INVALID_ARG";
     case FLINT_ERR_UNSUPPORTED: return "FLINT_ERR_UNSUPPORTED";
@@ -246,8 +269,9 @@ flint_status flint_moe_create(const flint_moe_config* cfg, flint_moe_t* out) {
                     hipGetErrorString(e));
     }
     carve(*cfg, static_cast<char*>(h->mem), &h->ws);
-    // zero everything once: the last-block ticket must start at 0
+    // zero everything once: the last-block tickets must start at 0
     e = hipMemset(h->mem, 0, h->mem_bytes);
+    if (e == hipSuccess && (cfg->flags & FLINT_DEBUG_POISON_WORKSPACE)) e = poison(h, nullptr);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         (void)hipFree(h->mem);
@@ -329,6 +353,10 @@ flint_status flint_moe_forward(flint_moe_t h, int32_t T, const void* hidden, con
     }
 
     hipError_t e;
+    if (c.flags & FLINT_DEBUG_POISON_WORKSPACE) {
+        e = poison(h, stream);
+        if (e != hipSuccess) return hip_fail(e, "workspace poison");
+    }
     if (prefill) {
         {
             Timer tm(h, FLINT_KERNEL_ROUTE, stream);
@@ -357,7 +385,7 @@ flint_status flint_moe_forward(flint_moe_t h, int32_t T, const void* hidden, con
         if (e != hipSuccess) return hip_fail(e, "down kernel");
         {
             Timer tm(h, FLINT_KERNEL_COMBINE, stream);
-            e = launch_combine(a, h->ws, true, stream);
+            e = launch_combine(a, h->ws, stream);
         }
         if (e != hipSuccess) return hip_fail(e, "combine kernel");
         h->last_T = T;
@@ -383,7 +411,7 @@ flint_status flint_moe_forward(flint_moe_t h, int32_t T, const void* hidden, con
     if (e != hipSuccess) return hip_fail(e, "down kernel");
     if (!down_decode_combines(a.dm)) {
         Timer tm(h, FLINT_KERNEL_COMBINE, stream);
-        e = launch_combine(a, h->ws, false, stream);
+        e = launch_combine(a, h->ws, stream);
     }
     if (e != hipSuccess) return hip_fail(e, "combine kernel");
     h->last_T = T;

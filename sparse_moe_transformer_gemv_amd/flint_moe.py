@@ -26,6 +26,7 @@ FLINT_OK, FLINT_ERR_INVALID_ARG, FLINT_ERR_UNSUPPORTED = 0, 1, 2
 FLINT_ERR_OUT_OF_MEMORY, FLINT_ERR_NO_DEVICE, FLINT_ERR_HIP = 3, 4, 5
 FLINT_F32, FLINT_BF16, FLINT_NVFP4 = 0, 1, 2
 FLINT_FORCE_DECODE_PATH, FLINT_FORCE_PREFILL_PATH = 0x1, 0x2
+FLINT_DEBUG_POISON_WORKSPACE = 0x4
 KERNEL_ROUTE, KERNEL_SORT, KERNEL_EXPERT_UP, KERNEL_EXPERT_DOWN, KERNEL_COMBINE = range(5)
 
 EXPORTED = [
@@ -124,6 +125,78 @@ _TORCH_ACT = {FLINT_F32: torch.float32, FLINT_BF16: torch.bfloat16}
 _TORCH_W = {FLINT_F32: torch.float32, FLINT_BF16: torch.bfloat16, FLINT_NVFP4: torch.uint8}
 
 
+def _expect(t, name, numel, dtype, device):
+    """t must be a contiguous tensor of `numel` elements of `dtype` on `device`."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.device != device:
+        raise ValueError("%s is on %s, the layer runs on %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.numel() != numel:
+        raise ValueError("%s holds %d elements, the configuration needs %d" % (name, t.numel(), numel))
+
+
+def check_expert_weights(w, cfg, n: int, f: int, device, name: str) -> None:
+    """Sizes, dtypes and device of one expert set of n experts of width f
+    (layouts of include/flint_moe.h)."""
+    d, wd = cfg.d_model, cfg.weight_dtype
+    if not isinstance(w, ExpertWeights):
+        raise TypeError("%s must be ExpertWeights" % name)
+    if wd == FLINT_NVFP4:
+        _expect(w.gate_up, name + ".gate_up", n * 2 * f * d // 2, torch.uint8, device)
+        _expect(w.down, name + ".down", n * d * f // 2, torch.uint8, device)
+        _expect(w.gate_up_scales, name + ".gate_up_scales", n * 2 * f * d // 16, torch.uint8, device)
+        _expect(w.down_scales, name + ".down_scales", n * d * f // 16, torch.uint8, device)
+        _expect(w.tensor_scales, name + ".tensor_scales", n * 3, torch.float32, device)
+    else:
+        _expect(w.gate_up, name + ".gate_up", n * 2 * f * d, _TORCH_W[wd], device)
+        _expect(w.down, name + ".down", n * d * f, _TORCH_W[wd], device)
+        for s in ("gate_up_scales", "down_scales", "tensor_scales"):
+            if getattr(w, s) is not None:
+                raise ValueError("%s.%s must be None unless the weights are NVFP4" % (name, s))
+
+
+def check_forward_args(cfg, device, x, router_w, experts, shared, router_bias=None,
+                       residual=None, out=None) -> None:
+    """Every tensor of a forward against the layer configuration, before any
+    pointer reaches the library: the C ABI sees raw device pointers and cannot
+    tell an undersized or misplaced tensor from a good one.
+
+    x [T, d] act dtype; router_w [E, d] fp32; router_bias None or [E] fp32;
+    experts / shared: ExpertWeights of E experts of width f / one of width f_s
+    (shared None exactly when f_s == 0); residual None or [T, d] fp32; out
+    None or [T, d], fp32 when a residual is given, else the act dtype.  All on
+    `device`."""
+    d, E = cfg.d_model, cfg.n_experts
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.shape[1] != d:
+        raise ValueError("x must be [T, %d]" % d)
+    T = x.shape[0]
+    _expect(x, "x", T * d, _TORCH_ACT[cfg.act_dtype], device)
+    _expect(router_w, "router_w", E * d, torch.float32, device)
+    if router_bias is not None:
+        _expect(router_bias, "router_bias", E, torch.float32, device)
+    check_expert_weights(experts, cfg, E, cfg.d_ff, device, "experts")
+    if cfg.d_ff_shared > 0:
+        if shared is None:
+            raise ValueError("the layer has a shared expert (d_ff_shared = %d): pass its weights"
+                             % cfg.d_ff_shared)
+        check_expert_weights(shared, cfg, 1, cfg.d_ff_shared, device, "shared")
+    elif shared is not None:
+        raise ValueError("shared weights given but d_ff_shared == 0")
+    if residual is not None:
+        _expect(residual, "residual", T * d, torch.float32, device)
+        if residual.shape != (T, d):
+            raise ValueError("residual must be [T, d] = [%d, %d]" % (T, d))
+    if out is not None:
+        odt = torch.float32 if residual is not None else _TORCH_ACT[cfg.act_dtype]
+        _expect(out, "out", T * d, odt, device)
+        if out.shape != (T, d):
+            raise ValueError("out must be [T, d] = [%d, %d]" % (T, d))
+
+
 @dataclass
 class ExpertWeights:
     """Device tensors of one expert set (layouts as in include/flint_moe.h)."""
@@ -174,6 +247,7 @@ class MoELayer:
         load_library()
         self.cfg = flint_moe_config(ctypes.sizeof(flint_moe_config), d_model, n_experts, top_k,
                                     d_ff, d_ff_shared, act_dtype, weight_dtype, max_tokens, flags)
+        self.device = torch.device("cuda", torch.cuda.current_device())
         self.handle = flint_moe_create(self.cfg)
 
     def close(self):
@@ -192,8 +266,8 @@ class MoELayer:
                 residual: Optional[torch.Tensor] = None,
                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
         c = self.cfg
-        if x.dim() != 2 or x.shape[1] != c.d_model:
-            raise ValueError("x must be [T, %d]" % c.d_model)
+        check_forward_args(c, self.device, x, router_w, experts, shared, router_bias, residual,
+                           out)
         T = x.shape[0]
         if out is None:
             odt = torch.float32 if residual is not None else _TORCH_ACT[c.act_dtype]

@@ -107,3 +107,98 @@ def test_status_strings():
     for s in range(6):
         assert L.flint_status_string(s).startswith(b"FLINT_")
     assert L.flint_status_string(42) == b"FLINT_ERR_UNKNOWN"
+
+
+# ------------------------------------------------ binding checks of forward tensors
+
+def _tensors(wd=1, T=3, d=128, E=8, f=32, fs=32, residual=False, out=True):
+    import torch
+    act = torch.bfloat16
+    wt = {0: torch.float32, 1: torch.bfloat16, 2: torch.uint8}[wd]
+
+    def ws(n, F):
+        if wd == 2:
+            return fm.ExpertWeights(torch.zeros(n, 2 * F, d // 2, dtype=torch.uint8),
+                                    torch.zeros(n, d, F // 2, dtype=torch.uint8),
+                                    torch.zeros(n, 2 * F, d // 16, dtype=torch.uint8),
+                                    torch.zeros(n, d, F // 16, dtype=torch.uint8),
+                                    torch.ones(n, 3, dtype=torch.float32))
+        return fm.ExpertWeights(torch.zeros(n, 2 * F, d, dtype=wt), torch.zeros(n, d, F, dtype=wt))
+
+    a = dict(x=torch.zeros(T, d, dtype=act), router_w=torch.zeros(E, d), experts=ws(E, f),
+             shared=ws(1, fs) if fs else None, router_bias=None,
+             residual=torch.zeros(T, d) if residual else None)
+    a["out"] = (torch.zeros(T, d) if residual else torch.zeros(T, d, dtype=act)) if out else None
+    return a
+
+
+def _check(a, wd=1, fs=32):
+    import torch
+    cfg = _cfg(d_model=128, n_experts=8, d_ff=32, d_ff_shared=fs, weight_dtype=wd)
+    b.check_forward_args(cfg, torch.device("cpu"), a["x"], a["router_w"], a["experts"],
+                         a["shared"], a["router_bias"], a["residual"], a["out"])
+
+
+@pytest.mark.parametrize("wd", [0, 1, 2])
+@pytest.mark.parametrize("residual", [False, True])
+def test_binding_accepts_matching_tensors(wd, residual):
+    _check(_tensors(wd, residual=residual), wd)
+    _check(_tensors(wd, fs=0), wd, fs=0)
+
+
+def _bad_cases():
+    import torch
+    cases = []
+
+    def mk(label, fn, wd=1, fs=32, exc=(ValueError, TypeError)):
+        cases.append(pytest.param(fn, wd, fs, exc, id=label))
+
+    mk("bf16 out with fp32 residual",
+       lambda a: a.update(residual=torch.zeros(3, 128), out=torch.zeros(3, 128, dtype=torch.bfloat16)))
+    mk("out too short", lambda a: a.update(out=torch.zeros(2, 128, dtype=torch.bfloat16)))
+    mk("out fp32 without residual", lambda a: a.update(out=torch.zeros(3, 128)))
+    mk("residual wrong shape", lambda a: a.update(residual=torch.zeros(3, 64), out=torch.zeros(3, 128)))
+    mk("x wrong width", lambda a: a.update(x=torch.zeros(3, 64, dtype=torch.bfloat16)))
+    mk("x fp32 for a bf16 layer", lambda a: a.update(x=torch.zeros(3, 128)))
+    mk("router rows short", lambda a: a.update(router_w=torch.zeros(7, 128)))
+    mk("router bf16", lambda a: a.update(router_w=torch.zeros(8, 128, dtype=torch.bfloat16)))
+    mk("bias length", lambda a: a.update(router_bias=torch.zeros(7)))
+    mk("gate_up short",
+       lambda a: a.update(experts=fm.ExpertWeights(torch.zeros(7, 64, 128, dtype=torch.bfloat16),
+                                                   a["experts"].down)))
+    mk("down short",
+       lambda a: a.update(experts=fm.ExpertWeights(a["experts"].gate_up,
+                                                   torch.zeros(8, 128, 16, dtype=torch.bfloat16))))
+    mk("shared missing", lambda a: a.update(shared=None))
+    mk("shared given without width", lambda a: None, fs=0)
+    mk("scales on bf16 weights",
+       lambda a: a.update(experts=fm.ExpertWeights(a["experts"].gate_up, a["experts"].down,
+                                                   torch.zeros(8, 64, 8, dtype=torch.uint8))))
+    mk("non-contiguous x", lambda a: a.update(x=torch.zeros(128, 3, dtype=torch.bfloat16).t()))
+    mk("nvfp4 scales short",
+       lambda a: a.update(experts=fm.ExpertWeights(a["experts"].gate_up, a["experts"].down,
+                                                   a["experts"].gate_up_scales[:7],
+                                                   a["experts"].down_scales,
+                                                   a["experts"].tensor_scales)), wd=2)
+    mk("nvfp4 tensor scales missing",
+       lambda a: a.update(shared=fm.ExpertWeights(a["shared"].gate_up, a["shared"].down,
+                                                  a["shared"].gate_up_scales,
+                                                  a["shared"].down_scales, None)), wd=2)
+    return cases
+
+
+@pytest.mark.parametrize("mutate,wd,fs,exc", _bad_cases())
+def test_binding_rejects_mismatched_tensors(mutate, wd, fs, exc):
+    a = _tensors(wd)
+    mutate(a)
+    with pytest.raises(exc):
+        _check(a, wd, fs=fs)
+
+
+def test_binding_rejects_tensor_on_another_device():
+    import torch
+    a = _tensors(1)
+    cfg = _cfg(d_model=128, n_experts=8, d_ff=32, d_ff_shared=32)
+    with pytest.raises(ValueError, match="is on"):
+        b.check_forward_args(cfg, torch.device("meta"), a["x"], a["router_w"], a["experts"],
+                             a["shared"], None, None, a["out"])
