@@ -136,6 +136,32 @@ flint_status flint_moe_forward(flint_moe_t h, int32_t T, const void* hidden,
                                void* out, hipStream_t stream);
 
 /*
+ * The same forward without a handle and without allocating, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Arguments as flint_moe_forward,
+ * with the configuration passed directly (cfg->max_tokens is ignored; the
+ * layout is sized for exactly T tokens).
+ *   Scratch: the workspace lives in one static 16 MiB device array per GPU
+ *   (loaded with the library, held until the process ends); a call whose
+ *   workspace for T tokens would be larger returns FLINT_ERR_INVALID_ARG
+ *   (at d = 2048, E = 256, k = 6, f = 512 every T up to 128 fits).
+ *   No hipMalloc, hipFree or other allocation; the first call on a device
+ *   looks up the array's device address (hipGetSymbolAddress) and checks the
+ *   device once.  Each call first clears its hand-off tickets with a small
+ *   fill kernel (one extra launch), since the array keeps whatever the
+ *   previous call left.
+ *   Every call on a GPU shares that GPU's array: calls that overlap on one
+ *   GPU (two streams, two threads) race and must be serialised by the caller.
+ * Errors as flint_moe_forward, plus FLINT_ERR_NO_DEVICE on a non-gfx950
+ * device.  FLINT_FORCE_* and FLINT_DEBUG_POISON_WORKSPACE flags apply.
+ */
+flint_status flint_moe_forward_noalloc(const flint_moe_config* cfg, int32_t T, const void* hidden,
+                                       const float* router_w, const float* router_bias,
+                                       const flint_expert_weights* experts,
+                                       const flint_expert_weights* shared, const float* residual,
+                                       void* out, hipStream_t stream);
+
+/*
  * Device-to-device copies of the routing of the handle's last forward
  * (enqueued on `stream`, after that forward).  Any output may be NULL.
  *   idx         [T][k] int32  chosen experts, slot order = descending logit

@@ -8,5 +8,5 @@ from .flint_moe import (  # noqa: F401
     FLINT_FORCE_PREFILL_PATH, check_forward_args,
     FLINT_NVFP4, KERNEL_COMBINE, KERNEL_EXPERT_DOWN, KERNEL_EXPERT_UP, KERNEL_ROUTE, KERNEL_SORT,
     DenseFFN, ExpertWeights, FlintError, MoELayer, flint_expert_weights, flint_moe_config,
-    flint_moe_create, flint_moe_destroy, flint_rmsnorm_forward, load_library,
+    flint_moe_create, flint_moe_destroy, flint_moe_forward_noalloc, flint_rmsnorm_forward, load_library,
 )

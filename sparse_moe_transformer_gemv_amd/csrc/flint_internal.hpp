@@ -99,6 +99,11 @@ hipError_t launch_rmsnorm(int T, int d, const float* in, float eps, void* out, h
 // p[0 .. n) = v (a plain kernel, no memset node, so it is safe under graph capture)
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 
+// Size of the static device scratch of the allocation-free forward, and its
+// device address on the current device (set up on first use per device).
+constexpr size_t kScratchBytes = 16u << 20;
+hipError_t scratch_for_current_device(void** ptr);
+
 // Prefill tile height (rows of A per MFMA tile); the sort builds its tile list with it.
 constexpr int kPrefillBM = 256;
 

@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -116,6 +117,32 @@ flint_status check_device(int* dev_out, int* n_cu) {
     return FLINT_OK;
 }
 
+// Per-device result of check_device for the allocation-free entry point, so
+// that its calls after the first make no property query.
+std::mutex g_dev_mu;
+int g_dev_ncu[64];  // 0: not checked yet
+
+flint_status cached_device(int* dev_out, int* n_cu) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return fail(FLINT_ERR_NO_DEVICE, "no usable current HIP device");
+    std::lock_guard<std::mutex> lock(g_dev_mu);
+    if (!g_dev_ncu[dev]) {
+        int d2 = 0, n = 0;
+        flint_status st = check_device(&d2, &n);
+        if (st != FLINT_OK) return st;
+        g_dev_ncu[dev] = n > 0 ? n : 1;
+    }
+    *dev_out = dev;
+    *n_cu = g_dev_ncu[dev];
+    return FLINT_OK;
+}
+
+int decode_max_t_default() {
+    if (const char* s = std::getenv("FLINT_MOE_DECODE_MAX_T")) return std::atoi(s);
+    return 64;
+}
+
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Lay the workspace out in `base` (nullptr: just measure).  Three regions, in
@@ -217,86 +244,12 @@ struct Timer {
     }
 };
 
-}  // namespace
-
-extern "C" {
-
-const char* flint_status_string(flint_status s) {
-    // A C caller may pass any int; reading it through the C++ enum type would
-    // be undefined for values outside the enumerators' range, so take the bits.
-    int v;
-    std::memcpy(&v, &s, sizeof v);
-    switch (v) {
-    case FLINT_OK: return "FLINT_OK";
-    case FLINT_ERR_INVALID_ARG: return "FLINT_ERR_INVALID_ARG";
-    case FLINT_ERR_UNSUPPORTED: return "FLINT_ERR_UNSUPPORTED";
-    case FLINT_ERR_OUT_OF_MEMORY: return "FLINT_ERR_OUT_OF_MEMORY";
-    case FLINT_ERR_NO_DEVICE: return "FLINT_ERR_NO_DEVICE";
-    case FLINT_ERR_HIP: return "FLINT_ERR_HIP";
-    }
-    return "FLINT_ERR_UNKNOWN";
-}
-
-const char* flint_last_error(void) { return g_err; }
-
-flint_status flint_moe_create(const flint_moe_config* cfg, flint_moe_t* out) {
-    if (!out) return fail(FLINT_ERR_INVALID_ARG, "out handle pointer is NULL");
-    *out = nullptr;
-    flint_status st = check_config(cfg);
-    if (st != FLINT_OK) return st;
-    int dev = 0, n_cu = 0;
-    st = check_device(&dev, &n_cu);
-    if (st != FLINT_OK) return st;
-    flint_moe* h = new (std::nothrow) flint_moe();
-    if (!h) return fail(FLINT_ERR_OUT_OF_MEMORY, "host allocation failed");
-    h->cfg = *cfg;
-    h->device = dev;
-    h->n_cu = n_cu;
-    h->last_T = 0;
-    h->prof_kernel = -1;
-    h->prof_cap = 0;
-    h->prof_n = 0;
-    h->decode_max_t = 64;
-    if (const char* s = std::getenv("FLINT_MOE_DECODE_MAX_T")) h->decode_max_t = std::atoi(s);
-    Workspace dummy{};
-    h->mem_bytes = carve(*cfg, nullptr, &dummy);
-    const size_t bytes = h->mem_bytes;
-    hipError_t e = hipMalloc(&h->mem, bytes);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        delete h;
-        return fail(FLINT_ERR_OUT_OF_MEMORY, "workspace of %zu bytes: %s", bytes,
-                    hipGetErrorString(e));
-    }
-    carve(*cfg, static_cast<char*>(h->mem), &h->ws);
-    // zero everything once: the last-block tickets must start at 0
-    e = hipMemset(h->mem, 0, h->mem_bytes);
-    if (e == hipSuccess && (cfg->flags & FLINT_DEBUG_POISON_WORKSPACE)) e = poison(h, nullptr);
-    if (e == hipSuccess) e = hipDeviceSynchronize();
-    if (e != hipSuccess) {
-        (void)hipFree(h->mem);
-        delete h;
-        return hip_fail(e, "workspace init");
-    }
-    *out = h;
-    return ok();
-}
-
-flint_status flint_moe_destroy(flint_moe_t h) {
-    if (!h) return fail(FLINT_ERR_INVALID_ARG, "handle is NULL");
-    (void)hipDeviceSynchronize();
-    for (hipEvent_t ev : h->prof_ev) (void)hipEventDestroy(ev);
-    hipError_t e = hipFree(h->mem);
-    delete h;
-    if (e != hipSuccess) return hip_fail(e, "hipFree");
-    return ok();
-}
-
-flint_status flint_moe_forward(flint_moe_t h, int32_t T, const void* hidden, const float* router_w,
-                               const float* router_bias, const flint_expert_weights* experts,
-                               const flint_expert_weights* shared, const float* residual,
-                               void* out, hipStream_t stream) {
-    if (!h) return fail(FLINT_ERR_INVALID_ARG, "handle is NULL");
+// The forward on handle state h (a created handle, or the stack-built state of
+// flint_moe_forward_noalloc over the static scratch).
+flint_status forward_impl(flint_moe* h, int32_t T, const void* hidden, const float* router_w,
+                          const float* router_bias, const flint_expert_weights* experts,
+                          const flint_expert_weights* shared, const float* residual, void* out,
+                          hipStream_t stream) {
     const flint_moe_config& c = h->cfg;
     if (T < 0 || T > c.max_tokens)
         return fail(FLINT_ERR_INVALID_ARG, "T=%d outside 0..max_tokens=%d", T, c.max_tokens);
@@ -416,6 +369,130 @@ flint_status flint_moe_forward(flint_moe_t h, int32_t T, const void* hidden, con
     if (e != hipSuccess) return hip_fail(e, "combine kernel");
     h->last_T = T;
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* flint_status_string(flint_status s) {
+    // A C caller may pass any int; reading it through the C++ enum type would
+    // be undefined for values outside the enumerators' range, so take the bits.
+    int v;
+    std::memcpy(&v, &s, sizeof v);
+    switch (v) {
+    case FLINT_OK: return "FLINT_OK";
+    case FLINT_ERR_INVALID_ARG: return "FLINT_ERR_INVALID_ARG";
+    case FLINT_ERR_UNSUPPORTED: return "FLINT_ERR_UNSUPPORTED";
+    case FLINT_ERR_OUT_OF_MEMORY: return "FLINT_ERR_OUT_OF_MEMORY";
+    case FLINT_ERR_NO_DEVICE: return "FLINT_ERR_NO_DEVICE";
+    case FLINT_ERR_HIP: return "FLINT_ERR_HIP";
+    }
+    return "FLINT_ERR_UNKNOWN";
+}
+
+const char* flint_last_error(void) { return g_err; }
+
+flint_status flint_moe_create(const flint_moe_config* cfg, flint_moe_t* out) {
+    if (!out) return fail(FLINT_ERR_INVALID_ARG, "out handle pointer is NULL");
+    *out = nullptr;
+    flint_status st = check_config(cfg);
+    if (st != FLINT_OK) return st;
+    int dev = 0, n_cu = 0;
+    st = check_device(&dev, &n_cu);
+    if (st != FLINT_OK) return st;
+    flint_moe* h = new (std::nothrow) flint_moe();
+    if (!h) return fail(FLINT_ERR_OUT_OF_MEMORY, "host allocation failed");
+    h->cfg = *cfg;
+    h->device = dev;
+    h->n_cu = n_cu;
+    h->last_T = 0;
+    h->prof_kernel = -1;
+    h->prof_cap = 0;
+    h->prof_n = 0;
+    h->decode_max_t = decode_max_t_default();
+    Workspace dummy{};
+    h->mem_bytes = carve(*cfg, nullptr, &dummy);
+    const size_t bytes = h->mem_bytes;
+    hipError_t e = hipMalloc(&h->mem, bytes);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        delete h;
+        return fail(FLINT_ERR_OUT_OF_MEMORY, "workspace of %zu bytes: %s", bytes,
+                    hipGetErrorString(e));
+    }
+    carve(*cfg, static_cast<char*>(h->mem), &h->ws);
+    // zero everything once: the last-block tickets must start at 0
+    e = hipMemset(h->mem, 0, h->mem_bytes);
+    if (e == hipSuccess && (cfg->flags & FLINT_DEBUG_POISON_WORKSPACE)) e = poison(h, nullptr);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        (void)hipFree(h->mem);
+        delete h;
+        return hip_fail(e, "workspace init");
+    }
+    *out = h;
+    return ok();
+}
+
+flint_status flint_moe_destroy(flint_moe_t h) {
+    if (!h) return fail(FLINT_ERR_INVALID_ARG, "handle is NULL");
+    (void)hipDeviceSynchronize();
+    for (hipEvent_t ev : h->prof_ev) (void)hipEventDestroy(ev);
+    hipError_t e = hipFree(h->mem);
+    delete h;
+    if (e != hipSuccess) return hip_fail(e, "hipFree");
+    return ok();
+}
+
+flint_status flint_moe_forward(flint_moe_t h, int32_t T, const void* hidden, const float* router_w,
+                               const float* router_bias, const flint_expert_weights* experts,
+                               const flint_expert_weights* shared, const float* residual,
+                               void* out, hipStream_t stream) {
+    if (!h) return fail(FLINT_ERR_INVALID_ARG, "handle is NULL");
+    return forward_impl(h, T, hidden, router_w, router_bias, experts, shared, residual, out, stream);
+}
+
+flint_status flint_moe_forward_noalloc(const flint_moe_config* cfg, int32_t T, const void* hidden,
+                                       const float* router_w, const float* router_bias,
+                                       const flint_expert_weights* experts,
+                                       const flint_expert_weights* shared, const float* residual,
+                                       void* out, hipStream_t stream) {
+    flint_status st = check_config(cfg);
+    if (st != FLINT_OK) return st;
+    if (T < 0 || T > 65536) return fail(FLINT_ERR_INVALID_ARG, "T=%d outside 0..65536", T);
+    if (T == 0) return ok();
+    // the state of a handle sized for exactly T tokens, on the stack
+    flint_moe hs;
+    hs.cfg = *cfg;
+    hs.cfg.max_tokens = T;
+    Workspace need{};
+    const size_t bytes = carve(hs.cfg, nullptr, &need);
+    if (bytes > (size_t)kScratchBytes)
+        return fail(FLINT_ERR_INVALID_ARG,
+                    "T=%d needs a workspace of %zu bytes, above the %zu-byte static scratch", T, bytes,
+                    (size_t)kScratchBytes);
+    int dev = 0, n_cu = 0;
+    st = cached_device(&dev, &n_cu);
+    if (st != FLINT_OK) return st;
+    void* base = nullptr;
+    hipError_t e = scratch_for_current_device(&base);
+    if (e != hipSuccess) return hip_fail(e, "static scratch address");
+    hs.device = dev;
+    hs.n_cu = n_cu;
+    hs.mem = base;
+    hs.mem_bytes = bytes;
+    hs.last_T = 0;
+    hs.prof_kernel = -1;
+    hs.prof_cap = 0;
+    hs.prof_n = 0;
+    hs.decode_max_t = decode_max_t_default();
+    carve(hs.cfg, static_cast<char*>(base), &hs.ws);
+    // earlier calls (other layouts) leave their bytes in the scratch: the
+    // tickets of this layout start at zero (a fill kernel, not a memset node)
+    e = launch_fill_u32(static_cast<uint32_t*>(base), hs.ws.ticket_bytes / 4, 0u, stream);
+    if (e != hipSuccess) return hip_fail(e, "ticket clear");
+    return forward_impl(&hs, T, hidden, router_w, router_bias, experts, shared, residual, out, stream);
 }
 
 flint_status flint_moe_get_routing(flint_moe_t h, int32_t* idx, float* weights,

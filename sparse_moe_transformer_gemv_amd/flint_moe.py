@@ -32,7 +32,7 @@ KERNEL_ROUTE, KERNEL_SORT, KERNEL_EXPERT_UP, KERNEL_EXPERT_DOWN, KERNEL_COMBINE 
 EXPORTED = [
     "flint_moe_create", "flint_moe_forward", "flint_moe_get_routing", "flint_moe_profile_begin",
     "flint_moe_profile_end", "flint_moe_destroy", "flint_status_string", "flint_last_error",
-    "flint_rmsnorm_forward",
+    "flint_rmsnorm_forward", "flint_moe_forward_noalloc",
 ]
 
 
@@ -74,6 +74,10 @@ def load_library(path: str = LIB_PATH):
     L.flint_moe_forward.argtypes = [vp, i32, vp, vp, vp, ctypes.POINTER(flint_expert_weights),
                                     ctypes.POINTER(flint_expert_weights), vp, vp, vp]
     L.flint_moe_forward.restype = st
+    L.flint_moe_forward_noalloc.argtypes = [ctypes.POINTER(flint_moe_config), i32, vp, vp, vp,
+                                            ctypes.POINTER(flint_expert_weights),
+                                            ctypes.POINTER(flint_expert_weights), vp, vp, vp]
+    L.flint_moe_forward_noalloc.restype = st
     L.flint_moe_get_routing.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(i32), vp]
     L.flint_moe_get_routing.restype = st
     L.flint_moe_profile_begin.argtypes = [vp, i32, i32]
@@ -235,6 +239,24 @@ def flint_rmsnorm_forward(x: torch.Tensor, eps: float = 1e-6,
     _check(load_library().flint_rmsnorm_forward(x.shape[0], x.shape[1],
                                                 _ptr(x, "x", torch.float32), eps,
                                                 _ptr(out, "out", torch.bfloat16), _stream()))
+    return out
+
+
+def flint_moe_forward_noalloc(cfg: flint_moe_config, x: torch.Tensor, router_w: torch.Tensor,
+                              experts: ExpertWeights, shared: Optional[ExpertWeights],
+                              out: torch.Tensor, router_bias: Optional[torch.Tensor] = None,
+                              residual: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The layer through the allocation-free entry point (static device
+    scratch; no handle).  `out` must be given: nothing is allocated here."""
+    device = torch.device("cuda", torch.cuda.current_device())
+    check_forward_args(cfg, device, x, router_w, experts, shared, router_bias, residual, out)
+    ew = experts.as_c(cfg.weight_dtype)
+    sw = shared.as_c(cfg.weight_dtype) if shared is not None else None
+    _check(load_library().flint_moe_forward_noalloc(
+        ctypes.byref(cfg), x.shape[0], _ptr(x, "x"), _ptr(router_w, "router_w"),
+        _ptr(router_bias, "router_bias"), ctypes.byref(ew),
+        ctypes.byref(sw) if sw is not None else None, _ptr(residual, "residual"),
+        _ptr(out, "out"), _stream()))
     return out
 
 

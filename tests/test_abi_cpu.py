@@ -202,3 +202,21 @@ def test_binding_rejects_tensor_on_another_device():
     with pytest.raises(ValueError, match="is on"):
         b.check_forward_args(cfg, torch.device("meta"), a["x"], a["router_w"], a["experts"],
                              a["shared"], None, None, a["out"])
+
+
+def test_noalloc_entry_point_checks_before_device():
+    L = fm.load_library()
+    args = (None,) * 8
+    # a bad configuration and a T out of range are argument errors
+    assert L.flint_moe_forward_noalloc(ctypes.byref(_cfg(top_k=9)), 4, *args) == b.FLINT_ERR_INVALID_ARG
+    assert L.flint_moe_forward_noalloc(None, 4, *args) == b.FLINT_ERR_INVALID_ARG
+    assert L.flint_moe_forward_noalloc(ctypes.byref(_cfg()), -1, *args) == b.FLINT_ERR_INVALID_ARG
+    # T = 0 is a no-op
+    assert L.flint_moe_forward_noalloc(ctypes.byref(_cfg()), 0, *args) == b.FLINT_OK
+    # a workspace larger than the static scratch is refused by size, before any device call
+    assert L.flint_moe_forward_noalloc(ctypes.byref(_cfg()), 4096, *args) == b.FLINT_ERR_INVALID_ARG
+    assert b"static scratch" in L.flint_last_error()
+    import torch
+    if not torch.cuda.is_available():
+        # a size that fits gets as far as the device check
+        assert L.flint_moe_forward_noalloc(ctypes.byref(_cfg()), 128, *args) == b.FLINT_ERR_NO_DEVICE
