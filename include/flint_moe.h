@@ -71,6 +71,9 @@ typedef enum {
  * makes the output NaN.  The hand-off tickets and the integer routing tables
  * keep their contents.  Adds one fill launch per forward; for tests only. */
 #define FLINT_DEBUG_POISON_WORKSPACE 0x4u
+/* Run small bf16 decode batches as separate route, gate/up and down launches
+ * instead of the single-launch decode kernel (for comparison and tests). */
+#define FLINT_UNFUSED_DECODE 0x8u
 
 typedef struct {
     uint32_t struct_size;   /* = sizeof(flint_moe_config) */
@@ -82,7 +85,7 @@ typedef struct {
     int32_t act_dtype;      /* flint_dtype of hidden/out: FLINT_F32 or FLINT_BF16 */
     int32_t weight_dtype;   /* flint_dtype of expert and shared weights */
     int32_t max_tokens;     /* largest T a forward may pass; sizes the workspace; 1..65536 */
-    uint32_t flags;         /* FLINT_FORCE_*, FLINT_DEBUG_POISON_WORKSPACE */
+    uint32_t flags;         /* FLINT_FORCE_*, FLINT_DEBUG_POISON_WORKSPACE, FLINT_UNFUSED_DECODE */
 } flint_moe_config;
 
 /*
@@ -188,7 +191,9 @@ flint_status flint_moe_get_routing(flint_moe_t h, int32_t* idx, float* weights,
                                         decode batches: bf16 weights up to 16 tokens, NVFP4
                                         up to 4; no combine launch is then recorded) */
 #define FLINT_KERNEL_COMBINE      4  /* weighted unpermute + shared + residual */
-#define FLINT_KERNEL_COUNT        5
+#define FLINT_KERNEL_FUSED        5  /* single-launch decode (the whole layer) */
+#define FLINT_KERNEL_FORWARD      6  /* a whole forward: before its first launch to after its last */
+#define FLINT_KERNEL_COUNT        7
 flint_status flint_moe_profile_begin(flint_moe_t h, int32_t kernel_id, int32_t n_launches);
 flint_status flint_moe_profile_end(flint_moe_t h, float* ms_out, int32_t cap, int32_t* n_out);
 

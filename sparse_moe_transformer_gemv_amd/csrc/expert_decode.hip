@@ -348,8 +348,10 @@ __device__ __forceinline__ void gateup_load_x(const ExpertParams& p, const int4&
     for (int s = 0; s < NSTEP; ++s) a[s] = buffer_load16(xv, xo + 64 * s);
 }
 
-// a: the tile's activation fragments (gateup_load_x)
-template <int NSTEP>
+// a: the tile's activation fragments (gateup_load_x).  COH: h is read by other
+// workgroups of the same launch (single-launch decode), so it is stored at
+// agent scope.
+template <int NSTEP, bool COH = false>
 __device__ __forceinline__ void gateup_mfma_tile(const ExpertParams& p, const int4& g, int r0,
                                                  const uint4 (&a)[NSTEP], const uint4 (&b)[NSTEP], int j0,
                                                  float (&s_part)[4][256], uint16_t (&s_h)[16][3][8]) {
@@ -382,8 +384,12 @@ __device__ __forceinline__ void gateup_mfma_tile(const ExpertParams& p, const in
     if (tid < 48 && r0 + tid / 3 < g.z) {
         const int r = tid / 3, pl = tid % 3;
         const size_t plane = (size_t)(p.dm.k + 1) * p.dm.T * p.hstride;
-        uint16_t* dst = static_cast<uint16_t*>(p.ws.h) + pl * plane + (size_t)(g.w + r0 + r) * p.hstride + j0;
-        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(&s_h[r][pl][0]);
+        const size_t e_off = pl * plane + (size_t)(g.w + r0 + r) * p.hstride + j0;
+        const uint4 v = *reinterpret_cast<const uint4*>(&s_h[r][pl][0]);
+        if constexpr (COH)
+            buffer_store16_agent(v, buffer_view(p.ws.h, (uint32_t)(3 * plane * 2)), (uint32_t)(e_off * 2));
+        else
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.ws.h) + e_off) = v;
     }
 }
 
@@ -474,7 +480,8 @@ __global__ __launch_bounds__(256) void gateup_mfma_kernel(ExpertParams p) {
 // One 16-token tile of a bf16 down block; ws is the routing weight of the
 // token row this thread stores.  h arrives as its three bf16 planes; padding
 // rows read as zeros.
-template <int NSMAX, int NT>
+// COH: h was written by other workgroups of the same launch (agent-scope loads).
+template <int NSMAX, int NT, bool COH = false>
 __device__ __forceinline__ void down_mfma_tile(const ExpertParams& p, const int4& g, int r0, int nsteps, int kl,
                                                int n0, const __amdgpu_buffer_rsrc_t (&hv)[3],
                                                const uint4 (&b)[NT][NSMAX], float ws, float (&s_part)[4][NT][256],
@@ -487,7 +494,8 @@ __device__ __forceinline__ void down_mfma_tile(const ExpertParams& p, const int4
 #pragma unroll
     for (int s = 0; s < NSMAX; ++s)
 #pragma unroll
-        for (int pl = 0; pl < 3; ++pl) ah[pl][s] = buffer_load16(hv[pl], ho + 64 * s);
+        for (int pl = 0; pl < 3; ++pl)
+            ah[pl][s] = COH ? buffer_load16_agent(hv[pl], ho + 64 * s) : buffer_load16(hv[pl], ho + 64 * s);
     __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the first MFMA
     floatx4_t acc[NT];
 #pragma unroll
@@ -1243,6 +1251,600 @@ hipError_t launch_down_decode(const LayerArgs& a, const Workspace& w, hipStream_
         break;
     }
     return hipGetLastError();
+}
+
+
+// ---------------------------------------------------------------------------
+// Single-launch decode for small bf16 batches (T <= kFusedMaxT).
+//
+// A small decode batch is bound by latency, not bytes: with one kernel per
+// step (route, gate/up, down) every step pays a launch, the first HBM round
+// trip and the tail of its grid.  This kernel runs the whole layer in one
+// launch over a grid that is resident at once (kFusedBlocksPerCU workgroups
+// per CU), with two grid-wide barriers and the last-arrival combine:
+//   phase 0  workgroup e < E computes router logit e for every token (fp32
+//            FMA over exact bf16 x fp32 products, a fixed reduction order);
+//            the next fs / 8 workgroups run the shared expert's gate/up items
+//            meanwhile (the shared expert needs no routing);
+//   barrier  every router workgroup has written its logits;
+//   phase 1  every workgroup selects the top-k of every token and sorts the
+//            pairs itself, in LDS (at most 16 x 8 pairs), so no further
+//            hand-off is needed to learn the routing; workgroup 0 publishes it
+//            for flint_moe_get_routing;
+//   phase 2  the routed gate/up items (group, 8 features), spread round-robin;
+//            h leaves as its exact three-plane bf16 split at agent scope;
+//   barrier  every gate/up item is done; each workgroup issues the weight
+//            loads of its first down item before it waits here;
+//   phase 3  the down items (group, 64 output rows): y rows at agent scope,
+//            and the last item of each 64-column block sums those columns of
+//            every token (residual, shared row, routed rows in pair order);
+// The barriers are trees of counters taken with agent-scope atomics after each
+// writer has waited for its stores (vmcnt 0), with per-group release flags
+// polled by one thread per workgroup (see tree_arrive); data crosses
+// workgroups only through agent-scope (sc1) stores and loads, which are served
+// coherently across the XCDs' separate L2 caches.  A poll gives up after
+// kFusedPollCap tries and records a fault word, so the kernel always ends even
+// if a workgroup were never scheduled (the host sizes the grid from the
+// occupancy query, so all of it is resident).
+// ---------------------------------------------------------------------------
+// Largest batch it takes: measured against the separate launches on the full
+// layer (d = 2048, 256 experts, f = 512), it is 13-14% faster at T = 1 and 2,
+// 5% at T = 4, even at T = 8, and slower from T = 12 (the separate gate/up and
+// down launches balance their work better than the persistent grid does).
+constexpr int kFusedMaxT = 8;
+constexpr int kFusedBlocksPerCU = 2;
+constexpr int kFusedPollCap = 1 << 20;
+constexpr int kFusedMaxPairs = kFusedMaxT * kCombineMaxK;
+
+struct FusedParams {
+    ExpertParams e;    // dims, activations, weights, workspace, residual, out
+    const float* wr;   // router [E][d] fp32
+    const float* bias; // [E] or null
+    int nblocks;       // grid size (every workgroup resident)
+};
+
+// Grid barriers as trees: an arriving workgroup adds to its group's counter
+// (kBarGroup workgroups per group), the last of a group adds to the root
+// counter, and the last group releases every waiting group by writing the
+// launch's generation number into the group's flag; a waiting workgroup polls
+// its own group's flag.  Counters and flags sit kBarSlot ints apart, so no
+// line takes more than kBarGroup atomics or polls (hundreds of atomics on one
+// address serialise for microseconds, and hundreds of pollers on one line
+// slow the memory channel that holds it).  Every counter is reset by its own
+// last arrival, and flags are never cleared: a launch waits for its own
+// generation, which the release of its last barrier advances (every
+// workgroup has read it by then), so no exit barrier is needed.
+// Barrier ids: 0 = router logits written, 1 = h written.
+constexpr int kBarGroup = 16;
+constexpr int kBarMaxGroups = 64;  // grids of up to 1024 workgroups
+constexpr int kBarSlot = 256;      // ints between two group slots (1 KiB)
+__device__ __forceinline__ int* bar_cnt(int* fbar, int b, int g) { return fbar + (b * kBarMaxGroups + g) * kBarSlot; }
+__device__ __forceinline__ int* bar_flag(int* fbar, int b, int g) { return bar_cnt(fbar, b, g) + 32; }
+__device__ __forceinline__ int* bar_root(int* fbar, int b) { return fbar + (2 * kBarMaxGroups + b) * kBarSlot; }
+__device__ __forceinline__ int* bar_gen(int* fbar) { return fbar + (2 * kBarMaxGroups + 2) * kBarSlot; }
+__device__ __forceinline__ int* bar_fault(int* fbar) { return fbar + (2 * kBarMaxGroups + 3) * kBarSlot; }
+// work counter q of the gate/up (q = XCD 0..7) and down (q = 8 + XCD) phases,
+// zero when the phase starts
+__device__ __forceinline__ int* bar_queue(int* fbar, int q) { return fbar + (2 * kBarMaxGroups + 4 + q) * kBarSlot; }
+static_assert((2 * kBarMaxGroups + 20) * kBarSlot == kFusedBarrierInts, "barrier region size");
+
+// Workgroup `id` of the n that arrive at barrier b (all threads call it).  The
+// writer's stores complete before its arrival; returns true in thread 0 of
+// the workgroup that arrived last overall.
+__device__ __forceinline__ bool tree_arrive(int* fbar, int b, int id, int n) {
+    wait_stores();
+    __syncthreads();
+    bool last = false;
+    if (threadIdx.x == 0) {
+        const int g = id / kBarGroup;
+        const int gsize = min(kBarGroup, n - g * kBarGroup);
+        int* cnt = bar_cnt(fbar, b, g);
+        if (__hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gsize - 1) {
+            st_agent(cnt, 0);  // every arrival of this launch is in
+            const int ngroups = (n + kBarGroup - 1) / kBarGroup;
+            int* root = bar_root(fbar, b);
+            last = __hip_atomic_fetch_add(root, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ngroups - 1;
+            if (last) st_agent(root, 0);
+        }
+    }
+    return last;
+}
+
+// The last arrival (thread 0) releases the nwait waiting groups of generation gen.
+__device__ __forceinline__ void tree_release(int* fbar, int b, int nwait, int gen) {
+    for (int g = 0; g < nwait; ++g) st_agent(bar_flag(fbar, b, g), gen);
+}
+
+// Wait (all threads) until barrier b releases generation gen for workgroup
+// id's group.  A poll gives up after kFusedPollCap tries and records a fault
+// word, so the kernel ends even if a workgroup never arrived.
+__device__ __forceinline__ void tree_wait(int* fbar, int b, int id, int gen) {
+    if (threadIdx.x == 0) {
+        const int* f = bar_flag(fbar, b, id / kBarGroup);
+        int n = 0;
+        while (ld_agent(f) != gen) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++n >= kFusedPollCap) {
+                st_agent(bar_fault(fbar), 1);
+                break;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// Router logits of expert e for every token: 8 consecutive k per thread and
+// pass, fp32 FMA chains, then a wavefront sum and the four waves in order.
+__device__ void fused_router_expert(const FusedParams& P, int e, float (&s_red)[4][kFusedMaxT]) {
+    const ExpertParams& p = P.e;
+    const int T = p.dm.T, d = p.dm.d, E = p.dm.E;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const __amdgpu_buffer_rsrc_t xv = buffer_view(p.x, (uint32_t)T * d * 2);
+    float acc[kFusedMaxT];
+#pragma unroll
+    for (int t = 0; t < kFusedMaxT; ++t) acc[t] = 0.f;
+    for (int c = tid * 8; c < d; c += 2048) {
+        const float4 w0 = *reinterpret_cast<const float4*>(P.wr + (size_t)e * d + c);
+        const float4 w1 = *reinterpret_cast<const float4*>(P.wr + (size_t)e * d + c + 4);
+        uint4 xa[kFusedMaxT];
+#pragma unroll
+        for (int t = 0; t < kFusedMaxT; ++t) xa[t] = buffer_load16(xv, t < T ? (uint32_t)(t * d + c) * 2 : kOffNone);
+#pragma unroll
+        for (int t = 0; t < kFusedMaxT; ++t) {
+            float a = acc[t];
+            a = fmaf(w0.x, bf16_lo(xa[t].x), a);
+            a = fmaf(w0.y, bf16_hi(xa[t].x), a);
+            a = fmaf(w0.z, bf16_lo(xa[t].y), a);
+            a = fmaf(w0.w, bf16_hi(xa[t].y), a);
+            a = fmaf(w1.x, bf16_lo(xa[t].z), a);
+            a = fmaf(w1.y, bf16_hi(xa[t].z), a);
+            a = fmaf(w1.z, bf16_lo(xa[t].w), a);
+            a = fmaf(w1.w, bf16_hi(xa[t].w), a);
+            acc[t] = a;
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < kFusedMaxT; ++t) {
+        if (t >= T) break;  // uniform
+        const float v = wave_sum(acc[t]);
+        if (lane == 0) s_red[wave][t] = v;
+    }
+    __syncthreads();
+    if (tid < T) {
+        const float v = ((s_red[0][tid] + s_red[1][tid]) + s_red[2][tid]) + s_red[3][tid];
+        st_agent(p.ws.logits + (size_t)tid * E + e, v + (P.bias ? P.bias[e] : 0.f));
+    }
+}
+
+// Top-k of every token, one wavefront per token (tokens wave, wave + 4, ...).
+// The logits come into LDS first, with one round of 16-byte agent-scope loads
+// by the whole workgroup.  Lane l holds the order-preserving keys of experts
+// 4 l .. 4 l + 3; each round takes the wavefront maximum, and the lowest lane
+// holding it, then the lowest slot in that lane, give the lowest expert index
+// among equal logits.  Weights: softmax of the chosen logits.  Results in LDS.
+__device__ void fused_topk(const ExpertParams& p, float* s_logit, int* s_sel, float* s_wt) {
+    const int T = p.dm.T, E = p.dm.E, k = p.dm.k;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t bytes = (uint32_t)(T * E * 4 + 15) & ~15u;  // within the 256-byte padded region
+    const __amdgpu_buffer_rsrc_t lv = buffer_view(p.ws.logits, bytes);
+    // every load of the (at most 16 KiB) block is issued before the first
+    // store; loads past the view return zeros and are not stored
+    constexpr int kChunks = kFusedMaxT * 256 * 4 / (16 * 256);
+    uint4 lg[kChunks];
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) lg[i] = buffer_load16_agent(lv, (threadIdx.x + 256 * i) * 16);
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+        const uint32_t o = (threadIdx.x + 256 * i) * 16;
+        if (o < bytes) *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(s_logit) + o) = lg[i];
+    }
+    __syncthreads();
+    for (int t = wave; t < T; t += 4) {
+        // the lane's 4 keys sorted in descending order (equal keys keep the
+        // lower expert first), with their expert ids
+        uint32_t key[4];
+        int eid[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * lane + i;
+            key[i] = e < E ? order_key(s_logit[t * E + e]) : 0u;
+            eid[i] = e;
+        }
+#pragma unroll
+        for (int a = 0; a < 3; ++a)
+#pragma unroll
+            for (int b2 = 0; b2 < 3 - a; ++b2)
+                if (key[b2 + 1] > key[b2]) {
+                    const uint32_t tk = key[b2];
+                    key[b2] = key[b2 + 1];
+                    key[b2 + 1] = tk;
+                    const int te = eid[b2];
+                    eid[b2] = eid[b2 + 1];
+                    eid[b2 + 1] = te;
+                }
+        // each round: the wavefront maximum of the lanes' heads; the lowest lane
+        // holding it wins (lane l holds experts 4 l .. 4 l + 3, so that is the
+        // lowest expert index among equal logits) and pops its head
+        float lsel = 0.f;
+        int esel = 0;
+        float l0 = 0.f;
+#pragma unroll
+        for (int j = 0; j < kCombineMaxK; ++j) {
+            if (j >= k) break;  // uniform
+            const uint32_t M = wave_max_u32(key[0]);
+            const int L = __builtin_ctzll(__ballot(key[0] == M));
+            const int ej = __builtin_amdgcn_readlane(eid[0], L);
+            if (lane == L) {
+                key[0] = key[1]; key[1] = key[2]; key[2] = key[3]; key[3] = 0u;
+                eid[0] = eid[1]; eid[1] = eid[2]; eid[2] = eid[3];
+            }
+            const float lj = key_value(M);
+            if (j == 0) l0 = lj;
+            if (lane == j) {
+                lsel = lj;
+                esel = ej;
+            }
+        }
+        // weights: softmax of the chosen logits (hardware exp2 and reciprocal;
+        // about 1 ulp each)
+        const float pj = lane < k ? __builtin_amdgcn_exp2f((lsel - l0) * 1.4426950408889634f) : 0.f;
+        const float sum = wave_sum(pj);
+        if (lane < k) {
+            s_sel[t * k + lane] = esel;
+            s_wt[t * k + lane] = pj * __builtin_amdgcn_rcpf(sum);
+        }
+    }
+}
+
+// Stable counting sort of the k T pairs by expert, in LDS.  A token picks an
+// expert at most once, so a bitmask of the tokens that picked each expert
+// (s_mask, T <= 32) gives both the count (its population) and each pair's rank
+// among the earlier pairs of its expert (the tokens below its own); then the
+// exclusive scan of the counts, the sorted pair list, its inverse, the weight
+// of each sorted pair, and the group list (the shared expert first, then every
+// expert with tokens, ascending).
+__device__ void fused_sort(const ExpertParams& p, const int* s_sel, const float* s_wt, unsigned* s_mask, int* s_off,
+                           int* s_sp, int* s_pos, float* s_swt, int4* s_groups, int* s_ng) {
+    const int T = p.dm.T, k = p.dm.k, E = p.dm.E, P = k * T;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < E; i += blockDim.x) s_mask[i] = 0u;
+    __syncthreads();
+    if (tid < P) atomicOr(&s_mask[s_sel[tid]], 1u << (tid / k));
+    __syncthreads();
+    if (wave == 0) {
+        int c[4], local = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * lane + i;
+            c[i] = e < E ? __popc(s_mask[e]) : 0;
+            local += c[i];
+        }
+        int inc = local;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int v = __shfl_up(inc, off, 64);
+            if (lane >= off) inc += v;
+        }
+        int run = inc - local;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * lane + i;
+            if (e < E) s_off[e] = run;
+            run += c[i];
+        }
+        if (lane == 63) s_off[E] = inc;
+    }
+    __syncthreads();
+    if (tid < P) {
+        const int key = s_sel[tid];
+        const int pos = s_off[key] + __popc(s_mask[key] & ((1u << (tid / k)) - 1u));
+        s_sp[pos] = tid;
+        s_pos[tid] = pos;
+        s_swt[pos] = s_wt[tid];
+    }
+    if (wave == 0) {
+        const unsigned long long lt = (1ull << lane) - 1ull;
+        int n = 0;
+        if (p.dm.fs > 0) {
+            if (lane == 0) s_groups[0] = make_int4(E, 0, T, P);
+            n = 1;
+        }
+        for (int e0 = 0; e0 < E; e0 += 64) {
+            const int e = e0 + lane;
+            const int c = e < E ? __popc(s_mask[e]) : 0;
+            const unsigned long long act = __ballot(c > 0);
+            if (c > 0) s_groups[n + __popcll(act & lt)] = make_int4(e, s_off[e], c, s_off[e]);
+            n += __popcll(act);
+        }
+        if (lane == 0) *s_ng = n;
+    }
+    __syncthreads();
+}
+
+// One gate/up item (group g, features 8 fb .. 8 fb + 7): the body of
+// gateup_mfma_kernel with the sorted pairs from LDS and h stored at agent scope.
+template <int NSTEP>
+__device__ void fused_gateup_item(const ExpertParams& p, const int4& g, int fb, const int* s_sp, unsigned char* s_w,
+                                  float (&s_part)[4][256], uint16_t (&s_h)[16][3][8]) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = lane & 15, q = lane >> 4;
+    const int d = p.dm.d;
+    const bool is_shared = g.x == p.dm.E;
+    const int F = is_shared ? p.dm.fs : p.dm.f;
+    const int j0 = fb * 8;
+    const int sp = is_shared ? 0 : s_sp[g.y + (row < g.z ? row : g.z - 1)];
+    const size_t e = is_shared ? 0 : (size_t)g.x;
+    const uint16_t* gu = static_cast<const uint16_t*>(is_shared ? p.shared.gu : p.routed.gu);
+    const int kl = wave * (d / 4) + 8 * q;
+    const __amdgpu_buffer_rsrc_t xv = buffer_view(p.x, (uint32_t)p.dm.T * d * 2);
+    uint4 b[NSTEP];
+    unsigned char* sw = s_w + wave * (16 * 64 * NSTEP);
+    const int kw = wave * (d / 4);
+#pragma unroll
+    for (int i = 0; i < NSTEP; ++i) {
+        const int r = 8 * (i & 1) + (lane >> 3);
+        const size_t wrr = e * 2 * F + (r < 8 ? (size_t)(j0 + r) : (size_t)(F + j0 + r - 8));
+        const int c = (lane & 7) ^ (r & 7);
+        __builtin_amdgcn_global_load_lds(gu + wrr * d + kw + 64 * (i >> 1) + 8 * c, sw + i * 1024, 16, 0, 2);
+    }
+    uint4 a0[NSTEP];
+    gateup_load_x<NSTEP>(p, g, is_shared, 0, sp, xv, kl, a0);
+    const uint32_t rbase = (uint32_t)((row >> 3) * 1024 + (row & 7) * 128);
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+        const uint32_t off = (s >> 1) * 2048 + rbase + ((((4 * (s & 1)) + q) ^ (row & 7)) << 4);
+        b[s] = *reinterpret_cast<const uint4*>(sw + off);
+    }
+    gateup_mfma_tile<NSTEP, true>(p, g, 0, a0, b, j0, s_part, s_h);
+    for (int r0 = 16; r0 < g.z; r0 += 16) {
+        const int m = r0 + row;
+        const int spn = is_shared ? 0 : s_sp[g.y + (m < g.z ? m : g.z - 1)];
+        uint4 a[NSTEP];
+        gateup_load_x<NSTEP>(p, g, is_shared, r0, spn, xv, kl, a);
+        gateup_mfma_tile<NSTEP, true>(p, g, r0, a, b, j0, s_part, s_h);
+    }
+}
+
+// Weight fragments of one down item (group g, output rows 64 rb .. + 63).
+template <int NSMAX>
+__device__ __forceinline__ void fused_down_weights(const ExpertParams& p, const int4& g, int rb,
+                                                   uint4 (&b)[kDownMfmaTiles][NSMAX]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row = lane & 15, q = lane >> 4;
+    const int d = p.dm.d;
+    const bool is_shared = g.x == p.dm.E;
+    const int F = is_shared ? p.dm.fs : p.dm.f;
+    const int nsteps = F / 128;
+    const int kl = wave * (F / 4) + 8 * q;
+    const size_t e = is_shared ? 0 : (size_t)g.x;
+    const uint16_t* dn = static_cast<const uint16_t*>(is_shared ? p.shared.dn : p.routed.dn);
+    const int n0 = rb * 16 * kDownMfmaTiles;
+#pragma unroll
+    for (int t = 0; t < kDownMfmaTiles; ++t) {
+        const uint16_t* drow = dn + (e * d + (size_t)(n0 + 16 * t + row)) * F + kl;
+#pragma unroll
+        for (int s = 0; s < NSMAX; ++s) b[t][s] = *reinterpret_cast<const uint4*>(drow + 32 * (s < nsteps ? s : 0));
+    }
+}
+
+// One down item with its weights in b: y rows at agent scope, then the
+// last-arrival combine of the item's 64 columns.
+template <int NSMAX>
+__device__ void fused_down_item(const ExpertParams& p, const int4& g, int rb, int ng,
+                                const uint4 (&b)[kDownMfmaTiles][NSMAX], const float* s_swt, const int* s_pos,
+                                float (&s_dpart)[4][kDownMfmaTiles][256], int* s_flag) {
+    constexpr int NT = kDownMfmaTiles;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int q = lane >> 4;
+    const int mm = tid >> 4;
+    const bool is_shared = g.x == p.dm.E;
+    const int F = is_shared ? p.dm.fs : p.dm.f;
+    const int nsteps = F / 128;
+    const int kl = wave * (F / 4) + 8 * q;
+    const int n0 = rb * 16 * NT;
+    const uint16_t* h16 = static_cast<const uint16_t*>(p.ws.h);
+    const size_t plane = (size_t)(p.dm.k + 1) * p.dm.T * p.hstride;
+    const uint32_t vbytes = (uint32_t)g.z * p.hstride * 2;
+    __amdgpu_buffer_rsrc_t hv[3];
+#pragma unroll
+    for (int pl = 0; pl < 3; ++pl) hv[pl] = buffer_view(h16 + pl * plane + (size_t)g.w * p.hstride, vbytes);
+    float* y = static_cast<float*>(p.ws.y);
+    for (int r0 = 0; r0 < g.z; r0 += 16) {
+        const int m = r0 + mm;
+        const float rw = is_shared ? 1.f : s_swt[g.y + (m < g.z ? m : g.z - 1)];
+        down_mfma_tile<NSMAX, NT, true>(p, g, r0, nsteps, kl, n0, hv, b, rw, s_dpart, y, true);
+    }
+    if (last_arrival(&p.ws.dcount[rb], ng, s_flag)) {
+        const int n = p.dm.T * 16 * NT;  // uniform
+        if (n <= 256) combine_columns_n<NT, 1>(p, n0, s_pos);
+        else if (n <= 512) combine_columns_n<NT, 2>(p, n0, s_pos);
+        else combine_columns_n<NT, 4>(p, n0, s_pos);
+    }
+}
+
+template <int NSTEP, int NSMAX>
+__global__ __launch_bounds__(256) void decode_fused_kernel(FusedParams P) {
+    constexpr int kStage = GateupWeightLds<NSTEP>::kBytes > 16384 ? GateupWeightLds<NSTEP>::kBytes : 16384;
+    __shared__ __attribute__((aligned(16))) unsigned char s_w[kStage];
+    __shared__ float s_part[4][256];
+    __shared__ __attribute__((aligned(16))) uint16_t s_h[16][3][8];
+    __shared__ float s_red[4][kFusedMaxT];
+    __shared__ int s_sel[kFusedMaxPairs];
+    __shared__ float s_wt[kFusedMaxPairs];
+    __shared__ int s_sp[kFusedMaxPairs];
+    __shared__ int s_pos[kFusedMaxPairs];
+    __shared__ float s_swt[kFusedMaxPairs];
+    __shared__ unsigned s_mask[256];
+    __shared__ int s_off[257];
+    __shared__ int4 s_groups[257];
+    __shared__ int s_ng, s_flag, s_next;
+    // the down partial sums reuse the gate/up weight stage (free after phase 2)
+    float(&s_dpart)[4][kDownMfmaTiles][256] = *reinterpret_cast<float(*)[4][kDownMfmaTiles][256]>(s_w);
+    static_assert(sizeof(float) * 4 * kDownMfmaTiles * 256 <= kStage, "stage too small for the down partials");
+
+    const ExpertParams& p = P.e;
+    const int G = P.nblocks, bid = blockIdx.x;
+    const int E = p.dm.E, T = p.dm.T, k = p.dm.k;
+    int* fbar = p.ws.fbar;
+    const int nwait = (G + kBarGroup - 1) / kBarGroup;  // groups of waiting workgroups
+    // this launch's generation: flags of earlier launches hold smaller ones
+    // (the count wraps after 2^32 launches, far apart in time)
+    __shared__ int s_gen;
+    if (threadIdx.x == 0) s_gen = ld_agent(bar_gen(fbar)) + 1;
+    __syncthreads();
+    const int gen = s_gen;
+    const int fs_items = p.dm.fs / 8, f_items = p.dm.f / 8;
+
+    // ---- phase 0: router logits; the shared expert's gate/up meanwhile ----
+    if (bid < E) {
+        fused_router_expert(P, bid, s_red);
+        if (tree_arrive(fbar, 0, bid, E)) {
+            // the previous launch has ended: its down work counters start over
+            for (int x = 0; x < 8; ++x) st_agent(bar_queue(fbar, 8 + x), 0);
+            tree_release(fbar, 0, nwait, gen);
+        }
+    } else if (bid - E < fs_items) {
+        fused_gateup_item<NSTEP>(p, make_int4(E, 0, T, k * T), bid - E, s_sp, s_w, s_part, s_h);
+    }
+    tree_wait(fbar, 0, bid, gen);
+
+    // ---- phase 1: routing, redundantly in every workgroup ----
+    fused_topk(p, reinterpret_cast<float*>(s_w), s_sel, s_wt);
+    __syncthreads();
+    fused_sort(p, s_sel, s_wt, s_mask, s_off, s_sp, s_pos, s_swt, s_groups, &s_ng);
+    const int ng = s_ng;
+    if (bid == 0) {  // the routing of this forward, for flint_moe_get_routing
+        for (int i = threadIdx.x; i < k * T; i += blockDim.x) {
+            p.ws.sel[i] = s_sel[i];
+            p.ws.wts[i] = s_wt[i];
+            p.ws.sorted_pair[i] = s_sp[i];
+            p.ws.pair_pos[i] = s_pos[i];
+            p.ws.sorted_wt[i] = s_swt[i];
+        }
+        for (int i = threadIdx.x; i < E; i += blockDim.x) {
+            p.ws.counts[i] = __popc(s_mask[i]);
+            p.ws.offsets[i] = s_off[i];
+        }
+    }
+
+    // ---- phase 2: routed gate/up items.  Item j of XCD x is routed item
+    // x + 8 j (workgroups are dispatched round-robin over the 8 XCDs): a
+    // workgroup's first item is its rank in its XCD, the following ones come
+    // from the XCD's counter, fetched while the current item runs, so the
+    // workgroups that stream faster take more items. ----
+    const int g0 = p.dm.fs > 0 ? 1 : 0;
+    const int n_up = (ng - g0) * f_items;
+    {
+        const int x = bid & 7, per_xcd = G >> 3;
+        int* ctr = bar_queue(fbar, x);
+        int i = bid >> 3;
+        while (x + 8 * i < n_up) {  // uniform
+            int next = 0;
+            if (threadIdx.x == 0)
+                next = per_xcd + __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int j = x + 8 * i;
+            fused_gateup_item<NSTEP>(p, s_groups[g0 + j / f_items], j % f_items, s_sp, s_w, s_part, s_h);
+            if (threadIdx.x == 0) s_next = next;
+            __syncthreads();
+            i = s_next;
+            __syncthreads();
+        }
+    }
+
+    // ---- barrier: every h row is written.  Down items are scheduled like the
+    // gate/up ones (item x + 8 i, first by rank, then from the XCD's counter);
+    // a workgroup with a first down item issues its weight loads before it
+    // waits, one without skips the wait. ----
+    const int rblocks = p.dm.d / (16 * kDownMfmaTiles);
+    const int n_down = ng * rblocks;
+    const int xd = bid & 7, per_xcd = G >> 3;
+    int id = bid >> 3;               // this workgroup's down item: xd + 8 id
+    const int j0 = xd + 8 * id;
+    uint4 bw[kDownMfmaTiles][NSMAX];
+    if (tree_arrive(fbar, 1, bid, G)) {
+        // every workgroup has arrived: each has read the generation and taken
+        // its last gate/up work index
+        st_agent(bar_gen(fbar), gen);
+        for (int x = 0; x < 8; ++x) st_agent(bar_queue(fbar, x), 0);
+        tree_release(fbar, 1, nwait, gen);
+    }
+    if (j0 < n_down) {
+        fused_down_weights<NSMAX>(p, s_groups[j0 / rblocks], j0 % rblocks, bw);
+        tree_wait(fbar, 1, bid, gen);
+    }
+
+    // ---- phase 3: down items and the combine ----
+    while (xd + 8 * id < n_down) {  // uniform
+        const int j = xd + 8 * id;
+        if (j != j0) fused_down_weights<NSMAX>(p, s_groups[j / rblocks], j % rblocks, bw);
+        int next = 0;
+        if (threadIdx.x == 0)
+            next = per_xcd + __hip_atomic_fetch_add(bar_queue(fbar, 8 + xd), 1, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        fused_down_item<NSMAX>(p, s_groups[j / rblocks], j % rblocks, ng, bw, s_swt, s_pos, s_dpart, &s_flag);
+        if (threadIdx.x == 0) s_next = next;
+        __syncthreads();
+        id = s_next;
+        __syncthreads();
+    }
+}
+
+template <int NSTEP, int NSMAX>
+static const void* fused_kernel_ptr() {
+    return reinterpret_cast<const void*>(&decode_fused_kernel<NSTEP, NSMAX>);
+}
+
+// The kernel instance for the shape, or null: NSTEP = d / 128 k steps per wave,
+// NSMAX = the widest expert / 128.
+static const void* fused_kernel_for(const Dims& dm) {
+    const int fmax = dm.f > dm.fs ? dm.f : dm.fs;
+    const int ns = dm.d / 128, nm = (fmax + 127) / 128;
+#define FLINT_FUSED_CASE(S)                                  \
+    if (ns == S) {                                           \
+        if (nm <= 1) return fused_kernel_ptr<S, 1>();        \
+        if (nm <= 2) return fused_kernel_ptr<S, 2>();        \
+        if (nm <= 4) return fused_kernel_ptr<S, 4>();        \
+        return fused_kernel_ptr<S, 8>();                     \
+    }
+    FLINT_FUSED_CASE(2)
+    FLINT_FUSED_CASE(4)
+    FLINT_FUSED_CASE(8)
+    FLINT_FUSED_CASE(16)
+#undef FLINT_FUSED_CASE
+    return nullptr;
+}
+
+int fused_decode_grid(const Dims& dm, int n_cu) {
+    const int fmax = dm.f > dm.fs ? dm.f : dm.fs;
+    const int ns = dm.d / 128;
+    if (!(dm.act == DT_BF16 && dm.wdt == DT_BF16 && dm.T >= 1 && dm.T <= kFusedMaxT && dm.k <= kCombineMaxK &&
+          dm.E <= 256 && dm.d % 256 == 0 && (ns == 2 || ns == 4 || ns == 8 || ns == 16) && dm.f % 128 == 0 &&
+          dm.fs % 128 == 0 && fmax <= kDownKChunk))
+        return 0;
+    const void* kp = fused_kernel_for(dm);
+    if (!kp) return 0;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kp, 256, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    per_cu = per_cu < kFusedBlocksPerCU ? per_cu : kFusedBlocksPerCU;
+    const int G = (per_cu * n_cu) & ~7;  // the gate/up work is split over the 8 XCDs
+    // the router takes one workgroup per expert and the shared gate/up items the next ones
+    if (per_cu < 1 || dm.E + dm.fs / 8 > G || G > kBarGroup * kBarMaxGroups) return 0;
+    return G;
+}
+
+hipError_t launch_decode_fused(const LayerArgs& a, const Workspace& w, int nblocks, hipStream_t s) {
+    FusedParams P;
+    P.e = make_params(a, w);
+    P.wr = a.wr;
+    P.bias = a.bias;
+    P.nblocks = nblocks;
+    const void* kp = fused_kernel_for(a.dm);
+    if (!kp) return hipErrorInvalidValue;
+    void* args[] = {&P};
+    return hipLaunchKernel(kp, dim3(nblocks), dim3(256), args, 0, s);
 }
 
 }  // namespace flint

@@ -20,9 +20,11 @@
 // gate rows then the matching 32 up rows of features 32q..32q+31, so each wave
 // holds matching gate and up columns and applies SwiGLU in registers.  The
 // MFMAs take the weights as their first operand, which leaves 4 consecutive
-// output columns of one row in each lane; the weight rows of each pair of
-// column tiles are interleaved so that a lane holds 8, and the results leave
-// as 16-byte stores straight from registers.
+// output columns of one row in each lane.  For gate/up (bf16 h) the weight
+// rows of each pair of column tiles are interleaved so that a lane holds 8;
+// down (fp32 y) keeps each tile's order, so the 4 lanes of a row store 64
+// contiguous bytes; either way the results leave as 16-byte stores straight
+// from registers.
 //
 // K advances in pairs of 32-wide sub-stages through two 64 KiB LDS buffers,
 // filled straight from global memory with direct-to-LDS 16-byte loads of whole
@@ -245,7 +247,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
             const int wrow = (up ? F : 0) + nb0 + HS * wb + out_col<NI / 2>(tn % (NI / 2), jr);
             boff[j] = (uint32_t)(((size_t)wrow * K + 8 * c) * 2);
         } else {
-            boff[j] = (uint32_t)(((size_t)(nb0 + 16 * NI * wb + out_col<NI>(tn, jr)) * K + 8 * c) * 2);
+            // down writes fp32: tiles keep their own order (column 16 tn + jr),
+            // so each store instruction covers 64 contiguous bytes of a row
+            boff[j] = (uint32_t)(((size_t)(nb0 + 16 * NI * wb + 16 * tn + jr) * K + 8 * c) * 2);
         }
     }
 
@@ -306,9 +310,11 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
 
     // ---- epilogue, straight from registers.  The MFMAs take the B rows (weights)
     // as their first operand, so lane (row16, q) holds, for each (mi, ni), rows
-    // 4 q .. 4 q + 3 of B tile ni for output row 16 mi + row16, which out_col()
-    // made consecutive output columns: 16-byte stores (8 bytes for a lone tile),
-    // 64 contiguous bytes per row and instruction. ----
+    // 4 q .. 4 q + 3 of B tile ni for output row 16 mi + row16.  Gate/up: out_col()
+    // made the two tiles of a pair 8 consecutive features, one 16-byte bf16 store
+    // (8 bytes for a lone tile).  Down: columns 16 ni + 4 q .. + 3, one 16-byte
+    // fp32 store per tile.  Either way 64 contiguous bytes per row and
+    // instruction. ----
     const int wrows = min(max(rows - 128 * wm, 0), 128);
     if (MODE == MODE_GATEUP) {
         // gate tile t and up tile t + NI / 2 hold the same features
@@ -337,7 +343,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
         }
     } else {
         float* dst = static_cast<float*>(p.ws.y) + (size_t)(g.w + m0 + 128 * wm + row16) * d + nb0 +
-                     16 * NI * wn + 8 * q;
+                     16 * NI * wn + 4 * q;
         // routing weights of the lane's 8 rows, loaded before any store (loads and
         // stores share one in-order counter, so a load after a store waits for it)
         // (unconditional buffer loads: a load behind a branch makes every later use
@@ -357,11 +363,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
                 const float ws = wv[mi];
                 float* o = dst + (size_t)16 * mi * d;
 #pragma unroll
-                for (int t = 0; t < NI / 2; ++t) {
-                    const floatx4_t& a0 = acc[mi][2 * t];
-                    const floatx4_t& a1 = acc[mi][2 * t + 1];
-                    *reinterpret_cast<float4*>(o + 32 * t) = make_float4(ws * a0[0], ws * a0[1], ws * a0[2], ws * a0[3]);
-                    *reinterpret_cast<float4*>(o + 32 * t + 4) = make_float4(ws * a1[0], ws * a1[1], ws * a1[2], ws * a1[3]);
+                for (int t = 0; t < NI; ++t) {
+                    const floatx4_t& a = acc[mi][t];
+                    *reinterpret_cast<float4*>(o + 16 * t) = make_float4(ws * a[0], ws * a[1], ws * a[2], ws * a[3]);
                 }
             }
         }

@@ -38,6 +38,8 @@ struct Workspace {
     int* dcount;         // [ceil(d/16)] decode down tickets (combine folded in), zero between launches
     float* part;         // [kchunks][kSplitRowsMax][d] split-K partial sums of the decode down (f > 1024)
     int* kcount;         // [(E+1) ceil(d/16)] split-K tickets, zero between launches
+    int* fbar;           // [kFusedBarrierInts] single-launch decode: grid-barrier counters and
+                         // flags (zero between launches) and a sticky fault word
     void* h;             // [(k+1)*Tm][fmax] x 8 B: fp32 (decode VALU), three exact bf16 planes (decode
                          // MFMA), two f16 planes (NVFP4), or bf16 (prefill)
     void* y;             // [(k+1)*Tm][d] fp32 rows (weighted expert outputs; split-K sums)
@@ -92,6 +94,13 @@ hipError_t launch_down_decode(const LayerArgs& a, const Workspace& w, hipStream_
 // true when launch_down_decode also performs the combine (no launch_combine then)
 bool down_decode_combines(const Dims& dm);
 bool decode_fp4_ok(const Dims& dm);
+// Ints of the single-launch decode's barrier region: 2 barriers x 64 group slots
+// + 4 slots (roots, generation, fault word) + 16 work counters, 256 ints each.
+constexpr int kFusedBarrierInts = (2 * 64 + 20) * 256;
+// Single-launch decode: its grid size for this shape on n_cu compute units (every
+// workgroup resident), or 0 where it does not apply; and its launch.
+int fused_decode_grid(const Dims& dm, int n_cu);
+hipError_t launch_decode_fused(const LayerArgs& a, const Workspace& w, int nblocks, hipStream_t s);
 hipError_t launch_gateup_prefill(const LayerArgs& a, const Workspace& w, int n_cu, hipStream_t s);
 hipError_t launch_down_prefill(const LayerArgs& a, const Workspace& w, int n_cu, hipStream_t s);
 hipError_t launch_combine(const LayerArgs& a, const Workspace& w, hipStream_t s);
@@ -191,6 +200,32 @@ __device__ __forceinline__ bool last_arrival(int* counter, int n_arrivals, int* 
     return *s_flag != 0;
 }
 
+// Maximum over the 64 lanes: quad swaps, half-row and row mirrors reduce
+// each row of 16 lanes, the row broadcasts carry the result to lane 63, and
+// it is read back as a wave-uniform value.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#define FLINT_DPP_MAX(ctrl, rmask) \
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, ctrl, rmask, 0xF, false))
+    FLINT_DPP_MAX(0xB1, 0xF);   // quad_perm [1,0,3,2]
+    FLINT_DPP_MAX(0x4E, 0xF);   // quad_perm [2,3,0,1]
+    FLINT_DPP_MAX(0x141, 0xF);  // row_half_mirror
+    FLINT_DPP_MAX(0x140, 0xF);  // row_mirror
+    FLINT_DPP_MAX(0x142, 0xA);  // row_bcast:15 into rows 1 and 3
+    FLINT_DPP_MAX(0x143, 0xC);  // row_bcast:31 into rows 2 and 3
+#undef FLINT_DPP_MAX
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Order-preserving map of a float to an unsigned key (-0 taken as +0); key 0
+// marks an expert that can no longer be chosen.
+__device__ __forceinline__ uint32_t order_key(float f) {
+    const uint32_t u = __float_as_uint(f + 0.0f);
+    return (u >> 31) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t key) {
+    return __uint_as_float((key >> 31) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
 // Raw buffer view of [base, base + bytes): a load whose offset lies at or past
 // the end returns zeros without touching memory, which is how kernels skip the
 // rows of a 16-row MFMA tile that hold no token.  Offsets are 32-bit; kOffNone
@@ -203,6 +238,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(const void* base, 
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
     return make_uint4(v.x, v.y, v.z, v.w);
+}
+// The same load and a 16-byte store at agent scope (cache policy sc1, as the
+// agent-scope atomics above): data handed between workgroups of one launch.
+constexpr int kCpolAgent = 16;
+__device__ __forceinline__ uint4 buffer_load16_agent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCpolAgent);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void buffer_store16_agent(uint4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b128((u32x4_t){v.x, v.y, v.z, v.w}, r, (int)off, 0, kCpolAgent);
 }
 // MFMA operand types (gfx950 v_mfma_f32_16x16x32_bf16).  Lane l of a wave
 // supplies A row (l & 15) and B column (l & 15), each with the 8 consecutive

@@ -87,7 +87,8 @@ flint_status check_config(const flint_moe_config* c) {
         return fail(FLINT_ERR_INVALID_ARG, "weight_dtype %d unknown", c->weight_dtype);
     if (c->max_tokens < 1 || c->max_tokens > 65536)
         return fail(FLINT_ERR_INVALID_ARG, "max_tokens %d: need 1..65536", c->max_tokens);
-    if (c->flags & ~(FLINT_FORCE_DECODE_PATH | FLINT_FORCE_PREFILL_PATH | FLINT_DEBUG_POISON_WORKSPACE))
+    if (c->flags & ~(FLINT_FORCE_DECODE_PATH | FLINT_FORCE_PREFILL_PATH | FLINT_DEBUG_POISON_WORKSPACE |
+                     FLINT_UNFUSED_DECODE))
         return fail(FLINT_ERR_INVALID_ARG, "unknown flags 0x%x", c->flags);
     if ((c->flags & FLINT_FORCE_DECODE_PATH) && (c->flags & FLINT_FORCE_PREFILL_PATH))
         return fail(FLINT_ERR_INVALID_ARG, "both path-forcing flags set");
@@ -165,6 +166,7 @@ size_t carve(const flint_moe_config& c, char* base, Workspace* w) {
     w->counter = static_cast<int*>(take((1 + (Tm + 15) / 16) * 4));
     w->dcount = static_cast<int*>(take((size_t)((c.d_model + 15) / 16) * 4));
     w->kcount = static_cast<int*>(take((E + 1) * (size_t)((c.d_model + 15) / 16) * 4));
+    w->fbar = static_cast<int*>(take((size_t)kFusedBarrierInts * 4));
     w->ticket_bytes = off;
     // integer routing tables
     w->sel = static_cast<int*>(take(Tm * k * 4));
@@ -294,6 +296,7 @@ flint_status forward_impl(flint_moe* h, int32_t T, const void* hidden, const flo
     a.residual = residual;
     a.out = out;
 
+    Timer whole(h, FLINT_KERNEL_FORWARD, stream);  // records only when that id is profiled
     const bool mfma_ok = prefill_ok(a.dm);
     bool prefill = false;
     if (c.flags & FLINT_FORCE_PREFILL_PATH) {
@@ -343,6 +346,18 @@ flint_status forward_impl(flint_moe* h, int32_t T, const void* hidden, const flo
         if (e != hipSuccess) return hip_fail(e, "combine kernel");
         h->last_T = T;
         return ok();
+    }
+    if (!(c.flags & FLINT_UNFUSED_DECODE)) {
+        const int G = fused_decode_grid(a.dm, h->n_cu);
+        if (G > 0) {
+            {
+                Timer tm(h, FLINT_KERNEL_FUSED, stream);
+                e = launch_decode_fused(a, h->ws, G, stream);
+            }
+            if (e != hipSuccess) return hip_fail(e, "single-launch decode kernel");
+            h->last_T = T;
+            return ok();
+        }
     }
     {
         Timer tm(h, FLINT_KERNEL_ROUTE, stream);

@@ -537,32 +537,6 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(RouteMfmaParams p) {
 // in flight (a block per 16 experts would be bound by one CU's miss queue),
 // and spreading the selection over token tiles keeps it off one CU.
 // ---------------------------------------------------------------------------
-// Maximum over the 64 lanes: quad swaps, half-row and row mirrors reduce
-// each row of 16 lanes, the row broadcasts carry the result to lane 63, and
-// it is read back as a wave-uniform value.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#define FLINT_DPP_MAX(ctrl, rmask) \
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, ctrl, rmask, 0xF, false))
-    FLINT_DPP_MAX(0xB1, 0xF);   // quad_perm [1,0,3,2]
-    FLINT_DPP_MAX(0x4E, 0xF);   // quad_perm [2,3,0,1]
-    FLINT_DPP_MAX(0x141, 0xF);  // row_half_mirror
-    FLINT_DPP_MAX(0x140, 0xF);  // row_mirror
-    FLINT_DPP_MAX(0x142, 0xA);  // row_bcast:15 into rows 1 and 3
-    FLINT_DPP_MAX(0x143, 0xC);  // row_bcast:31 into rows 2 and 3
-#undef FLINT_DPP_MAX
-    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
-// Order-preserving map of a float to an unsigned key (-0 taken as +0); key 0
-// marks an expert that can no longer be chosen.
-__device__ __forceinline__ uint32_t order_key(float f) {
-    const uint32_t u = __float_as_uint(f + 0.0f);
-    return (u >> 31) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float key_value(uint32_t key) {
-    return __uint_as_float((key >> 31) ? (key & 0x7FFFFFFFu) : ~key);
-}
-
 // Top-k of U tokens by one wavefront (tokens t0 + wave + 8 u), rounds interleaved
 // across the tokens.  Lane l holds the keys of experts 4 l .. 4 l + 3.  Each
 // round takes the wave maximum key; the lowest lane holding it, and inside

@@ -27,7 +27,9 @@ FLINT_ERR_OUT_OF_MEMORY, FLINT_ERR_NO_DEVICE, FLINT_ERR_HIP = 3, 4, 5
 FLINT_F32, FLINT_BF16, FLINT_NVFP4 = 0, 1, 2
 FLINT_FORCE_DECODE_PATH, FLINT_FORCE_PREFILL_PATH = 0x1, 0x2
 FLINT_DEBUG_POISON_WORKSPACE = 0x4
-KERNEL_ROUTE, KERNEL_SORT, KERNEL_EXPERT_UP, KERNEL_EXPERT_DOWN, KERNEL_COMBINE = range(5)
+FLINT_UNFUSED_DECODE = 0x8
+(KERNEL_ROUTE, KERNEL_SORT, KERNEL_EXPERT_UP, KERNEL_EXPERT_DOWN, KERNEL_COMBINE, KERNEL_FUSED,
+ KERNEL_FORWARD) = range(7)
 
 EXPORTED = [
     "flint_moe_create", "flint_moe_forward", "flint_moe_get_routing", "flint_moe_profile_begin",

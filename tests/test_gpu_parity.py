@@ -481,3 +481,84 @@ def test_wide_shared_expert_splits_k(T):
 def test_wide_nvfp4_shared_expert_splits_k(T):
     # an NVFP4 shared expert twice as wide as one K chunk of the NVFP4 down kernel
     _case(4, T, d=512, E=64, f=512, fs=4096)
+
+
+# ------------------------------------------------------- single-launch decode
+
+FUSED_SHAPES = [
+    dict(d=256, E=64, f=128, fs=256),
+    dict(d=512, E=100, k=8, f=256, fs=128),   # odd expert count, k = 8
+    dict(d=256, E=32, f=128, fs=0),           # no shared expert
+    dict(d=1024, E=128, f=256, fs=512),       # shared expert wider than a routed one
+]
+
+
+@pytest.mark.parametrize("T", [1, 2, 5, 8])
+@pytest.mark.parametrize("over", FUSED_SHAPES, ids=["d256", "E100k8", "noshared", "d1024"])
+def test_single_launch_decode(T, over):
+    # small bf16 batches run as one launch (the timing hook sees exactly one
+    # launch of it); the result meets the oracle, and the routing equals that of
+    # the separate route / gate-up / down launches
+    from sparse_moe_transformer_gemv_amd import FLINT_UNFUSED_DECODE, KERNEL_FUSED
+    over = dict(over)
+    no_shared = over.get("fs") == 0
+    if no_shared:
+        over["fs"] = 32
+    L = synth.layer(1, **over)
+    c = L["cfg"]
+    if no_shared:
+        L["shared"] = None
+        c = dict(c, fs=0)
+        L["cfg"] = c
+    x = synth.hidden(1, T, c["d"], c["act"], draw=T)
+    D = dev_layer(L)
+    ref = oracle.moe_forward(x, L["router_w"], L["experts"], L["shared"], top_k=c["k"],
+                             wdtype=synth.BF16)
+    fused = make_layer_obj(c, 16)
+    rep, rout = check_layer(fused, D, x, ref, c)
+    check_permutation(rout, T, c["k"], c["E"])
+    fused.profile_begin(KERNEL_FUSED, 4)
+    run_gpu(fused, D, x, routing=False)
+    assert len(fused.profile_end()) == 1, "the single-launch decode kernel did not run"
+    sep = make_layer_obj(c, 16, FLINT_UNFUSED_DECODE)
+    rep2, rout2 = check_layer(sep, D, x, ref, c)
+    assert all(set(a) == set(b) for a, b in zip(rout["idx"], rout2["idx"]))
+    print("single launch T=%d %s: %s | separate launches: %s" % (T, over, rep, rep2), flush=True)
+
+
+def test_single_launch_decode_back_to_back_and_graph():
+    # consecutive launches (barrier counters and work queues reset themselves),
+    # changing batch sizes (T = 16 runs as separate launches on the same
+    # handle), and replay from a HIP graph
+    L = synth.layer(1, d=256, E=64, f=128, fs=256)
+    c = L["cfg"]
+    D = dev_layer(L)
+    layer = make_layer_obj(c, 16)
+    for i, T in enumerate([3, 16, 1, 16, 7, 7, 2]):
+        x = synth.hidden(1, T, c["d"], c["act"], draw=40 + i)
+        out, rout = run_gpu(layer, D, x, residual=torch.zeros((T, c["d"]), device="cuda"))
+        compare(out, rout, run_oracle(L, x), c["k"], c["wdtype"])
+    T = 5
+    xs = [x_device(synth.hidden(1, T, c["d"], c["act"], draw=60 + i)) for i in range(2)]
+    fwd = lambda x, out=None: layer.forward(x, D["router_w"], D["experts"], D["shared"], out=out)
+    ref = [out_host(fwd(x)) for x in xs]
+    torch.cuda.synchronize()
+    x_static = xs[0].clone()
+    out_static = torch.empty_like(fwd(x_static))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fwd(x_static, out_static)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fwd(x_static, out_static)
+    for rep in range(6):
+        i = rep % 2
+        x_static.copy_(xs[i])
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out_host(out_static), ref[i]), "replay %d differs" % rep
+        fwd(xs[1 - i])
+        torch.cuda.synchronize()
