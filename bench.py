@@ -1,24 +1,40 @@
 #!/usr/bin/env python3
 """Benchmark of the Flint routed-expert MoE layer on one MI355X.
 
-    python bench.py [--workload decode|fp4|prefill|stack|tiny|dense] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload all|decode|prefill|stack|nvfp4|tiny|dense]
 
-Prints ONE JSON line.  A step is one forward of the whole layer (router +
-top-k + permutation + experts + combine) over one batch of seeded synthetic
-tokens, with inputs already resident in HBM.  Decode steps rotate through
-several independently seeded layers (and a pool of token batches), as
-consecutive layers of the model would, so no weight byte is served from the
-256 MB last-level cache left warm by the previous step.
+Prints ONE JSON line.  A step is one forward of the whole layer (router, top-k,
+permutation, experts, combine) over one batch of seeded synthetic tokens, with
+every input already resident in HBM; for the 47-layer stack a step is the
+whole pass.  The headline (`value`) is the bf16 decode layer at T = 64 tokens;
+the line also carries every workload of the five configurations under
+`workloads`:
+  tiny     fp32 layer, d = 128, f = 32, T = 64 (correctness scale)
+  decode   bf16 layer, d = 2048, 256 experts, top-6 + shared, f = 512, T = 1, 4, 16, 64
+  prefill  the same layer at T = 4096 with the Zipf router bias
+  stack    47 such layers (76 GB resident), pre-RMSNorm and fp32 residual, T = 32
+  nvfp4    the layer with NVFP4 expert weights, T = 1, 16
+Decode steps rotate through several independently seeded layers and 16 token
+batches, as consecutive layers of a model would, so weights come from HBM and
+not from the 256 MB last-level cache.  The stack's pass is one HIP graph,
+replayed once per step.
 
-Besides the driver's fields the line carries:
-  roofline      the dominant kernel's algorithmic bytes (or flops) per launch
-                over its average duration, timed with HIP events on the
-                forward's stream inside the timed region, against the MI355X
-                peak; `traffic` is the HBM bytes per launch measured with
-                rocprofv3 counters (profiles/*_traffic.json) when those were
-                taken on the current kernel source, else null
-  cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload
-  t_sweep       every token count of the workload (decode/fp4)
+Per workload and token count:
+  us          mean = the timed region (K eager steps between two HIP events) / K;
+              median, min, p90 of the per-forward times (events the library
+              records before a forward's first launch and after its last, on
+              its stream) over K more steps; the stack: per replayed pass
+  layer_frac  algorithmic bytes (decode) or bf16 flops (prefill) of the whole
+              layer per step over the step time, against the HBM (8 TB/s) or
+              dense bf16 MFMA (2.5 PFLOP/s) peak
+  roofline    the dominant kernel: its algorithmic bytes (or flops) per launch
+              over its mean launch time, timed with HIP events on the forward's
+              stream over K eager steps after the timed region; `traffic` is
+              its HBM bytes per
+              launch from rocprofv3 counters (profiles/*_traffic.json) when
+              they were taken on the current kernel source, else null
+  cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload,
+              with the thread count and CPU model
 """
 from __future__ import annotations
 
@@ -32,35 +48,26 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
-# logical dominant kernel (gate/up + SwiGLU of the chosen path) -> its source
-KERNEL_SRC = {
-    "gateup_decode": "sparse_moe_transformer_gemv_amd/csrc/expert_decode.hip",
-    "gateup_prefill": "sparse_moe_transformer_gemv_amd/csrc/expert_prefill.hip",
-}
-
-WORKLOADS = {
-    # name: (config id, token counts (last = headline), distinct layers to rotate)
-    "decode": (1, (1, 4, 16, 64), 8),
-    "fp4": (4, (1, 16), 8),
-    "prefill": (2, (4096,), 2),
-    "stack": (3, (32,), 47),
-    "tiny": (0, (64,), 1),
-    # dense SwiGLU FFN (the model's first layers), width DENSE_F, on the same engine
-    "dense": (1, (32, 4096), 2),
-}
-DENSE_F = 16384  # about 0.1B parameters per dense layer at d = 2048
+METRIC = "MoE-layer tokens/s; % peak HBM BW (decode), % MFMA peak (prefill)"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+CSRC = "sparse_moe_transformer_gemv_amd/csrc/"
+# dominant kernel -> the source it is built from (for the counter-traffic sha)
+KERNEL_SRC = {"gateup_decode": CSRC + "expert_decode.hip", "decode_fused": CSRC + "expert_decode.hip",
+              "gateup_prefill": CSRC + "expert_prefill.hip"}
+DENSE_F = 16384  # width of the dense SwiGLU layer workload (about 0.1B parameters at d = 2048)
+ALL = ("decode", "prefill", "stack", "nvfp4", "tiny")
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="all", choices=("all",) + ALL + ("dense",))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU time of the headline oracle sample (the other workloads get half)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for HBM counters)")
     return ap.parse_args()
@@ -75,25 +82,119 @@ def file_sha(path):
         return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
+def cpu_info():
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    return model, threads
+
+
 def expert_bytes(c, F, parts=("gate_up", "down")):
-    d = c["d"]
-    per = 0
+    d, per = c["d"], 0
     for part in parts:
         n = 2 * F * d if part == "gate_up" else d * F
-        if c["wdtype"] == 2:   # NVFP4: codes + E4M3 scales (+ 2 tensor scales, ignored)
+        if c["wdtype"] == 2:   # NVFP4: codes + E4M3 scales (tensor scales: 12 B, ignored)
             per += n // 2 + n // 16
         else:
             per += n * (4 if c["wdtype"] == 0 else 2)
     return per
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
-        sys.exit(2)
+def layer_bytes(c, T, distinct, out_bytes=None):
+    """Bytes the layer must move: active experts (+ shared), router, x, out."""
+    act = 4 if c["act"] == 0 else 2
+    return (distinct * expert_bytes(c, c["f"]) + expert_bytes(c, c["fs"]) + c["E"] * c["d"] * 4 +
+            T * c["d"] * act + T * c["d"] * (out_bytes or act))
 
+
+def gateup_bytes(c, T, distinct):
+    """Dominant decode kernel: active gate/up weights, x, and h (fp32 values)."""
+    act = 4 if c["act"] == 0 else 2
+    return (distinct * expert_bytes(c, c["f"], ("gate_up",)) + expert_bytes(c, c["fs"], ("gate_up",)) +
+            T * c["d"] * act + (c["k"] * T * c["f"] + T * c["fs"]) * 4)
+
+
+def layer_flops(c, T):
+    return 2.0 * (c["k"] * T * c["f"] + T * c["fs"]) * c["d"] * 3
+
+
+def step_stats(per_ms, total_ms, steps):
+    import numpy as np
+    a = np.asarray(per_ms) * 1e3
+    return {"mean": round(total_ms * 1e3 / steps, 2), "median": round(float(np.median(a)), 2),
+            "min": round(float(a.min()), 2), "p90": round(float(np.percentile(a, 90)), 2)}
+
+
+def timed_steps(fn, steps, warmup, stream, per_step=True):
+    """W untimed steps, then K steps between two HIP events (and, with per_step,
+    an event after each), synchronised before and after; returns (total ms,
+    per-step ms or None)."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1 if per_step else 2)]
+    ev[0].record(stream)
+    for i in range(steps):
+        fn(i)
+        if per_step:
+            ev[i + 1].record(stream)
+    if not per_step:
+        ev[1].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)] if per_step else None
+    return ev[0].elapsed_time(ev[-1]), per
+
+
+def traffic_for(kname, workload, T):
+    path = os.path.join(ROOT, "profiles", "%s_%s_T%d_traffic.json" % (kname, workload, T))
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        tr = json.load(fh)
+    return tr.get("bytes_per_launch") if tr.get("source_sha") == file_sha(KERNEL_SRC[kname]) else None
+
+
+def hbm_roofline(kname, nbytes, us, traffic):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kname,
+            "bytes_per_launch": int(nbytes), "us_per_launch": round(us, 2)}
+
+
+def mfma_roofline(kname, flops, us, traffic):
+    tf = flops / (us * 1e-6) / 1e12
+    return {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": traffic, "kernel": kname,
+            "flops_per_launch": flops, "us_per_launch": round(us, 2)}
+
+
+def cpu_baseline(run_once, tokens_per_call, seconds, sample, scale=1.0):
+    """The oracle (as it stands) on a bounded sample: repeated calls for about
+    `seconds`; tokens/s, divided by `scale` (layers per pass for the stack)."""
+    model, threads = cpu_info()
+    n = 0
+    t0 = time.time()
+    while True:
+        run_once()
+        n += 1
+        if time.time() - t0 >= seconds:
+            break
+    dt = time.time() - t0
+    return {"value": round(n * tokens_per_call / dt / scale, 3), "unit": "tokens/s", "cores": threads,
+            "cpu_model": model, "kind": "oracle", "sample": sample % n}
+
+
+# ----------------------------------------------------------------- workloads
+
+def run_layer_workload(name, cfg_id, Ts, n_layers, args, cpu_seconds):
+    """One forward of one layer per step (decode, nvfp4, tiny, prefill)."""
     import numpy as np
     import torch
 
@@ -101,258 +202,96 @@ def main():
     from synth.device import dev_layer, make_layer_obj, x_device
     import sparse_moe_transformer_gemv_amd as fm
 
-    torch.cuda.set_device(0)
-    cfg_id, Ts, n_layers = WORKLOADS[args.workload]
     c = dict(synth.CONFIGS[cfg_id])
-    if args.workload == "stack":
-        return bench_stack(args, c, cfg_id, Ts[0], n_layers)
-    if args.workload == "dense":
-        return bench_dense(args, c, cfg_id, Ts, n_layers)
-    Tmax = max(Ts)
-
     t0 = time.time()
-    layers = []
-    host0 = None
+    layers, host0 = [], None
     for l in range(n_layers):
         L = synth.layer(cfg_id, l)
         layers.append(dev_layer(L))
         if l == 0:
             host0 = L
-        else:
-            del L
-    log("generated %d layer(s) in %.1fs" % (n_layers, time.time() - t0))
-    n_x = 16
-    xs = {T: [x_device(synth.hidden(cfg_id, T, c["d"], c["act"], draw=i)) for i in range(n_x)]
-          for T in Ts}
+    log("%s: generated %d layer(s) in %.1fs" % (name, n_layers, time.time() - t0))
+    Tmax = max(Ts)
+    n_x = 16 if Tmax <= 64 else 2
     moe = make_layer_obj(c, Tmax)
     stream = torch.cuda.current_stream()
-
-    def forward(T, i):
-        D = layers[i % n_layers]
-        return moe.forward(xs[T][i % n_x], D["router_w"], D["experts"], D["shared"],
-                           D["router_bias"])
-
-    def distinct_experts(T, i):
-        forward(T, i)
-        cnt = moe.routing()["counts"]
-        return int((cnt > 0).sum().item())
-
-    results = {}
+    prefill = name == "prefill"
+    sweep = {}
     for T in Ts:
-        steps, warm = args.steps, args.warmup
-        nd = [distinct_experts(T, i) for i in range(steps)]
-        for i in range(warm):
-            forward(T, i)
-        torch.cuda.synchronize()
-        dominant = fm.KERNEL_EXPERT_UP
-        moe.profile_begin(dominant, steps)
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        ev0.record(stream)
-        for i in range(steps):
-            forward(T, i)
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        ms = ev0.elapsed_time(ev1) / steps
-        kms = moe.profile_end()
-        f, fs, d, k = c["f"], c["fs"], c["d"], c["k"]
-        act_b = 4 if c["act"] == 0 else 2
-        up_flops = 2.0 * (k * T * f + T * fs) * d * 2
-        # whole-layer algorithmic bytes: active expert weights + router + x + out
-        layer_bytes = [(n * expert_bytes(c, f) + expert_bytes(c, fs)) + c["E"] * d * 4 +
-                       2 * T * d * act_b for n in nd]
-        # dominant kernel (gate/up + SwiGLU): active gate/up weights + x + h out (fp32)
-        up_bytes = [n * expert_bytes(c, f, ("gate_up",)) + expert_bytes(c, fs, ("gate_up",)) +
-                    T * d * act_b + (k * T * f + T * fs) * 4 for n in nd]
-        results[T] = dict(
-            ms=ms, tok_s=T / (ms * 1e-3),
-            hbm_frac=float(np.mean(layer_bytes)) / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
-            distinct=float(np.mean(nd)), layer_bytes=float(np.mean(layer_bytes)),
-            up_us=float(np.mean(kms)) * 1e3, up_bytes=float(np.mean(up_bytes)),
-            layer_flops=2.0 * (k * T * f + T * fs) * d * 3, up_flops=up_flops)
-        results[T]["mfma_frac"] = results[T]["layer_flops"] / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)
-        log("T=%d: %.1f us/step, %.0f tok/s, %.1f%% HBM / %.1f%% MFMA (layer), dominant %.1f us" % (
-            T, ms * 1e3, results[T]["tok_s"], 100 * results[T]["hbm_frac"],
-            100 * results[T]["mfma_frac"], results[T]["up_us"]))
+        xs = [x_device(synth.hidden(cfg_id, T, c["d"], c["act"], draw=i)) for i in range(n_x)]
 
-    if args.copy_calibration:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        log("copy calibration: 1 GiB device-to-device copy done")
+        def fwd(i, xs=xs):
+            D = layers[i % n_layers]
+            return moe.forward(xs[i % n_x], D["router_w"], D["experts"], D["shared"], D["router_bias"])
 
-    H = results[Tmax]
-    prefill = args.workload == "prefill"
-    kname = "gateup_prefill" if prefill else "gateup_decode"
-    traffic = None
-    tpath = os.path.join(ROOT, "profiles", "%s_%s_T%d_traffic.json" % (kname, args.workload, Tmax))
-    if os.path.exists(tpath):
-        with open(tpath) as fh:
-            tr = json.load(fh)
-        if tr.get("source_sha") == file_sha(KERNEL_SRC[kname]):
-            traffic = tr.get("bytes_per_launch")
-    if prefill:
-        achieved = H["up_flops"] / (H["up_us"] * 1e-6) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                    "traffic": traffic, "kernel": kname, "flops_per_launch": H["up_flops"],
-                    "us_per_launch": round(H["up_us"], 2)}
-    else:
-        achieved = H["up_bytes"] / (H["up_us"] * 1e-6) / 1e9
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                    "kernel": kname, "bytes_per_launch": int(H["up_bytes"]),
-                    "us_per_launch": round(H["up_us"], 2)}
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-        x0 = synth.hidden(cfg_id, Tmax, c["d"], c["act"], draw=0)
-        # bounded sample: batches of up to 64 tokens of the same workload
-        sample = x0[:64]
-        ntok = 0
-        t1 = time.time()
-        while True:
-            oracle.moe_forward(sample, host0["router_w"], host0["experts"], host0["shared"],
-                               top_k=c["k"], router_bias=host0["router_bias"],
-                               wdtype=c["wdtype"])
-            ntok += sample.shape[0]
-            if time.time() - t1 >= args.cpu_seconds:
-                break
-        dt = time.time() - t1
-        cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
-        cpu = {"value": round(ntok / dt, 2), "unit": "tokens/s", "cores": cores,
-               "kind": "oracle",
-               "sample": "%d forwards of the first %d tokens of the same batch, layer 0, fp64" % (
-                   ntok // sample.shape[0], sample.shape[0])}
-
-    line = {
-        "metric": "MoE-layer tokens/s",
-        "value": round(H["tok_s"], 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(H["ms"], 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": {0: "f32", 1: "bf16", 2: "nvfp4"}[c["wdtype"]],
-        "data": "synthetic",
-        "config": {"workload": "%s T=%d (d=%d, E=%d, top-%d + shared, f=%d)" % (
-            c["name"], Tmax, c["d"], c["E"], c["k"], c["f"]), "tokens": Tmax,
-            "layers_rotated": n_layers, "hbm_frac_layer": round(H["hbm_frac"], 4),
-            "mfma_frac_layer": round(H["mfma_frac"], 4), "distinct_experts": H["distinct"]},
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-        "t_sweep": {str(T): {"tok_s": round(r["tok_s"], 1), "us": round(r["ms"] * 1e3, 2),
-                             "hbm_frac_layer": round(r["hbm_frac"], 4),
-                             "mfma_frac_layer": round(r["mfma_frac"], 4),
-                             "dominant_us": round(r["up_us"], 2),
-                             "distinct_experts": r["distinct"]} for T, r in results.items()},
-    }
-    print(json.dumps(line), flush=True)
-
-
-def bench_dense(args, c, cfg_id, Ts, n_layers):
-    """Dense SwiGLU FFN of width DENSE_F: out = D (SiLU(G x) * (U x)) for T tokens."""
-    import numpy as np
-    import torch
-
-    import synth
-    from synth.device import dev_weights, x_device
-    import sparse_moe_transformer_gemv_amd as fm
-
-    d, F, wd = c["d"], DENSE_F, c["wdtype"]
-    t0 = time.time()
-    hosts = [synth.expert_set(cfg_id, l, 1, d, F, wd) for l in range(n_layers)]
-    ws = [dev_weights(h, wd) for h in hosts]
-    log("generated %d dense layer(s) of width %d in %.1fs" % (n_layers, F, time.time() - t0))
-    Tmax = max(Ts)
-    ffn = fm.DenseFFN(d, F, c["act"], wd, max_tokens=Tmax)
-    stream = torch.cuda.current_stream()
-    n_x = 4
-    results = {}
-    for T in Ts:
-        xs = [x_device(synth.hidden(cfg_id, T, d, c["act"], draw=i)) for i in range(n_x)]
-        for i in range(args.warmup):
-            ffn.forward(xs[i % n_x], ws[i % n_layers])
-        torch.cuda.synchronize()
-        ffn.layer.profile_begin(fm.KERNEL_EXPERT_UP, args.steps)
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
+        # distinct experts each timed step selects (read back outside the timed region)
+        nd = []
         for i in range(args.steps):
-            ffn.forward(xs[i % n_x], ws[i % n_layers])
-        ev1.record(stream)
+            fwd(i)
+            nd.append(int((moe.routing()["counts"] > 0).sum().item()))
+        # the dominant kernel: the single-launch decode where it runs, else gate/up
+        moe.profile_begin(fm.KERNEL_FUSED, 1)
+        fwd(0)
+        fused = len(moe.profile_end()) == 1
+        # timed region: K eager steps between two events (per-step events would
+        # make the host's launch loop, not the GPU, the limit at small T)
+        total, _ = timed_steps(fwd, args.steps, args.warmup, stream, per_step=False)
+        ms = total / args.steps
+        # per-forward times (first launch to last, events recorded by the library
+        # on the forward's stream) and the dominant kernel's launches, each over
+        # K more eager steps
+        moe.profile_begin(fm.KERNEL_FORWARD, args.steps)
+        for i in range(args.steps):
+            fwd(i)
         torch.cuda.synchronize()
-        ms = ev0.elapsed_time(ev1) / args.steps
-        up_us = float(np.mean(ffn.layer.profile_end())) * 1e3
-        w_bytes = 3.0 * F * d * 2
-        up_flops = 2.0 * T * 2 * F * d
-        results[T] = dict(ms=ms, tok_s=T / (ms * 1e-3), up_us=up_us, up_flops=up_flops,
-                          up_bytes=2.0 * F * d * 2 + T * d * 2 + T * F * 4,
-                          hbm_frac=(w_bytes + 2 * T * d * 2) / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
-                          mfma_frac=3 * up_flops / 2 / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12))
-        log("T=%d: %.1f us/step, %.0f tok/s, %.1f%% HBM / %.1f%% MFMA (layer), gate/up %.1f us" % (
-            T, ms * 1e3, results[T]["tok_s"], 100 * results[T]["hbm_frac"],
-            100 * results[T]["mfma_frac"], up_us))
-    if args.copy_calibration:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        b = torch.empty_like(a)
-        b.copy_(a)
+        per = moe.profile_end()
+        moe.profile_begin(fm.KERNEL_FUSED if fused else fm.KERNEL_EXPERT_UP, args.steps)
+        for i in range(args.steps):
+            fwd(i)
         torch.cuda.synchronize()
-        log("copy calibration: 1 GiB device-to-device copy done")
-    H = results[Tmax]
-    traffic = None
-    tpath = os.path.join(ROOT, "profiles", "gateup_prefill_dense_T%d_traffic.json" % Tmax)
-    if os.path.exists(tpath):
-        with open(tpath) as fh:
-            tr = json.load(fh)
-        if tr.get("source_sha") == file_sha(KERNEL_SRC["gateup_prefill"]):
-            traffic = tr.get("bytes_per_launch")
-    achieved = H["up_flops"] / (H["up_us"] * 1e-6) / 1e12
-    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
-                "kernel": "gateup_prefill", "flops_per_launch": H["up_flops"],
-                "us_per_launch": round(H["up_us"], 2)}
-    cpu = None
+        kus = float(np.mean(moe.profile_end())) * 1e3
+        lb = float(np.mean([layer_bytes(c, T, n) for n in nd]))
+        rec = {"tok_s": round(T / (ms * 1e-3), 1), "us": step_stats(per, total, args.steps),
+               "distinct_experts": float(np.mean(nd))}
+        if prefill:
+            fl = layer_flops(c, T)
+            rec["layer_frac"] = {"bound": "mfma", "frac": round(fl / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
+                                 "flops": fl}
+            upf = 2.0 * (c["k"] * T * c["f"] + T * c["fs"]) * c["d"] * 2
+            rec["roofline"] = mfma_roofline("gateup_prefill", upf, kus, traffic_for("gateup_prefill", name, T))
+        else:
+            rec["layer_frac"] = {"bound": "hbm", "frac": round(lb / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                                 "bytes": int(lb)}
+            if fused:
+                rec["roofline"] = hbm_roofline("decode_fused", lb, kus, traffic_for("decode_fused", name, T))
+            else:
+                gb = float(np.mean([gateup_bytes(c, T, n) for n in nd]))
+                rec["roofline"] = hbm_roofline("gateup_decode", gb, kus, traffic_for("gateup_decode", name, T))
+        sweep[T] = rec
+        log("%s T=%d: %.1f us/step (median %.1f, p90 %.1f), %.0f tok/s, layer %.1f%% of %s peak, %s %.1f us" % (
+            name, T, ms * 1e3, rec["us"]["median"], rec["us"]["p90"], rec["tok_s"],
+            100 * rec["layer_frac"]["frac"], rec["layer_frac"]["bound"], rec["roofline"]["kernel"], kus))
+    out = {"config": "%s (d=%d, E=%d, top-%d + shared, f=%d, %s weights%s)" % (
+        c["name"], c["d"], c["E"], c["k"], c["f"], {0: "fp32", 1: "bf16", 2: "NVFP4"}[c["wdtype"]],
+        ", Zipf router bias" if c["bias"] else ""), "layers_rotated": n_layers,
+        "t_sweep": {str(T): r for T, r in sweep.items()}}
     if not args.no_cpu_baseline:
         import oracle
-        sample = synth.hidden(cfg_id, 2, d, c["act"], draw=0)
-        ntok = 0
-        t1 = time.time()
-        while True:
-            oracle.ffn_forward(sample, hosts[0], wdtype=wd)
-            ntok += sample.shape[0]
-            if time.time() - t1 >= args.cpu_seconds:
-                break
-        dt = time.time() - t1
-        cpu = {"value": round(ntok / dt, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": "%d forwards of 2 tokens, layer 0, fp64" % (ntok // 2)}
-    line = {
-        "metric": "dense-FFN tokens/s", "value": round(H["tok_s"], 1), "unit": "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(H["ms"], 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": {0: "f32", 1: "bf16", 2: "nvfp4"}[wd], "data": "synthetic",
-        "config": {"workload": "dense SwiGLU FFN T=%d (d=%d, f=%d)" % (Tmax, d, F), "tokens": Tmax,
-                   "layers_rotated": n_layers, "hbm_frac_layer": round(H["hbm_frac"], 4),
-                   "mfma_frac_layer": round(H["mfma_frac"], 4)},
-        "roofline": roofline, "cpu_baseline": cpu,
-        "t_sweep": {str(T): {"tok_s": round(r["tok_s"], 1), "us": round(r["ms"] * 1e3, 2),
-                             "hbm_frac_layer": round(r["hbm_frac"], 4),
-                             "mfma_frac_layer": round(r["mfma_frac"], 4),
-                             "dominant_us": round(r["up_us"], 2)} for T, r in results.items()},
-    }
-    print(json.dumps(line), flush=True)
+        tc = min(Tmax, 64)
+        xh = synth.hidden(cfg_id, Tmax, c["d"], c["act"], draw=0)[:tc]
+        out["cpu_baseline"] = cpu_baseline(
+            lambda: oracle.moe_forward(xh, host0["router_w"], host0["experts"], host0["shared"],
+                                       top_k=c["k"], router_bias=host0["router_bias"], wdtype=c["wdtype"]),
+            tc, cpu_seconds, "%%d fp64 oracle forwards of the first %d tokens of the T=%d batch, layer 0" % (
+                tc, Tmax))
+    del layers, moe
+    torch.cuda.empty_cache()
+    return out, sweep
 
 
-def bench_stack(args, c, cfg_id, T, n_layers):
-    """47 resident layers, T tokens: h <- h + MoE_l(bf16(RMSNorm(h))) per layer.
-    One step = the whole pass (rmsnorm + layer for every layer), captured once
-    as a HIP graph and replayed."""
+def run_stack(args, cpu_seconds):
+    """47 resident layers, T = 32: h <- h + MoE_l(bf16(RMSNorm(h))) per layer; one
+    step is the whole pass, captured once as a HIP graph and replayed."""
     import numpy as np
     import torch
 
@@ -360,108 +299,166 @@ def bench_stack(args, c, cfg_id, T, n_layers):
     from synth.device import dev_array, dev_layer, make_layer_obj
     import sparse_moe_transformer_gemv_amd as fm
 
-    xbuf = torch.empty((T, c["d"]), dtype=torch.bfloat16, device="cuda")
-
-    def stack_gpu(moe, h, layers):
-        for D in layers:
-            fm.flint_rmsnorm_forward(h, 1e-6, out=xbuf)
-            moe.forward(xbuf, D["router_w"], D["experts"], D["shared"], None, residual=h, out=h)
-
+    cfg_id, T = 3, 32
+    c = dict(synth.CONFIGS[cfg_id])
+    n_layers = c["layers"]
     t0 = time.time()
-    layers, nd = [], []
-    host0 = None
+    layers, host0 = [], None
     for l in range(n_layers):
         L = synth.layer(cfg_id, l)
         layers.append(dev_layer(L))
         if l == 0:
             host0 = L
-        del L
-    log("generated %d layer(s) in %.1fs" % (n_layers, time.time() - t0))
+    log("stack: generated %d layers in %.1fs" % (n_layers, time.time() - t0))
     h0 = dev_array(synth.hidden(cfg_id, T, c["d"], synth.F32))
     h = h0.clone()
     moe = make_layer_obj(c, T)
-    # distinct experts per layer for this batch (eager pass with routing read-back)
+    xbuf = torch.empty((T, c["d"]), dtype=torch.bfloat16, device="cuda")
+
+    def one_pass(record=False):
+        nd = []
+        for D in layers:
+            fm.flint_rmsnorm_forward(h, 1e-6, out=xbuf)
+            moe.forward(xbuf, D["router_w"], D["experts"], D["shared"], None, residual=h, out=h)
+            if record:
+                nd.append(int((moe.routing()["counts"] > 0).sum().item()))
+        return nd
+
     h.copy_(h0)
-    from sparse_moe_transformer_gemv_amd import flint_rmsnorm_forward
-    x = torch.empty((T, c["d"]), dtype=torch.bfloat16, device="cuda")
-    for D in layers:
-        flint_rmsnorm_forward(h, 1e-6, out=x)
-        moe.forward(x, D["router_w"], D["experts"], D["shared"], None, residual=h, out=h)
-        nd.append(int((moe.routing()["counts"] > 0).sum().item()))
-    # dominant kernel timing: one eager pass with the event hook
+    nd = one_pass(record=True)  # distinct experts per layer (read back, untimed)
+    # the gate/up kernel time from one eager pass with the event hook
     h.copy_(h0)
     torch.cuda.synchronize()
     moe.profile_begin(fm.KERNEL_EXPERT_UP, n_layers)
-    stack_gpu(moe, h, layers)
+    one_pass()
     torch.cuda.synchronize()
-    kms = moe.profile_end()
-    # graph of one full pass
-    stream = torch.cuda.Stream()
-    stream.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(stream):
+    kus = float(np.mean(moe.profile_end())) * 1e3
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
         for _ in range(2):
             h.copy_(h0)
-            stack_gpu(moe, h, layers)
-    torch.cuda.current_stream().wait_stream(stream)
+            one_pass()
+    torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         h.copy_(h0)
-        stack_gpu(moe, h, layers)
-    for _ in range(args.warmup):
-        g.replay()
-    torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for _ in range(args.steps):
-        g.replay()
-    ev1.record()
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
-    f, fs, d, k = c["f"], c["fs"], c["d"], c["k"]
-    pass_bytes = sum(n * expert_bytes(c, f) + expert_bytes(c, fs) + c["E"] * d * 4 +
-                     T * d * (2 + 4 + 4) for n in nd)
-    up_bytes = float(np.mean([n * expert_bytes(c, f, ("gate_up",)) +
-                              expert_bytes(c, fs, ("gate_up",)) + T * d * 2 +
-                              (k * T * f + T * fs) * 4 for n in nd]))
-    up_us = float(np.mean(kms)) * 1e3
-    achieved = up_bytes / (up_us * 1e-6) / 1e9
-    log("stack: %.3f ms/pass, %.0f tok/s, %.1f%% HBM, gate/up %.1f us" % (
-        ms, T / (ms * 1e-3), 100 * pass_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), up_us))
-    cpu = None
+        one_pass()
+    total, per = timed_steps(lambda i: g.replay(), args.steps, args.warmup, torch.cuda.current_stream())
+    ms = total / args.steps
+    pass_bytes = sum(layer_bytes(c, T, n, out_bytes=4) + T * c["d"] * (4 + 2) for n in nd)
+    gb = float(np.mean([gateup_bytes(c, T, n) for n in nd]))
+    rec = {"config": "%d x (RMSNorm + MoE layer + fp32 residual), graph-replayed pass (d=%d, E=%d, top-%d + "
+                     "shared, f=%d, bf16)" % (n_layers, c["d"], c["E"], c["k"], c["f"]),
+           "tokens": T, "tok_s": round(T / (ms * 1e-3), 1), "us": step_stats(per, total, args.steps),
+           "distinct_experts_per_layer": float(np.mean(nd)),
+           "layer_frac": {"bound": "hbm", "frac": round(pass_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                          "bytes": int(pass_bytes)},
+           "roofline": hbm_roofline("gateup_decode", gb, kus, traffic_for("gateup_decode", "stack", T))}
+    log("stack: %.3f ms/pass (median %.3f), %.0f tok/s, %.1f%% HBM per pass, gate/up %.1f us" % (
+        ms, rec["us"]["median"] / 1e3, rec["tok_s"], 100 * rec["layer_frac"]["frac"], kus))
     if not args.no_cpu_baseline:
         import oracle
-        # one layer's forward on the same T tokens stands for 1/47 of a pass
-        xs = synth.hidden(cfg_id, T, d, c["act"], draw=0)
-        t1 = time.time()
-        n = 0
-        while True:
-            oracle.moe_forward(xs, host0["router_w"], host0["experts"], host0["shared"],
-                               top_k=k, wdtype=c["wdtype"])
-            n += 1
-            if time.time() - t1 >= args.cpu_seconds:
-                break
-        per_layer = (time.time() - t1) / n
-        cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
-        cpu = {"value": round(T / (per_layer * n_layers), 3), "unit": "tokens/s", "cores": cores,
-               "kind": "oracle",
-               "sample": "%d single-layer forwards of T=%d (layer 0), scaled to %d layers" % (
-                   n, T, n_layers)}
+        xs = synth.hidden(cfg_id, T, c["d"], c["act"], draw=0)
+        rec["cpu_baseline"] = cpu_baseline(
+            lambda: oracle.moe_forward(xs, host0["router_w"], host0["experts"], host0["shared"], top_k=c["k"],
+                                       wdtype=c["wdtype"]),
+            T, cpu_seconds, "%%d fp64 oracle forwards of one layer at T=%d, scaled to %d layers" % (T, n_layers),
+            scale=n_layers)
+    del layers, g, moe
+    torch.cuda.empty_cache()
+    return rec
+
+
+def run_dense(args, cpu_seconds):
+    """Dense SwiGLU FFN of width DENSE_F (the model's dense layers), T = 32 and 4096."""
+    import numpy as np
+    import torch
+
+    import synth
+    from synth.device import dev_weights, x_device
+    import sparse_moe_transformer_gemv_amd as fm
+
+    cfg_id = 1
+    c = dict(synth.CONFIGS[cfg_id])
+    d, F, wd = c["d"], DENSE_F, c["wdtype"]
+    hosts = [synth.expert_set(cfg_id, l, 1, d, F, wd) for l in range(2)]
+    ws = [dev_weights(h_, wd) for h_ in hosts]
+    Ts = (32, 4096)
+    ffn = fm.DenseFFN(d, F, c["act"], wd, max_tokens=max(Ts))
+    stream = torch.cuda.current_stream()
+    sweep = {}
+    for T in Ts:
+        xs = [x_device(synth.hidden(cfg_id, T, d, c["act"], draw=i)) for i in range(4)]
+        ffn.layer.profile_begin(fm.KERNEL_EXPERT_UP, args.steps)
+        total, per = timed_steps(lambda i: ffn.forward(xs[i % 4], ws[i % 2]), args.steps, args.warmup, stream)
+        kus = float(np.mean(ffn.layer.profile_end())) * 1e3
+        ms = total / args.steps
+        fl = 2.0 * T * 3 * F * d
+        wb = 3.0 * F * d * 2 + 2 * T * d * 2
+        rec = {"tok_s": round(T / (ms * 1e-3), 1), "us": step_stats(per, total, args.steps),
+               "layer_frac": {"hbm": round(wb / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                              "mfma": round(fl / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4)}}
+        if T > 64:
+            rec["roofline"] = mfma_roofline("gateup_prefill", 2.0 * T * 2 * F * d, kus,
+                                            traffic_for("gateup_prefill", "dense", T))
+        else:
+            rec["roofline"] = hbm_roofline("gateup_decode", 2.0 * F * d * 2 + T * d * 2 + T * F * 4, kus, None)
+        sweep[str(T)] = rec
+        log("dense T=%d: %.1f us/step, %.0f tok/s" % (T, ms * 1e3, rec["tok_s"]))
+    out = {"config": "dense SwiGLU FFN (d=%d, f=%d, bf16)" % (d, F), "t_sweep": sweep}
+    if not args.no_cpu_baseline:
+        import oracle
+        xh = synth.hidden(cfg_id, 2, d, c["act"], draw=0)
+        out["cpu_baseline"] = cpu_baseline(lambda: oracle.ffn_forward(xh, hosts[0], wdtype=wd), 2,
+                                           cpu_seconds, "%d fp64 oracle forwards of 2 tokens")
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    torch.cuda.set_device(0)
+    half = args.cpu_seconds / 2
+    todo = ALL if args.workload == "all" else (args.workload,)
+    work, headline = {}, None
+    t_start = time.time()
+    for name in todo:
+        if name == "stack":
+            rec = run_stack(args, half)
+            cand = ("stack", 32, rec, rec)
+        elif name == "dense":
+            rec = run_dense(args, half)
+            cand = ("dense", 4096, rec["t_sweep"]["4096"], rec)
+        else:
+            cfg_id, Ts, n_layers = {"decode": (1, (1, 4, 16, 64), 8), "nvfp4": (4, (1, 16), 8),
+                                    "tiny": (0, (64,), 1), "prefill": (2, (4096,), 2)}[name]
+            rec, sweep = run_layer_workload(name, cfg_id, Ts, n_layers, args,
+                                            args.cpu_seconds if name == "decode" else half)
+            cand = (name, max(Ts), sweep[max(Ts)], rec)
+        work[name] = rec
+        if headline is None or name == "decode":
+            headline = cand
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy calibration: 1 GiB device-to-device copy done")
+    wname, T, H, R = headline
     line = {
-        "metric": "MoE-layer tokens/s", "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "%s: %d layers x (RMSNorm + MoE + residual), T=%d" % (
-            c["name"], n_layers, T), "tokens": T, "layers": n_layers,
-            "hbm_frac_pass": round(pass_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
-            "pass_bytes": int(pass_bytes), "graph": True},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "gateup_decode", "bytes_per_launch": int(up_bytes),
-                     "us_per_launch": round(up_us, 2)},
-        "cpu_baseline": cpu,
+        "metric": METRIC, "value": H["tok_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(H["us"]["mean"] / 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "nvfp4" if wname == "nvfp4" else "bf16",
+        "data": "synthetic", "config": {"workload": "%s T=%d: %s" % (wname, T, R["config"]), "tokens": T},
+        "roofline": H["roofline"], "cpu_baseline": R.get("cpu_baseline"),
+        "layer_frac": H["layer_frac"], "step_us": H["us"], "workloads": work,
+        "wall_s": round(time.time() - t_start, 1),
     }
     print(json.dumps(line), flush=True)
 
