@@ -14,6 +14,7 @@ the line also carries every workload of the five configurations under
   prefill  the same layer at T = 4096 with the Zipf router bias
   stack    47 such layers (76 GB resident), pre-RMSNorm and fp32 residual, T = 32
   nvfp4    the layer with NVFP4 expert weights, T = 1, 16
+  nvfp4_prefill  the NVFP4 layer at T = 4096 with the Zipf router bias
 Decode steps rotate through several independently seeded layers and 16 token
 batches, as consecutive layers of a model would, so weights come from HBM and
 not from the 256 MB last-level cache.  The stack's pass is one HIP graph,
@@ -56,7 +57,7 @@ CSRC = "sparse_moe_transformer_gemv_amd/csrc/"
 KERNEL_SRC = {"gateup_decode": CSRC + "expert_decode.hip", "decode_fused": CSRC + "expert_decode.hip",
               "gateup_prefill": CSRC + "expert_prefill.hip"}
 DENSE_F = 16384  # width of the dense SwiGLU layer workload (about 0.1B parameters at d = 2048)
-ALL = ("decode", "prefill", "stack", "nvfp4", "tiny")
+ALL = ("decode", "prefill", "stack", "nvfp4", "tiny", "nvfp4_prefill")
 
 
 def parse():
@@ -193,7 +194,7 @@ def cpu_baseline(run_once, tokens_per_call, seconds, sample, scale=1.0):
 
 # ----------------------------------------------------------------- workloads
 
-def run_layer_workload(name, cfg_id, Ts, n_layers, args, cpu_seconds):
+def run_layer_workload(name, cfg_id, Ts, n_layers, args, cpu_seconds, **override):
     """One forward of one layer per step (decode, nvfp4, tiny, prefill)."""
     import numpy as np
     import torch
@@ -202,11 +203,11 @@ def run_layer_workload(name, cfg_id, Ts, n_layers, args, cpu_seconds):
     from synth.device import dev_layer, make_layer_obj, x_device
     import sparse_moe_transformer_gemv_amd as fm
 
-    c = dict(synth.CONFIGS[cfg_id])
+    c = dict(synth.CONFIGS[cfg_id], **override)
     t0 = time.time()
     layers, host0 = [], None
     for l in range(n_layers):
-        L = synth.layer(cfg_id, l)
+        L = synth.layer(cfg_id, l, **override)
         layers.append(dev_layer(L))
         if l == 0:
             host0 = L
@@ -215,7 +216,7 @@ def run_layer_workload(name, cfg_id, Ts, n_layers, args, cpu_seconds):
     n_x = 16 if Tmax <= 64 else 2
     moe = make_layer_obj(c, Tmax)
     stream = torch.cuda.current_stream()
-    prefill = name == "prefill"
+    prefill = max(Ts) > 64
     sweep = {}
     for T in Ts:
         xs = [x_device(synth.hidden(cfg_id, T, c["d"], c["act"], draw=i)) for i in range(n_x)]
@@ -272,7 +273,7 @@ def run_layer_workload(name, cfg_id, Ts, n_layers, args, cpu_seconds):
             name, T, ms * 1e3, rec["us"]["median"], rec["us"]["p90"], rec["tok_s"],
             100 * rec["layer_frac"]["frac"], rec["layer_frac"]["bound"], rec["roofline"]["kernel"], kus))
     out = {"config": "%s (d=%d, E=%d, top-%d + shared, f=%d, %s weights%s)" % (
-        c["name"], c["d"], c["E"], c["k"], c["f"], {0: "fp32", 1: "bf16", 2: "NVFP4"}[c["wdtype"]],
+        name, c["d"], c["E"], c["k"], c["f"], {0: "fp32", 1: "bf16", 2: "NVFP4"}[c["wdtype"]],
         ", Zipf router bias" if c["bias"] else ""), "layers_rotated": n_layers,
         "t_sweep": {str(T): r for T, r in sweep.items()}}
     if not args.no_cpu_baseline:
@@ -437,9 +438,11 @@ def main():
             cand = ("dense", 4096, rec["t_sweep"]["4096"], rec)
         else:
             cfg_id, Ts, n_layers = {"decode": (1, (1, 4, 16, 64), 8), "nvfp4": (4, (1, 16), 8),
-                                    "tiny": (0, (64,), 1), "prefill": (2, (4096,), 2)}[name]
+                                    "tiny": (0, (64,), 1), "prefill": (2, (4096,), 2),
+                                    "nvfp4_prefill": (4, (4096,), 2)}[name]
+            over = {"bias": True} if name == "nvfp4_prefill" else {}
             rec, sweep = run_layer_workload(name, cfg_id, Ts, n_layers, args,
-                                            args.cpu_seconds if name == "decode" else half)
+                                            args.cpu_seconds if name == "decode" else half, **over)
             cand = (name, max(Ts), sweep[max(Ts)], rec)
         work[name] = rec
         if headline is None or name == "decode":

@@ -64,7 +64,8 @@ typedef enum {
 
 /* flags of flint_moe_config */
 #define FLINT_FORCE_DECODE_PATH  0x1u  /* always use the expert-GEMV path */
-#define FLINT_FORCE_PREFILL_PATH 0x2u  /* always use the grouped-MFMA path (bf16 only) */
+#define FLINT_FORCE_PREFILL_PATH 0x2u  /* always use the grouped-MFMA path (bf16 activations;
+                                          bf16 or NVFP4 weights) */
 /* Debug: at create and before every forward, fill the floating-point part of
  * the workspace (logits, weights, partial sums, h, y) with NaN bit patterns,
  * so that a kernel reading a value that no kernel of the same forward wrote

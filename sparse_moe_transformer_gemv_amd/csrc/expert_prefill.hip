@@ -178,7 +178,7 @@ __device__ __forceinline__ int out_col(int tn, int jr) {
 // gate/up the B rows are taken in quarters of 16 NI rows: 8 NI gate rows, then
 // the 8 NI up rows of the same features (in out_col order), so wave wn's NI
 // column tiles hold matching gate (ni < NI / 2) and up (ni >= NI / 2) columns.
-template <int MODE, int NI>
+template <int MODE, int NI, int WF>
 __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned char* lds, const int4& g, int m0,
                                              int nb0) {
     constexpr int BN = 64 * NI;  // B rows of the tile
@@ -253,6 +253,74 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
         }
     }
 
+    // NVFP4 weights (WF): the B rows are dequantised in registers and written to
+    // LDS as bf16 in the layout the direct-to-LDS loads give them.  FL = 512 / BN
+    // lanes share a B row (fr), each covering FW words of 8 E2M1 codes (8 FW
+    // consecutive k of the 64 of a pair, part fh) and their E4M3 block scales.
+    constexpr int FL = kThreads / BN, FW = 8 / FL;
+    const int fr = tid / FL, fh = tid % FL;
+    __amdgpu_buffer_rsrc_t cview, sview;
+    uint32_t coff = 0, soff = 0;  // byte offsets of the lane's codes / the row's scales at k = 0
+    float ts_a = 1.f, ts_b = 1.f;  // tensor scales: gate and up (gate/up), down twice (down)
+    if constexpr (WF == DT_NVFP4) {
+        const int wb = fr / (16 * NI), tn = (fr >> 4) % NI, jr = fr & 15;
+        int wrow;
+        if (MODE == MODE_GATEUP)
+            wrow = (tn >= NI / 2 ? F : 0) + nb0 + HS * wb + out_col<NI / 2>(tn % (NI / 2), jr);
+        else
+            wrow = nb0 + 16 * NI * wb + 16 * tn + jr;
+        const size_t erows = MODE == MODE_GATEUP ? (size_t)2 * F : (size_t)d;
+        const uint8_t* codes = static_cast<const uint8_t*>(MODE == MODE_GATEUP ? wp.gu : wp.dn) + e * erows * (K / 2);
+        const uint8_t* scales = (MODE == MODE_GATEUP ? wp.gus : wp.dns) + e * erows * (K / 16);
+        cview = buffer_view(codes, (uint32_t)(erows * (K / 2)));
+        sview = buffer_view(scales, (uint32_t)(erows * (K / 16)));
+        coff = (uint32_t)(wrow * (K / 2) + 4 * FW * fh);
+        soff = (uint32_t)(wrow * (K / 16));
+        if (MODE == MODE_GATEUP) {
+            ts_a = wp.ts[e * 3 + 0];
+            ts_b = wp.ts[e * 3 + 1];
+        } else {
+            ts_a = ts_b = wp.ts[e * 3 + 2];
+        }
+    }
+    // the lane's codes (FW words) and its row's 4 scales of pair pp
+    auto fp4_load = [&](int pp, uint32_t (&cw)[FW], uint32_t& sw) {
+        if constexpr (FW == 4) {
+            const uint4 v = buffer_load16(cview, coff + 32 * pp);
+            cw[0] = v.x; cw[1] = v.y; cw[2] = v.z; cw[3] = v.w;
+        } else {
+            const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(cview, (int)(coff + 32 * pp), 0, 0));
+            cw[0] = v.x; cw[1] = v.y;
+        }
+        sw = __builtin_amdgcn_raw_buffer_load_b32(sview, (int)(soff + 4 * pp), 0, 0);
+    };
+    // E2M1 x E4M3 is exact in bf16 (at most 6 significant bits): the hardware
+    // convert applies the scale's power of two, an fp32 multiply its 3-bit
+    // significand, and the pack to bf16 rounds nothing
+    auto fp4_store = [&](int pp, const uint32_t (&cw)[FW], uint32_t sw) {
+        unsigned char* bb = lds + (pp & 1) * kPairBytes + PBM * kRowBytes;
+#pragma unroll
+        for (int i = 0; i < FW; ++i) {
+            // word i holds k = 8 (FW fh + i) .. + 7 of the pair: scale (FW fh + i) / 2
+            const int kw = FW * fh + i;
+            const float sv = __builtin_amdgcn_cvt_f32_fp8(sw >> (8 * (kw >> 1)), 0);
+            const uint32_t sb = __float_as_uint(sv);
+            const float p2 = __uint_as_float(sb & 0xFF800000u);
+            const float mt = __uint_as_float((sb & 0x007FFFFFu) | 0x3F800000u);
+            uint32_t pk[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                floatx2_t v;
+                if (b == 0) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[i], p2, 0);
+                else if (b == 1) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[i], p2, 1);
+                else if (b == 2) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[i], p2, 2);
+                else v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[i], p2, 3);
+                pk[b] = pack_bf16x2_hw(v.x * mt, v.y * mt);
+            }
+            *reinterpret_cast<uint4*>(bb + swz(fr, kw)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        }
+    };
+
     floatx4_t acc[8][NI];
 #pragma unroll
     for (int mi = 0; mi < 8; ++mi)
@@ -267,21 +335,39 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
         for (int j = 0; j < 4; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(aview, st_ + (32 * wave + 8 * j) * kRowBytes, 16, aoff[j] + kb,
                                                      0, 0, 0);
+        if constexpr (WF != DT_NVFP4) {
 #pragma unroll
-        for (int j = 0; j < NI; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(bview, st_ + PBM * kRowBytes + (BN / 8 * wave + 8 * j) * kRowBytes,
-                                                     16, boff[j] + kb, 0, 0, 0);
+            for (int j = 0; j < NI; ++j)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(bview,
+                                                         st_ + PBM * kRowBytes + (BN / 8 * wave + 8 * j) * kRowBytes,
+                                                         16, boff[j] + kb, 0, 0, 0);
+        }
     };
 
     const int np = K / (2 * PBK);  // pairs (K is a multiple of 64)
     // Buffer 0 is free: the previous tile's last pair (np is even) was in buffer 1,
     // and every wave read its pair np - 2 before that pair's barrier.
+    uint32_t cw[FW], sw = 0;
+    if constexpr (WF == DT_NVFP4) {
+        fp4_load(0, cw, sw);
+        fp4_store(0, cw, sw);
+    }
     issue(0);
+    if constexpr (WF == DT_NVFP4) {
+        if (np > 1) fp4_load(1, cw, sw);  // in flight behind pair 0's A loads
+    }
     for (int pp = 0; pp < np; ++pp) {
         // this wave's part of pair pp has landed; after the barrier every wave's has,
         // and every wave is done reading pair pp - 1, whose buffer pair pp + 1 refills
-        // while the two sub-stages of pair pp run
-        __builtin_amdgcn_s_waitcnt(0x0F70);
+        // while the two sub-stages of pair pp run.  NVFP4: the two code / scale loads
+        // of pair pp + 1 may stay in flight, and the LDS writes of pair pp's weights
+        // must be done
+        if (WF == DT_NVFP4 && pp + 1 < np)
+            __builtin_amdgcn_s_waitcnt(0x0072);  // vmcnt(2) lgkmcnt(0)
+        else if (WF == DT_NVFP4)
+            __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+        else
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         phase_barrier();
         if (pp + 1 < np) issue(pp + 1);
         const uint32_t st = lds0 + (pp & 1) * kPairBytes;
@@ -289,6 +375,12 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
         for (int h = 0; h < 2; ++h) {
             const uint32_t hx = (uint32_t)h << 6;
             uint4 fa[8], fb[NI];
+            if (WF == DT_NVFP4 && h == 1 && pp + 1 < np) {
+                // pair pp + 1's weights into the free buffer, then its successor's loads
+                fp4_store(pp + 1, cw, sw);
+                if (pp + 2 < np) fp4_load(pp + 2, cw, sw);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             if (nmi > 0) read_frags<NI>(st + (a_rd ^ hx), st + (b_rd ^ hx), fa, fb);
             // 16-row blocks past the group's end are skipped
             if (nmi == 8) {
@@ -328,15 +420,15 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
                     float hv[8];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        hv[i] = silu_f32(acc[mi][0][i]) * acc[mi][2][i];
-                        hv[4 + i] = silu_f32(acc[mi][1][i]) * acc[mi][3][i];
+                        hv[i] = silu_f32(ts_a * acc[mi][0][i]) * (ts_b * acc[mi][2][i]);
+                        hv[4 + i] = silu_f32(ts_a * acc[mi][1][i]) * (ts_b * acc[mi][3][i]);
                     }
                     *reinterpret_cast<uint4*>(o) = make_uint4(pack_bf16x2_hw(hv[0], hv[1]), pack_bf16x2_hw(hv[2], hv[3]),
                                                               pack_bf16x2_hw(hv[4], hv[5]), pack_bf16x2_hw(hv[6], hv[7]));
                 } else {
                     float hv[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) hv[i] = silu_f32(acc[mi][0][i]) * acc[mi][1][i];
+                    for (int i = 0; i < 4; ++i) hv[i] = silu_f32(ts_a * acc[mi][0][i]) * (ts_b * acc[mi][1][i]);
                     *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2_hw(hv[0], hv[1]), pack_bf16x2_hw(hv[2], hv[3]));
                 }
             }
@@ -355,7 +447,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
             const int m = 128 * wm + 16 * mi + row16;
             const uint32_t off = (is_shared || m >= rows) ? kOffNone : (uint32_t)(m * 4);
             const float w = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(wview, (int)off, 0, 0));
-            wv[mi] = is_shared ? 1.f : w;
+            wv[mi] = (is_shared ? 1.f : w) * ts_a;  // ts_a: the down tensor scale (1 for bf16)
         }
 #pragma unroll
         for (int mi = 0; mi < 8; ++mi) {
@@ -379,7 +471,7 @@ constexpr int kNMajorBlocks = 64;  // B-row blocks per m-tile from which items r
 // When the last round of a chunk would leave at least half of the XCD's
 // workgroups idle, its items are split into two half tiles (half the B rows
 // each), so that round takes about half as long.
-template <int MODE>
+template <int MODE, int WF>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_gemm_kernel(PrefillParams p) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
@@ -411,9 +503,9 @@ void prefill_gemm_kernel(PrefillParams p) {
             const int F = g.x == p.dm.E ? p.dm.fs : p.dm.f;
             const int nb0 = jb * (PBN / 2);  // first h feature of this tile
             if (nb0 >= F) continue;
-            prefill_tile<MODE, 4>(p, lds, g, m0, nb0);
+            prefill_tile<MODE, 4, WF>(p, lds, g, m0, nb0);
         } else {
-            prefill_tile<MODE, 4>(p, lds, g, m0, jb * PBN);
+            prefill_tile<MODE, 4, WF>(p, lds, g, m0, jb * PBN);
         }
     }
     if (split && j < 2 * rem) {
@@ -424,9 +516,9 @@ void prefill_gemm_kernel(PrefillParams p) {
         if (MODE == MODE_GATEUP) {
             const int F = g.x == p.dm.E ? p.dm.fs : p.dm.f;
             const int nb0 = jb * (PBN / 2) + h * (PBN / 4);  // first h feature of this half
-            if (nb0 < F) prefill_tile<MODE, 2>(p, lds, g, m0, nb0);
+            if (nb0 < F) prefill_tile<MODE, 2, WF>(p, lds, g, m0, nb0);
         } else {
-            prefill_tile<MODE, 2>(p, lds, g, m0, jb * PBN + h * (PBN / 2));
+            prefill_tile<MODE, 2, WF>(p, lds, g, m0, jb * PBN + h * (PBN / 2));
         }
     }
 }
@@ -446,7 +538,8 @@ static PrefillParams make_prefill_params(const LayerArgs& a, const Workspace& w,
 bool prefill_ok(const Dims& dm) {
     // the activation rows are read through one buffer view, whose offsets are 32-bit
     // and must stay below kOffNone
-    return dm.act == DT_BF16 && dm.wdt == DT_BF16 && dm.d % PBN == 0 && dm.f % (PBN / 2) == 0 &&
+    return dm.act == DT_BF16 && (dm.wdt == DT_BF16 || dm.wdt == DT_NVFP4) && dm.d % PBN == 0 &&
+           dm.f % (PBN / 2) == 0 &&
            dm.fs % (PBN / 2) == 0 && dm.d % PBK == 0 && dm.f % PBK == 0 &&
            (size_t)dm.T * dm.d * 2 < (size_t)kOffNone;
 }
@@ -454,7 +547,10 @@ bool prefill_ok(const Dims& dm) {
 template <int MODE>
 static hipError_t launch_prefill(const PrefillParams& p, int n_cu, hipStream_t s) {
     const int grid = ((n_cu > 0 ? n_cu : 256) + 7) / 8 * 8;
-    hipLaunchKernelGGL(prefill_gemm_kernel<MODE>, dim3(grid), dim3(kThreads), 0, s, p);
+    if (p.dm.wdt == DT_NVFP4)
+        hipLaunchKernelGGL((prefill_gemm_kernel<MODE, DT_NVFP4>), dim3(grid), dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((prefill_gemm_kernel<MODE, DT_BF16>), dim3(grid), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

@@ -93,8 +93,9 @@ flint_status check_config(const flint_moe_config* c) {
     if ((c->flags & FLINT_FORCE_DECODE_PATH) && (c->flags & FLINT_FORCE_PREFILL_PATH))
         return fail(FLINT_ERR_INVALID_ARG, "both path-forcing flags set");
     if ((c->flags & FLINT_FORCE_PREFILL_PATH) &&
-        (c->act_dtype != FLINT_BF16 || c->weight_dtype != FLINT_BF16))
-        return fail(FLINT_ERR_UNSUPPORTED, "the grouped-MFMA path needs bf16 activations and weights");
+        (c->act_dtype != FLINT_BF16 || (c->weight_dtype != FLINT_BF16 && c->weight_dtype != FLINT_NVFP4)))
+        return fail(FLINT_ERR_UNSUPPORTED,
+                    "the grouped-MFMA path needs bf16 activations and bf16 or NVFP4 weights");
     return FLINT_OK;
 }
 

@@ -62,11 +62,12 @@ def test_create_rejects_wrong_struct_size_and_nulls():
     assert L.flint_moe_create(ctypes.byref(_cfg()), None) == b.FLINT_ERR_INVALID_ARG
 
 
-def test_prefill_flag_needs_bf16():
+def test_prefill_flag_needs_bf16_activations_and_bf16_or_nvfp4_weights():
     L = fm.load_library()
     h = ctypes.c_void_p()
-    st = L.flint_moe_create(ctypes.byref(_cfg(flags=0x2, weight_dtype=2)), ctypes.byref(h))
-    assert st == b.FLINT_ERR_UNSUPPORTED
+    for bad in (dict(weight_dtype=0), dict(act_dtype=0)):
+        st = L.flint_moe_create(ctypes.byref(_cfg(flags=0x2, **bad)), ctypes.byref(h))
+        assert st == b.FLINT_ERR_UNSUPPORTED, bad
 
 
 def test_valid_config_without_gpu_reports_no_device():

@@ -52,12 +52,29 @@ def test_small_nvfp4_decode(T):
     _case(4, T, d=256, E=32, k=4, f=64, fs=64)
 
 
-@pytest.mark.parametrize("T", [1, 9, 16, 23, 64, 150])
+@pytest.mark.parametrize("T", [1, 9, 16, 23, 64])
 def test_small_nvfp4_matrix_core_path(T):
     # d, f, fs multiples of 512 select the NVFP4 matrix-core expert kernels;
-    # the shared expert has more features than a routed one; NVFP4 layers
-    # always take the decode path, so T = 150 runs it above 64 tokens
+    # the shared expert has more features than a routed one
     _case(4, T, d=512, E=32, k=4, f=512, fs=1024)
+
+
+def test_nvfp4_decode_path_above_64_tokens():
+    # the expert-GEMV kernels at a prefill-sized batch (forced)
+    _case(4, 150, flags=FLINT_FORCE_DECODE_PATH, d=512, E=32, k=4, f=512, fs=1024)
+
+
+@pytest.mark.parametrize("T,flags", [(150, 0), (37, FLINT_FORCE_PREFILL_PATH), (1, FLINT_FORCE_PREFILL_PATH)])
+def test_nvfp4_prefill_path(T, flags):
+    # grouped GEMM with the NVFP4 weights dequantised in registers; above 64
+    # tokens the host picks it by itself
+    _case(4, T, flags=flags, d=512, E=32, k=4, f=512, fs=1024)
+
+
+def test_nvfp4_prefill_zipf_ragged():
+    # Zipf-skewed routing, a group spanning several tiles, ragged tails, and
+    # widths that take half tiles (f = 384: three 128-wide halves per feature block)
+    _case(4, 700, d=512, E=64, f=384, fs=128, bias=True)
 
 
 @pytest.mark.parametrize("T", [5, 19])
@@ -381,6 +398,39 @@ def test_full_prefill_zipf(prefill_layer):
           "outputs of %d tokens (%d from group ends), groups used %d, largest %d: %s" % (
               int(near.sum()), int((near & ~sel_ok).sum()), dl, len(pick), n_group_tokens,
               int((counts > 0).sum()), int(counts.max()), rep), flush=True)
+
+
+@pytest.fixture(scope="module")
+def fp4_prefill_layer():
+    L = synth.layer(4, bias=True)  # NVFP4 weights, the Zipf router bias
+    return L, dev_layer(L)
+
+
+def test_full_prefill_nvfp4_zipf(fp4_prefill_layer):
+    # the 4-bit layer at T = 4096: selection of every token, outputs of >= 512
+    # tokens covering every non-empty group, both output forms at the plain bound
+    L, D = fp4_prefill_layer
+    c = L["cfg"]
+    T, k, E = 4096, c["k"], c["E"]
+    x = synth.hidden(4, T, c["d"], c["act"], draw=7)
+    layer = make_layer_obj(c, T)
+    out, rout = run_gpu(layer, D, x)
+    check_permutation(rout, T, k, E)
+    rref = oracle.route(x, L["router_w"], top_k=k, router_bias=L["router_bias"])
+    sel_ok, near = check_selection(rout["idx"], rout["weights"], rref, k)
+    counts = rout["counts"]
+    pick = set()
+    for e in np.where(counts > 0)[0]:
+        toks = np.where((rout["idx"] == e).any(1))[0]
+        pick.update((int(toks[0]), int(toks[-1])))
+    rng = np.random.default_rng(11)
+    rest = np.setdiff1d(np.arange(T), np.array(sorted(pick)))
+    pick.update(rng.choice(rest, max(0, 512 - len(pick)), replace=False).tolist())
+    pick = np.array(sorted(pick))
+    ref = run_oracle(L, x[pick])
+    rep, _ = check_layer(layer, D, x, ref, c, full=True, rows=pick, tokens=pick)
+    print("nvfp4 prefill T=4096: near ties %d (mismatched %d); outputs of %d tokens, groups used %d: %s" % (
+        int(near.sum()), int((near & ~sel_ok).sum()), len(pick), int((counts > 0).sum()), rep), flush=True)
 
 
 def _stack_teacher_forced(n_layers, T, **override):
