@@ -179,6 +179,15 @@ flint_status flint_moe_get_routing(flint_moe_t h, int32_t* idx, float* weights,
                                    int32_t* sorted_pair, int32_t* counts, float* logits,
                                    int32_t* T_out, hipStream_t stream);
 
+/* Debug: the fault word of the single-launch decode kernel, copied
+ * asynchronously on `stream` to the device int32 at fault_out.  0 means every
+ * grid-barrier wait of every single-launch forward on this handle ended
+ * normally; 1 means some wait gave up after its poll limit (the kernel still
+ * ended, but that forward's output is not to be trusted).  The word is sticky
+ * for the handle's lifetime.  FLINT_ERR_INVALID_ARG for a NULL handle or
+ * fault_out. */
+flint_status flint_moe_get_fault(flint_moe_t h, int32_t* fault_out, hipStream_t stream);
+
 /* Kernel timing hook for measurement.  After flint_moe_profile_begin(h, id,
  * n), the next n launches of kernel `id` (see FLINT_KERNEL_*) inside
  * flint_moe_forward are bracketed by HIP events on the forward's stream.

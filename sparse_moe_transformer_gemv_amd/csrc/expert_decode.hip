@@ -1327,6 +1327,7 @@ __device__ __forceinline__ int* bar_fault(int* fbar) { return fbar + (2 * kBarMa
 // zero when the phase starts
 __device__ __forceinline__ int* bar_queue(int* fbar, int q) { return fbar + (2 * kBarMaxGroups + 4 + q) * kBarSlot; }
 static_assert((2 * kBarMaxGroups + 20) * kBarSlot == kFusedBarrierInts, "barrier region size");
+static_assert((2 * kBarMaxGroups + 3) * kBarSlot == kFusedFaultInt, "fault word index");
 
 // Workgroup `id` of the n that arrive at barrier b (all threads call it).  The
 // writer's stores complete before its arrival; returns true in thread 0 of

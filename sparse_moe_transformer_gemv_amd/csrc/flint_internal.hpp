@@ -97,6 +97,8 @@ bool decode_fp4_ok(const Dims& dm);
 // Ints of the single-launch decode's barrier region: 2 barriers x 64 group slots
 // + 4 slots (roots, generation, fault word) + 16 work counters, 256 ints each.
 constexpr int kFusedBarrierInts = (2 * 64 + 20) * 256;
+// Index of the fault word in that region (sticky: set when a wait gave up).
+constexpr int kFusedFaultInt = (2 * 64 + 3) * 256;
 // Single-launch decode: its grid size for this shape on n_cu compute units (every
 // workgroup resident), or 0 where it does not apply; and its launch.
 int fused_decode_grid(const Dims& dm, int n_cu);

@@ -535,6 +535,15 @@ flint_status flint_moe_get_routing(flint_moe_t h, int32_t* idx, float* weights,
     return ok();
 }
 
+flint_status flint_moe_get_fault(flint_moe_t h, int32_t* fault_out, hipStream_t stream) {
+    if (!h) return fail(FLINT_ERR_INVALID_ARG, "handle is NULL");
+    if (!fault_out) return fail(FLINT_ERR_INVALID_ARG, "fault_out is NULL");
+    hipError_t e = hipMemcpyAsync(fault_out, h->ws.fbar + kFusedFaultInt, sizeof(int32_t),
+                                  hipMemcpyDeviceToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "fault word copy");
+    return ok();
+}
+
 flint_status flint_moe_profile_begin(flint_moe_t h, int32_t kernel_id, int32_t n_launches) {
     if (!h) return fail(FLINT_ERR_INVALID_ARG, "handle is NULL");
     if (kernel_id < 0 || kernel_id >= FLINT_KERNEL_COUNT || n_launches < 1 || n_launches > 100000)

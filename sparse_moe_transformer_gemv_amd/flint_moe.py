@@ -34,7 +34,7 @@ FLINT_UNFUSED_DECODE = 0x8
 EXPORTED = [
     "flint_moe_create", "flint_moe_forward", "flint_moe_get_routing", "flint_moe_profile_begin",
     "flint_moe_profile_end", "flint_moe_destroy", "flint_status_string", "flint_last_error",
-    "flint_rmsnorm_forward", "flint_moe_forward_noalloc",
+    "flint_rmsnorm_forward", "flint_moe_forward_noalloc", "flint_moe_get_fault",
 ]
 
 
@@ -82,6 +82,8 @@ def load_library(path: str = LIB_PATH):
     L.flint_moe_forward_noalloc.restype = st
     L.flint_moe_get_routing.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(i32), vp]
     L.flint_moe_get_routing.restype = st
+    L.flint_moe_get_fault.argtypes = [vp, vp, vp]
+    L.flint_moe_get_fault.restype = st
     L.flint_moe_profile_begin.argtypes = [vp, i32, i32]
     L.flint_moe_profile_begin.restype = st
     L.flint_moe_profile_end.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i32,
@@ -326,6 +328,13 @@ class MoELayer:
             r["sorted_pair"].data_ptr(), r["counts"].data_ptr(), r["logits"].data_ptr(), None,
             _stream()))
         return r
+
+    def fault(self) -> int:
+        """The single-launch decode kernel's sticky fault word (0: no wait gave up)."""
+        dev = torch.device("cuda", torch.cuda.current_device())
+        f = torch.full((1,), -1, dtype=torch.int32, device=dev)
+        _check(load_library().flint_moe_get_fault(self.handle, f.data_ptr(), _stream()))
+        return int(f.item())
 
     def profile_begin(self, kernel_id: int, n_launches: int) -> None:
         _check(load_library().flint_moe_profile_begin(self.handle, kernel_id, n_launches))

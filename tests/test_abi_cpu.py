@@ -88,6 +88,7 @@ def test_null_handle_calls_are_rejected():
     assert L.flint_moe_get_routing(None, None, None, None, None, None, None,
                                    None) == b.FLINT_ERR_INVALID_ARG
     assert L.flint_moe_profile_begin(None, 0, 1) == b.FLINT_ERR_INVALID_ARG
+    assert L.flint_moe_get_fault(None, None, None) == b.FLINT_ERR_INVALID_ARG
     n = ctypes.c_int32(0)
     assert L.flint_moe_profile_end(None, None, 0, ctypes.byref(n)) == b.FLINT_ERR_INVALID_ARG
 

@@ -279,6 +279,7 @@ def test_full_decode_bf16(decode_layer, T):
     ref = run_oracle(L, x)
     rep, rout = check_layer(layer, D, x, ref, c, full=True)
     check_permutation(rout, T, c["k"], c["E"])
+    assert layer.fault() == 0
     print("decode bf16 T=%d: %s" % (T, rep), flush=True)
 
 
@@ -570,6 +571,7 @@ def test_single_launch_decode(T, over):
     fused.profile_begin(KERNEL_FUSED, 4)
     run_gpu(fused, D, x, routing=False)
     assert len(fused.profile_end()) == 1, "the single-launch decode kernel did not run"
+    assert fused.fault() == 0, "a grid-barrier wait gave up"
     sep = make_layer_obj(c, 16, FLINT_UNFUSED_DECODE)
     rep2, rout2 = check_layer(sep, D, x, ref, c)
     assert all(set(a) == set(b) for a, b in zip(rout["idx"], rout2["idx"]))
@@ -612,3 +614,4 @@ def test_single_launch_decode_back_to_back_and_graph():
         assert np.array_equal(out_host(out_static), ref[i]), "replay %d differs" % rep
         fwd(xs[1 - i])
         torch.cuda.synchronize()
+    assert layer.fault() == 0, "a grid-barrier wait gave up"
