@@ -85,6 +85,7 @@ constexpr int kThreads = 512;
 // these reads from the direct-to-LDS loads still in flight into the other buffer
 // and would otherwise wait for all of them (vmcnt 0) first.
 typedef __attribute__((ext_vector_type(4))) uint32_t frag_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -172,21 +173,146 @@ __device__ __forceinline__ int out_col(int tn, int jr) {
     return 32 * (tn >> 1) + 8 * (jr >> 2) + 4 * (tn & 1) + (jr & 3);
 }
 
+// A tile: 256 rows of group g (from row m0 of the group) times the B rows from
+// nb0 (gate/up: first feature; down: first output row).
+struct TileRef {
+    int4 g;
+    int m0, nb0;
+};
+
+// Operand views of a tile (bf16 weights).  Both operands go through buffer
+// views: the lanes of A padding rows (past the group's end) fetch nothing, and
+// every offset fits 32 bits.
+template <int MODE>
+__device__ __forceinline__ void tile_views(const PrefillParams& p, const TileRef& t, __amdgpu_buffer_rsrc_t& aview,
+                                           __amdgpu_buffer_rsrc_t& bview) {
+    const bool is_shared = t.g.x == p.dm.E;
+    const int F = is_shared ? p.dm.fs : p.dm.f;
+    const size_t e = is_shared ? 0 : (size_t)t.g.x;
+    const WeightPtrs& wp = is_shared ? p.shared : p.routed;
+    const int d = p.dm.d;
+    if (MODE == MODE_GATEUP) {
+        aview = buffer_view(p.x, (uint32_t)((size_t)p.dm.T * d * 2));
+        bview = buffer_view(static_cast<const uint16_t*>(wp.gu) + e * 2 * F * (size_t)d, (uint32_t)((size_t)2 * F * d * 2));
+    } else {
+        // the tile's rows of h are contiguous: view exactly those
+        const int rows = min(PBM, t.g.z - t.m0);
+        aview = buffer_view(static_cast<const uint16_t*>(p.ws.h) + (size_t)(t.g.w + t.m0) * p.hstride,
+                            (uint32_t)((size_t)rows * p.hstride * 2));
+        bview = buffer_view(static_cast<const uint16_t*>(wp.dn) + e * (size_t)d * F, (uint32_t)((size_t)d * F * 2));
+    }
+}
+
+// Load slots: A slot j (< 4) of wave w fills LDS rows 32 w + 8 j .. +7 of the
+// A part of a pair buffer, B slot j (< NI) rows BN / 8 w + 8 j .. +7 of the B
+// part; lane l fills row (l >> 3) of a slot, physical chunk l & 7, so each load
+// moves whole 128-byte lines of 8 rows.
+//
+// Gate/up A rows are gathered through the sorted pair list: a_rows_load issues
+// the lane's 4 list loads (unconditional, through a view; padding rows and the
+// shared group, whose rows are the tokens themselves, load nothing), and
+// a_offsets turns them into the byte offsets of the lane's A chunks at k = 0
+// (kOffNone: padding).  Down A rows are the tile's h rows.
+template <int MODE>
+__device__ __forceinline__ void a_rows_load(const PrefillParams& p, const TileRef& t, uint32_t (&raw)[4]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (MODE != MODE_GATEUP) return;
+    const int rows = min(PBM, t.g.z - t.m0);
+    const bool is_shared = t.g.x == p.dm.E;
+    const __amdgpu_buffer_rsrc_t sview = buffer_view(p.ws.sorted_pair, (uint32_t)((size_t)p.dm.k * p.dm.T * 4));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 32 * wave + 8 * j + (lane >> 3);
+        const uint32_t off = (is_shared || r >= rows) ? kOffNone : (uint32_t)((t.g.y + t.m0 + r) * 4);
+        raw[j] = __builtin_amdgcn_raw_buffer_load_b32(sview, (int)off, 0, 0);
+    }
+}
+template <int MODE>
+__device__ __forceinline__ void a_offsets(const PrefillParams& p, const TileRef& t, const uint32_t (&raw)[4],
+                                          uint32_t (&aoff)[4]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rows = min(PBM, t.g.z - t.m0);
+    const bool is_shared = t.g.x == p.dm.E;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 32 * wave + 8 * j + (lane >> 3);
+        const int c = (lane & 7) ^ (r & 7);  // logical chunk landing in physical chunk lane & 7
+        if (r >= rows) {
+            aoff[j] = kOffNone;
+        } else if (MODE == MODE_GATEUP) {
+            const int tok = is_shared ? t.m0 + r : (int)raw[j] / p.dm.k;
+            aoff[j] = (uint32_t)(((size_t)tok * p.dm.d + 8 * c) * 2);
+        } else {
+            aoff[j] = (uint32_t)(((size_t)r * p.hstride + 8 * c) * 2);
+        }
+    }
+}
+// Byte offsets of the lane's B chunks at k = 0.  B row r is row jr of column
+// tile tn of the wave block wb that reads it; out_col() gives the output
+// column (gate/up: feature) it produces.
+template <int MODE, int NI>
+__device__ __forceinline__ int b_row(const PrefillParams& p, const TileRef& t, int r) {
+    constexpr int HS = 8 * NI;
+    const int wb = r / (16 * NI), tn = (r >> 4) % NI, jr = r & 15;
+    if (MODE == MODE_GATEUP) {
+        // tiles < NI / 2 gate, the rest the matching up rows
+        const int F = t.g.x == p.dm.E ? p.dm.fs : p.dm.f;
+        return (tn >= NI / 2 ? F : 0) + t.nb0 + HS * wb + out_col<NI / 2>(tn % (NI / 2), jr);
+    }
+    // down writes fp32: tiles keep their own order (column 16 tn + jr), so each
+    // store instruction covers 64 contiguous bytes of a row
+    return t.nb0 + 16 * NI * wb + 16 * tn + jr;
+}
+template <int MODE, int NI>
+__device__ __forceinline__ void b_offsets(const PrefillParams& p, const TileRef& t, uint32_t (&boff)[NI]) {
+    constexpr int BN = 64 * NI;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int K = MODE == MODE_GATEUP ? p.dm.d : (t.g.x == p.dm.E ? p.dm.fs : p.dm.f);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+        const int r = BN / 8 * wave + 8 * j + (lane >> 3);
+        const int c = (lane & 7) ^ (r & 7);
+        boff[j] = (uint32_t)(((size_t)b_row<MODE, NI>(p, t, r) * K + 8 * c) * 2);
+    }
+}
+
+// Vector memory operations a full bf16 tile's epilogue issues per wave, all of
+// them stores (the down kernel's weight loads come before the next tile's
+// loads): the next tile's first wait lets exactly these stay in flight.
+template <int MODE>
+constexpr int epilogue_stores() { return MODE == MODE_GATEUP ? 8 : 32; }
+// s_waitcnt immediate for vmcnt(n) alone (gfx9 encoding: vmcnt in bits 3..0
+// and 15..14, expcnt and lgkmcnt at their no-wait values)
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
 // One tile: 256 rows of one group (from m0) times 64 NI B rows (NI = 4: a
 // full tile; NI = 2: a half tile, see prefill_gemm_kernel) from B row nb0 of
 // the weights (gate/up: first feature nb0; down: first output row nb0).  For
 // gate/up the B rows are taken in quarters of 16 NI rows: 8 NI gate rows, then
 // the 8 NI up rows of the same features (in out_col order), so wave wn's NI
 // column tiles hold matching gate (ni < NI / 2) and up (ni >= NI / 2) columns.
-template <int MODE, int NI, int WF>
-__device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned char* lds, const int4& g, int m0,
-                                             int nb0) {
+//
+// aoff / boff hold the tile's operand offsets on entry.  `prefetched`: pair 0
+// is already in flight into buffer 0 (issued by the previous tile before its
+// epilogue, whose stores may still be in flight behind it).  HAS_NEXT
+// (bf16 weights, full tiles only; a separate instance, so that the waits the
+// compiler places in the epilogue count the next tile's loads): after the last pair's barrier the tile
+// issues the next tile's row-list loads, after its MFMAs the next tile's pair
+// 0, then runs its epilogue; aoff / boff then hold the next tile's offsets.
+// The pipeline thus runs across tiles: the next tile's first loads fly while
+// this one computes its last pair and writes its results.
+template <int MODE, int NI, int WF, bool HAS_NEXT>
+__device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned char* lds, const TileRef& t,
+                                             uint32_t (&aoff)[4], uint32_t (&boff)[NI], bool prefetched,
+                                             const TileRef& nxt) {
     constexpr int BN = 64 * NI;  // B rows of the tile
     constexpr int HS = 8 * NI;   // gate/up: features per wave (gate rows, then as many up rows)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;
     const int row16 = lane & 15, q = lane >> 4;
     const int d = p.dm.d;
+    const int4 g = t.g;
+    const int m0 = t.m0, nb0 = t.nb0;
     const uint32_t lds0 = lds_addr(lds);
     // this lane's fragment base addresses within a pair buffer, sub-stage 0
     // (sub-stage 1 reads logical chunk q + 4: address bit 6 flipped)
@@ -200,58 +326,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
     const int K = MODE == MODE_GATEUP ? d : F;
     // 16-row MFMA blocks of this wave's 128 rows that hold rows of the group
     const int nmi = (min(max(rows - 128 * wm, 0), 128) + 15) >> 4;
-
-    // Load slots: A slot j (< 4) of this wave fills LDS rows 32 wave + 8 j .. +7
-    // of the A part of a pair buffer, B slot j (< NI) rows BN / 8 wave + 8 j ..
-    // +7 of the B part; lane l fills row (l >> 3) of a slot, physical chunk l & 7,
-    // so each load moves whole 128-byte lines of 8 rows.  Both operands go through
-    // buffer views: the lanes of A padding rows (past the group's end) fetch
-    // nothing, and every offset fits 32 bits.
     __amdgpu_buffer_rsrc_t aview, bview;
-    uint32_t aoff[4];   // byte offset of the lane's A chunk at k = 0 (kOffNone: padding)
-    uint32_t boff[NI];  // byte offset of the lane's B chunk at k = 0
-    if (MODE == MODE_GATEUP) {
-        aview = buffer_view(p.x, (uint32_t)((size_t)p.dm.T * d * 2));
-        bview = buffer_view(static_cast<const uint16_t*>(wp.gu) + e * 2 * F * (size_t)K,
-                            (uint32_t)((size_t)2 * F * K * 2));
-    } else {
-        // the tile's rows of h are contiguous: view exactly those
-        aview = buffer_view(static_cast<const uint16_t*>(p.ws.h) + (size_t)(g.w + m0) * p.hstride,
-                            (uint32_t)((size_t)rows * p.hstride * 2));
-        bview = buffer_view(static_cast<const uint16_t*>(wp.dn) + e * (size_t)d * K, (uint32_t)((size_t)d * K * 2));
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = 32 * wave + 8 * j + (lane >> 3);
-        const int c = (lane & 7) ^ (r & 7);  // logical chunk landing in physical chunk lane & 7
-        if (r >= rows) {
-            aoff[j] = kOffNone;
-        } else if (MODE == MODE_GATEUP) {
-            const int mm = m0 + r;
-            const int tok = is_shared ? mm : p.ws.sorted_pair[g.y + mm] / p.dm.k;
-            aoff[j] = (uint32_t)(((size_t)tok * d + 8 * c) * 2);
-        } else {
-            aoff[j] = (uint32_t)(((size_t)r * p.hstride + 8 * c) * 2);
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-        const int r = BN / 8 * wave + 8 * j + (lane >> 3);
-        const int c = (lane & 7) ^ (r & 7);
-        // B row r is row jr of column tile tn of the wave block wb that reads it;
-        // out_col() gives the output column (gate/up: feature) it produces
-        const int wb = r / (16 * NI), tn = (r >> 4) % NI, jr = r & 15;
-        if (MODE == MODE_GATEUP) {
-            // tiles < NI / 2 gate, the rest the matching up rows
-            const bool up = tn >= NI / 2;
-            const int wrow = (up ? F : 0) + nb0 + HS * wb + out_col<NI / 2>(tn % (NI / 2), jr);
-            boff[j] = (uint32_t)(((size_t)wrow * K + 8 * c) * 2);
-        } else {
-            // down writes fp32: tiles keep their own order (column 16 tn + jr),
-            // so each store instruction covers 64 contiguous bytes of a row
-            boff[j] = (uint32_t)(((size_t)(nb0 + 16 * NI * wb + 16 * tn + jr) * K + 8 * c) * 2);
-        }
-    }
+    tile_views<MODE>(p, t, aview, bview);
 
     // NVFP4 weights (WF): the B rows are dequantised in registers and written to
     // LDS as bf16 in the layout the direct-to-LDS loads give them.  FL = 512 / BN
@@ -263,12 +339,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
     uint32_t coff = 0, soff = 0;  // byte offsets of the lane's codes / the row's scales at k = 0
     float ts_a = 1.f, ts_b = 1.f;  // tensor scales: gate and up (gate/up), down twice (down)
     if constexpr (WF == DT_NVFP4) {
-        const int wb = fr / (16 * NI), tn = (fr >> 4) % NI, jr = fr & 15;
-        int wrow;
-        if (MODE == MODE_GATEUP)
-            wrow = (tn >= NI / 2 ? F : 0) + nb0 + HS * wb + out_col<NI / 2>(tn % (NI / 2), jr);
-        else
-            wrow = nb0 + 16 * NI * wb + 16 * tn + jr;
+        const int wrow = b_row<MODE, NI>(p, t, fr);
         const size_t erows = MODE == MODE_GATEUP ? (size_t)2 * F : (size_t)d;
         const uint8_t* codes = static_cast<const uint8_t*>(MODE == MODE_GATEUP ? wp.gu : wp.dn) + e * erows * (K / 2);
         const uint8_t* scales = (MODE == MODE_GATEUP ? wp.gus : wp.dns) + e * erows * (K / 16);
@@ -327,49 +398,55 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-    // k advances in pairs of sub-stages (k = 64 per pair); pair pp lands in buffer pp & 1
-    auto issue = [&](int pp) {
-        unsigned char* st_ = lds + (pp & 1) * kPairBytes;
-        const uint32_t kb = (uint32_t)pp * kRowBytes;  // byte offset of k = 64 pp in a row
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(aview, st_ + (32 * wave + 8 * j) * kRowBytes, 16, aoff[j] + kb,
-                                                     0, 0, 0);
-        if constexpr (WF != DT_NVFP4) {
-#pragma unroll
-            for (int j = 0; j < NI; ++j)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(bview,
-                                                         st_ + PBM * kRowBytes + (BN / 8 * wave + 8 * j) * kRowBytes,
-                                                         16, boff[j] + kb, 0, 0, 0);
-        }
-    };
-
+    // pair pp (k = 64 pp .. + 63) of a tile into LDS buffer pp & 1: this wave's 4 A
+    // and (bf16 weights) NI B direct-to-LDS loads, through views av / bv
+#define FLINT_ISSUE_PAIR(av, bv, load_b, pp_)                                                                    \
+    do {                                                                                                         \
+        unsigned char* st_ = lds + ((pp_) & 1) * kPairBytes;                                                     \
+        const uint32_t kb = (uint32_t)(pp_) * kRowBytes; /* byte offset of k = 64 pp in a row */                \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                            \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(av, st_ + (32 * wave + 8 * j) * kRowBytes, 16, aoff[j] + kb, \
+                                                     0, 0, 0);                                                   \
+        if (load_b) {                                                                                            \
+            _Pragma("unroll") for (int j = 0; j < NI; ++j)                                                       \
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(bv, st_ + PBM * kRowBytes + (BN / 8 * wave + 8 * j) * kRowBytes, \
+                                                         16, boff[j] + kb, 0, 0, 0);                             \
+        }                                                                                                        \
+    } while (0)
+    constexpr bool kLoadB = WF != DT_NVFP4;
     const int np = K / (2 * PBK);  // pairs (K is a multiple of 64)
     // Buffer 0 is free: the previous tile's last pair (np is even) was in buffer 1,
     // and every wave read its pair np - 2 before that pair's barrier.
     uint32_t cw[FW], sw = 0;
-    if constexpr (WF == DT_NVFP4) {
-        fp4_load(0, cw, sw);
-        fp4_store(0, cw, sw);
+    if (!prefetched) {
+        if constexpr (WF == DT_NVFP4) {
+            fp4_load(0, cw, sw);
+            fp4_store(0, cw, sw);
+        }
+        FLINT_ISSUE_PAIR(aview, bview, kLoadB, 0);
+        if constexpr (WF == DT_NVFP4) {
+            if (np > 1) fp4_load(1, cw, sw);  // in flight behind pair 0's A loads
+        }
     }
-    issue(0);
-    if constexpr (WF == DT_NVFP4) {
-        if (np > 1) fp4_load(1, cw, sw);  // in flight behind pair 0's A loads
-    }
+    uint32_t nraw[4];  // the next tile's row-list entries (gate/up)
     for (int pp = 0; pp < np; ++pp) {
         // this wave's part of pair pp has landed; after the barrier every wave's has,
         // and every wave is done reading pair pp - 1, whose buffer pair pp + 1 refills
-        // while the two sub-stages of pair pp run.  NVFP4: the two code / scale loads
-        // of pair pp + 1 may stay in flight, and the LDS writes of pair pp's weights
-        // must be done
+        // while the two sub-stages of pair pp run.  A prefetched pair 0 may have the
+        // previous tile's epilogue stores in flight behind it.  NVFP4: the two code /
+        // scale loads of pair pp + 1 may stay in flight, and the LDS writes of pair
+        // pp's weights must be done
         if (WF == DT_NVFP4 && pp + 1 < np)
             __builtin_amdgcn_s_waitcnt(0x0072);  // vmcnt(2) lgkmcnt(0)
         else if (WF == DT_NVFP4)
             __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+        else if (pp == 0 && prefetched)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(epilogue_stores<MODE>()));
         else
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         phase_barrier();
-        if (pp + 1 < np) issue(pp + 1);
+        if (pp + 1 < np) FLINT_ISSUE_PAIR(aview, bview, kLoadB, pp + 1);
+        else if (HAS_NEXT) a_rows_load<MODE>(p, nxt, nraw);
         const uint32_t st = lds0 + (pp & 1) * kPairBytes;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -406,62 +483,102 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
     // made the two tiles of a pair 8 consecutive features, one 16-byte bf16 store
     // (8 bytes for a lone tile).  Down: columns 16 ni + 4 q .. + 3, one 16-byte
     // fp32 store per tile.  Either way 64 contiguous bytes per row and
-    // instruction. ----
-    const int wrows = min(max(rows - 128 * wm, 0), 128);
-    if (MODE == MODE_GATEUP) {
-        // gate tile t and up tile t + NI / 2 hold the same features
-        uint16_t* dst = static_cast<uint16_t*>(p.ws.h) + (size_t)(g.w + m0 + 128 * wm + row16) * p.hstride + nb0 +
-                        HS * wn + (NI == 4 ? 8 : 4) * q;
-#pragma unroll
-        for (int mi = 0; mi < 8; ++mi) {
-            if (16 * mi + row16 < wrows) {
-                uint16_t* o = dst + (size_t)16 * mi * p.hstride;
-                if (NI == 4) {
-                    float hv[8];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        hv[i] = silu_f32(ts_a * acc[mi][0][i]) * (ts_b * acc[mi][2][i]);
-                        hv[4 + i] = silu_f32(ts_a * acc[mi][1][i]) * (ts_b * acc[mi][3][i]);
-                    }
-                    *reinterpret_cast<uint4*>(o) = make_uint4(pack_bf16x2_hw(hv[0], hv[1]), pack_bf16x2_hw(hv[2], hv[3]),
-                                                              pack_bf16x2_hw(hv[4], hv[5]), pack_bf16x2_hw(hv[6], hv[7]));
-                } else {
-                    float hv[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) hv[i] = silu_f32(ts_a * acc[mi][0][i]) * (ts_b * acc[mi][1][i]);
-                    *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2_hw(hv[0], hv[1]), pack_bf16x2_hw(hv[2], hv[3]));
-                }
-            }
-        }
-    } else {
-        float* dst = static_cast<float*>(p.ws.y) + (size_t)(g.w + m0 + 128 * wm + row16) * d + nb0 +
-                     16 * NI * wn + 4 * q;
-        // routing weights of the lane's 8 rows, loaded before any store (loads and
-        // stores share one in-order counter, so a load after a store waits for it)
-        // (unconditional buffer loads: a load behind a branch makes every later use
-        // wait for all of this wave's memory operations)
+    // instruction.  Every store is issued (rows past the group's end get an
+    // offset past the view), so a wave always issues the same number. ----
+    float wv[8];
+    if (MODE == MODE_DOWN) {
+        // routing weights of the lane's 8 rows, loaded before any store and before
+        // the next tile's loads (loads and stores share one in-order counter, so a
+        // load waits for every memory operation issued before it)
         const __amdgpu_buffer_rsrc_t wview = buffer_view(p.ws.sorted_wt + g.y + m0, (uint32_t)(rows * 4));
-        float wv[8];
 #pragma unroll
         for (int mi = 0; mi < 8; ++mi) {
             const int m = 128 * wm + 16 * mi + row16;
             const uint32_t off = (is_shared || m >= rows) ? kOffNone : (uint32_t)(m * 4);
-            const float w = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(wview, (int)off, 0, 0));
-            wv[mi] = (is_shared ? 1.f : w) * ts_a;  // ts_a: the down tensor scale (1 for bf16)
+            wv[mi] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(wview, (int)off, 0, 0));
         }
+    }
+    if constexpr (HAS_NEXT) {
+        // the next tile's offsets (its row-list loads have landed by now) and pair 0
+        __amdgpu_buffer_rsrc_t nav, nbv;
+        tile_views<MODE>(p, nxt, nav, nbv);
+        a_offsets<MODE>(p, nxt, nraw, aoff);
+        b_offsets<MODE, NI>(p, nxt, boff);
+        FLINT_ISSUE_PAIR(nav, nbv, true, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (MODE == MODE_GATEUP) {
+        // gate tile t and up tile t + NI / 2 hold the same features
+        const __amdgpu_buffer_rsrc_t hview = buffer_view(static_cast<uint16_t*>(p.ws.h) + (size_t)(g.w + m0) * p.hstride,
+                                                         (uint32_t)((size_t)rows * p.hstride * 2));
+        const int col = nb0 + HS * wn + (NI == 4 ? 8 : 4) * q;
 #pragma unroll
         for (int mi = 0; mi < 8; ++mi) {
-            if (16 * mi + row16 < wrows) {
-                const float ws = wv[mi];
-                float* o = dst + (size_t)16 * mi * d;
+            const int m = 128 * wm + 16 * mi + row16;
+            const uint32_t off = m < rows ? (uint32_t)(((size_t)m * p.hstride + col) * 2) : kOffNone;
+            if (NI == 4) {
+                float hv[8];
 #pragma unroll
-                for (int t = 0; t < NI; ++t) {
-                    const floatx4_t& a = acc[mi][t];
-                    *reinterpret_cast<float4*>(o + 16 * t) = make_float4(ws * a[0], ws * a[1], ws * a[2], ws * a[3]);
+                for (int i = 0; i < 4; ++i) {
+                    hv[i] = silu_f32(ts_a * acc[mi][0][i]) * (ts_b * acc[mi][2][i]);
+                    hv[4 + i] = silu_f32(ts_a * acc[mi][1][i]) * (ts_b * acc[mi][3][i]);
                 }
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    (u32x4_t){pack_bf16x2_hw(hv[0], hv[1]), pack_bf16x2_hw(hv[2], hv[3]),
+                              pack_bf16x2_hw(hv[4], hv[5]), pack_bf16x2_hw(hv[6], hv[7])},
+                    hview, (int)off, 0, 0);
+            } else {
+                float hv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) hv[i] = silu_f32(ts_a * acc[mi][0][i]) * (ts_b * acc[mi][1][i]);
+                __builtin_amdgcn_raw_buffer_store_b64(
+                    (u32x2_t){pack_bf16x2_hw(hv[0], hv[1]), pack_bf16x2_hw(hv[2], hv[3])}, hview, (int)off, 0, 0);
+            }
+        }
+    } else {
+        const __amdgpu_buffer_rsrc_t yview = buffer_view(static_cast<float*>(p.ws.y) + (size_t)(g.w + m0) * d,
+                                                         (uint32_t)((size_t)rows * d * 4));
+        const int col = nb0 + 16 * NI * wn + 4 * q;
+#pragma unroll
+        for (int mi = 0; mi < 8; ++mi) {
+            const int m = 128 * wm + 16 * mi + row16;
+            const float ws = (is_shared ? 1.f : wv[mi]) * ts_a;  // ts_a: the down tensor scale (1 for bf16)
+            const uint32_t off = m < rows ? (uint32_t)(((size_t)m * d + col) * 4) : kOffNone;
+#pragma unroll
+            for (int t4 = 0; t4 < NI; ++t4) {
+                const floatx4_t& a = acc[mi][t4];
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    (u32x4_t){__float_as_uint(ws * a[0]), __float_as_uint(ws * a[1]), __float_as_uint(ws * a[2]),
+                              __float_as_uint(ws * a[3])},
+                    yview, (int)(off == kOffNone ? kOffNone : off + 64 * t4), 0, 0);
             }
         }
     }
+    // keeps the two instances' epilogues apart: merged into one block, the
+    // compiler's waits before the stores would have to allow for both and would
+    // then wait for the next tile's loads as well
+    if constexpr (HAS_NEXT) asm volatile("; next tile in flight" ::: "memory");
+}
+
+#undef FLINT_ISSUE_PAIR
+
+// Wave-uniform loads of the tile and group lists through the scalar cache,
+// complete on return (the wait is in the same asm block).  As vector loads
+// they would share the in-order vector-memory counter with the stores of the
+// previous tile's epilogue, and waiting for them would wait for those stores.
+// The lists are written by an earlier launch, so the scalar cache holds no
+// stale copy of them.
+typedef __attribute__((ext_vector_type(2))) int sint2_t;
+typedef __attribute__((ext_vector_type(4))) int sint4_t;
+__device__ __forceinline__ int2 sload_int2(const int2* ptr) {
+    sint2_t v;
+    asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+    return make_int2(v.x, v.y);
+}
+__device__ __forceinline__ int4 sload_int4(const int4* ptr) {
+    sint4_t v;
+    asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+    return make_int4(v.x, v.y, v.z, v.w);
 }
 
 constexpr int kNMajorBlocks = 64;  // B-row blocks per m-tile from which items run B-block-major
@@ -470,7 +587,9 @@ constexpr int kNMajorBlocks = 64;  // B-row blocks per m-tile from which items r
 // contiguous chunks, one per XCD, walked by that XCD's workgroups in rounds.
 // When the last round of a chunk would leave at least half of the XCD's
 // workgroups idle, its items are split into two half tiles (half the B rows
-// each), so that round takes about half as long.
+// each), so that round takes about half as long.  With bf16 weights each full
+// item issues the first loads of the workgroup's next full item before its
+// epilogue (see prefill_tile).
 template <int MODE, int WF>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_gemm_kernel(PrefillParams p) {
@@ -489,36 +608,75 @@ void prefill_gemm_kernel(PrefillParams p) {
     // once, rather than every XCD reading all of them.
     const int ntl = *p.ws.n_tiles;
     const bool nmajor = p.nblk >= kNMajorBlocks;
-    auto coords = [&](int t, int4& g, int& m0, int& jb) {
-        const int2 tile = p.ws.tiles[nmajor ? t % ntl : t / p.nblk];
-        jb = nmajor ? t / ntl : t % p.nblk;
-        g = p.ws.groups[tile.x];
-        m0 = tile.y;
-    };
-    for (int i = j; i < nfull; i += nper) {
-        int4 g;
-        int m0, jb;
-        coords(t0 + i, g, m0, jb);
+    // item i of this XCD as a full tile; false when it holds no work (gate/up
+    // blocks past a narrower group's width)
+    // (every field is loaded into scalar registers: the operand views built from
+    // them then live there too, and each buffer load is one instruction rather
+    // than a loop over possibly distinct descriptors)
+    auto item = [&](int i, TileRef& t) -> bool {
+        const int it = __builtin_amdgcn_readfirstlane(t0 + i);
+        const int2 tile = sload_int2(p.ws.tiles + (nmajor ? it % ntl : it / p.nblk));
+        const int jb = nmajor ? it / ntl : it % p.nblk;
+        t.g = sload_int4(p.ws.groups + tile.x);
+        t.m0 = tile.y;
         if (MODE == MODE_GATEUP) {
-            const int F = g.x == p.dm.E ? p.dm.fs : p.dm.f;
-            const int nb0 = jb * (PBN / 2);  // first h feature of this tile
-            if (nb0 >= F) continue;
-            prefill_tile<MODE, 4, WF>(p, lds, g, m0, nb0);
-        } else {
-            prefill_tile<MODE, 4, WF>(p, lds, g, m0, jb * PBN);
+            const int F = t.g.x == p.dm.E ? p.dm.fs : p.dm.f;
+            t.nb0 = jb * (PBN / 2);  // first h feature of this tile
+            return t.nb0 < F;
+        }
+        t.nb0 = jb * PBN;
+        return true;
+    };
+    auto next_item = [&](int i, TileRef& t) -> int {  // first item from i with work, or nfull
+        for (; i < nfull; i += nper)
+            if (item(i, t)) return i;
+        return nfull;
+    };
+    TileRef cur, nxt;
+    int i = next_item(j, cur);
+    if (i < nfull) {
+        uint32_t aoff[4], boff[4], raw[4];
+        a_rows_load<MODE>(p, cur, raw);
+        a_offsets<MODE>(p, cur, raw, aoff);
+        b_offsets<MODE, 4>(p, cur, boff);
+        bool prefetched = false;
+        while (i < nfull) {
+            const int inext = next_item(i + nper, nxt);
+            const bool chain = WF != DT_NVFP4 && inext < nfull;
+            if constexpr (WF != DT_NVFP4) {
+                if (chain) prefill_tile<MODE, 4, WF, true>(p, lds, cur, aoff, boff, prefetched, nxt);
+                else prefill_tile<MODE, 4, WF, false>(p, lds, cur, aoff, boff, prefetched, nxt);
+            } else {
+                prefill_tile<MODE, 4, WF, false>(p, lds, cur, aoff, boff, false, nxt);
+            }
+            if (!chain && inext < nfull) {
+                a_rows_load<MODE>(p, nxt, raw);
+                a_offsets<MODE>(p, nxt, raw, aoff);
+                b_offsets<MODE, 4>(p, nxt, boff);
+            }
+            prefetched = chain;
+            cur = nxt;
+            i = inext;
         }
     }
     if (split && j < 2 * rem) {
-        int4 g;
-        int m0, jb;
-        coords(t0 + nfull + (j >> 1), g, m0, jb);
+        TileRef t;
+        item(nfull + (j >> 1), t);
         const int h = j & 1;  // which half of the item's B rows
+        bool work = true;
         if (MODE == MODE_GATEUP) {
-            const int F = g.x == p.dm.E ? p.dm.fs : p.dm.f;
-            const int nb0 = jb * (PBN / 2) + h * (PBN / 4);  // first h feature of this half
-            if (nb0 < F) prefill_tile<MODE, 2, WF>(p, lds, g, m0, nb0);
+            const int F = t.g.x == p.dm.E ? p.dm.fs : p.dm.f;
+            t.nb0 += h * (PBN / 4);  // first h feature of this half
+            work = t.nb0 < F;
         } else {
-            prefill_tile<MODE, 2, WF>(p, lds, g, m0, jb * PBN + h * (PBN / 2));
+            t.nb0 += h * (PBN / 2);
+        }
+        if (work) {
+            uint32_t aoff[4], boff[2], raw[4];
+            a_rows_load<MODE>(p, t, raw);
+            a_offsets<MODE>(p, t, raw, aoff);
+            b_offsets<MODE, 2>(p, t, boff);
+            prefill_tile<MODE, 2, WF, false>(p, lds, t, aoff, boff, false, t);
         }
     }
 }

@@ -370,49 +370,6 @@ __device__ void block_sort_and_groups(const int* __restrict__ keys, const float*
     if (w == 0) write_groups(s_off, E, T, k, has_shared, bm, ws, lane);
 }
 
-// ---------------------------------------------------------------------------
-// Decode path, one launch: router GEMV over all experts, then the last block
-// to finish runs top-k for every token and the counting sort.
-// ---------------------------------------------------------------------------
-struct RouteDecodeParams {
-    const void* x;
-    const float* wr;
-    const float* bias;
-    int T, d, E, k;
-    int has_shared;
-    Workspace ws;
-};
-
-template <typename ActT>
-__global__ __launch_bounds__(256) void route_decode_kernel(RouteDecodeParams p) {
-    __shared__ int s_hist[4 * 256];
-    __shared__ int s_off[257];
-    __shared__ int s_last;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int e = blockIdx.x * 4 + wave;
-    if (e < p.E)
-        router_row_logits<ActT>(static_cast<const ActT*>(p.x), p.wr + (size_t)e * p.d,
-                                p.bias ? p.bias[e] : 0.f, 0, p.T, p.d, p.E, e, p.ws.logits, lane);
-    // the last block to finish runs top-k for every token, then the sort
-    if (!last_arrival(p.ws.counter, (int)gridDim.x, &s_last)) return;
-    for (int t = wave; t < p.T; t += 4)
-        wave_topk_token(p.ws.logits + (size_t)t * p.E, p.E, p.k, lane, p.ws.sel + (size_t)t * p.k,
-                        p.ws.wts + (size_t)t * p.k);
-    wait_stores();
-    __syncthreads();
-    block_sort_and_groups<256>(p.ws.sel, p.ws.wts, p.k * p.T, p.E, p.T, p.k, p.has_shared != 0, 0, p.ws,
-                               s_hist, s_off);
-}
-
-hipError_t launch_route_decode(const LayerArgs& a, const Workspace& w, hipStream_t s) {
-    RouteDecodeParams p{a.x, a.wr, a.bias, a.dm.T, a.dm.d, a.dm.E, a.dm.k, a.dm.fs > 0, w};
-    dim3 grid((a.dm.E + 3) / 4);
-    if (a.dm.act == DT_F32)
-        hipLaunchKernelGGL(route_decode_kernel<float>, grid, dim3(256), 0, s, p);
-    else
-        hipLaunchKernelGGL(route_decode_kernel<uint16_t>, grid, dim3(256), 0, s, p);
-    return hipGetLastError();
-}
 
 // ---------------------------------------------------------------------------
 // Router on the matrix cores (bf16 activations): logits of a 16-token x
@@ -608,6 +565,53 @@ __device__ __forceinline__ void wave_topk_tokens(const float* __restrict__ logit
                 }
             }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Decode path without the matrix cores (fp32 activations, or shapes the
+// matrix-core router does not take), one launch of (E / 4) x (T / 16) blocks:
+// wave w of block (bx, by) computes router logit 4 bx + w of the 16 tokens of
+// tile by; the last expert block of each token tile to finish selects the
+// top-k of its tokens (two per wave per pass), and the last token tile to
+// finish runs the counting sort.
+// ---------------------------------------------------------------------------
+struct RouteDecodeParams {
+    const void* x;
+    const float* wr;
+    const float* bias;
+    int T, d, E, k;
+    int has_shared;
+    Workspace ws;
+};
+
+template <typename ActT>
+__global__ __launch_bounds__(256) void route_decode_kernel(RouteDecodeParams p) {
+    __shared__ int s_hist[4 * 256];
+    __shared__ int s_off[257];
+    __shared__ int s_last;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int e = blockIdx.x * 4 + wave;
+    const int t0 = blockIdx.y * 16, t1 = min(p.T, t0 + 16);
+    if (e < p.E)
+        router_row_logits<ActT>(static_cast<const ActT*>(p.x), p.wr + (size_t)e * p.d,
+                                p.bias ? p.bias[e] : 0.f, t0, t1, p.d, p.E, e, p.ws.logits, lane);
+    if (!last_arrival(p.ws.counter + 1 + blockIdx.y, (int)gridDim.x, &s_last)) return;
+    // tokens t0 + wave + {0, 4, 8, 12}
+    wave_topk_tokens<2>(p.ws.logits, t0, t1, p.E, p.k, wave, lane, p.ws.sel, p.ws.wts, nullptr, nullptr);
+    wave_topk_tokens<2>(p.ws.logits, t0 + 4, t1, p.E, p.k, wave, lane, p.ws.sel, p.ws.wts, nullptr, nullptr);
+    if (!last_arrival(p.ws.counter, (int)gridDim.y, &s_last)) return;
+    block_sort_and_groups<256>(p.ws.sel, p.ws.wts, p.k * p.T, p.E, p.T, p.k, p.has_shared != 0, 0, p.ws,
+                               s_hist, s_off);
+}
+
+hipError_t launch_route_decode(const LayerArgs& a, const Workspace& w, hipStream_t s) {
+    RouteDecodeParams p{a.x, a.wr, a.bias, a.dm.T, a.dm.d, a.dm.E, a.dm.k, a.dm.fs > 0, w};
+    dim3 grid((a.dm.E + 3) / 4, (a.dm.T + 15) / 16);
+    if (a.dm.act == DT_F32)
+        hipLaunchKernelGGL(route_decode_kernel<float>, grid, dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL(route_decode_kernel<uint16_t>, grid, dim3(256), 0, s, p);
+    return hipGetLastError();
 }
 
 constexpr int kRouteSplitMaxT = 64;
