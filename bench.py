@@ -314,13 +314,16 @@ def run_stack(args, cpu_seconds):
     h0 = dev_array(synth.hidden(cfg_id, T, c["d"], synth.F32))
     h = h0.clone()
     moe = make_layer_obj(c, T)
-    xbuf = torch.empty((T, c["d"]), dtype=torch.bfloat16, device="cuda")
+    xbufs = [torch.empty((T, c["d"]), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
 
     def one_pass(record=False):
+        # the first pre-norm by the RMSNorm kernel; each layer's own launches
+        # then produce the next layer's pre-norm with its output
         nd = []
-        for D in layers:
-            fm.flint_rmsnorm_forward(h, 1e-6, out=xbuf)
-            moe.forward(xbuf, D["router_w"], D["experts"], D["shared"], None, residual=h, out=h)
+        fm.flint_rmsnorm_forward(h, 1e-6, out=xbufs[0])
+        for l, D in enumerate(layers):
+            moe.forward_prenorm(xbufs[l & 1], D["router_w"], D["experts"], D["shared"], residual=h, eps=1e-6,
+                                out=h, norm_out=xbufs[(l + 1) & 1])
             if record:
                 nd.append(int((moe.routing()["counts"] > 0).sum().item()))
         return nd

@@ -140,6 +140,29 @@ flint_status flint_moe_forward(flint_moe_t h, int32_t T, const void* hidden,
                                void* out, hipStream_t stream);
 
 /*
+ * One step of a stack of layers with pre-norm residual blocks:
+ *   out[t]      = residual[t] + MoE(hidden)[t]                    (fp32, as flint_moe_forward)
+ *   norm_out[t] = bf16(out[t] / sqrt(mean(out[t]^2) + eps))       (unit gain, fp32 arithmetic)
+ * norm_out is the next layer's input, bit for bit what flint_rmsnorm_forward
+ * gives from out.  The model has 47 MoE layers [evermx.com, "Recursive
+ * Flint: Open-Weight MoE Coding Model, 2.5B Active", Feature Overview,
+ * "Sparse architecture"]; the residual form with a unit-gain RMSNorm before
+ * each layer is the reading taken for running them in sequence.  Where the
+ * path sums the layer output in a launch of its own, that launch also
+ * normalises it, which saves a launch per layer.
+ *   residual: [T][d] fp32, required (may equal out); out: [T][d] fp32;
+ *   norm_out: [T][d] bf16 (device, 16-byte aligned, disjoint from hidden,
+ *   residual and out); eps in [0, 1].
+ * Errors as flint_moe_forward; FLINT_ERR_INVALID_ARG for a NULL residual or
+ * norm_out, an eps outside [0, 1] or an overlapping norm_out.
+ */
+flint_status flint_moe_forward_prenorm(flint_moe_t h, int32_t T, const void* hidden,
+                                       const float* router_w, const float* router_bias,
+                                       const flint_expert_weights* experts,
+                                       const flint_expert_weights* shared, const float* residual,
+                                       float* out, float eps, void* norm_out, hipStream_t stream);
+
+/*
  * The same forward without a handle and without allocating, for callers that
  * cannot allocate device memory: code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc.  Arguments as flint_moe_forward,

@@ -71,8 +71,94 @@ hipError_t launch_combine(const LayerArgs& a, const Workspace& w, hipStream_t s)
 }
 
 // ---------------------------------------------------------------------------
+// The combine followed by the next layer's pre-norm, one block per token:
+// out[t] as combine_kernel computes it (fp32 output), then
+// norm[t] = bf16(out[t] / sqrt(mean(out[t]^2) + eps)) as rmsnorm_kernel
+// computes it from out[t]: the same thread owns the same columns and sums
+// their squares in the same order, so both give the same bits as the two
+// separate launches.  d <= 4 * 1024 (the row stays in registers).
+// ---------------------------------------------------------------------------
+constexpr int kNormChunks = 4;
+__device__ __forceinline__ float rms_scale(float ss, int d, float eps, float* s_part);
+
+__global__ __launch_bounds__(256) void combine_norm_kernel(CombineParams p, float eps, uint16_t* __restrict__ norm) {
+    __shared__ float s_part[4];
+    const int t = blockIdx.x;
+    const size_t kT = (size_t)p.k * p.T;
+    int slot[kCombineMaxK];
+#pragma unroll
+    for (int j = 0; j < kCombineMaxK; ++j) slot[j] = j < p.k ? p.pair_pos[(size_t)t * p.k + j] : 0;
+    float4 v[kNormChunks];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < kNormChunks; ++i) {
+        const int c = threadIdx.x * 4 + 1024 * i;
+        if (c >= p.d) break;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        if (p.residual) {
+            const float4 r = *reinterpret_cast<const float4*>(p.residual + (size_t)t * p.d + c);
+            acc[0] = r.x; acc[1] = r.y; acc[2] = r.z; acc[3] = r.w;
+        }
+        if (p.has_shared) {
+            const float4 y = *reinterpret_cast<const float4*>(p.y + (kT + t) * p.d + c);
+            acc[0] += y.x; acc[1] += y.y; acc[2] += y.z; acc[3] += y.w;
+        }
+#pragma unroll
+        for (int j = 0; j < kCombineMaxK; ++j) {
+            if (j >= p.k) break;
+            const float4 y = *reinterpret_cast<const float4*>(p.y + (size_t)slot[j] * p.d + c);
+            acc[0] += y.x; acc[1] += y.y; acc[2] += y.z; acc[3] += y.w;
+        }
+        v[i] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        *reinterpret_cast<float4*>(static_cast<float*>(p.out) + (size_t)t * p.d + c) = v[i];
+        ss = fmaf(v[i].x, v[i].x, ss);
+        ss = fmaf(v[i].y, v[i].y, ss);
+        ss = fmaf(v[i].z, v[i].z, ss);
+        ss = fmaf(v[i].w, v[i].w, ss);
+    }
+    const float r = rms_scale(ss, p.d, eps, s_part);
+    uint16_t* orow = norm + (size_t)t * p.d;
+#pragma unroll
+    for (int i = 0; i < kNormChunks; ++i) {
+        const int c = threadIdx.x * 4 + 1024 * i;
+        if (c >= p.d) break;
+        uint2 o;
+        o.x = (uint32_t)f32_to_bf16(v[i].x * r) | ((uint32_t)f32_to_bf16(v[i].y * r) << 16);
+        o.y = (uint32_t)f32_to_bf16(v[i].z * r) | ((uint32_t)f32_to_bf16(v[i].w * r) << 16);
+        *reinterpret_cast<uint2*>(orow + c) = o;
+    }
+}
+
+bool combine_norm_ok(const Dims& dm) { return dm.d % 4 == 0 && dm.d <= 1024 * kNormChunks; }
+
+hipError_t launch_combine_norm(const LayerArgs& a, const Workspace& w, float eps, void* norm, hipStream_t s) {
+    CombineParams p;
+    p.T = a.dm.T;
+    p.d = a.dm.d;
+    p.k = a.dm.k;
+    p.y = static_cast<const float*>(w.y);
+    p.pair_pos = w.pair_pos;
+    p.residual = a.residual;
+    p.out = a.out;
+    p.out_f32 = 1;
+    p.has_shared = a.dm.fs > 0 ? 1 : 0;
+    hipLaunchKernelGGL(combine_norm_kernel, dim3(a.dm.T), dim3(256), 0, s, p, eps, static_cast<uint16_t*>(norm));
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // RMSNorm, unit gain: out = bf16(v / sqrt(mean(v^2) + eps)); one block per row.
 // ---------------------------------------------------------------------------
+// 1 / sqrt(mean + eps) from each thread's sum of squares: wave sums, then the
+// four waves' sums in wave order
+__device__ __forceinline__ float rms_scale(float ss, int d, float eps, float* s_part) {
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = s_part[0] + s_part[1] + s_part[2] + s_part[3];
+    return 1.0f / sqrtf(tot / (float)d + eps);
+}
+
 __global__ __launch_bounds__(256) void rmsnorm_kernel(int d, const float* __restrict__ in,
                                                       float eps, uint16_t* __restrict__ out) {
     __shared__ float s_part[4];
@@ -85,11 +171,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(int d, const float* __rest
         ss = fmaf(v.z, v.z, ss);
         ss = fmaf(v.w, v.w, ss);
     }
-    ss = wave_sum(ss);
-    if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    const float tot = s_part[0] + s_part[1] + s_part[2] + s_part[3];
-    const float r = 1.0f / sqrtf(tot / (float)d + eps);
+    const float r = rms_scale(ss, d, eps, s_part);
     uint16_t* orow = out + (size_t)blockIdx.x * d;
     for (int c = threadIdx.x * 4; c < d; c += 1024) {
         float4 v = *reinterpret_cast<const float4*>(row + c);

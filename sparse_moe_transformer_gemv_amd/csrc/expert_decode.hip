@@ -538,7 +538,6 @@ __device__ __forceinline__ void down_mfma_tile(const ExpertParams& p, const int4
 // unused terms selected away), so the tail costs two memory round trips.
 // kPer elements per thread cover T x 16 NT outputs.
 constexpr int kDownCombineMaxT = 16;
-constexpr int kCombineMaxK = 8;
 template <int NT, int kPer>
 __device__ __forceinline__ void combine_columns_n(const ExpertParams& p, int n0, const int* s_pos) {
     constexpr int nc = 16 * NT;
@@ -1268,9 +1267,11 @@ hipError_t launch_down_decode(const LayerArgs& a, const Workspace& w, hipStream_
 //            meanwhile (the shared expert needs no routing);
 //   barrier  every router workgroup has written its logits;
 //   phase 1  every workgroup selects the top-k of every token and sorts the
-//            pairs itself, in LDS (at most 16 x 8 pairs), so no further
-//            hand-off is needed to learn the routing; workgroup 0 publishes it
-//            for flint_moe_get_routing;
+//            pairs itself, in LDS (at most 8 x 8 pairs), so no further
+//            hand-off is needed to learn the routing; it issues the weight
+//            loads of its first gate/up item as soon as the group list is
+//            known; workgroup 0 publishes the routing for
+//            flint_moe_get_routing;
 //   phase 2  the routed gate/up items (group, 8 features), spread round-robin;
 //            h leaves as its exact three-plane bf16 split at agent scope;
 //   barrier  every gate/up item is done; each workgroup issues the weight
@@ -1497,15 +1498,30 @@ __device__ void fused_topk(const ExpertParams& p, float* s_logit, int* s_sel, fl
     }
 }
 
-// Stable counting sort of the k T pairs by expert, in LDS.  A token picks an
-// expert at most once, so a bitmask of the tokens that picked each expert
-// (s_mask, T <= 32) gives both the count (its population) and each pair's rank
-// among the earlier pairs of its expert (the tokens below its own); then the
-// exclusive scan of the counts, the sorted pair list, its inverse, the weight
-// of each sorted pair, and the group list (the shared expert first, then every
-// expert with tokens, ascending).
-__device__ void fused_sort(const ExpertParams& p, const int* s_sel, const float* s_wt, unsigned* s_mask, int* s_off,
-                           int* s_sp, int* s_pos, float* s_swt, int4* s_groups, int* s_ng) {
+// Stable counting sort of the k T pairs by expert, in LDS, in two parts so
+// that a workgroup can start loading the weights of its first gate/up item
+// between them.  A token picks an expert at most once, so a bitmask of the
+// tokens that picked each expert (s_mask, T <= 32) gives both the count (its
+// population) and each pair's rank among the earlier pairs of its expert (the
+// tokens below its own).
+//   fused_groups: the masks, the exclusive scan of the counts (s_off) and the
+//     group list (the shared expert first, then every expert with tokens,
+//     ascending), from one pass of wave 0 over 4 experts per lane;
+//   fused_place: the sorted pair list, its inverse and the weight of each
+//     sorted pair.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    // rows of 16 lanes (row_shr 1, 2, 4, 8; lanes shifted in from outside the
+    // row read 0), then row 15's total into rows 1 and 3, row 31's into 2 and 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);
+    return v;
+}
+__device__ void fused_groups(const ExpertParams& p, const int* s_sel, unsigned* s_mask, int* s_off, int4* s_groups,
+                             int* s_ng) {
     const int T = p.dm.T, k = p.dm.k, E = p.dm.E, P = k * T;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int i = tid; i < E; i += blockDim.x) s_mask[i] = 0u;
@@ -1513,29 +1529,38 @@ __device__ void fused_sort(const ExpertParams& p, const int* s_sel, const float*
     if (tid < P) atomicOr(&s_mask[s_sel[tid]], 1u << (tid / k));
     __syncthreads();
     if (wave == 0) {
-        int c[4], local = 0;
+        int c[4], local = 0, nact = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int e = 4 * lane + i;
             c[i] = e < E ? __popc(s_mask[e]) : 0;
             local += c[i];
+            nact += c[i] > 0 ? 1 : 0;
         }
-        int inc = local;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int v = __shfl_up(inc, off, 64);
-            if (lane >= off) inc += v;
-        }
-        int run = inc - local;
+        // (count, active experts) of the lanes below, packed in one int: at most
+        // 256 pairs and 256 experts, so 16 bits each
+        const int inc = wave_incl_scan(local | (nact << 16));
+        int run = (inc & 0xFFFF) - local;
+        int gi = (p.dm.fs > 0 ? 1 : 0) + (inc >> 16) - nact;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int e = 4 * lane + i;
             if (e < E) s_off[e] = run;
+            if (c[i] > 0) s_groups[gi++] = make_int4(e, run, c[i], run);
             run += c[i];
         }
-        if (lane == 63) s_off[E] = inc;
+        if (lane == 63) {
+            s_off[E] = inc & 0xFFFF;
+            *s_ng = (p.dm.fs > 0 ? 1 : 0) + (inc >> 16);
+        }
+        if (lane == 0 && p.dm.fs > 0) s_groups[0] = make_int4(E, 0, T, P);
     }
     __syncthreads();
+}
+__device__ void fused_place(const ExpertParams& p, const int* s_sel, const float* s_wt, const unsigned* s_mask,
+                            const int* s_off, int* s_sp, int* s_pos, float* s_swt) {
+    const int k = p.dm.k, P = k * p.dm.T;
+    const int tid = threadIdx.x;
     if (tid < P) {
         const int key = s_sel[tid];
         const int pos = s_off[key] + __popc(s_mask[key] & ((1u << (tid / k)) - 1u));
@@ -1543,42 +1568,25 @@ __device__ void fused_sort(const ExpertParams& p, const int* s_sel, const float*
         s_pos[tid] = pos;
         s_swt[pos] = s_wt[tid];
     }
-    if (wave == 0) {
-        const unsigned long long lt = (1ull << lane) - 1ull;
-        int n = 0;
-        if (p.dm.fs > 0) {
-            if (lane == 0) s_groups[0] = make_int4(E, 0, T, P);
-            n = 1;
-        }
-        for (int e0 = 0; e0 < E; e0 += 64) {
-            const int e = e0 + lane;
-            const int c = e < E ? __popc(s_mask[e]) : 0;
-            const unsigned long long act = __ballot(c > 0);
-            if (c > 0) s_groups[n + __popcll(act & lt)] = make_int4(e, s_off[e], c, s_off[e]);
-            n += __popcll(act);
-        }
-        if (lane == 0) *s_ng = n;
-    }
-    __syncthreads();
+    // a workgroup barrier for the LDS writes alone: the gate/up weight loads
+    // issued before it stay in flight
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    barrier_keep_loads();
 }
 
 // One gate/up item (group g, features 8 fb .. 8 fb + 7): the body of
 // gateup_mfma_kernel with the sorted pairs from LDS and h stored at agent scope.
+// Its weight loads (16 rows x d into the wave's part of s_w), on their own so
+// that they can be issued before the item runs.
 template <int NSTEP>
-__device__ void fused_gateup_item(const ExpertParams& p, const int4& g, int fb, const int* s_sp, unsigned char* s_w,
-                                  float (&s_part)[4][256], uint16_t (&s_h)[16][3][8]) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int row = lane & 15, q = lane >> 4;
+__device__ __forceinline__ void fused_gateup_issue(const ExpertParams& p, const int4& g, int fb, unsigned char* s_w) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int d = p.dm.d;
     const bool is_shared = g.x == p.dm.E;
     const int F = is_shared ? p.dm.fs : p.dm.f;
     const int j0 = fb * 8;
-    const int sp = is_shared ? 0 : s_sp[g.y + (row < g.z ? row : g.z - 1)];
     const size_t e = is_shared ? 0 : (size_t)g.x;
     const uint16_t* gu = static_cast<const uint16_t*>(is_shared ? p.shared.gu : p.routed.gu);
-    const int kl = wave * (d / 4) + 8 * q;
-    const __amdgpu_buffer_rsrc_t xv = buffer_view(p.x, (uint32_t)p.dm.T * d * 2);
-    uint4 b[NSTEP];
     unsigned char* sw = s_w + wave * (16 * 64 * NSTEP);
     const int kw = wave * (d / 4);
 #pragma unroll
@@ -1588,8 +1596,32 @@ __device__ void fused_gateup_item(const ExpertParams& p, const int4& g, int fb, 
         const int c = (lane & 7) ^ (r & 7);
         __builtin_amdgcn_global_load_lds(gu + wrr * d + kw + 64 * (i >> 1) + 8 * c, sw + i * 1024, 16, 0, 2);
     }
+}
+// issued: fused_gateup_issue has run for this item already
+template <int NSTEP>
+__device__ void fused_gateup_item(const ExpertParams& p, const int4& g, int fb, const int* s_sp, unsigned char* s_w,
+                                  float (&s_part)[4][256], uint16_t (&s_h)[16][3][8], bool issued) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = lane & 15, q = lane >> 4;
+    const int d = p.dm.d;
+    const bool is_shared = g.x == p.dm.E;
+    const int j0 = fb * 8;
+    const int sp = is_shared ? 0 : s_sp[g.y + (row < g.z ? row : g.z - 1)];
+    const int kl = wave * (d / 4) + 8 * q;
+    const __amdgpu_buffer_rsrc_t xv = buffer_view(p.x, (uint32_t)p.dm.T * d * 2);
+    uint4 b[NSTEP];
+    unsigned char* sw = s_w + wave * (16 * 64 * NSTEP);
+    if (!issued) fused_gateup_issue<NSTEP>(p, g, fb, s_w);
     uint4 a0[NSTEP];
     gateup_load_x<NSTEP>(p, g, is_shared, 0, sp, xv, kl, a0);
+    // the weights have landed once at most the NSTEP activation loads issued
+    // after them are in flight (vector loads retire in order).  Stated here
+    // because the weights may have been issued before this item's code: the
+    // compiler does not wait for them by itself then.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (NSTEP & 15) | ((NSTEP >> 4) << 14));  // vmcnt(NSTEP)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
     const uint32_t rbase = (uint32_t)((row >> 3) * 1024 + (row & 7) * 128);
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
@@ -1705,15 +1737,22 @@ __global__ __launch_bounds__(256) void decode_fused_kernel(FusedParams P) {
             tree_release(fbar, 0, nwait, gen);
         }
     } else if (bid - E < fs_items) {
-        fused_gateup_item<NSTEP>(p, make_int4(E, 0, T, k * T), bid - E, s_sp, s_w, s_part, s_h);
+        fused_gateup_item<NSTEP>(p, make_int4(E, 0, T, k * T), bid - E, s_sp, s_w, s_part, s_h, false);
     }
     tree_wait(fbar, 0, bid, gen);
 
-    // ---- phase 1: routing, redundantly in every workgroup ----
+    // ---- phase 1: routing, redundantly in every workgroup.  Once the group
+    // list is known, the weight loads of the workgroup's first gate/up item
+    // are issued; the rest of the sort runs while they fly. ----
     fused_topk(p, reinterpret_cast<float*>(s_w), s_sel, s_wt);
     __syncthreads();
-    fused_sort(p, s_sel, s_wt, s_mask, s_off, s_sp, s_pos, s_swt, s_groups, &s_ng);
+    fused_groups(p, s_sel, s_mask, s_off, s_groups, &s_ng);
     const int ng = s_ng;
+    const int g0 = p.dm.fs > 0 ? 1 : 0;
+    const int n_up = (ng - g0) * f_items;
+    const int first_up = (bid & 7) + 8 * (bid >> 3);
+    if (first_up < n_up) fused_gateup_issue<NSTEP>(p, s_groups[g0 + first_up / f_items], first_up % f_items, s_w);
+    fused_place(p, s_sel, s_wt, s_mask, s_off, s_sp, s_pos, s_swt);
     if (bid == 0) {  // the routing of this forward, for flint_moe_get_routing
         for (int i = threadIdx.x; i < k * T; i += blockDim.x) {
             p.ws.sel[i] = s_sel[i];
@@ -1733,18 +1772,20 @@ __global__ __launch_bounds__(256) void decode_fused_kernel(FusedParams P) {
     // workgroup's first item is its rank in its XCD, the following ones come
     // from the XCD's counter, fetched while the current item runs, so the
     // workgroups that stream faster take more items. ----
-    const int g0 = p.dm.fs > 0 ? 1 : 0;
-    const int n_up = (ng - g0) * f_items;
     {
         const int x = bid & 7, per_xcd = G >> 3;
         int* ctr = bar_queue(fbar, x);
+        // with no more items than workgroups every item is some workgroup's
+        // first: no counter (its fetch would wait for everything in flight)
+        const bool dyn = n_up > 8 * per_xcd;
         int i = bid >> 3;
         while (x + 8 * i < n_up) {  // uniform
-            int next = 0;
-            if (threadIdx.x == 0)
+            int next = per_xcd;
+            if (dyn && threadIdx.x == 0)
                 next = per_xcd + __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             const int j = x + 8 * i;
-            fused_gateup_item<NSTEP>(p, s_groups[g0 + j / f_items], j % f_items, s_sp, s_w, s_part, s_h);
+            fused_gateup_item<NSTEP>(p, s_groups[g0 + j / f_items], j % f_items, s_sp, s_w, s_part, s_h,
+                                     j == first_up);
             if (threadIdx.x == 0) s_next = next;
             __syncthreads();
             i = s_next;
@@ -1775,11 +1816,12 @@ __global__ __launch_bounds__(256) void decode_fused_kernel(FusedParams P) {
     }
 
     // ---- phase 3: down items and the combine ----
+    const bool dyn_down = n_down > 8 * per_xcd;
     while (xd + 8 * id < n_down) {  // uniform
         const int j = xd + 8 * id;
         if (j != j0) fused_down_weights<NSMAX>(p, s_groups[j / rblocks], j % rblocks, bw);
-        int next = 0;
-        if (threadIdx.x == 0)
+        int next = per_xcd;
+        if (dyn_down && threadIdx.x == 0)
             next = per_xcd + __hip_atomic_fetch_add(bar_queue(fbar, 8 + xd), 1, __ATOMIC_RELAXED,
                                                     __HIP_MEMORY_SCOPE_AGENT);
         fused_down_item<NSMAX>(p, s_groups[j / rblocks], j % rblocks, ng, bw, s_swt, s_pos, s_dpart, &s_flag);

@@ -107,6 +107,11 @@ hipError_t launch_gateup_prefill(const LayerArgs& a, const Workspace& w, int n_c
 hipError_t launch_down_prefill(const LayerArgs& a, const Workspace& w, int n_cu, hipStream_t s);
 hipError_t launch_combine(const LayerArgs& a, const Workspace& w, hipStream_t s);
 hipError_t launch_rmsnorm(int T, int d, const float* in, float eps, void* out, hipStream_t s);
+constexpr int kCombineMaxK = 8;  // the largest top_k a configuration may ask for
+// The combine and the next layer's pre-norm in one launch (out fp32, norm bf16);
+// combine_norm_ok: the shapes it takes
+bool combine_norm_ok(const Dims& dm);
+hipError_t launch_combine_norm(const LayerArgs& a, const Workspace& w, float eps, void* norm, hipStream_t s);
 // p[0 .. n) = v (a plain kernel, no memset node, so it is safe under graph capture)
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 

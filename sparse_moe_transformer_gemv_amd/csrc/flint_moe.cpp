@@ -249,10 +249,22 @@ struct Timer {
 
 // The forward on handle state h (a created handle, or the stack-built state of
 // flint_moe_forward_noalloc over the static scratch).
+// The combine launch, or with norm_out the combine and the next layer's
+// pre-norm (one launch where the shape allows, else the combine and then the
+// RMSNorm kernel).
+hipError_t combine_step(flint_moe* h, const LayerArgs& a, hipStream_t stream, float eps, void* norm_out) {
+    Timer tm(h, FLINT_KERNEL_COMBINE, stream);
+    if (!norm_out) return launch_combine(a, h->ws, stream);
+    if (combine_norm_ok(a.dm)) return launch_combine_norm(a, h->ws, eps, norm_out, stream);
+    hipError_t e = launch_combine(a, h->ws, stream);
+    if (e == hipSuccess) e = launch_rmsnorm(a.dm.T, a.dm.d, static_cast<const float*>(a.out), eps, norm_out, stream);
+    return e;
+}
+
 flint_status forward_impl(flint_moe* h, int32_t T, const void* hidden, const float* router_w,
                           const float* router_bias, const flint_expert_weights* experts,
                           const flint_expert_weights* shared, const float* residual, void* out,
-                          hipStream_t stream) {
+                          hipStream_t stream, float eps = 0.f, void* norm_out = nullptr) {
     const flint_moe_config& c = h->cfg;
     if (T < 0 || T > c.max_tokens)
         return fail(FLINT_ERR_INVALID_ARG, "T=%d outside 0..max_tokens=%d", T, c.max_tokens);
@@ -277,6 +289,18 @@ flint_status forward_impl(flint_moe* h, int32_t T, const void* hidden, const flo
     if (residual && residual != out &&
         overlap(residual, (size_t)T * c.d_model * 4, out, obytes))
         return fail(FLINT_ERR_INVALID_ARG, "out partially overlaps residual");
+    if (norm_out) {
+        const size_t nbytes = (size_t)T * c.d_model * 2;
+        if (!residual)
+            return fail(FLINT_ERR_INVALID_ARG, "the pre-norm output needs the fp32 residual form");
+        if (!aligned(norm_out, 16))
+            return fail(FLINT_ERR_INVALID_ARG, "norm_out must be 16-byte aligned");
+        if (!(eps >= 0.f) || eps > 1.f)
+            return fail(FLINT_ERR_INVALID_ARG, "eps %g outside 0..1", (double)eps);
+        if (overlap(norm_out, nbytes, out, obytes) || overlap(norm_out, nbytes, hidden, xbytes) ||
+            overlap(norm_out, nbytes, residual, (size_t)T * c.d_model * 4))
+            return fail(FLINT_ERR_INVALID_ARG, "norm_out overlaps hidden, residual or out");
+    }
 
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
@@ -340,10 +364,7 @@ flint_status forward_impl(flint_moe* h, int32_t T, const void* hidden, const flo
             e = launch_down_prefill(a, h->ws, h->n_cu, stream);
         }
         if (e != hipSuccess) return hip_fail(e, "down kernel");
-        {
-            Timer tm(h, FLINT_KERNEL_COMBINE, stream);
-            e = launch_combine(a, h->ws, stream);
-        }
+        e = combine_step(h, a, stream, eps, norm_out);
         if (e != hipSuccess) return hip_fail(e, "combine kernel");
         h->last_T = T;
         return ok();
@@ -356,6 +377,8 @@ flint_status forward_impl(flint_moe* h, int32_t T, const void* hidden, const flo
                 e = launch_decode_fused(a, h->ws, G, stream);
             }
             if (e != hipSuccess) return hip_fail(e, "single-launch decode kernel");
+            if (norm_out) e = launch_rmsnorm(T, c.d_model, static_cast<const float*>(out), eps, norm_out, stream);
+            if (e != hipSuccess) return hip_fail(e, "rmsnorm kernel");
             h->last_T = T;
             return ok();
         }
@@ -378,10 +401,10 @@ flint_status forward_impl(flint_moe* h, int32_t T, const void* hidden, const flo
         e = launch_down_decode(a, h->ws, stream);
     }
     if (e != hipSuccess) return hip_fail(e, "down kernel");
-    if (!down_decode_combines(a.dm)) {
-        Timer tm(h, FLINT_KERNEL_COMBINE, stream);
-        e = launch_combine(a, h->ws, stream);
-    }
+    if (!down_decode_combines(a.dm))
+        e = combine_step(h, a, stream, eps, norm_out);
+    else if (norm_out)
+        e = launch_rmsnorm(T, c.d_model, static_cast<const float*>(out), eps, norm_out, stream);
     if (e != hipSuccess) return hip_fail(e, "combine kernel");
     h->last_T = T;
     return ok();
@@ -467,6 +490,16 @@ flint_status flint_moe_forward(flint_moe_t h, int32_t T, const void* hidden, con
                                void* out, hipStream_t stream) {
     if (!h) return fail(FLINT_ERR_INVALID_ARG, "handle is NULL");
     return forward_impl(h, T, hidden, router_w, router_bias, experts, shared, residual, out, stream);
+}
+
+flint_status flint_moe_forward_prenorm(flint_moe_t h, int32_t T, const void* hidden, const float* router_w,
+                                       const float* router_bias, const flint_expert_weights* experts,
+                                       const flint_expert_weights* shared, const float* residual, float* out,
+                                       float eps, void* norm_out, hipStream_t stream) {
+    if (!h) return fail(FLINT_ERR_INVALID_ARG, "handle is NULL");
+    if (!residual || !norm_out) return fail(FLINT_ERR_INVALID_ARG, "residual and norm_out must be non-NULL");
+    return forward_impl(h, T, hidden, router_w, router_bias, experts, shared, residual, out, stream, eps,
+                        norm_out);
 }
 
 flint_status flint_moe_forward_noalloc(const flint_moe_config* cfg, int32_t T, const void* hidden,

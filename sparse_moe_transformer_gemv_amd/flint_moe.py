@@ -35,6 +35,7 @@ EXPORTED = [
     "flint_moe_create", "flint_moe_forward", "flint_moe_get_routing", "flint_moe_profile_begin",
     "flint_moe_profile_end", "flint_moe_destroy", "flint_status_string", "flint_last_error",
     "flint_rmsnorm_forward", "flint_moe_forward_noalloc", "flint_moe_get_fault",
+    "flint_moe_forward_prenorm",
 ]
 
 
@@ -83,6 +84,9 @@ def load_library(path: str = LIB_PATH):
     L.flint_moe_get_routing.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(i32), vp]
     L.flint_moe_get_routing.restype = st
     L.flint_moe_get_fault.argtypes = [vp, vp, vp]
+    L.flint_moe_forward_prenorm.argtypes = [vp, i32, vp, vp, vp, ctypes.POINTER(flint_expert_weights),
+                                            ctypes.POINTER(flint_expert_weights), vp, vp, ctypes.c_float, vp, vp]
+    L.flint_moe_forward_prenorm.restype = st
     L.flint_moe_get_fault.restype = st
     L.flint_moe_profile_begin.argtypes = [vp, i32, i32]
     L.flint_moe_profile_begin.restype = st
@@ -309,6 +313,33 @@ class MoELayer:
         return out
 
     __call__ = forward
+
+    def forward_prenorm(self, x: torch.Tensor, router_w: torch.Tensor, experts: ExpertWeights,
+                        shared: Optional[ExpertWeights], residual: torch.Tensor, eps: float = 1e-6,
+                        router_bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                        norm_out: Optional[torch.Tensor] = None):
+        """One pre-norm residual step: out = residual + MoE(x) (fp32) and
+        norm_out = bf16(RMSNorm(out)), the next layer's input.  Returns (out, norm_out)."""
+        c = self.cfg
+        if residual is None:
+            raise ValueError("forward_prenorm needs the fp32 residual")
+        check_forward_args(c, self.device, x, router_w, experts, shared, router_bias, residual, out)
+        T = x.shape[0]
+        if out is None:
+            out = torch.empty((T, c.d_model), dtype=torch.float32, device=x.device)
+        if norm_out is None:
+            norm_out = torch.empty((T, c.d_model), dtype=torch.bfloat16, device=x.device)
+        _expect(norm_out, "norm_out", T * c.d_model, torch.bfloat16, self.device)
+        ew = experts.as_c(c.weight_dtype)
+        sw = shared.as_c(c.weight_dtype) if shared is not None else None
+        _check(load_library().flint_moe_forward_prenorm(
+            self.handle, T, _ptr(x, "x", _TORCH_ACT[c.act_dtype]),
+            _ptr(router_w, "router_w", torch.float32),
+            _ptr(router_bias, "router_bias", torch.float32), ctypes.byref(ew),
+            ctypes.byref(sw) if sw is not None else None,
+            _ptr(residual, "residual", torch.float32), _ptr(out, "out"), float(eps),
+            _ptr(norm_out, "norm_out"), _stream()))
+        return out, norm_out
 
     def routing(self) -> dict:
         """Routing of the last forward: idx, weights, sorted_pair, counts, logits."""

@@ -139,18 +139,18 @@ def check_permutation(rout, T, k, E):
     assert np.array_equal(rout["counts"], np.bincount(keys, minlength=E))
 
 
-def stack_layer_gpu(moe, h: torch.Tensor, D: dict, x: torch.Tensor, eps: float = 1e-6,
-                    record: bool = False):
+def stack_layer_gpu(moe, h: torch.Tensor, D: dict, x: torch.Tensor, x_next: torch.Tensor,
+                    eps: float = 1e-6, record: bool = False):
     """One layer of the stacked workload on the GPU, in place on the fp32
-    residual h [T, d]: x = bf16(RMSNorm(h)) (rmsnorm kernel), then
-    h += MoE(x) (the layer's combine adds the fp32 residual).  With record,
-    returns host copies of h before and after, x, and the routing."""
-    from sparse_moe_transformer_gemv_amd import flint_rmsnorm_forward
+    residual h [T, d]: x holds bf16(RMSNorm(h)) on entry; h += MoE(x) (the
+    layer's combine adds the fp32 residual) and x_next = bf16(RMSNorm(h)),
+    the next layer's input, from the same launch where the path allows.  With
+    record, returns host copies of h before and after, x, and the routing."""
     rec = None
     if record:
         h_before = out_host(h)
-    flint_rmsnorm_forward(h, eps, out=x)
-    moe.forward(x, D["router_w"], D["experts"], D["shared"], D["router_bias"], residual=h, out=h)
+    moe.forward_prenorm(x, D["router_w"], D["experts"], D["shared"], residual=h, eps=eps,
+                        router_bias=D["router_bias"], out=h, norm_out=x_next)
     if record:
         r = moe.routing()
         torch.cuda.synchronize()
@@ -162,10 +162,15 @@ def stack_layer_gpu(moe, h: torch.Tensor, D: dict, x: torch.Tensor, eps: float =
 
 
 def stack_gpu(moe, h: torch.Tensor, layers, eps: float = 1e-6):
-    """The whole stacked pass on the GPU (no read-back)."""
+    """The whole stacked pass on the GPU (no read-back): the first pre-norm by
+    the RMSNorm kernel, every later one by the layer before it."""
+    from sparse_moe_transformer_gemv_amd import flint_rmsnorm_forward
     x = torch.empty(h.shape, dtype=torch.bfloat16, device=h.device)
+    xn = torch.empty_like(x)
+    flint_rmsnorm_forward(h, eps, out=x)
     for D in layers:
-        stack_layer_gpu(moe, h, D, x, eps)
+        stack_layer_gpu(moe, h, D, x, xn, eps)
+        x, xn = xn, x
 
 
 def teacher_forced_layer(rec: dict, L: dict, k: int, eps: float = 1e-6):

@@ -89,6 +89,8 @@ def test_null_handle_calls_are_rejected():
                                    None) == b.FLINT_ERR_INVALID_ARG
     assert L.flint_moe_profile_begin(None, 0, 1) == b.FLINT_ERR_INVALID_ARG
     assert L.flint_moe_get_fault(None, None, None) == b.FLINT_ERR_INVALID_ARG
+    assert L.flint_moe_forward_prenorm(None, 1, None, None, None, None, None, None, None, 1e-6, None,
+                                       None) == b.FLINT_ERR_INVALID_ARG
     n = ctypes.c_int32(0)
     assert L.flint_moe_profile_end(None, None, 0, ctypes.byref(n)) == b.FLINT_ERR_INVALID_ARG
 

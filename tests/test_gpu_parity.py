@@ -19,7 +19,7 @@ from gpu_helpers import (check_layer, check_permutation, check_selection, compar
                          dev_layer, make_layer_obj, out_host, run_gpu, run_oracle,
                          stack_layer_gpu, teacher_forced_layer, x_device)
 from sparse_moe_transformer_gemv_amd import (FLINT_FORCE_DECODE_PATH, FLINT_FORCE_PREFILL_PATH,
-                                             FlintError)
+                                             FlintError, flint_rmsnorm_forward)
 
 pytestmark = pytest.mark.gpu
 
@@ -447,12 +447,15 @@ def _stack_teacher_forced(n_layers, T, **override):
     h0 = synth.hidden(cfg, T, c["d"], synth.F32)
     h = dev_array(h0.copy())
     x = torch.empty((T, c["d"]), dtype=torch.bfloat16, device="cuda")
+    xn = torch.empty_like(x)
+    flint_rmsnorm_forward(h, 1e-6, out=x)
     h_ref = h0.astype(np.float64)
     worst, flips, flipped = 0.0, 0, np.zeros(T, bool)
     for l in range(n_layers):
         L = synth.layer(cfg, l, **override)
         D = dev_layer(L)
-        rec = stack_layer_gpu(moe, h, D, x, record=True)
+        rec = stack_layer_gpu(moe, h, D, x, xn, record=True)
+        x, xn = xn, x
         rep = teacher_forced_layer(rec, L, c["k"])
         worst = max(worst, rep["ratio"])
         if l % 8 == 0 or l == n_layers - 1:
@@ -472,6 +475,34 @@ def _stack_teacher_forced(n_layers, T, **override):
     print("stack %d layers T=%d %s: worst teacher-forced layer ratio %.4f; end to end (reported): "
           "max|err|/RMS %.4f, %d selection flips in %d tokens" % (
               n_layers, T, override, worst, e2e, flips, int(flipped.sum())), flush=True)
+
+
+@pytest.mark.parametrize("cfg_id,T,flags,over", [
+    (1, 32, 0, dict(d=512, E=64, f=128, fs=128)),                          # combine kernel with the norm
+    (1, 4, 0, dict(d=512, E=64, f=128, fs=128)),                           # single launch, then the norm
+    (1, 12, 0, dict(d=512, E=64, f=128, fs=128)),                          # combine folded into down
+    (1, 200, FLINT_FORCE_PREFILL_PATH, dict(d=256, E=64, f=128, fs=128)),  # prefill path
+    (4, 2, 0, dict(d=512, E=32, k=4, f=512, fs=512)),                      # NVFP4
+    (1, 32, 0, dict(d=8192, E=16, k=2, f=128, fs=128)),                    # d past the one-launch form
+])
+def test_forward_prenorm_matches_forward_then_rmsnorm(cfg_id, T, flags, over):
+    # the pre-norm output of the stacked step equals, bit for bit, the layer's
+    # forward followed by the RMSNorm kernel; out may be the residual itself
+    L = synth.layer(cfg_id, **over)
+    c = L["cfg"]
+    D = dev_layer(L)
+    x = x_device(synth.hidden(cfg_id, T, c["d"], c["act"], draw=5))
+    h0 = dev_array(np.random.default_rng(8).standard_normal((T, c["d"])).astype(np.float32))
+    layer = make_layer_obj(c, max(T, 64), flags)
+    ref_out = layer.forward(x, D["router_w"], D["experts"], D["shared"], D["router_bias"], residual=h0)
+    ref_norm = flint_rmsnorm_forward(ref_out, 1e-6)
+    h = h0.clone()
+    out, norm = layer.forward_prenorm(x, D["router_w"], D["experts"], D["shared"], residual=h, eps=1e-6,
+                                      router_bias=D["router_bias"], out=h)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out), "the layer output differs"
+    assert torch.equal(norm.view(torch.int16), ref_norm.view(torch.int16)), "the pre-norm output differs"
+    print("prenorm cfg=%d T=%d %s: equal to forward + rmsnorm" % (cfg_id, T, over), flush=True)
 
 
 def test_stack_47_layers_small_shape():
