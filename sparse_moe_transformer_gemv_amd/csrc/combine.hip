@@ -88,48 +88,75 @@ __global__ __launch_bounds__(256) void combine_norm_kernel(CombineParams p, floa
     int slot[kCombineMaxK];
 #pragma unroll
     for (int j = 0; j < kCombineMaxK; ++j) slot[j] = j < p.k ? p.pair_pos[(size_t)t * p.k + j] : 0;
+    // every load of the row is issued before the first store (a load issued
+    // after a store would wait for it: they share one in-order counter); loads
+    // of absent terms get an offset past their view and return zeros
+    const __amdgpu_buffer_rsrc_t rview =
+        buffer_view(p.residual ? p.residual + (size_t)t * p.d : p.y, p.residual ? (uint32_t)p.d * 4 : 0u);
+    const __amdgpu_buffer_rsrc_t yview = buffer_view(p.y, (uint32_t)((kT + p.T) * p.d * 4));
+    float4 r[kNormChunks], sh[kNormChunks], yv[kNormChunks][kCombineMaxK];
+#pragma unroll
+    for (int i = 0; i < kNormChunks; ++i) {
+        const int c = threadIdx.x * 4 + 1024 * i;
+        const bool in = c < p.d;
+        r[i] = __builtin_bit_cast(float4, buffer_load16(rview, in ? (uint32_t)c * 4 : kOffNone));
+        sh[i] = __builtin_bit_cast(
+            float4, buffer_load16(yview, in && p.has_shared ? (uint32_t)(((kT + t) * p.d + c) * 4) : kOffNone));
+#pragma unroll
+        for (int j = 0; j < kCombineMaxK; ++j)
+            yv[i][j] = __builtin_bit_cast(
+                float4, buffer_load16(yview, in && j < p.k ? (uint32_t)(((size_t)slot[j] * p.d + c) * 4) : kOffNone));
+    }
     float4 v[kNormChunks];
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < kNormChunks; ++i) {
         const int c = threadIdx.x * 4 + 1024 * i;
-        if (c >= p.d) break;
+        if (c >= p.d) continue;
+        // residual, shared row, routed rows in pair order, as combine_kernel
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         if (p.residual) {
-            const float4 r = *reinterpret_cast<const float4*>(p.residual + (size_t)t * p.d + c);
-            acc[0] = r.x; acc[1] = r.y; acc[2] = r.z; acc[3] = r.w;
+            acc[0] = r[i].x; acc[1] = r[i].y; acc[2] = r[i].z; acc[3] = r[i].w;
         }
         if (p.has_shared) {
-            const float4 y = *reinterpret_cast<const float4*>(p.y + (kT + t) * p.d + c);
-            acc[0] += y.x; acc[1] += y.y; acc[2] += y.z; acc[3] += y.w;
+            acc[0] += sh[i].x; acc[1] += sh[i].y; acc[2] += sh[i].z; acc[3] += sh[i].w;
         }
 #pragma unroll
         for (int j = 0; j < kCombineMaxK; ++j) {
-            if (j >= p.k) break;
-            const float4 y = *reinterpret_cast<const float4*>(p.y + (size_t)slot[j] * p.d + c);
-            acc[0] += y.x; acc[1] += y.y; acc[2] += y.z; acc[3] += y.w;
+            if (j < p.k) {
+                acc[0] += yv[i][j].x; acc[1] += yv[i][j].y; acc[2] += yv[i][j].z; acc[3] += yv[i][j].w;
+            }
         }
         v[i] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        *reinterpret_cast<float4*>(static_cast<float*>(p.out) + (size_t)t * p.d + c) = v[i];
         ss = fmaf(v[i].x, v[i].x, ss);
         ss = fmaf(v[i].y, v[i].y, ss);
         ss = fmaf(v[i].z, v[i].z, ss);
         ss = fmaf(v[i].w, v[i].w, ss);
     }
-    const float r = rms_scale(ss, p.d, eps, s_part);
+#pragma unroll
+    for (int i = 0; i < kNormChunks; ++i) {
+        const int c = threadIdx.x * 4 + 1024 * i;
+        if (c >= p.d) break;
+        *reinterpret_cast<float4*>(static_cast<float*>(p.out) + (size_t)t * p.d + c) = v[i];
+    }
+    const float rs = rms_scale(ss, p.d, eps, s_part);
     uint16_t* orow = norm + (size_t)t * p.d;
 #pragma unroll
     for (int i = 0; i < kNormChunks; ++i) {
         const int c = threadIdx.x * 4 + 1024 * i;
         if (c >= p.d) break;
         uint2 o;
-        o.x = (uint32_t)f32_to_bf16(v[i].x * r) | ((uint32_t)f32_to_bf16(v[i].y * r) << 16);
-        o.y = (uint32_t)f32_to_bf16(v[i].z * r) | ((uint32_t)f32_to_bf16(v[i].w * r) << 16);
+        o.x = (uint32_t)f32_to_bf16(v[i].x * rs) | ((uint32_t)f32_to_bf16(v[i].y * rs) << 16);
+        o.y = (uint32_t)f32_to_bf16(v[i].z * rs) | ((uint32_t)f32_to_bf16(v[i].w * rs) << 16);
         *reinterpret_cast<uint2*>(orow + c) = o;
     }
 }
 
-bool combine_norm_ok(const Dims& dm) { return dm.d % 4 == 0 && dm.d <= 1024 * kNormChunks; }
+bool combine_norm_ok(const Dims& dm) {
+    // the y rows are read through one buffer view, whose offsets are 32-bit
+    return dm.d % 4 == 0 && dm.d <= 1024 * kNormChunks &&
+           (size_t)(dm.k + 1) * dm.T * dm.d * 4 < (size_t)kOffNone;
+}
 
 hipError_t launch_combine_norm(const LayerArgs& a, const Workspace& w, float eps, void* norm, hipStream_t s) {
     CombineParams p;

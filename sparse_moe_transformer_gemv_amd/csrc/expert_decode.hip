@@ -1418,12 +1418,9 @@ __device__ void fused_router_expert(const FusedParams& P, int e, float (&s_red)[
     }
 }
 
-// Top-k of every token, one wavefront per token (tokens wave, wave + 4, ...).
-// The logits come into LDS first, with one round of 16-byte agent-scope loads
-// by the whole workgroup.  Lane l holds the order-preserving keys of experts
-// 4 l .. 4 l + 3; each round takes the wavefront maximum, and the lowest lane
-// holding it, then the lowest slot in that lane, give the lowest expert index
-// among equal logits.  Weights: softmax of the chosen logits.  Results in LDS.
+// Top-k of every token, one wavefront per token (tokens wave, wave + 4, ...,
+// topk_token_lds).  The logits come into LDS first, with one round of 16-byte
+// agent-scope loads by the whole workgroup.  Results in LDS.
 __device__ void fused_topk(const ExpertParams& p, float* s_logit, int* s_sel, float* s_wt) {
     const int T = p.dm.T, E = p.dm.E, k = p.dm.k;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1442,58 +1439,12 @@ __device__ void fused_topk(const ExpertParams& p, float* s_logit, int* s_sel, fl
     }
     __syncthreads();
     for (int t = wave; t < T; t += 4) {
-        // the lane's 4 keys sorted in descending order (equal keys keep the
-        // lower expert first), with their expert ids
-        uint32_t key[4];
-        int eid[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = 4 * lane + i;
-            key[i] = e < E ? order_key(s_logit[t * E + e]) : 0u;
-            eid[i] = e;
-        }
-#pragma unroll
-        for (int a = 0; a < 3; ++a)
-#pragma unroll
-            for (int b2 = 0; b2 < 3 - a; ++b2)
-                if (key[b2 + 1] > key[b2]) {
-                    const uint32_t tk = key[b2];
-                    key[b2] = key[b2 + 1];
-                    key[b2 + 1] = tk;
-                    const int te = eid[b2];
-                    eid[b2] = eid[b2 + 1];
-                    eid[b2 + 1] = te;
-                }
-        // each round: the wavefront maximum of the lanes' heads; the lowest lane
-        // holding it wins (lane l holds experts 4 l .. 4 l + 3, so that is the
-        // lowest expert index among equal logits) and pops its head
-        float lsel = 0.f;
-        int esel = 0;
-        float l0 = 0.f;
-#pragma unroll
-        for (int j = 0; j < kCombineMaxK; ++j) {
-            if (j >= k) break;  // uniform
-            const uint32_t M = wave_max_u32(key[0]);
-            const int L = __builtin_ctzll(__ballot(key[0] == M));
-            const int ej = __builtin_amdgcn_readlane(eid[0], L);
-            if (lane == L) {
-                key[0] = key[1]; key[1] = key[2]; key[2] = key[3]; key[3] = 0u;
-                eid[0] = eid[1]; eid[1] = eid[2]; eid[2] = eid[3];
-            }
-            const float lj = key_value(M);
-            if (j == 0) l0 = lj;
-            if (lane == j) {
-                lsel = lj;
-                esel = ej;
-            }
-        }
-        // weights: softmax of the chosen logits (hardware exp2 and reciprocal;
-        // about 1 ulp each)
-        const float pj = lane < k ? __builtin_amdgcn_exp2f((lsel - l0) * 1.4426950408889634f) : 0.f;
-        const float sum = wave_sum(pj);
+        int e;
+        float w;
+        topk_token_lds(s_logit + t * E, E, k, lane, &e, &w);
         if (lane < k) {
-            s_sel[t * k + lane] = esel;
-            s_wt[t * k + lane] = pj * __builtin_amdgcn_rcpf(sum);
+            s_sel[t * k + lane] = e;
+            s_wt[t * k + lane] = w;
         }
     }
 }
@@ -1509,17 +1460,6 @@ __device__ void fused_topk(const ExpertParams& p, float* s_logit, int* s_sel, fl
 //     ascending), from one pass of wave 0 over 4 experts per lane;
 //   fused_place: the sorted pair list, its inverse and the weight of each
 //     sorted pair.
-__device__ __forceinline__ int wave_incl_scan(int v) {
-    // rows of 16 lanes (row_shr 1, 2, 4, 8; lanes shifted in from outside the
-    // row read 0), then row 15's total into rows 1 and 3, row 31's into 2 and 3
-    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);
-    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);
-    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);
-    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);
-    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);
-    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);
-    return v;
-}
 __device__ void fused_groups(const ExpertParams& p, const int* s_sel, unsigned* s_mask, int* s_off, int4* s_groups,
                              int* s_ng) {
     const int T = p.dm.T, k = p.dm.k, E = p.dm.E, P = k * T;

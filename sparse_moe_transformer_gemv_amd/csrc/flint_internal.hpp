@@ -233,6 +233,72 @@ __device__ __forceinline__ float key_value(uint32_t key) {
     return __uint_as_float((key >> 31) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
+// Inclusive sum over the 64 lanes: rows of 16 lanes (row_shr 1, 2, 4, 8;
+// lanes shifted in from outside the row read 0), then row 15's total into
+// rows 1 and 3 and row 31's into rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);
+    return v;
+}
+
+// Top-k (k <= 8) of one token's E <= 256 logits held in LDS, by one
+// wavefront: lane l takes the order-preserving keys of experts 4 l .. 4 l + 3
+// and sorts them (equal keys keep the lower expert first); each round takes
+// the wavefront maximum of the lanes' heads, the lowest lane holding it wins
+// (which is the lowest expert index among equal logits) and pops its head.
+// Weights: softmax of the chosen logits, hardware exp2 and reciprocal (about
+// 1 ulp each).  Lane j < k returns slot j: *sel (expert) and *w (weight).
+__device__ __forceinline__ void topk_token_lds(const float* lrow, int E, int k, int lane, int* sel, float* w) {
+    uint32_t key[4];
+    int eid[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = 4 * lane + i;
+        key[i] = e < E ? order_key(lrow[e]) : 0u;
+        eid[i] = e;
+    }
+#pragma unroll
+    for (int a = 0; a < 3; ++a)
+#pragma unroll
+        for (int b2 = 0; b2 < 3 - a; ++b2)
+            if (key[b2 + 1] > key[b2]) {
+                const uint32_t tk = key[b2];
+                key[b2] = key[b2 + 1];
+                key[b2 + 1] = tk;
+                const int te = eid[b2];
+                eid[b2] = eid[b2 + 1];
+                eid[b2 + 1] = te;
+            }
+    float lsel = 0.f, l0 = 0.f;
+    int esel = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (j >= k) break;  // uniform
+        const uint32_t M = wave_max_u32(key[0]);
+        const int L = __builtin_ctzll(__ballot(key[0] == M));
+        const int ej = __builtin_amdgcn_readlane(eid[0], L);
+        if (lane == L) {
+            key[0] = key[1]; key[1] = key[2]; key[2] = key[3]; key[3] = 0u;
+            eid[0] = eid[1]; eid[1] = eid[2]; eid[2] = eid[3];
+        }
+        const float lj = key_value(M);
+        if (j == 0) l0 = lj;
+        if (lane == j) {
+            lsel = lj;
+            esel = ej;
+        }
+    }
+    const float pj = lane < k ? __builtin_amdgcn_exp2f((lsel - l0) * 1.4426950408889634f) : 0.f;
+    const float sum = wave_sum(pj);
+    *sel = esel;
+    *w = pj * __builtin_amdgcn_rcpf(sum);
+}
+
 // Raw buffer view of [base, base + bytes): a load whose offset lies at or past
 // the end returns zeros without touching memory, which is how kernels skip the
 // rows of a 16-row MFMA tile that hold no token.  Offsets are 32-bit; kOffNone

@@ -173,81 +173,6 @@ __device__ void write_groups(const int* s_off, int E, int T, int k, bool has_sha
     }
 }
 
-// The same results as block_sort_and_groups (decode lists, no tiles) for at
-// most 64 pairs, by one wavefront.  Each pair's rank comes from ballots over
-// the 8 key bits (the pairs with a smaller expert id, then those with the same
-// id and a lower index: a stable order); the keys are put in sorted order
-// through LDS, group starts come from one neighbour exchange, and the counts
-// are built in LDS and scanned once.  Chains of cross-lane exchanges (a
-// bitonic network, binary searches) measured several microseconds here:
-// each exchange waits for the previous one.  keys/wts: the block's pairs in
-// LDS; s_tmp: LDS scratch of 64 + 256 ints.
-__device__ void wave_sort_small(const int* keys, const float* wts, int P, int E, int T, int k, bool has_shared,
-                                const Workspace& ws, int* s_tmp, int lane) {
-    int* s_key = s_tmp;       // [64] expert ids in sorted order
-    int* s_cnt = s_tmp + 64;  // [256] pairs per expert
-    const unsigned long long lt = (1ull << lane) - 1ull;
-    const bool valid = lane < P;
-    const int key = valid ? keys[lane] : 0;
-    const float w = valid ? wts[lane] : 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s_cnt[4 * lane + i] = 0;
-    unsigned long long eq = __ballot(valid);  // lanes equal to this one on the bits seen so far
-    int below = 0;
-#pragma unroll
-    for (int b = 7; b >= 0; --b) {
-        const bool bit = (key >> b) & 1;
-        const unsigned long long ones = __ballot(valid && bit);
-        if (bit) below += __popcll(eq & ~ones);
-        eq &= bit ? ones : ~ones;
-    }
-    const int rank = below + __popcll(eq & lt);
-    if (valid) {
-        ws.sorted_pair[rank] = lane;
-        ws.pair_pos[lane] = rank;
-        ws.sorted_wt[rank] = w;
-        s_key[rank] = key;
-    }
-    // (LDS operations of one wavefront take effect in program order)
-    const int skey = valid ? s_key[lane] : E;  // lane p: the expert of the p-th sorted pair
-    const int prev = __shfl_up(skey, 1, 64);
-    const bool start = valid && (lane == 0 || skey != prev);
-    const unsigned long long sm = __ballot(start);
-    const int base = has_shared ? 1 : 0;
-    if (start) {
-        const unsigned long long later = lane < 63 ? sm >> (lane + 1) : 0ull;
-        const int end = later ? lane + 1 + __builtin_ctzll(later) : P;
-        ws.groups[base + __popcll(sm & lt)] = make_int4(skey, lane, end - lane, lane);
-        s_cnt[skey] = end - lane;
-    }
-    if (has_shared && lane == 0) ws.groups[0] = make_int4(E, 0, T, k * T);
-    if (lane == 0) *ws.n_groups = base + __popcll(sm);
-    // counts and their exclusive scan, experts 4 lane .. 4 lane + 3 per lane
-    int c[4], local = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        c[i] = s_cnt[4 * lane + i];
-        local += c[i];
-    }
-    int inc = local;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int v = __shfl_up(inc, off, 64);
-        if (lane >= off) inc += v;
-    }
-    int run = inc - local;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int e = 4 * lane + i;
-        if (e < E) {
-            ws.offsets[e] = run;
-            ws.counts[e] = c[i];
-        }
-        run += c[i];
-    }
-    if (lane == 63) ws.offsets[E] = inc;
-}
-
 // ---------------------------------------------------------------------------
 // Stable counting sort of P pair keys (expert ids < E <= 256) by one block.
 // Writes counts[E], offsets[E+1], sorted_pair[P], pair_pos[P], sorted_wt[P]
@@ -614,16 +539,71 @@ hipError_t launch_route_decode(const LayerArgs& a, const Workspace& w, hipStream
     return hipGetLastError();
 }
 
+// Stable counting sort of the P = k T pairs (T <= 64) by one block of 512
+// threads, from their experts and weights in LDS, with the decode lists of
+// block_sort_and_groups as results.  A token picks an expert at most once, so
+// a 64-bit mask of the tokens that picked each expert gives its count (the
+// population) and each pair's rank among that expert's pairs (the tokens
+// below its own): one LDS OR per pair, one scan by wave 0 over four experts
+// per lane (offsets and the group list together), one placement per pair.
+__device__ void mask_sort_small(const int* s_key, const float* s_w, int P, int E, int T, int k, bool has_shared,
+                                const Workspace& ws, unsigned long long* s_mask, int* s_off) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < E; i += 512) s_mask[i] = 0ull;
+    __syncthreads();
+    if (tid < P) atomicOr(&s_mask[s_key[tid]], 1ull << (tid / k));
+    __syncthreads();
+    if (wave == 0) {
+        int c[4], local = 0, nact = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * lane + i;
+            c[i] = e < E ? __popcll(s_mask[e]) : 0;
+            local += c[i];
+            nact += c[i] > 0 ? 1 : 0;
+        }
+        // (pairs, active experts) up to this lane, packed: at most 512 and 256
+        const int inc = wave_incl_scan(local | (nact << 16));
+        int run = (inc & 0xFFFF) - local;
+        int gi = (has_shared ? 1 : 0) + (inc >> 16) - nact;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * lane + i;
+            if (e < E) {
+                s_off[e] = run;
+                ws.offsets[e] = run;
+                ws.counts[e] = c[i];
+            }
+            if (c[i] > 0) ws.groups[gi++] = make_int4(e, run, c[i], run);
+            run += c[i];
+        }
+        if (lane == 63) {
+            ws.offsets[E] = inc & 0xFFFF;
+            *ws.n_groups = (has_shared ? 1 : 0) + (inc >> 16);
+        }
+        if (lane == 0 && has_shared) ws.groups[0] = make_int4(E, 0, T, P);
+    }
+    __syncthreads();
+    if (tid < P) {
+        const int e = s_key[tid];
+        const int pos = s_off[e] + __popcll(s_mask[e] & ((1ull << (tid / k)) - 1ull));
+        ws.sorted_pair[pos] = tid;
+        ws.pair_pos[tid] = pos;
+        ws.sorted_wt[pos] = s_w[tid];
+    }
+}
+
 constexpr int kRouteSplitMaxT = 64;
 
 template <int NS>  // NS = d / 256 k-chunks
 __global__ __launch_bounds__(512) void route_splitk_kernel(RouteMfmaParams p) {
     constexpr int NW = 8;
     __shared__ float s_part[NW][256];
-    __shared__ int s_hist[NW * 256];
+    __shared__ __attribute__((aligned(16))) float s_logit[16 * 256];
+    __shared__ unsigned long long s_mask[256];
     __shared__ int s_off[257];
-    __shared__ int s_sel[16 * 8];
-    __shared__ float s_wt[16 * 8];
+    __shared__ int s_sel[kRouteSplitMaxT * 8];
+    __shared__ float s_wt[kRouteSplitMaxT * 8];
     __shared__ int s_flag;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, q = lane >> 4;
@@ -682,23 +662,52 @@ __global__ __launch_bounds__(512) void route_splitk_kernel(RouteMfmaParams p) {
         for (int c = 1; c < NS; ++c) v += pv[c];
         st_agent(p.ws.logits + o, v + (p.bias ? p.bias[e0 + n] : 0.f));
     }
-    // 3. the last expert tile of token tile tt selects its tokens' experts
+    // 3. the last expert tile of token tile tt selects its tokens' experts:
+    //    the tile's logits into LDS (16-byte agent-scope loads, all issued
+    //    before the first LDS store), then one wavefront per token
     if (!last_arrival(&p.ws.rcount[ntt * NE + tt], NE, &s_flag)) return;
-    wave_topk_tokens<2>(p.ws.logits, t0, T, E, p.k, wave, lane, p.ws.sel, p.ws.wts, s_sel, s_wt);
-    // 4. the last token tile sorts every pair (from LDS when it is the only one)
-    if (ntt == 1) {
-        __syncthreads();
-        if (p.k * T <= 64) {
-            if (wave == 0) wave_sort_small(s_sel, s_wt, p.k * T, E, T, p.k, p.has_shared != 0, p.ws, s_hist, lane);
-        } else {
-            block_sort_and_groups<512, false>(s_sel, s_wt, p.k * T, E, T, p.k, p.has_shared != 0, 0, p.ws, s_hist,
-                                              s_off);
+    {
+        const int nt = min(16, T - t0);
+        // rounded up within the logits buffer's 256-byte padding
+        const uint32_t bytes = (uint32_t)(nt * E * 4 + 15) & ~15u;
+        const __amdgpu_buffer_rsrc_t lv = buffer_view(p.ws.logits + (size_t)t0 * E, bytes);
+        uint4 lg[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) lg[i] = buffer_load16_agent(lv, (uint32_t)(tid + 512 * i) * 16);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t o = (uint32_t)(tid + 512 * i) * 16;
+            if (o < bytes) *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(s_logit) + o) = lg[i];
         }
-        return;
+        __syncthreads();
+        for (int m = wave; m < nt; m += NW) {
+            const int t = t0 + m;
+            int e;
+            float w;
+            topk_token_lds(s_logit + m * E, E, p.k, lane, &e, &w);
+            if (lane < p.k) {
+                st_agent(p.ws.sel + t * p.k + lane, e);
+                st_agent(p.ws.wts + t * p.k + lane, w);
+                s_sel[t * p.k + lane] = e;
+                s_wt[t * p.k + lane] = w;
+            }
+        }
     }
-    if (!last_arrival(&p.ws.rcount[ntt * NE + ntt], ntt, &s_flag)) return;
-    block_sort_and_groups<512, true>(p.ws.sel, p.ws.wts, p.k * T, E, T, p.k, p.has_shared != 0, 0, p.ws, s_hist,
-                                     s_off);
+    // 4. the last token tile sorts every pair (its own tile's from LDS; with
+    //    several tiles the others' selections are read back first)
+    const int P = p.k * T;
+    if (ntt > 1) {
+        if (!last_arrival(&p.ws.rcount[ntt * NE + ntt], ntt, &s_flag)) return;
+        for (int i = tid; i < P; i += 512) {
+            const int t = i / p.k;
+            if (t < t0 || t >= t0 + 16) {
+                s_sel[i] = ld_agent(p.ws.sel + i);
+                s_wt[i] = ld_agent(p.ws.wts + i);
+            }
+        }
+    }
+    __syncthreads();
+    mask_sort_small(s_sel, s_wt, P, E, T, p.k, p.has_shared != 0, p.ws, s_mask, s_off);
 }
 
 bool route_mfma_ok(const Dims& dm) {
