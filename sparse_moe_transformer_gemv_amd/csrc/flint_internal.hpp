@@ -211,8 +211,10 @@ __device__ __forceinline__ bool last_arrival(int* counter, int n_arrivals, int* 
 // each row of 16 lanes, the row broadcasts carry the result to lane 63, and
 // it is read back as a wave-uniform value.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+// (lanes a step does not write read 0, the identity of the maximum, which
+// lets the compiler fold each step into one v_max_u32 with a DPP operand)
 #define FLINT_DPP_MAX(ctrl, rmask) \
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, ctrl, rmask, 0xF, false))
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ctrl, rmask, 0xF, false))
     FLINT_DPP_MAX(0xB1, 0xF);   // quad_perm [1,0,3,2]
     FLINT_DPP_MAX(0x4E, 0xF);   // quad_perm [2,3,0,1]
     FLINT_DPP_MAX(0x141, 0xF);  // row_half_mirror
@@ -231,6 +233,21 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 }
 __device__ __forceinline__ float key_value(uint32_t key) {
     return __uint_as_float((key >> 31) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// Sum over the 64 lanes, as wave_max_u32 reduces (DPP steps within rows, then
+// row broadcasts; lanes a step does not write read 0), read from lane 63.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+#define FLINT_DPP_ADD(ctrl, rmask) \
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, rmask, 0xF, false))
+    FLINT_DPP_ADD(0xB1, 0xF);   // quad_perm [1,0,3,2]
+    FLINT_DPP_ADD(0x4E, 0xF);   // quad_perm [2,3,0,1]
+    FLINT_DPP_ADD(0x141, 0xF);  // row_half_mirror
+    FLINT_DPP_ADD(0x140, 0xF);  // row_mirror
+    FLINT_DPP_ADD(0x142, 0xA);  // row_bcast:15 into rows 1 and 3
+    FLINT_DPP_ADD(0x143, 0xC);  // row_bcast:31 into rows 2 and 3
+#undef FLINT_DPP_ADD
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Inclusive sum over the 64 lanes: rows of 16 lanes (row_shr 1, 2, 4, 8;
@@ -256,11 +273,23 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 __device__ __forceinline__ void topk_token_lds(const float* lrow, int E, int k, int lane, int* sel, float* w) {
     uint32_t key[4];
     int eid[4];
+    if ((E & 3) == 0 && (reinterpret_cast<uintptr_t>(lrow) & 15) == 0) {
+        // one 16-byte read per lane (no read past the row: 4 lane < E covers it whole)
+        const float4 v = 4 * lane < E ? *reinterpret_cast<const float4*>(lrow + 4 * lane)
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int e = 4 * lane + i;
-        key[i] = e < E ? order_key(lrow[e]) : 0u;
-        eid[i] = e;
+        for (int i = 0; i < 4; ++i) {
+            key[i] = 4 * lane < E ? order_key(vv[i]) : 0u;
+            eid[i] = 4 * lane + i;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * lane + i;
+            key[i] = e < E ? order_key(lrow[e]) : 0u;
+            eid[i] = e;
+        }
     }
 #pragma unroll
     for (int a = 0; a < 3; ++a)
@@ -294,7 +323,7 @@ __device__ __forceinline__ void topk_token_lds(const float* lrow, int E, int k, 
         }
     }
     const float pj = lane < k ? __builtin_amdgcn_exp2f((lsel - l0) * 1.4426950408889634f) : 0.f;
-    const float sum = wave_sum(pj);
+    const float sum = wave_sum_dpp(pj);
     *sel = esel;
     *w = pj * __builtin_amdgcn_rcpf(sum);
 }
