@@ -778,7 +778,7 @@ __device__ __forceinline__ float x_tile_to_f16(uint4 (&a)[NG][4]) {
 
 // One 16-token tile of an NVFP4 gate/up block (see gateup_fp4_kernel).  sp is
 // the sorted pair of this lane's token row.
-template <int NG, int NW, int FT>
+template <int NG, int NW, int FT, bool COH = false>
 __device__ __forceinline__ void gateup_fp4_tile(const ExpertParams& p, const int4& g, bool is_shared, int r0,
                                                 int sp, __amdgpu_buffer_rsrc_t xv, int kl, uint4 (&cw)[2 * FT][NG],
                                                 const uint8_t* s_sc, bool first, uint4* sc_dst, const uint4& sc_val,
@@ -859,8 +859,15 @@ __device__ __forceinline__ void gateup_fp4_tile(const ExpertParams& p, const int
         uint16_t* h16 = static_cast<uint16_t*>(p.ws.h);
         const size_t plane = (size_t)(p.dm.k + 1) * p.dm.T * p.hstride;
         const size_t off = (size_t)(g.w + r0 + mm) * p.hstride + j0 + 16 * ft + n;
-        h16[off] = __builtin_bit_cast(uint16_t, hi);
-        h16[plane + off] = __builtin_bit_cast(uint16_t, lo);
+        if (COH) {  // read by other workgroups of this launch: agent-scope stores
+            const __amdgpu_buffer_rsrc_t hv2 = buffer_view(h16, (uint32_t)(2 * plane * 2));
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, hi), hv2, (int)(off * 2), 0, kCpolAgent);
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, lo), hv2, (int)((plane + off) * 2), 0,
+                                                  kCpolAgent);
+        } else {
+            h16[off] = __builtin_bit_cast(uint16_t, hi);
+            h16[plane + off] = __builtin_bit_cast(uint16_t, lo);
+        }
     }
     __syncthreads();
 }
@@ -926,7 +933,7 @@ __global__ __launch_bounds__(64 * NW) void gateup_fp4_kernel(ExpertParams p) {
 // One 16-token tile of an NVFP4 down block (see down_fp4_kernel); ws is the
 // routing weight of the token row this thread stores, times the tensor scale
 // and the inverse of the h scale.
-template <int NT, int NGMAX>
+template <int NT, int NGMAX, bool COH = false>
 __device__ __forceinline__ void down_fp4_tile(const ExpertParams& p, const int4& g, int r0, int ng, int kl, int kls,
                                               int n0,
                                               __amdgpu_buffer_rsrc_t hv_hi, __amdgpu_buffer_rsrc_t hv_lo,
@@ -946,8 +953,11 @@ __device__ __forceinline__ void down_fp4_tile(const ExpertParams& p, const int4&
         uint4 hhi[4], hlo[4];
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-            hhi[st] = buffer_load16(hv_hi, ho + (128 * gg + 8 * st) * 2);
-            hlo[st] = buffer_load16(hv_lo, ho + (128 * gg + 8 * st) * 2);
+            // (h written by other workgroups of this launch: agent-scope loads)
+            hhi[st] = COH ? buffer_load16_agent(hv_hi, ho + (128 * gg + 8 * st) * 2)
+                          : buffer_load16(hv_hi, ho + (128 * gg + 8 * st) * 2);
+            hlo[st] = COH ? buffer_load16_agent(hv_lo, ho + (128 * gg + 8 * st) * 2)
+                          : buffer_load16(hv_lo, ho + (128 * gg + 8 * st) * 2);
         }
         __builtin_amdgcn_sched_barrier(0);
         // first tile (uniform): the block's scales go to LDS once the first h
@@ -1772,6 +1782,259 @@ __global__ __launch_bounds__(256) void decode_fused_kernel(FusedParams P) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Single-launch decode with NVFP4 weights: the phases of decode_fused_kernel
+// (router, routing in every workgroup, gate/up items, down items with the
+// last-arrival combine, the same tree barriers) with the NVFP4 tiles of the
+// separate kernels.  A gate/up item is (group, 16 features): 16 gate and 16
+// up rows, K split over the 4 waves, NG groups of 128 per wave (d = 512 NG),
+// h written as its two f16 planes at agent scope.  A down item is (group, 64
+// output rows) with the whole K (F <= kFp4DownKChunk) in one workgroup.
+// ---------------------------------------------------------------------------
+constexpr int kFusedFp4Features = 16;  // features per gate/up item
+
+template <int NG>
+__device__ void fused_fp4_gateup_item(const ExpertParams& p, const int4& g, int fb, const int* s_sp, uint8_t* s_sc,
+                                      float (&s_part)[4][2][256]) {
+    constexpr int NW = 4, FT = 1;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = lane & 15, q = lane >> 4;
+    const int d = p.dm.d;
+    const bool is_shared = g.x == p.dm.E;
+    const int F = is_shared ? p.dm.fs : p.dm.f;
+    const int j0 = fb * 16 * FT;
+    const size_t e = is_shared ? 0 : (size_t)g.x;
+    const WeightPtrs& wp = is_shared ? p.shared : p.routed;
+    const int kl = wave * (d / NW) + 32 * q;  // this lane's first element in each group
+    const int sp = is_shared ? 0 : s_sp[g.y + (row < g.z ? row : g.z - 1)];
+    // the item's scales (2 FT x 16 rows of d / 16 bytes), one 16-byte chunk per thread
+    constexpr int kCpr = NG * NW / 2;
+    constexpr int kChunks = 2 * FT * 16 * kCpr;
+    static_assert(kChunks <= 64 * NW, "one scale chunk per thread");
+    const int sc_c = tid < kChunks ? tid : kChunks - 1;
+    const int sc_r = sc_c / kCpr, sc_cc = sc_c % kCpr, sc_t = sc_r >> 4;
+    const size_t sc_wr = e * 2 * F + (size_t)(sc_t >= FT ? F : 0) + j0 + 16 * (sc_t % FT) + (sc_r & 15);
+    const uint4 sc_val = *reinterpret_cast<const uint4*>(wp.gus + sc_wr * (d / 16) + 16 * sc_cc);
+    uint4* sc_dst = reinterpret_cast<uint4*>(s_sc + sc_r * kFp4ScRow<NG, NW> + 16 * sc_cc);
+    uint4 cw[2 * FT][NG];
+#pragma unroll
+    for (int t = 0; t < 2 * FT; ++t) {
+        const size_t wr = e * 2 * F + (size_t)(t >= FT ? F : 0) + j0 + 16 * (t % FT) + row;
+        const uint8_t* crow = static_cast<const uint8_t*>(wp.gu) + wr * (d / 2) + kl / 2;
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) cw[t][gg] = *reinterpret_cast<const uint4*>(crow + 64 * gg);
+    }
+    const float tsg = wp.ts[e * 3 + 0], tsu = wp.ts[e * 3 + 1];
+    const __amdgpu_buffer_rsrc_t xv = buffer_view(p.x, (uint32_t)p.dm.T * d * 2);
+    gateup_fp4_tile<NG, NW, FT, true>(p, g, is_shared, 0, sp, xv, kl, cw, s_sc, true, tid < kChunks ? sc_dst : nullptr,
+                                      sc_val, tsg, tsu, j0, s_part);
+    for (int r0 = 16; r0 < g.z; r0 += 16) {
+        const int m = r0 + row;
+        const int spn = is_shared ? 0 : s_sp[g.y + (m < g.z ? m : g.z - 1)];
+        gateup_fp4_tile<NG, NW, FT, true>(p, g, is_shared, r0, spn, xv, kl, cw, s_sc, false, nullptr, sc_val, tsg,
+                                          tsu, j0, s_part);
+    }
+}
+
+// The weights of one NVFP4 down item (group g, output rows 64 rb .. + 63):
+// the lane's codes, and up to two 16-byte chunks of the item's block scales
+// with their LDS offsets (-1: none), written to LDS by the item's first tile.
+template <int NGMAX>
+struct Fp4DownRegs {
+    uint4 cw[kDownFp4Tiles][NGMAX];
+    u32x4_t sc_v0, sc_v1;
+    int sc_o0, sc_o1;
+};
+template <int NGMAX>
+__device__ __forceinline__ void fused_fp4_down_weights(const ExpertParams& p, const int4& g, int rb,
+                                                       Fp4DownRegs<NGMAX>& w) {
+    constexpr int NT = kDownFp4Tiles;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = lane & 15, q = lane >> 4;
+    const int d = p.dm.d;
+    const bool is_shared = g.x == p.dm.E;
+    const int F = is_shared ? p.dm.fs : p.dm.f;
+    const int ng = F / 512;
+    const int kl = wave * (F / 4) + 32 * q;
+    const size_t e = is_shared ? 0 : (size_t)g.x;
+    const WeightPtrs& wp = is_shared ? p.shared : p.routed;
+    const int n0 = rb * 16 * NT;
+    const int cpr = F / 256, nchunks = 16 * NT * cpr;
+    auto sc_chunk = [&](int ci, u32x4_t& v) {  // LDS offset of chunk ci, or -1 past the last
+        const int cc = ci < nchunks ? ci : nchunks - 1;
+        const int r = cc / cpr, col = cc % cpr;
+        const size_t wr = e * (size_t)d + (size_t)(n0 + r);
+        v = *reinterpret_cast<const u32x4_t*>(wp.dns + wr * (F / 16) + 16 * col);
+        return ci < nchunks ? r * kFp4DownScRow<NGMAX> + 16 * col : -1;
+    };
+    w.sc_o0 = sc_chunk(tid, w.sc_v0);
+    w.sc_o1 = sc_chunk(tid + 256, w.sc_v1);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const size_t wr = e * (size_t)d + (size_t)(n0 + 16 * t + row);
+        const uint8_t* crow = static_cast<const uint8_t*>(wp.dn) + wr * (F / 2) + kl / 2;
+#pragma unroll
+        for (int gg = 0; gg < NGMAX; ++gg) w.cw[t][gg] = *reinterpret_cast<const uint4*>(crow + 64 * (gg < ng ? gg : 0));
+    }
+}
+
+// One NVFP4 down item with its weights in w: y rows at agent scope, then the
+// last-arrival combine of the item's 64 columns.
+template <int NGMAX>
+__device__ void fused_fp4_down_item(const ExpertParams& p, const int4& g, int rb, int ngroups, Fp4DownRegs<NGMAX>& w,
+                                    const float* s_swt, const int* s_pos, uint8_t* s_sc,
+                                    float (&s_part)[4][kDownFp4Tiles][256], int* s_flag) {
+    constexpr int NT = kDownFp4Tiles;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int q = lane >> 4;
+    const int mm = tid >> 4;
+    const bool is_shared = g.x == p.dm.E;
+    const int F = is_shared ? p.dm.fs : p.dm.f;
+    const int ng = F / 512;
+    const int kl = wave * (F / 4) + 32 * q;
+    const int n0 = rb * 16 * NT;
+    const size_t e = is_shared ? 0 : (size_t)g.x;
+    const WeightPtrs& wp = is_shared ? p.shared : p.routed;
+    const float tsd = wp.ts[e * 3 + 2] / kHScale;
+    const uint16_t* h16 = static_cast<const uint16_t*>(p.ws.h);
+    const size_t plane = (size_t)(p.dm.k + 1) * p.dm.T * p.hstride;
+    const uint32_t vbytes = (uint32_t)g.z * p.hstride * 2;
+    const __amdgpu_buffer_rsrc_t hv_hi = buffer_view(h16 + (size_t)g.w * p.hstride, vbytes);
+    const __amdgpu_buffer_rsrc_t hv_lo = buffer_view(h16 + plane + (size_t)g.w * p.hstride, vbytes);
+    float* y = static_cast<float*>(p.ws.y);
+    for (int r0 = 0; r0 < g.z; r0 += 16) {
+        const int m = r0 + mm;
+        const float rw = is_shared ? 1.f : s_swt[g.y + (m < g.z ? m : g.z - 1)];
+        down_fp4_tile<NT, NGMAX, true>(p, g, r0, ng, kl, kl, n0, hv_hi, hv_lo, w.cw, s_sc, r0 == 0, w.sc_o0, w.sc_o1,
+                                       w.sc_v0, w.sc_v1, tsd * rw, s_part, y, true);
+    }
+    if (last_arrival(&p.ws.dcount[rb], ngroups, s_flag)) {
+        const int n = p.dm.T * 16 * NT;  // uniform
+        if (n <= 256) combine_columns_n<NT, 1>(p, n0, s_pos);
+        else if (n <= 512) combine_columns_n<NT, 2>(p, n0, s_pos);
+        else combine_columns_n<NT, 4>(p, n0, s_pos);
+    }
+}
+
+template <int NG, int NGMAX>
+__global__ __launch_bounds__(256) void decode_fused_fp4_kernel(FusedParams P) {
+    constexpr int kScUp = 2 * 16 * kFp4ScRow<NG, 4>, kScDown = 16 * kDownFp4Tiles * kFp4DownScRow<NGMAX>;
+    __shared__ __attribute__((aligned(16))) float s_logit[kFusedMaxT * 256];
+    __shared__ __attribute__((aligned(16))) uint8_t s_sc[kScUp > kScDown ? kScUp : kScDown];
+    __shared__ float s_upart[4][2][256];
+    __shared__ float s_dpart[4][kDownFp4Tiles][256];
+    __shared__ float s_red[4][kFusedMaxT];
+    __shared__ int s_sel[kFusedMaxPairs];
+    __shared__ float s_wt[kFusedMaxPairs];
+    __shared__ int s_sp[kFusedMaxPairs];
+    __shared__ int s_pos[kFusedMaxPairs];
+    __shared__ float s_swt[kFusedMaxPairs];
+    __shared__ unsigned s_mask[256];
+    __shared__ int s_off[257];
+    __shared__ int4 s_groups[257];
+    __shared__ int s_ng, s_flag, s_next, s_gen;
+
+    const ExpertParams& p = P.e;
+    const int G = P.nblocks, bid = blockIdx.x;
+    const int E = p.dm.E, T = p.dm.T, k = p.dm.k;
+    int* fbar = p.ws.fbar;
+    const int nwait = (G + kBarGroup - 1) / kBarGroup;
+    if (threadIdx.x == 0) s_gen = ld_agent(bar_gen(fbar)) + 1;
+    __syncthreads();
+    const int gen = s_gen;
+    const int fs_items = p.dm.fs / kFusedFp4Features, f_items = p.dm.f / kFusedFp4Features;
+
+    // ---- phase 0: router logits; the shared expert's gate/up meanwhile ----
+    if (bid < E) {
+        fused_router_expert(P, bid, s_red);
+        if (tree_arrive(fbar, 0, bid, E)) {
+            for (int x = 0; x < 8; ++x) st_agent(bar_queue(fbar, 8 + x), 0);
+            tree_release(fbar, 0, nwait, gen);
+        }
+    } else if (bid - E < fs_items) {
+        fused_fp4_gateup_item<NG>(p, make_int4(E, 0, T, k * T), bid - E, s_sp, s_sc, s_upart);
+    }
+    tree_wait(fbar, 0, bid, gen);
+
+    // ---- phase 1: routing, redundantly in every workgroup ----
+    fused_topk(p, s_logit, s_sel, s_wt);
+    __syncthreads();
+    fused_groups(p, s_sel, s_mask, s_off, s_groups, &s_ng);
+    const int ng = s_ng;
+    const int g0 = p.dm.fs > 0 ? 1 : 0;
+    const int n_up = (ng - g0) * f_items;
+    fused_place(p, s_sel, s_wt, s_mask, s_off, s_sp, s_pos, s_swt);
+    if (bid == 0) {  // the routing of this forward, for flint_moe_get_routing
+        for (int i = threadIdx.x; i < k * T; i += blockDim.x) {
+            p.ws.sel[i] = s_sel[i];
+            p.ws.wts[i] = s_wt[i];
+            p.ws.sorted_pair[i] = s_sp[i];
+            p.ws.pair_pos[i] = s_pos[i];
+            p.ws.sorted_wt[i] = s_swt[i];
+        }
+        for (int i = threadIdx.x; i < E; i += blockDim.x) {
+            p.ws.counts[i] = __popc(s_mask[i]);
+            p.ws.offsets[i] = s_off[i];
+        }
+    }
+
+    // ---- phase 2: routed gate/up items (item x + 8 j of XCD x first by rank,
+    // then from the XCD's counter when there are more items than workgroups) ----
+    const int per_xcd = G >> 3;
+    {
+        const int x = bid & 7;
+        int* ctr = bar_queue(fbar, x);
+        const bool dyn = n_up > 8 * per_xcd;
+        int i = bid >> 3;
+        while (x + 8 * i < n_up) {  // uniform
+            int next = per_xcd;
+            if (dyn && threadIdx.x == 0)
+                next = per_xcd + __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int j = x + 8 * i;
+            fused_fp4_gateup_item<NG>(p, s_groups[g0 + j / f_items], j % f_items, s_sp, s_sc, s_upart);
+            if (threadIdx.x == 0) s_next = next;
+            __syncthreads();
+            i = s_next;
+            __syncthreads();
+        }
+    }
+
+    // ---- barrier: every h row is written; a workgroup with a first down item
+    // loads its weights before it waits ----
+    const int rblocks = p.dm.d / (16 * kDownFp4Tiles);
+    const int n_down = ng * rblocks;
+    const int xd = bid & 7;
+    int id = bid >> 3;
+    const int j0 = xd + 8 * id;
+    Fp4DownRegs<NGMAX> w;
+    if (tree_arrive(fbar, 1, bid, G)) {
+        st_agent(bar_gen(fbar), gen);
+        for (int x = 0; x < 8; ++x) st_agent(bar_queue(fbar, x), 0);
+        tree_release(fbar, 1, nwait, gen);
+    }
+    if (j0 < n_down) {
+        fused_fp4_down_weights<NGMAX>(p, s_groups[j0 / rblocks], j0 % rblocks, w);
+        tree_wait(fbar, 1, bid, gen);
+    }
+
+    // ---- phase 3: down items and the combine ----
+    const bool dyn_down = n_down > 8 * per_xcd;
+    while (xd + 8 * id < n_down) {  // uniform
+        const int j = xd + 8 * id;
+        if (j != j0) fused_fp4_down_weights<NGMAX>(p, s_groups[j / rblocks], j % rblocks, w);
+        int next = per_xcd;
+        if (dyn_down && threadIdx.x == 0)
+            next = per_xcd + __hip_atomic_fetch_add(bar_queue(fbar, 8 + xd), 1, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        fused_fp4_down_item<NGMAX>(p, s_groups[j / rblocks], j % rblocks, ng, w, s_swt, s_pos, s_sc, s_dpart,
+                                   &s_flag);
+        if (threadIdx.x == 0) s_next = next;
+        __syncthreads();
+        id = s_next;
+        __syncthreads();
+    }
+}
+
 template <int NSTEP, int NSMAX>
 static const void* fused_kernel_ptr() {
     return reinterpret_cast<const void*>(&decode_fused_kernel<NSTEP, NSMAX>);
@@ -1781,6 +2044,20 @@ static const void* fused_kernel_ptr() {
 // NSMAX = the widest expert / 128.
 static const void* fused_kernel_for(const Dims& dm) {
     const int fmax = dm.f > dm.fs ? dm.f : dm.fs;
+    if (dm.wdt == DT_NVFP4) {  // NG = d / 512, NGMAX = the widest expert / 512
+        const int ng = dm.d / 512, nm = fmax / 512;
+#define FLINT_FUSED_FP4_CASE(S)                                                                   \
+        if (ng == S) {                                                                            \
+            if (nm <= 1) return reinterpret_cast<const void*>(&decode_fused_fp4_kernel<S, 1>);    \
+            if (nm <= 2) return reinterpret_cast<const void*>(&decode_fused_fp4_kernel<S, 2>);    \
+            return reinterpret_cast<const void*>(&decode_fused_fp4_kernel<S, 4>);                 \
+        }
+        FLINT_FUSED_FP4_CASE(1)
+        FLINT_FUSED_FP4_CASE(2)
+        FLINT_FUSED_FP4_CASE(4)
+#undef FLINT_FUSED_FP4_CASE
+        return nullptr;
+    }
     const int ns = dm.d / 128, nm = (fmax + 127) / 128;
 #define FLINT_FUSED_CASE(S)                                  \
     if (ns == S) {                                           \
@@ -1800,10 +2077,13 @@ static const void* fused_kernel_for(const Dims& dm) {
 int fused_decode_grid(const Dims& dm, int n_cu) {
     const int fmax = dm.f > dm.fs ? dm.f : dm.fs;
     const int ns = dm.d / 128;
-    if (!(dm.act == DT_BF16 && dm.wdt == DT_BF16 && dm.T >= 1 && dm.T <= kFusedMaxT && dm.k <= kCombineMaxK &&
-          dm.E <= 256 && dm.d % 256 == 0 && (ns == 2 || ns == 4 || ns == 8 || ns == 16) && dm.f % 128 == 0 &&
-          dm.fs % 128 == 0 && fmax <= kDownKChunk))
-        return 0;
+    const bool common = dm.act == DT_BF16 && dm.T >= 1 && dm.T <= kFusedMaxT && dm.k <= kCombineMaxK && dm.E <= 256;
+    const bool bf16 = dm.wdt == DT_BF16 && dm.d % 256 == 0 && (ns == 2 || ns == 4 || ns == 8 || ns == 16) &&
+                      dm.f % 128 == 0 && dm.fs % 128 == 0 && fmax <= kDownKChunk;
+    const int ng = dm.d / 512, nm = fmax / 512;
+    const bool fp4 = dm.wdt == DT_NVFP4 && dm.d % 512 == 0 && (ng == 1 || ng == 2 || ng == 4) && dm.f % 512 == 0 &&
+                     dm.fs % 512 == 0 && nm >= 1 && nm <= 4 && fmax <= kFp4DownKChunk;
+    if (!common || !(bf16 || fp4)) return 0;
     const void* kp = fused_kernel_for(dm);
     if (!kp) return 0;
     int per_cu = 0;
@@ -1814,7 +2094,8 @@ int fused_decode_grid(const Dims& dm, int n_cu) {
     per_cu = per_cu < kFusedBlocksPerCU ? per_cu : kFusedBlocksPerCU;
     const int G = (per_cu * n_cu) & ~7;  // the gate/up work is split over the 8 XCDs
     // the router takes one workgroup per expert and the shared gate/up items the next ones
-    if (per_cu < 1 || dm.E + dm.fs / 8 > G || G > kBarGroup * kBarMaxGroups) return 0;
+    const int fs_items = dm.fs / (dm.wdt == DT_NVFP4 ? kFusedFp4Features : 8);
+    if (per_cu < 1 || dm.E + fs_items > G || G > kBarGroup * kBarMaxGroups) return 0;
     return G;
 }
 

@@ -609,6 +609,45 @@ def test_single_launch_decode(T, over):
     print("single launch T=%d %s: %s | separate launches: %s" % (T, over, rep, rep2), flush=True)
 
 
+FUSED_FP4_SHAPES = [
+    dict(d=512, E=32, k=4, f=512, fs=512),
+    dict(d=1024, E=100, k=8, f=512, fs=0),     # odd expert count, k = 8, no shared expert
+    dict(d=2048, E=64, k=6, f=512, fs=1024),   # shared expert wider than a routed one
+]
+
+
+@pytest.mark.parametrize("T", [1, 3, 8])
+@pytest.mark.parametrize("over", FUSED_FP4_SHAPES, ids=["d512", "E100k8noshared", "d2048fs1024"])
+def test_single_launch_decode_nvfp4(T, over):
+    # NVFP4 weights take the single launch too: one launch of it, the oracle's
+    # result, the separate launches' routing, a clear fault word
+    from sparse_moe_transformer_gemv_amd import FLINT_UNFUSED_DECODE, KERNEL_FUSED
+    over = dict(over)
+    no_shared = over.get("fs") == 0
+    if no_shared:
+        over["fs"] = 512
+    L = synth.layer(4, **over)
+    c = L["cfg"]
+    if no_shared:
+        L["shared"] = None
+        c = dict(c, fs=0)
+        L["cfg"] = c
+    x = synth.hidden(4, T, c["d"], c["act"], draw=T)
+    D = dev_layer(L)
+    ref = oracle.moe_forward(x, L["router_w"], L["experts"], L["shared"], top_k=c["k"], wdtype=synth.NVFP4)
+    fused = make_layer_obj(c, 16)
+    rep, rout = check_layer(fused, D, x, ref, c)
+    check_permutation(rout, T, c["k"], c["E"])
+    fused.profile_begin(KERNEL_FUSED, 4)
+    run_gpu(fused, D, x, routing=False)
+    assert len(fused.profile_end()) == 1, "the single-launch decode kernel did not run"
+    assert fused.fault() == 0, "a grid-barrier wait gave up"
+    sep = make_layer_obj(c, 16, FLINT_UNFUSED_DECODE)
+    rep2, rout2 = check_layer(sep, D, x, ref, c)
+    assert all(set(a) == set(b) for a, b in zip(rout["idx"], rout2["idx"]))
+    print("single launch nvfp4 T=%d %s: %s | separate launches: %s" % (T, over, rep, rep2), flush=True)
+
+
 def test_single_launch_decode_back_to_back_and_graph():
     # consecutive launches (barrier counters and work queues reset themselves),
     # changing batch sizes (T = 16 runs as separate launches on the same
