@@ -140,11 +140,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
     return (uint16_t)(u >> 16);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
+__device__ __forceinline__ float wave_sum_dpp(float v);
+// Sum over the 64 lanes, returned in every lane (the DPP reduction below).
+__device__ __forceinline__ float wave_sum(float v) { return wave_sum_dpp(v); }
 
 // SiLU z * sigmoid(z) = z / (1 + e^-z) from the hardware base-2 exponential and
 // reciprocal (v_exp_f32, v_rcp_f32; about 1 ulp each): four instructions in
