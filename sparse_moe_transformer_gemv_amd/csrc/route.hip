@@ -405,100 +405,12 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(RouteMfmaParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode router for T <= 64, in one launch of (d/256) x (E/16) x (T/16)
-// blocks and four stages handed on by tickets:
-//   1. block (kc, et, tt) computes the partial logits of the 16 tokens of
-//      tile tt and the 16 experts of tile et over k in [256 kc, 256 kc + 256)
-//      (8 waves, one 32-wide MFMA step each) into rpart[kc];
-//   2. the last k-chunk block of (et, tt) sums the d/256 partials in kc order
-//      (so the result does not depend on timing) and adds the bias;
-//   3. the last expert tile of token tile tt selects the top-k of its tokens
-//      (two per wave);
-//   4. the last token tile runs the counting sort.
-// Spreading the 2 MB of fp32 router rows over >= 128 blocks keeps enough loads
-// in flight (a block per 16 experts would be bound by one CU's miss queue),
-// and spreading the selection over token tiles keeps it off one CU.
-// ---------------------------------------------------------------------------
-// Top-k of U tokens by one wavefront (tokens t0 + wave + 8 u), rounds interleaved
-// across the tokens.  Lane l holds the keys of experts 4 l .. 4 l + 3.  Each
-// round takes the wave maximum key; the lowest lane holding it, and inside
-// that lane the lowest slot, give the lowest expert index among equal logits.
-// The chosen logits are wave-uniform, so their softmax is formed directly.
-// Results go to global memory (device-coherent) and, when s_sel is not null,
-// to LDS copies indexed from t0.
-template <int U>
-__device__ __forceinline__ void wave_topk_tokens(const float* __restrict__ logits, int t0, int T, int E, int k,
-                                                 int wave, int lane, int* __restrict__ sel, float* __restrict__ wts,
-                                                 int* s_sel, float* s_wt) {
-    uint32_t key[U][4];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int t = t0 + wave + 8 * u;
-        const float* row = logits + (size_t)(t < T ? t : 0) * E;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = 4 * lane + i;
-            const float v = ld_agent(row + (e < E ? e : 0));
-            key[u][i] = e < E ? order_key(v) : 0u;
-        }
-    }
-    uint32_t cm[U][8];
-    int ce[U][8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        if (j >= k) break;  // uniform
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            uint32_t m = key[u][0];
-            int li = 0;
-#pragma unroll
-            for (int i = 1; i < 4; ++i)
-                if (key[u][i] > m) {
-                    m = key[u][i];
-                    li = i;
-                }
-            const uint32_t M = wave_max_u32(m);
-            const int L = __builtin_ctzll(__ballot(m == M));
-            const int lis = __builtin_amdgcn_readlane(li, L);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (lane == L && lis == i) key[u][i] = 0u;
-            cm[u][j] = M;
-            ce[u][j] = 4 * L + lis;
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int t = t0 + wave + 8 * u;
-        if (t >= T) break;  // uniform
-        const float v0 = key_value(cm[u][0]);
-        float pj[8], sum = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            pj[j] = j < k ? expf(key_value(cm[u][j]) - v0) : 0.f;
-            sum += pj[j];
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (j < k && lane == j) {
-                const float w = pj[j] / sum;
-                st_agent(sel + t * k + j, ce[u][j]);
-                st_agent(wts + t * k + j, w);
-                if (s_sel != nullptr) {
-                    s_sel[(t - t0) * k + j] = ce[u][j];
-                    s_wt[(t - t0) * k + j] = w;
-                }
-            }
-    }
-}
-
-// ---------------------------------------------------------------------------
 // Decode path without the matrix cores (fp32 activations, or shapes the
 // matrix-core router does not take), one launch of (E / 4) x (T / 16) blocks:
 // wave w of block (bx, by) computes router logit 4 bx + w of the 16 tokens of
-// tile by; the last expert block of each token tile to finish selects the
-// top-k of its tokens (two per wave per pass), and the last token tile to
-// finish runs the counting sort.
+// tile by; the last expert block of each token tile to finish stages the
+// tile's logits in LDS and selects the top-k of its tokens, one wavefront per
+// token, and the last token tile to finish runs the counting sort.
 // ---------------------------------------------------------------------------
 struct RouteDecodeParams {
     const void* x;
@@ -514,16 +426,40 @@ __global__ __launch_bounds__(256) void route_decode_kernel(RouteDecodeParams p) 
     __shared__ int s_hist[4 * 256];
     __shared__ int s_off[257];
     __shared__ int s_last;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ __attribute__((aligned(16))) float s_logit[16 * 256];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int e = blockIdx.x * 4 + wave;
     const int t0 = blockIdx.y * 16, t1 = min(p.T, t0 + 16);
     if (e < p.E)
         router_row_logits<ActT>(static_cast<const ActT*>(p.x), p.wr + (size_t)e * p.d,
                                 p.bias ? p.bias[e] : 0.f, t0, t1, p.d, p.E, e, p.ws.logits, lane);
     if (!last_arrival(p.ws.counter + 1 + blockIdx.y, (int)gridDim.x, &s_last)) return;
-    // tokens t0 + wave + {0, 4, 8, 12}
-    wave_topk_tokens<2>(p.ws.logits, t0, t1, p.E, p.k, wave, lane, p.ws.sel, p.ws.wts, nullptr, nullptr);
-    wave_topk_tokens<2>(p.ws.logits, t0 + 4, t1, p.E, p.k, wave, lane, p.ws.sel, p.ws.wts, nullptr, nullptr);
+    {
+        // the tile's logits into LDS (16-byte agent-scope loads: other blocks of
+        // this launch wrote them), then one wavefront per token
+        const int nt = t1 - t0;
+        const uint32_t bytes = (uint32_t)(nt * p.E * 4 + 15) & ~15u;  // within the 256-byte padding
+        const __amdgpu_buffer_rsrc_t lv = buffer_view(p.ws.logits + (size_t)t0 * p.E, bytes);
+        uint4 lg[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lg[i] = buffer_load16_agent(lv, (uint32_t)(tid + 256 * i) * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t o = (uint32_t)(tid + 256 * i) * 16;
+            if (o < bytes) *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(s_logit) + o) = lg[i];
+        }
+        __syncthreads();
+        for (int m = wave; m < nt; m += 4) {
+            const int t = t0 + m;
+            int se;
+            float w;
+            topk_token_lds(s_logit + m * p.E, p.E, p.k, lane, &se, &w);
+            if (lane < p.k) {
+                st_agent(p.ws.sel + t * p.k + lane, se);
+                st_agent(p.ws.wts + t * p.k + lane, w);
+            }
+        }
+    }
     if (!last_arrival(p.ws.counter, (int)gridDim.y, &s_last)) return;
     block_sort_and_groups<256>(p.ws.sel, p.ws.wts, p.k * p.T, p.E, p.T, p.k, p.has_shared != 0, 0, p.ws,
                                s_hist, s_off);
@@ -595,6 +531,21 @@ __device__ void mask_sort_small(const int* s_key, const float* s_w, int P, int E
 
 constexpr int kRouteSplitMaxT = 64;
 
+// ---------------------------------------------------------------------------
+// Decode router for T <= 64, in one launch of (d/256) x (E/16) x (T/16)
+// blocks and four stages handed on by tickets:
+//   1. block (kc, et, tt) computes the partial logits of the 16 tokens of
+//      tile tt and the 16 experts of tile et over k in [256 kc, 256 kc + 256)
+//      (8 waves, one 32-wide MFMA step each) into rpart[kc];
+//   2. the last k-chunk block of (et, tt) sums the d/256 partials in kc order
+//      (so the result does not depend on timing) and adds the bias;
+//   3. the last expert tile of token tile tt stages the tile's logits in LDS
+//      and selects the top-k of its tokens, one wavefront per token;
+//   4. the last token tile sorts every pair (mask_sort_small).
+// Spreading the 2 MB of fp32 router rows over >= 128 blocks keeps enough loads
+// in flight (a block per 16 experts would be bound by one CU's miss queue),
+// and spreading the selection over token tiles keeps it off one CU.
+// ---------------------------------------------------------------------------
 template <int NS>  // NS = d / 256 k-chunks
 __global__ __launch_bounds__(512) void route_splitk_kernel(RouteMfmaParams p) {
     constexpr int NW = 8;
@@ -941,9 +892,33 @@ hipError_t launch_router_gemm(const LayerArgs& a, const Workspace& w, hipStream_
 
 // Prefill top-k: 8 waves per block, two tokens per wave (16 per block).
 __global__ __launch_bounds__(512) void topk_kernel(RouteDecodeParams p) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    wave_topk_tokens<2>(p.ws.logits, blockIdx.x * 16, p.T, p.E, p.k, wave, lane, p.ws.sel, p.ws.wts, nullptr,
-                        nullptr);
+    // the block's 16 logit rows into LDS (16-byte loads, all issued before the
+    // first LDS store), then one wavefront per token (topk_token_lds)
+    __shared__ __attribute__((aligned(16))) float s_logit[16 * 256];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t0 = blockIdx.x * 16, nt = min(16, p.T - t0);
+    // rounded up within the logits buffer's 256-byte padding
+    const uint32_t bytes = (uint32_t)(nt * p.E * 4 + 15) & ~15u;
+    const __amdgpu_buffer_rsrc_t lv = buffer_view(p.ws.logits + (size_t)t0 * p.E, bytes);
+    uint4 lg[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) lg[i] = buffer_load16(lv, (uint32_t)(tid + 512 * i) * 16);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const uint32_t o = (uint32_t)(tid + 512 * i) * 16;
+        if (o < bytes) *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(s_logit) + o) = lg[i];
+    }
+    __syncthreads();
+    for (int m = wave; m < nt; m += 8) {
+        const int t = t0 + m;
+        int e;
+        float w;
+        topk_token_lds(s_logit + m * p.E, p.E, p.k, lane, &e, &w);
+        if (lane < p.k) {
+            p.ws.sel[t * p.k + lane] = e;
+            p.ws.wts[t * p.k + lane] = w;
+        }
+    }
 }
 
 hipError_t launch_topk(const LayerArgs& a, const Workspace& w, hipStream_t s) {
