@@ -72,8 +72,12 @@ typedef enum {
  * makes the output NaN.  The hand-off tickets and the integer routing tables
  * keep their contents.  Adds one fill launch per forward; for tests only. */
 #define FLINT_DEBUG_POISON_WORKSPACE 0x4u
-/* Run small bf16 decode batches as separate route, gate/up and down launches
- * instead of the single-launch decode kernel (for comparison and tests). */
+/* Run small decode batches as separate route, gate/up and down launches
+ * instead of the single-launch decode kernel (for comparison and tests).
+ * Without it the single launch takes bf16 activations with bf16 weights up to
+ * 5 tokens and with NVFP4 weights up to 4 (where it measured faster); the
+ * environment variable FLINT_MOE_FUSED_MAX_T, read at create time, sets that
+ * limit for both (0 turns the single launch off, the kernel's own limit is 8). */
 #define FLINT_UNFUSED_DECODE 0x8u
 
 typedef struct {

@@ -7,6 +7,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -27,6 +28,7 @@ struct flint_moe {
     Workspace ws;
     int last_T;
     int decode_max_t;
+    int fused_max_t;  // largest batch for the single-launch decode (0: by weight type)
     int n_cu;
     // measurement hook
     int prof_kernel;
@@ -143,6 +145,21 @@ flint_status cached_device(int* dev_out, int* n_cu) {
 int decode_max_t_default() {
     if (const char* s = std::getenv("FLINT_MOE_DECODE_MAX_T")) return std::atoi(s);
     return 64;
+}
+
+// Largest batch that runs as the single-launch decode.  Measured on the full
+// layer (d = 2048, 256 experts, f = 512) against the separate launches, the
+// single launch is faster up to 5 tokens with bf16 weights and up to 4 with
+// NVFP4 weights, and slower above (its persistent grid balances the gate/up
+// and down work less well).  FLINT_MOE_FUSED_MAX_T overrides both (at most
+// the kernel's own limit; 0 turns the single launch off).
+int fused_max_t_default() {
+    if (const char* s = std::getenv("FLINT_MOE_FUSED_MAX_T")) return std::max(0, std::atoi(s));
+    return -1;
+}
+int fused_max_t_for(int configured, int wdt) {
+    if (configured >= 0) return configured;
+    return wdt == DT_NVFP4 ? 4 : 5;
 }
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -369,7 +386,7 @@ flint_status forward_impl(flint_moe* h, int32_t T, const void* hidden, const flo
         h->last_T = T;
         return ok();
     }
-    if (!(c.flags & FLINT_UNFUSED_DECODE)) {
+    if (!(c.flags & FLINT_UNFUSED_DECODE) && T <= fused_max_t_for(h->fused_max_t, a.dm.wdt)) {
         const int G = fused_decode_grid(a.dm, h->n_cu);
         if (G > 0) {
             {
@@ -450,6 +467,7 @@ flint_status flint_moe_create(const flint_moe_config* cfg, flint_moe_t* out) {
     h->prof_cap = 0;
     h->prof_n = 0;
     h->decode_max_t = decode_max_t_default();
+    h->fused_max_t = fused_max_t_default();
     Workspace dummy{};
     h->mem_bytes = carve(*cfg, nullptr, &dummy);
     const size_t bytes = h->mem_bytes;
@@ -536,6 +554,7 @@ flint_status flint_moe_forward_noalloc(const flint_moe_config* cfg, int32_t T, c
     hs.prof_cap = 0;
     hs.prof_n = 0;
     hs.decode_max_t = decode_max_t_default();
+    hs.fused_max_t = fused_max_t_default();
     carve(hs.cfg, static_cast<char*>(base), &hs.ws);
     // earlier calls (other layouts) leave their bytes in the scratch: the
     // tickets of this layout start at zero (a fill kernel, not a memset node)

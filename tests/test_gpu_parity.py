@@ -577,11 +577,13 @@ FUSED_SHAPES = [
 
 @pytest.mark.parametrize("T", [1, 2, 5, 8])
 @pytest.mark.parametrize("over", FUSED_SHAPES, ids=["d256", "E100k8", "noshared", "d1024"])
-def test_single_launch_decode(T, over):
+def test_single_launch_decode(T, over, monkeypatch):
     # small bf16 batches run as one launch (the timing hook sees exactly one
     # launch of it); the result meets the oracle, and the routing equals that of
-    # the separate route / gate-up / down launches
+    # the separate route / gate-up / down launches.  The limit is raised to the
+    # kernel's own 8 tokens so that every batch size it takes is covered.
     from sparse_moe_transformer_gemv_amd import FLINT_UNFUSED_DECODE, KERNEL_FUSED
+    monkeypatch.setenv("FLINT_MOE_FUSED_MAX_T", "8")
     over = dict(over)
     no_shared = over.get("fs") == 0
     if no_shared:
@@ -618,10 +620,12 @@ FUSED_FP4_SHAPES = [
 
 @pytest.mark.parametrize("T", [1, 3, 8])
 @pytest.mark.parametrize("over", FUSED_FP4_SHAPES, ids=["d512", "E100k8noshared", "d2048fs1024"])
-def test_single_launch_decode_nvfp4(T, over):
+def test_single_launch_decode_nvfp4(T, over, monkeypatch):
     # NVFP4 weights take the single launch too: one launch of it, the oracle's
-    # result, the separate launches' routing, a clear fault word
+    # result, the separate launches' routing, a clear fault word (limit raised
+    # to the kernel's own 8 tokens, as above)
     from sparse_moe_transformer_gemv_amd import FLINT_UNFUSED_DECODE, KERNEL_FUSED
+    monkeypatch.setenv("FLINT_MOE_FUSED_MAX_T", "8")
     over = dict(over)
     no_shared = over.get("fs") == 0
     if no_shared:
@@ -648,10 +652,12 @@ def test_single_launch_decode_nvfp4(T, over):
     print("single launch nvfp4 T=%d %s: %s | separate launches: %s" % (T, over, rep, rep2), flush=True)
 
 
-def test_single_launch_decode_back_to_back_and_graph():
+def test_single_launch_decode_back_to_back_and_graph(monkeypatch):
     # consecutive launches (barrier counters and work queues reset themselves),
     # changing batch sizes (T = 16 runs as separate launches on the same
-    # handle), and replay from a HIP graph
+    # handle), and replay from a HIP graph; the limit is raised to 8 tokens so
+    # that T = 7 takes the single launch as well
+    monkeypatch.setenv("FLINT_MOE_FUSED_MAX_T", "8")
     L = synth.layer(1, d=256, E=64, f=128, fs=256)
     c = L["cfg"]
     D = dev_layer(L)
@@ -685,3 +691,29 @@ def test_single_launch_decode_back_to_back_and_graph():
         fwd(xs[1 - i])
         torch.cuda.synchronize()
     assert layer.fault() == 0, "a grid-barrier wait gave up"
+
+
+@pytest.mark.parametrize("cfg_id,T,env,fused", [
+    (1, 5, None, True), (1, 6, None, False),   # bf16 weights: single launch up to 5 tokens
+    (4, 4, None, True), (4, 5, None, False),   # NVFP4 weights: up to 4
+    (1, 1, "0", False), (4, 6, "6", True),     # the environment override
+])
+def test_single_launch_default_limits(cfg_id, T, env, fused, monkeypatch):
+    # which batches take the single launch by default, and the override; the
+    # result meets the oracle either way
+    from sparse_moe_transformer_gemv_amd import KERNEL_FUSED
+    if env is None:
+        monkeypatch.delenv("FLINT_MOE_FUSED_MAX_T", raising=False)
+    else:
+        monkeypatch.setenv("FLINT_MOE_FUSED_MAX_T", env)
+    over = dict(d=256, E=64, f=128, fs=256) if cfg_id == 1 else dict(d=512, E=32, k=4, f=512, fs=512)
+    L = synth.layer(cfg_id, **over)
+    c = L["cfg"]
+    x = synth.hidden(cfg_id, T, c["d"], c["act"], draw=70 + T)
+    D = dev_layer(L)
+    layer = make_layer_obj(c, 16)
+    check_layer(layer, D, x, run_oracle(L, x), c)
+    layer.profile_begin(KERNEL_FUSED, 4)
+    run_gpu(layer, D, x, routing=False)
+    assert (len(layer.profile_end()) == 1) == fused
+    assert layer.fault() == 0
