@@ -337,6 +337,18 @@ __global__ __launch_bounds__(256) void down_decode_kernel(ExpertParams p) {
 // One 16-token tile of a bf16 gate/up block; sp is the sorted pair of this
 // lane's token row.  Padding rows read as zeros (buffer view past T).
 // The lane's activation fragments of one 16-token tile (token row r0 + row).
+// The sorted pair of token row `row` of a group's first tile, read after the
+// weight loads are issued: 16 entries through the scalar cache (rows past the
+// group read the entries after it, which are never used).  A vector load
+// issued before direct-to-LDS weight loads is waited for with vmcnt(0) (the
+// compiler does not order the two kinds), which would hold the activation
+// loads back until every weight byte has arrived; the scalar path waits for
+// scalar loads alone.  The sorted pairs are followed by more workspace, so the
+// 16 entries stay inside the allocation.
+__device__ __forceinline__ int gateup_row_pair(const ExpertParams& p, const int4& g, int row) {
+    return pick16(sload_int16(p.ws.sorted_pair + g.y), row);
+}
+
 template <int NSTEP>
 __device__ __forceinline__ void gateup_load_x(const ExpertParams& p, const int4& g, bool is_shared, int r0, int sp,
                                               __amdgpu_buffer_rsrc_t xv, int kl, uint4 (&a)[NSTEP]) {
@@ -407,10 +419,15 @@ __device__ __forceinline__ void gateup_mfma_tile(const ExpertParams& p, const in
 // half fetch the line again; whole lines with the hint stream about 6% faster
 // than the split form without it.  Each wave reads only what it loaded, so no
 // barrier is needed; 16-byte chunks are XOR-swizzled by row so the reads are
-// free of bank conflicts.
+// free of bank conflicts.  With d = 2048 the fourth wave loads its weights
+// straight into registers instead: staging all four waves' 64 KiB leaves room
+// for two workgroups per CU, staging three (48 KiB) for three, and the weight
+// bytes a CU keeps in flight set the rate (as measured for down).
 template <int NSTEP>
 struct GateupWeightLds {
-    static constexpr int kBytes = NSTEP >= 2 ? 4 * 16 * 64 * NSTEP : 16;  // 4 waves x 16 rows x d / 2 bytes
+    static constexpr int kWaves = NSTEP >= 16 ? 3 : 4;  // waves that stage through LDS
+    static constexpr int kBytes = NSTEP >= 2 ? kWaves * 16 * 64 * NSTEP : 16;  // kWaves x 16 rows x d / 2 bytes
+    static constexpr int kAllBytes = 4 * 16 * 64 * NSTEP;  // all four waves (the single-launch kernel)
 };
 
 template <int NSTEP>
@@ -429,8 +446,6 @@ __global__ __launch_bounds__(256) void gateup_mfma_kernel(ExpertParams p) {
     const int F = is_shared ? p.dm.fs : p.dm.f;
     const int j0 = fb * 8;
     if (j0 >= F) return;
-    const int sp = p.ws.sorted_pair[g.y + (row < g.z ? row : g.z - 1)];
-    __builtin_amdgcn_sched_barrier(0);
     const size_t e = is_shared ? 0 : (size_t)g.x;
     const uint16_t* gu = static_cast<const uint16_t*>(is_shared ? p.shared.gu : p.routed.gu);
     const size_t wr = e * 2 * F + (row < 8 ? (size_t)(j0 + row) : (size_t)(F + j0 + row - 8));
@@ -438,26 +453,34 @@ __global__ __launch_bounds__(256) void gateup_mfma_kernel(ExpertParams p) {
     const __amdgpu_buffer_rsrc_t xv = buffer_view(p.x, (uint32_t)p.dm.T * d * 2);
     uint4 b[NSTEP];
     if constexpr (NSTEP >= 2) {
-        // load i: rows 8 (i & 1) + (lane >> 3) of this block, 128-byte segment i >> 1 of
-        // the wave's k range; the lane fetches logical chunk (lane & 7) ^ (row & 7)
-        unsigned char* sw = s_w + wave * (16 * 64 * NSTEP);
-        const int kw = wave * (d / 4);
-#pragma unroll
-        for (int i = 0; i < NSTEP; ++i) {
-            const int r = 8 * (i & 1) + (lane >> 3);
-            const size_t wrr = e * 2 * F + (r < 8 ? (size_t)(j0 + r) : (size_t)(F + j0 + r - 8));
-            const int c = (lane & 7) ^ (r & 7);
-            __builtin_amdgcn_global_load_lds(gu + wrr * d + kw + 64 * (i >> 1) + 8 * c, sw + i * 1024, 16, 0, 2);
-        }
         uint4 a0[NSTEP];
-        gateup_load_x<NSTEP>(p, g, is_shared, 0, sp, xv, kl, a0);
-        // every load above has landed before the reads below (the compiler waits for
-        // the direct-to-LDS loads before any LDS read)
-        const uint32_t rbase = (uint32_t)((row >> 3) * 1024 + (row & 7) * 128);
+        if (wave < GateupWeightLds<NSTEP>::kWaves) {  // uniform per wave
+            // load i: rows 8 (i & 1) + (lane >> 3) of this block, 128-byte segment i >> 1 of
+            // the wave's k range; the lane fetches logical chunk (lane & 7) ^ (row & 7)
+            unsigned char* sw = s_w + wave * (16 * 64 * NSTEP);
+            const int kw = wave * (d / 4);
 #pragma unroll
-        for (int s = 0; s < NSTEP; ++s) {
-            const uint32_t off = (s >> 1) * 2048 + rbase + ((((4 * (s & 1)) + q) ^ (row & 7)) << 4);
-            b[s] = *reinterpret_cast<const uint4*>(sw + off);
+            for (int i = 0; i < NSTEP; ++i) {
+                const int r = 8 * (i & 1) + (lane >> 3);
+                const size_t wrr = e * 2 * F + (r < 8 ? (size_t)(j0 + r) : (size_t)(F + j0 + r - 8));
+                const int c = (lane & 7) ^ (r & 7);
+                __builtin_amdgcn_global_load_lds(gu + wrr * d + kw + 64 * (i >> 1) + 8 * c, sw + i * 1024, 16, 0,
+                                                 2);
+            }
+            gateup_load_x<NSTEP>(p, g, is_shared, 0, gateup_row_pair(p, g, row), xv, kl, a0);
+            // every load above has landed before the reads below (the compiler waits for
+            // the direct-to-LDS loads before any LDS read)
+            const uint32_t rbase = (uint32_t)((row >> 3) * 1024 + (row & 7) * 128);
+#pragma unroll
+            for (int s = 0; s < NSTEP; ++s) {
+                const uint32_t off = (s >> 1) * 2048 + rbase + ((((4 * (s & 1)) + q) ^ (row & 7)) << 4);
+                b[s] = *reinterpret_cast<const uint4*>(sw + off);
+            }
+        } else {
+            const uint16_t* wrow = gu + wr * d + kl;
+#pragma unroll
+            for (int s = 0; s < NSTEP; ++s) b[s] = *reinterpret_cast<const uint4*>(wrow + 32 * s);
+            gateup_load_x<NSTEP>(p, g, is_shared, 0, gateup_row_pair(p, g, row), xv, kl, a0);
         }
         gateup_mfma_tile<NSTEP>(p, g, 0, a0, b, j0, s_part, s_h);
     } else {
@@ -465,7 +488,7 @@ __global__ __launch_bounds__(256) void gateup_mfma_kernel(ExpertParams p) {
 #pragma unroll
         for (int s = 0; s < NSTEP; ++s) b[s] = *reinterpret_cast<const uint4*>(wrow + 32 * s);
         uint4 a0[NSTEP];
-        gateup_load_x<NSTEP>(p, g, is_shared, 0, sp, xv, kl, a0);
+        gateup_load_x<NSTEP>(p, g, is_shared, 0, gateup_row_pair(p, g, row), xv, kl, a0);
         gateup_mfma_tile<NSTEP>(p, g, 0, a0, b, j0, s_part, s_h);
     }
     for (int r0 = 16; r0 < g.z; r0 += 16) {
@@ -1647,7 +1670,7 @@ __device__ void fused_down_item(const ExpertParams& p, const int4& g, int rb, in
 
 template <int NSTEP, int NSMAX>
 __global__ __launch_bounds__(256) void decode_fused_kernel(FusedParams P) {
-    constexpr int kStage = GateupWeightLds<NSTEP>::kBytes > 16384 ? GateupWeightLds<NSTEP>::kBytes : 16384;
+    constexpr int kStage = GateupWeightLds<NSTEP>::kAllBytes > 16384 ? GateupWeightLds<NSTEP>::kAllBytes : 16384;
     __shared__ __attribute__((aligned(16))) unsigned char s_w[kStage];
     __shared__ float s_part[4][256];
     __shared__ __attribute__((aligned(16))) uint16_t s_h[16][3][8];

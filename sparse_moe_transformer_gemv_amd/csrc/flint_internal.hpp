@@ -190,6 +190,24 @@ __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F7
 // compiler from moving memory accesses across the barrier.
 __device__ __forceinline__ void barrier_keep_loads() { asm volatile("s_barrier" ::: "memory"); }
 
+// 16 consecutive ints through the scalar cache, complete on return (the wait
+// is in the same asm block and covers scalar and LDS operations only, not
+// vector-memory loads in flight).  ptr 4-byte aligned; only for data written
+// by an earlier launch (the scalar cache holds no stale copy).  pick16 gives
+// each lane element i (a chain of selects, no memory).
+typedef __attribute__((ext_vector_type(16))) int sint16_t;
+__device__ __forceinline__ sint16_t sload_int16(const int* ptr) {
+    sint16_t v;
+    asm volatile("s_load_dwordx16 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+    return v;
+}
+__device__ __forceinline__ int pick16(const sint16_t& v, int i) {
+    int r = v[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) r = i == j ? v[j] : r;
+    return r;
+}
+
 // All threads: finish this workgroup's hand-off stores, then thread 0 takes a
 // ticket; returns true (in every thread) for the workgroup that arrives last.
 __device__ __forceinline__ bool last_arrival(int* counter, int n_arrivals, int* s_flag) {
