@@ -617,9 +617,92 @@ __device__ __forceinline__ void combine_columns(const ExpertParams& p, int n0) {
 // token tile as in gateup_mfma_kernel.
 constexpr int kDownMfmaTiles = 4;  // 64 output rows per block
 
-template <int NSMAX, int NT>
+// Down weights through LDS (groups 512 wide, 64 output rows: a wave's k slice
+// is 128 wide, 256 bytes per row).  Waves 0..2 fetch their 64 rows x 256 bytes
+// with direct-to-LDS loads of whole lines carrying the non-temporal hint (four
+// rows per load; the 16 chunks of a row are XOR-swizzled by row, so the
+// fragment reads are free of bank conflicts); wave 3 loads its own straight
+// into registers (64 bytes per row and instruction).  A staging wave's partial
+// sums then reuse its own region (its weights are in registers by then), so a
+// workgroup holds 3 x 16 + 4 KiB of LDS and three fit in a CU, as with the
+// registers-only form.
+constexpr int kDownLdsWaves = 3;
+constexpr int kDownLdsRegion = 64 * 256;  // bytes per staging wave
+constexpr int kDownLdsBytes = kDownLdsWaves * kDownLdsRegion + 4 * 4 * 256;  // + wave 3's partial sums
+__device__ __forceinline__ float* down_lds_part(unsigned char* s_lds, int w) {
+    return reinterpret_cast<float*>(s_lds + (w < kDownLdsWaves ? w * kDownLdsRegion : kDownLdsWaves * kDownLdsRegion));
+}
+
+// One 16-token tile of the LDS form (NSMAX = 4, NT = 4); the first tile reads
+// a staging wave's weights from LDS after its h loads are issued.
+__device__ __forceinline__ void down_mfma_tile_lds(const ExpertParams& p, const int4& g, int r0, int kl, int n0,
+                                                   const __amdgpu_buffer_rsrc_t (&hv)[3], uint4 (&b)[4][4], float ws,
+                                                   unsigned char* s_lds, float* ybase, bool handoff, bool first) {
+    constexpr int NT = 4, NSMAX = 4;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = lane & 15, q = lane >> 4;
+    const int m = r0 + row;
+    const uint32_t ho = m < g.z ? (uint32_t)(m * p.hstride + kl) * 2 : kOffNone;
+    uint4 ah[3][NSMAX];
+#pragma unroll
+    for (int s = 0; s < NSMAX; ++s)
+#pragma unroll
+        for (int pl = 0; pl < 3; ++pl) ah[pl][s] = buffer_load16(hv[pl], ho + 64 * s);
+    if (first && wave < kDownLdsWaves) {  // uniform per wave
+        // the compiler waits for the direct-to-LDS loads before these reads
+        const unsigned char* sw = s_lds + wave * kDownLdsRegion;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int s = 0; s < NSMAX; ++s)
+                b[t][s] = *reinterpret_cast<const uint4*>(sw + (16 * t + row) * 256 + (((4 * s + q) ^ row) << 4));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    floatx4_t acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NSMAX; ++s)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            acc[t] = mfma16x16x32(ah[0][s], b[t][s], acc[t]);
+            acc[t] = mfma16x16x32(ah[1][s], b[t][s], acc[t]);
+            acc[t] = mfma16x16x32(ah[2][s], b[t][s], acc[t]);
+        }
+    float* mine = down_lds_part(s_lds, wave);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mine[t * 256 + (4 * q + i) * 16 + row] = acc[t][i];
+    __syncthreads();
+    const int mm = tid >> 4, n = tid & 15;
+    if (r0 + mm < g.z) {
+        float* yr = ybase + (size_t)(g.w + r0 + mm) * p.dm.d + n0 + n;
+        const float* p0 = down_lds_part(s_lds, 0);
+        const float* p1 = down_lds_part(s_lds, 1);
+        const float* p2 = down_lds_part(s_lds, 2);
+        const float* p3 = down_lds_part(s_lds, 3);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int o = t * 256 + tid;
+            const float v = ((p0[o] + p1[o]) + p2[o]) + p3[o];
+            if (handoff)
+                st_agent(yr + 16 * t, ws * v);  // read by another workgroup of this launch
+            else
+                yr[16 * t] = ws * v;
+        }
+    }
+    __syncthreads();
+}
+
+// LDS: the routed and shared experts are both 128 NSMAX = 512 wide and NT = 4
+// (the LDS form above); otherwise every wave loads its weights into registers.
+template <int NSMAX, int NT, bool LDS = false>
 __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertParams p) {
-    __shared__ float s_part[4][NT][256];
+    constexpr bool kLds = LDS;  // weights of waves 0..2 through LDS
+    static_assert(!LDS || (NSMAX == 4 && NT == 4), "the LDS form holds 64 rows x 512");
+    __shared__ __attribute__((aligned(16))) unsigned char s_lds[kLds ? kDownLdsBytes : 4 * NT * 256 * 4];
+    float(&s_part)[4][NT][256] = *reinterpret_cast<float(*)[4][NT][256]>(s_lds);  // registers-only form
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, q = lane >> 4;
     const int d = p.dm.d;
@@ -645,13 +728,28 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertParams p) {
     const uint16_t* dn = static_cast<const uint16_t*>(is_shared ? p.shared.dn : p.routed.dn);
     const int n0 = rb * 16 * NT;
     uint4 b[NT][NSMAX];
+    const bool staged = kLds && wave < kDownLdsWaves;  // uniform per wave
+    if (staged) {
+        // load i: rows 4 i + (lane >> 4) of the block, 16-byte position lane & 15
+        // of the row holding chunk (lane & 15) ^ (row & 15) of the wave's k slice
+        unsigned char* sw = s_lds + wave * kDownLdsRegion;
+        const int kw = kc * Fc + wave * (Fc / 4);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        const uint16_t* drow = dn + (e * d + (size_t)(n0 + 16 * t + row)) * F + kl;
+        for (int i = 0; i < 16; ++i) {
+            const int r = 4 * i + (lane >> 4);
+            const int c = (lane & 15) ^ (r & 15);
+            __builtin_amdgcn_global_load_lds(dn + (e * d + (size_t)(n0 + r)) * F + kw + 8 * c, sw + i * 1024, 16, 0,
+                                             2);
+        }
+    } else {
 #pragma unroll
-        for (int s = 0; s < NSMAX; ++s) {
-            const int sc = s < nsteps ? s : 0;  // clamped: steps past nsteps are loaded but unused
-            b[t][s] = *reinterpret_cast<const uint4*>(drow + 32 * sc);
+        for (int t = 0; t < NT; ++t) {
+            const uint16_t* drow = dn + (e * d + (size_t)(n0 + 16 * t + row)) * F + kl;
+#pragma unroll
+            for (int s = 0; s < NSMAX; ++s) {
+                const int sc = s < nsteps ? s : 0;  // clamped: steps past nsteps are loaded but unused
+                b[t][s] = *reinterpret_cast<const uint4*>(drow + 32 * sc);
+            }
         }
     }
     const uint16_t* h16 = static_cast<const uint16_t*>(p.ws.h);
@@ -660,11 +758,21 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertParams p) {
     __amdgpu_buffer_rsrc_t hv[3];
 #pragma unroll
     for (int pl = 0; pl < 3; ++pl) hv[pl] = buffer_view(h16 + pl * plane + (size_t)g.w * p.hstride, vbytes);
-    down_mfma_tile<NSMAX, NT>(p, g, 0, nsteps, kl, n0, hv, b, is_shared ? 1.f : rw_load, s_part, ybase, handoff);
-    for (int r0 = 16; r0 < g.z; r0 += 16) {
-        const int m = r0 + mm;
-        const float rw = is_shared ? 1.f : p.ws.sorted_wt[g.y + (m < g.z ? m : g.z - 1)];
-        down_mfma_tile<NSMAX, NT>(p, g, r0, nsteps, kl, n0, hv, b, rw, s_part, ybase, handoff);
+    if constexpr (kLds) {
+        down_mfma_tile_lds(p, g, 0, kl, n0, hv, b, is_shared ? 1.f : rw_load, s_lds, ybase, handoff, true);
+        for (int r0 = 16; r0 < g.z; r0 += 16) {
+            const int m = r0 + mm;
+            const float rw = is_shared ? 1.f : p.ws.sorted_wt[g.y + (m < g.z ? m : g.z - 1)];
+            down_mfma_tile_lds(p, g, r0, kl, n0, hv, b, rw, s_lds, ybase, handoff, false);
+        }
+    } else {
+        down_mfma_tile<NSMAX, NT>(p, g, 0, nsteps, kl, n0, hv, b, is_shared ? 1.f : rw_load, s_part, ybase,
+                                  handoff);
+        for (int r0 = 16; r0 < g.z; r0 += 16) {
+            const int m = r0 + mm;
+            const float rw = is_shared ? 1.f : p.ws.sorted_wt[g.y + (m < g.z ? m : g.z - 1)];
+            down_mfma_tile<NSMAX, NT>(p, g, r0, nsteps, kl, n0, hv, b, rw, s_part, ybase, handoff);
+        }
     }
     if (split) {  // uniform: the last chunk of (group, rows) sums the partials in chunk order
         __shared__ int s_kflag;
@@ -1260,7 +1368,14 @@ hipError_t launch_down_decode(const LayerArgs& a, const Workspace& w, hipStream_
         case 1: hipLaunchKernelGGL((down_mfma_kernel<1, NT>), grid, dim3(256), 0, s, p); break;
         case 2: hipLaunchKernelGGL((down_mfma_kernel<2, NT>), grid, dim3(256), 0, s, p); break;
         case 3:
-        case 4: hipLaunchKernelGGL((down_mfma_kernel<4, NT>), grid, dim3(256), 0, s, p); break;
+        case 4:
+            // the LDS form measured faster without the folded combine (3 us at
+            // T = 64) and slower with it (2 us at T = 16)
+            if (a.dm.f == 512 && (a.dm.fs == 512 || a.dm.fs == 0) && NT == 4 && !p.combine)
+                hipLaunchKernelGGL((down_mfma_kernel<4, NT, true>), grid, dim3(256), 0, s, p);
+            else
+                hipLaunchKernelGGL((down_mfma_kernel<4, NT>), grid, dim3(256), 0, s, p);
+            break;
         default: hipLaunchKernelGGL((down_mfma_kernel<8, NT>), grid, dim3(256), 0, s, p); break;
         }
         return hipGetLastError();
