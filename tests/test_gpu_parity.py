@@ -89,6 +89,32 @@ def test_small_bf16_matrix_core_path(T):
     _case(1, T, d=256, E=64, f=128, fs=256)
 
 
+@pytest.mark.parametrize("T,shared", [(17, True), (40, True), (64, False)])
+def test_decode_down_through_lds(T, shared):
+    # routed and shared experts 512 wide, more than 16 tokens: the down kernel
+    # stages three waves' weights through LDS (the shared group spans several
+    # 16-token tiles; the last case has no shared expert)
+    if shared:
+        _case(1, T, d=512, E=64, k=6, f=512, fs=512)
+        return
+    L = synth.layer(1, d=512, E=64, k=6, f=512, fs=512)
+    L["shared"] = None
+    c = dict(L["cfg"], fs=0)
+    L["cfg"] = c
+    x = synth.hidden(1, T, c["d"], c["act"])
+    layer = make_layer_obj(c, T)
+    ref = oracle.moe_forward(x, L["router_w"], L["experts"], None, top_k=c["k"], wdtype=synth.BF16)
+    rep, rout = check_layer(layer, dev_layer(L), x, ref, c)
+    check_permutation(rout, T, c["k"], c["E"])
+
+
+@pytest.mark.parametrize("T", [16, 48])
+def test_decode_gateup_d2048(T):
+    # d = 2048: three gate/up waves stage weights through LDS and the fourth
+    # loads into registers; ragged groups over few experts
+    _case(1, T, d=2048, E=32, k=4, f=512, fs=512)
+
+
 def test_matrix_core_path_d128_k2():
     _case(1, 33, d=128, E=32, k=2, f=128, fs=128)
 
