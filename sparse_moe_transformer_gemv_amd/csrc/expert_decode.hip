@@ -560,7 +560,7 @@ __device__ __forceinline__ void down_mfma_tile(const ExpertParams& p, const int4
 // thread is issued before the first add (addresses clamped to valid rows, the
 // unused terms selected away), so the tail costs two memory round trips.
 // kPer elements per thread cover T x 16 NT outputs.
-constexpr int kDownCombineMaxT = 16;
+constexpr int kDownCombineMaxT = 8;
 template <int NT, int kPer>
 __device__ __forceinline__ void combine_columns_n(const ExpertParams& p, int n0, const int* s_pos) {
     constexpr int nc = 16 * NT;
@@ -1330,13 +1330,14 @@ hipError_t launch_gateup_decode(const LayerArgs& a, const Workspace& w, hipStrea
     return hipGetLastError();
 }
 
-// The matrix-core down kernels fold the combine in (bf16 weights up to 16
+// The matrix-core down kernels fold the combine in (bf16 weights up to 8
 // tokens, NVFP4 up to 4): the last workgroup of each block of output columns
 // sums those columns, which saves the combine launch.  Every workgroup then
 // waits for its write-through stores and takes a ticket; the short NVFP4
-// workgroups pay more for that at 16 tokens than the combine launch costs.
-// Above these sizes the combine kernel, which spreads the rows over the whole
-// chip, is as fast.
+// workgroups pay more for that at 16 tokens than the combine launch costs, and
+// at 16 tokens bf16 is faster with the LDS-staged down kernel and a separate
+// combine (measured).  Above these sizes the combine kernel, which spreads the
+// rows over the whole chip, is as fast.
 constexpr int kDownCombineMaxTFp4 = 4;
 bool down_decode_combines(const Dims& dm) {
     const bool fp4 = decode_fp4_ok(dm);

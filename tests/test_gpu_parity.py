@@ -327,16 +327,19 @@ def test_full_decode_nvfp4(fp4_layer, T):
     print("decode nvfp4 T=%d: %s" % (T, rep), flush=True)
 
 
-@pytest.mark.parametrize("which,T", [("bf16", 4), ("nvfp4", 1)])
-def test_decode_combine_in_down_with_residual(decode_layer, fp4_layer, which, T):
-    # small batches fold the combine into the down kernel; a nonzero residual
-    # is added there, also when the output aliases it
+@pytest.mark.parametrize("which,T,unfused", [("bf16", 4, True), ("bf16", 7, False), ("nvfp4", 3, True)])
+def test_decode_combine_in_down_with_residual(decode_layer, fp4_layer, which, T, unfused):
+    # small batches that run as separate launches fold the combine into the
+    # down kernel (bf16 up to 8 tokens, NVFP4 up to 4; the smallest batches
+    # take the single launch unless it is turned off); a nonzero residual is
+    # added there, also when the output aliases it
+    from sparse_moe_transformer_gemv_amd import FLINT_UNFUSED_DECODE
     L, D = decode_layer if which == "bf16" else fp4_layer
     c = L["cfg"]
     cfg_id = 1 if which == "bf16" else 4
     x = synth.hidden(cfg_id, T, c["d"], c["act"])
     res = np.random.default_rng(11).standard_normal((T, c["d"])).astype(np.float32)
-    layer = make_layer_obj(c, 16)
+    layer = make_layer_obj(c, 16, FLINT_UNFUSED_DECODE if unfused else 0)
     rd = dev_array(res)
     out, rout = run_gpu(layer, D, x, residual=rd)
     ref = run_oracle(L, x)
