@@ -407,10 +407,10 @@ __device__ __forceinline__ void gateup_mfma_tile(const ExpertParams& p, const in
 
 // gate/up: block = (group, 8 features): B columns 0..7 are gate rows j0..j0+7,
 // columns 8..15 the matching up rows.  NSTEP = k steps per wave = d / 128.
-// The token index is requested first (vector loads retire in order, so the
-// activation loads that need it wait for it alone), then the weights, then the
-// first token tile's activations, all before the first wait; that tile is
-// peeled off the loop so no loop-carried register forces an earlier wait.
+// The weights are requested first, then the token rows' sorted pairs (scalar
+// loads, see gateup_row_pair), then the first token tile's activations, all
+// before the first wait on the weights; that tile is peeled off the loop so no
+// loop-carried register forces an earlier wait.
 // With NSTEP >= 2 the weights travel through LDS: each wave fetches its 16
 // rows x d / 4 k with direct-to-LDS loads of whole 128-byte lines (8 rows per
 // load) carrying the non-temporal hint, then reads them back in the MFMA
