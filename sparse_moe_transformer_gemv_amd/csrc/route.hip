@@ -805,7 +805,10 @@ __device__ __forceinline__ void router_gemm_step(int s, int nk, const uint16_t* 
     unsigned char* nbuf = lds + ((s + 1) & 1) * TL::StageBytes;
 #pragma unroll
     for (int i = 0; i < TL::Chunks; ++i) *reinterpret_cast<u32x4_t*>(nbuf + dst[i]) = regb[i];
-    __syncthreads();
+    // a barrier for the LDS alone: __syncthreads() would also wait for the
+    // loads of stage s + 2 issued above (vmcnt 0), which defeats the prefetch
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this thread's LDS reads and writes are done
+    barrier_keep_loads();
 }
 
 // Block = BM tokens x 64 experts, 4 waves as 2 (tokens) x 2 (32 experts).
