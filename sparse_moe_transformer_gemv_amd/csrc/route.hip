@@ -755,13 +755,15 @@ struct RouterGemmParams {
 
 constexpr int kRgBN = 64, kRgBK = 64;
 constexpr int kRgPlaneBytes = kRgBN * kRgBK * 2;  // 8 KiB per router plane per stage
+constexpr int kRgThreads = 512;                   // 8 waves: 2 (tokens) x 4 (16 experts each)
 template <int BM>
 struct RgTile {
     static constexpr int ABytes = BM * kRgBK * 2;
     static constexpr int StageBytes = ABytes + 3 * kRgPlaneBytes;
-    static constexpr int AChunks = BM / 32;  // 16-byte A chunks per thread per stage (256 threads)
-    static constexpr int Chunks = AChunks + 6;
-    static constexpr int MI = BM / 32;       // 16-row A fragments per wave (2 waves along M)
+    static constexpr int AChunks = BM * 8 / kRgThreads;  // 16-byte A chunks per thread per stage
+    static constexpr int BChunks = 3 * kRgBN * 8 / kRgThreads;
+    static constexpr int Chunks = AChunks + BChunks;
+    static constexpr int MI = BM / 32;  // 16-row A fragments per wave (2 waves along M)
 };
 
 // byte offset of 16-byte chunk c of 128-byte LDS row r (chunks XOR-swizzled by row)
@@ -775,7 +777,7 @@ __device__ __forceinline__ void router_gemm_step(int s, int nk, const uint16_t* 
                                                  const int (&dst)[RgTile<BM>::Chunks], unsigned char* lds, int wm,
                                                  int wn, int row16, int q, u32x4_t (&rega)[RgTile<BM>::Chunks],
                                                  const u32x4_t (&regb)[RgTile<BM>::Chunks],
-                                                 floatx4_t (&acc)[RgTile<BM>::MI][2]) {
+                                                 floatx4_t (&acc)[RgTile<BM>::MI]) {
     using TL = RgTile<BM>;
     const int s2 = s + 2 < nk ? s + 2 : nk - 1;
 #pragma unroll
@@ -785,22 +787,17 @@ __device__ __forceinline__ void router_gemm_step(int s, int nk, const uint16_t* 
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
         const int c = 4 * ks + q;
-        uint4 a[TL::MI], b[3][2];
+        uint4 a[TL::MI], b[3];
 #pragma unroll
         for (int i = 0; i < TL::MI; ++i)
             a[i] = *reinterpret_cast<const uint4*>(buf + rg_swz((BM / 2) * wm + 16 * i + row16, c));
 #pragma unroll
         for (int pl = 0; pl < 3; ++pl)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                b[pl][j] = *reinterpret_cast<const uint4*>(buf + TL::ABytes + pl * kRgPlaneBytes +
-                                                           rg_swz(32 * wn + 16 * j + row16, c));
+            b[pl] = *reinterpret_cast<const uint4*>(buf + TL::ABytes + pl * kRgPlaneBytes + rg_swz(16 * wn + row16, c));
 #pragma unroll
         for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int pl = 0; pl < 3; ++pl) acc[i][j] = mfma16x16x32(a[i], b[pl][j], acc[i][j]);
+            for (int pl = 0; pl < 3; ++pl) acc[i] = mfma16x16x32(a[i], b[pl], acc[i]);
     }
     unsigned char* nbuf = lds + ((s + 1) & 1) * TL::StageBytes;
 #pragma unroll
@@ -811,34 +808,34 @@ __device__ __forceinline__ void router_gemm_step(int s, int nk, const uint16_t* 
     barrier_keep_loads();
 }
 
-// Block = BM tokens x 64 experts, 4 waves as 2 (tokens) x 2 (32 experts).
+// Block = BM tokens x 64 experts, 8 waves as 2 (tokens) x 4 (16 experts).
 template <int BM>
-__global__ __launch_bounds__(256) void router_gemm_kernel(RouterGemmParams p) {
+__global__ __launch_bounds__(kRgThreads) void router_gemm_kernel(RouterGemmParams p) {
     using TL = RgTile<BM>;
     __shared__ __attribute__((aligned(16))) unsigned char lds[2 * TL::StageBytes];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
     const int row16 = lane & 15, q = lane >> 4;
     const int t0 = blockIdx.x * BM, e0 = blockIdx.y * kRgBN;
     const int d = p.d;
     const size_t plane = (size_t)p.E * d;
-    // this thread's chunks of a stage: AChunks of A (x rows), 2 of each router plane;
-    // chunk id c = tid + 256 i -> row c >> 3, 16-byte column c & 7 (8 threads per row)
+    // this thread's chunks of a stage: AChunks of A (x rows), then BChunks of
+    // the router planes; chunk id c -> row c >> 3, 16-byte column c & 7 (8
+    // threads per row)
     const uint16_t* src[TL::Chunks];
     int dst[TL::Chunks];
 #pragma unroll
     for (int i = 0; i < TL::Chunks; ++i) {
         if (i < TL::AChunks) {
-            const int c = tid + 256 * i;
+            const int c = tid + kRgThreads * i;
             const int r = c >> 3, col = c & 7;
             const int t = t0 + r < p.T ? t0 + r : p.T - 1;  // rows past T repeat a valid row; never stored
             src[i] = p.x + (size_t)t * d + 8 * col;
             dst[i] = rg_swz(r, col);
         } else {
-            const int ib = i - TL::AChunks;
-            const int c = tid + 256 * (ib & 1);
-            const int r = c >> 3, col = c & 7;
-            const int pl = ib >> 1;
+            const int c = tid + kRgThreads * (i - TL::AChunks);  // over the 3 planes' 3 x 64 rows
+            const int pr = c >> 3, col = c & 7;
+            const int pl = pr / kRgBN, r = pr % kRgBN;
             const int e = e0 + r < p.E ? e0 + r : p.E - 1;
             src[i] = p.w3 + pl * plane + (size_t)e * d + 8 * col;
             dst[i] = TL::ABytes + pl * kRgPlaneBytes + rg_swz(r, col);
@@ -854,26 +851,22 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(RouterGemmParams p) {
 #pragma unroll
     for (int i = 0; i < TL::Chunks; ++i) *reinterpret_cast<u32x4_t*>(lds + dst[i]) = st0[i];
     __syncthreads();
-    floatx4_t acc[TL::MI][2];
+    floatx4_t acc[TL::MI];
 #pragma unroll
-    for (int i = 0; i < TL::MI; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < TL::MI; ++i) acc[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < nk; s += 2) {  // nk is even
         router_gemm_step<BM>(s, nk, src, dst, lds, wm, wn, row16, q, st0, st1, acc);
         router_gemm_step<BM>(s + 1, nk, src, dst, lds, wm, wn, row16, q, st1, st0, acc);
     }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int e = e0 + 32 * wn + 16 * j + row16;
-        if (e >= p.E) continue;
+    const int e = e0 + 16 * wn + row16;
+    if (e < p.E) {
         const float b = p.bias ? p.bias[e] : 0.f;
 #pragma unroll
         for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = t0 + (BM / 2) * wm + 16 * i + 4 * q + r;
-                if (t < p.T) p.logits[(size_t)t * p.E + e] = acc[i][j][r] + b;
+                if (t < p.T) p.logits[(size_t)t * p.E + e] = acc[i][r] + b;
             }
     }
 }
@@ -889,7 +882,7 @@ hipError_t launch_router_gemm(const LayerArgs& a, const Workspace& w, hipStream_
     hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)((n / 8 + 255) / 256)), dim3(256), 0, s, a.wr, w.w3, n);
     RouterGemmParams p{static_cast<const uint16_t*>(a.x), w.w3, a.bias, w.logits, a.dm.T, a.dm.d, a.dm.E};
     dim3 grid((a.dm.T + kRgBM - 1) / kRgBM, (a.dm.E + kRgBN - 1) / kRgBN);
-    hipLaunchKernelGGL(router_gemm_kernel<kRgBM>, grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL(router_gemm_kernel<kRgBM>, grid, dim3(kRgThreads), 0, s, p);
     return hipGetLastError();
 }
 
