@@ -225,8 +225,9 @@ flint_status flint_moe_get_fault(flint_moe_t h, int32_t* fault_out, hipStream_t 
 #define FLINT_KERNEL_SORT         1  /* prefill counting sort */
 #define FLINT_KERNEL_EXPERT_UP    2  /* gate/up + SwiGLU (decode GEMV or prefill MFMA) */
 #define FLINT_KERNEL_EXPERT_DOWN  3  /* down projection (with the combine folded in for small
-                                        decode batches: bf16 weights up to 16 tokens, NVFP4
-                                        up to 4; no combine launch is then recorded) */
+                                        decode batches run as separate launches: bf16
+                                        weights up to 8 tokens, NVFP4 up to 4; no combine
+                                        launch is then recorded) */
 #define FLINT_KERNEL_COMBINE      4  /* weighted unpermute + shared + residual */
 #define FLINT_KERNEL_FUSED        5  /* single-launch decode (the whole layer) */
 #define FLINT_KERNEL_FORWARD      6  /* a whole forward: before its first launch to after its last */
