@@ -12,7 +12,7 @@
 // design for CDNA4 matrix cores, not a port of those.
 //
 //   gate/up:  H[r][j] = SiLU(X_r . G_j) * (X_r . U_j)   (bf16 out, fp32 math)
-//   down:     Y[r][n] = w_r * (H_r . D_n)                (fp32 out, fp32 math)
+//   down:     Y[r][n] = w_r * (H_r . D_n)                (24-bit out, fp32 math)
 //
 // Tile 256 rows x 256 B rows, 8 waves as 2 (M) x 4 (N), each wave 128 x 64 =
 // 8 x 4 MFMA 16x16x32 tiles (128 fp32 accumulators per lane), two waves per
@@ -22,9 +22,12 @@
 // MFMAs take the weights as their first operand, which leaves 4 consecutive
 // output columns of one row in each lane.  For gate/up (bf16 h) the weight
 // rows of each pair of column tiles are interleaved so that a lane holds 8;
-// down (fp32 y) keeps each tile's order, so the 4 lanes of a row store 64
-// contiguous bytes; either way the results leave as 16-byte stores straight
-// from registers.
+// down keeps each tile's order, so the 4 lanes of a row store 16 contiguous
+// columns; the results leave as 16-byte (h) or 12-byte (y) stores straight
+// from registers.  y is fp32 rounded to its upper 24 bits (f32_to_f24: 15
+// fraction bits, relative error at most 2^-16), which keeps the combine's sum of
+// seven rows well inside the layer's tolerance while moving three quarters of
+// the bytes of fp32 rows through the down stores and the combine loads.
 //
 // K advances in pairs of 32-wide sub-stages through two 64 KiB LDS buffers,
 // filled straight from global memory with direct-to-LDS 16-byte loads of whole
@@ -481,9 +484,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
     // as their first operand, so lane (row16, q) holds, for each (mi, ni), rows
     // 4 q .. 4 q + 3 of B tile ni for output row 16 mi + row16.  Gate/up: out_col()
     // made the two tiles of a pair 8 consecutive features, one 16-byte bf16 store
-    // (8 bytes for a lone tile).  Down: columns 16 ni + 4 q .. + 3, one 16-byte
-    // fp32 store per tile.  Either way 64 contiguous bytes per row and
-    // instruction.  Every store is issued (rows past the group's end get an
+    // (8 bytes for a lone tile), 64 contiguous bytes per row and instruction.
+    // Down: columns 16 ni + 4 q .. + 3, one 12-byte store of four 24-bit values
+    // per tile, 48 contiguous bytes per row and instruction.  Every store is issued (rows past the group's end get an
     // offset past the view), so a wave always issues the same number. ----
     float wv[8];
     if (MODE == MODE_DOWN) {
@@ -536,21 +539,19 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
             }
         }
     } else {
-        const __amdgpu_buffer_rsrc_t yview = buffer_view(static_cast<float*>(p.ws.y) + (size_t)(g.w + m0) * d,
-                                                         (uint32_t)((size_t)rows * d * 4));
+        const __amdgpu_buffer_rsrc_t yview = buffer_view(static_cast<unsigned char*>(p.ws.y) + (size_t)(g.w + m0) * d * 3,
+                                                         (uint32_t)((size_t)rows * d * 3));
         const int col = nb0 + 16 * NI * wn + 4 * q;
 #pragma unroll
         for (int mi = 0; mi < 8; ++mi) {
             const int m = 128 * wm + 16 * mi + row16;
             const float ws = (is_shared ? 1.f : wv[mi]) * ts_a;  // ts_a: the down tensor scale (1 for bf16)
-            const uint32_t off = m < rows ? (uint32_t)(((size_t)m * d + col) * 4) : kOffNone;
+            const uint32_t off = m < rows ? (uint32_t)(((size_t)m * d + col) * 3) : kOffNone;
 #pragma unroll
             for (int t4 = 0; t4 < NI; ++t4) {
                 const floatx4_t& a = acc[mi][t4];
-                __builtin_amdgcn_raw_buffer_store_b128(
-                    (u32x4_t){__float_as_uint(ws * a[0]), __float_as_uint(ws * a[1]), __float_as_uint(ws * a[2]),
-                              __float_as_uint(ws * a[3])},
-                    yview, (int)(off == kOffNone ? kOffNone : off + 64 * t4), 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b96(pack_f24x4(ws * a[0], ws * a[1], ws * a[2], ws * a[3]), yview,
+                                                      (int)(off == kOffNone ? kOffNone : off + 48 * t4), 0, 0);
             }
         }
     }

@@ -42,7 +42,8 @@ struct Workspace {
                          // flags (zero between launches) and a sticky fault word
     void* h;             // [(k+1)*Tm][fmax] x 8 B: fp32 (decode VALU), three exact bf16 planes (decode
                          // MFMA), two f16 planes (NVFP4), or bf16 (prefill)
-    void* y;             // [(k+1)*Tm][d] fp32 rows (weighted expert outputs; split-K sums)
+    void* y;             // [(k+1)*Tm][d] weighted expert outputs: fp32 rows (decode), 24-bit rows
+                         // (prefill, 3 bytes per element, f32_to_f24)
     int max_tiles;
     size_t ticket_bytes;  // the tickets occupy [0, ticket_bytes) of the allocation
     size_t float_off;     // floating-point data from here to the end
@@ -105,13 +106,15 @@ int fused_decode_grid(const Dims& dm, int n_cu);
 hipError_t launch_decode_fused(const LayerArgs& a, const Workspace& w, int nblocks, hipStream_t s);
 hipError_t launch_gateup_prefill(const LayerArgs& a, const Workspace& w, int n_cu, hipStream_t s);
 hipError_t launch_down_prefill(const LayerArgs& a, const Workspace& w, int n_cu, hipStream_t s);
-hipError_t launch_combine(const LayerArgs& a, const Workspace& w, hipStream_t s);
+// y24: the y rows are 24-bit (the prefill down kernels' format), else fp32
+hipError_t launch_combine(const LayerArgs& a, const Workspace& w, bool y24, hipStream_t s);
 hipError_t launch_rmsnorm(int T, int d, const float* in, float eps, void* out, hipStream_t s);
 constexpr int kCombineMaxK = 8;  // the largest top_k a configuration may ask for
 // The combine and the next layer's pre-norm in one launch (out fp32, norm bf16);
 // combine_norm_ok: the shapes it takes
 bool combine_norm_ok(const Dims& dm);
-hipError_t launch_combine_norm(const LayerArgs& a, const Workspace& w, float eps, void* norm, hipStream_t s);
+hipError_t launch_combine_norm(const LayerArgs& a, const Workspace& w, bool y24, float eps, void* norm,
+                               hipStream_t s);
 // p[0 .. n) = v (a plain kernel, no memset node, so it is safe under graph capture)
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 
@@ -366,6 +369,26 @@ __device__ __forceinline__ uint4 buffer_load16_agent(__amdgpu_buffer_rsrc_t r, u
 }
 __device__ __forceinline__ void buffer_store16_agent(uint4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
     __builtin_amdgcn_raw_buffer_store_b128((u32x4_t){v.x, v.y, v.z, v.w}, r, (int)off, 0, kCpolAgent);
+}
+
+// 24-bit y elements (the prefill path's weighted expert rows): an fp32 value
+// rounded to nearest-even at its upper 24 bits (sign, 8 exponent bits, 15
+// fraction bits; relative error at most 2^-16), 3 bytes each, 4 consecutive
+// columns in 12 bytes.  A NaN stays a NaN (quiet bit set before the cut); a
+// finite value past the format's largest rounds to infinity.
+typedef __attribute__((ext_vector_type(3))) uint32_t u32x3_t;
+__device__ __forceinline__ uint32_t f32_to_f24(float v) {
+    const uint32_t u = __float_as_uint(v);
+    return v != v ? (u | 0x400000u) >> 8 : (u + 0x7Fu + ((u >> 8) & 1u)) >> 8;
+}
+__device__ __forceinline__ u32x3_t pack_f24x4(float a, float b, float c, float d) {
+    const uint32_t x = f32_to_f24(a), y = f32_to_f24(b), z = f32_to_f24(c), w = f32_to_f24(d);
+    return (u32x3_t){x | (y << 24), (y >> 8) | (z << 16), (z >> 16) | (w << 8)};
+}
+__device__ __forceinline__ float4 unpack_f24x4(u32x3_t v) {
+    return make_float4(__uint_as_float(v.x << 8), __uint_as_float(__builtin_amdgcn_alignbyte(v.y, v.x, 3) << 8),
+                       __uint_as_float(__builtin_amdgcn_alignbyte(v.z, v.y, 2) << 8),
+                       __uint_as_float(v.z & 0xFFFFFF00u));
 }
 // MFMA operand types (gfx950 v_mfma_f32_16x16x32_bf16).  Lane l of a wave
 // supplies A row (l & 15) and B column (l & 15), each with the 8 consecutive

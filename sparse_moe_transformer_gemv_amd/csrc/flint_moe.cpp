@@ -268,12 +268,12 @@ struct Timer {
 // flint_moe_forward_noalloc over the static scratch).
 // The combine launch, or with norm_out the combine and the next layer's
 // pre-norm (one launch where the shape allows, else the combine and then the
-// RMSNorm kernel).
-hipError_t combine_step(flint_moe* h, const LayerArgs& a, hipStream_t stream, float eps, void* norm_out) {
+// RMSNorm kernel).  y24: the y rows come from the prefill down kernels (24-bit).
+hipError_t combine_step(flint_moe* h, const LayerArgs& a, bool y24, hipStream_t stream, float eps, void* norm_out) {
     Timer tm(h, FLINT_KERNEL_COMBINE, stream);
-    if (!norm_out) return launch_combine(a, h->ws, stream);
-    if (combine_norm_ok(a.dm)) return launch_combine_norm(a, h->ws, eps, norm_out, stream);
-    hipError_t e = launch_combine(a, h->ws, stream);
+    if (!norm_out) return launch_combine(a, h->ws, y24, stream);
+    if (combine_norm_ok(a.dm)) return launch_combine_norm(a, h->ws, y24, eps, norm_out, stream);
+    hipError_t e = launch_combine(a, h->ws, y24, stream);
     if (e == hipSuccess) e = launch_rmsnorm(a.dm.T, a.dm.d, static_cast<const float*>(a.out), eps, norm_out, stream);
     return e;
 }
@@ -381,7 +381,7 @@ flint_status forward_impl(flint_moe* h, int32_t T, const void* hidden, const flo
             e = launch_down_prefill(a, h->ws, h->n_cu, stream);
         }
         if (e != hipSuccess) return hip_fail(e, "down kernel");
-        e = combine_step(h, a, stream, eps, norm_out);
+        e = combine_step(h, a, true, stream, eps, norm_out);
         if (e != hipSuccess) return hip_fail(e, "combine kernel");
         h->last_T = T;
         return ok();
@@ -419,7 +419,7 @@ flint_status forward_impl(flint_moe* h, int32_t T, const void* hidden, const flo
     }
     if (e != hipSuccess) return hip_fail(e, "down kernel");
     if (!down_decode_combines(a.dm))
-        e = combine_step(h, a, stream, eps, norm_out);
+        e = combine_step(h, a, false, stream, eps, norm_out);
     else if (norm_out)
         e = launch_rmsnorm(T, c.d_model, static_cast<const float*>(out), eps, norm_out, stream);
     if (e != hipSuccess) return hip_fail(e, "combine kernel");
