@@ -9,16 +9,16 @@
 // where the routed rows of y already carry their combine weight (a layer built
 // without a shared expert skips that term).  The sum runs
 // in a fixed order (residual, shared, slot 0..k-1), so results are
-// deterministic; no atomics.  The y rows are fp32 (decode) or 24-bit
-// (prefill: fp32 rounded to its upper 24 bits, see f32_to_f24); the kernels
-// take the format as a template parameter and sum in fp32 either way.
+// deterministic; no atomics.  The y rows are fp32 (decode) or 2 bytes per
+// element in 4-column blocks (prefill, see pack_bfp4); the kernels take the
+// format as a template parameter and sum in fp32 either way.
 #include "flint_internal.hpp"
 
 namespace flint {
 
 struct CombineParams {
     int T, d, k;
-    const void* y;        // [(k+1)T][d] fp32 or 24-bit rows
+    const void* y;        // [(k+1)T][d] fp32 or packed rows
     const int* pair_pos;  // [T][k]
     const float* residual;
     void* out;
@@ -26,29 +26,26 @@ struct CombineParams {
     int has_shared;  // 0: no shared expert (f_s = 0); its slots are never written
 };
 
-// the 4 y values from column c of slot row `row`
-struct U32x3 {
-    uint32_t x, y, z;
-};
-template <bool Y24>
+// the 4 y values from column c (a multiple of 4) of slot row `row`
+template <bool PACKED>
 __device__ __forceinline__ float4 y_row4(const void* y, size_t row, int d, int c) {
-    if constexpr (Y24) {
-        const U32x3 v = *reinterpret_cast<const U32x3*>(static_cast<const unsigned char*>(y) + (row * d + c) * 3);
-        return unpack_f24x4((u32x3_t){v.x, v.y, v.z});
+    if constexpr (PACKED) {
+        return unpack_bfp4(*reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(y) + row * d + c));
     } else {
         return *reinterpret_cast<const float4*>(static_cast<const float*>(y) + row * d + c);
     }
 }
 // the same through a buffer view of the y rows (element offset e, or kOffNone: zeros)
-template <bool Y24>
+template <bool PACKED>
 __device__ __forceinline__ float4 y_view4(__amdgpu_buffer_rsrc_t v, uint32_t e) {
-    if constexpr (Y24)
-        return unpack_f24x4(__builtin_amdgcn_raw_buffer_load_b96(v, (int)(e == kOffNone ? kOffNone : e * 3), 0, 0));
-    else
+    if constexpr (PACKED) {
+        const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(v, (int)(e == kOffNone ? kOffNone : e * 2), 0, 0);
+        return unpack_bfp4(make_uint2(w.x, w.y));
+    } else
         return __builtin_bit_cast(float4, buffer_load16(v, e == kOffNone ? kOffNone : e * 4));
 }
 
-template <bool Y24>
+template <bool PACKED>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     const int t = blockIdx.y;
     const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
@@ -60,12 +57,12 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     }
     const size_t kT = (size_t)p.k * p.T;
     if (p.has_shared) {
-        const float4 v = y_row4<Y24>(p.y, kT + t, p.d, c);
+        const float4 v = y_row4<PACKED>(p.y, kT + t, p.d, c);
         acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
     }
     for (int j = 0; j < p.k; ++j) {
         const int slot = p.pair_pos[(size_t)t * p.k + j];
-        const float4 v = y_row4<Y24>(p.y, (size_t)slot, p.d, c);
+        const float4 v = y_row4<PACKED>(p.y, (size_t)slot, p.d, c);
         acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
     }
     if (p.out_f32) {
@@ -79,7 +76,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     }
 }
 
-hipError_t launch_combine(const LayerArgs& a, const Workspace& w, bool y24, hipStream_t s) {
+hipError_t launch_combine(const LayerArgs& a, const Workspace& w, bool packed, hipStream_t s) {
     CombineParams p;
     p.T = a.dm.T;
     p.d = a.dm.d;
@@ -91,7 +88,7 @@ hipError_t launch_combine(const LayerArgs& a, const Workspace& w, bool y24, hipS
     p.out_f32 = (a.residual != nullptr || a.dm.act == DT_F32) ? 1 : 0;
     p.has_shared = a.dm.fs > 0 ? 1 : 0;
     dim3 grid((a.dm.d + 1023) / 1024, a.dm.T);
-    if (y24) hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s, p);
+    if (packed) hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s, p);
     else hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
@@ -107,7 +104,7 @@ hipError_t launch_combine(const LayerArgs& a, const Workspace& w, bool y24, hipS
 constexpr int kNormChunks = 4;
 __device__ __forceinline__ float rms_scale(float ss, int d, float eps, float* s_part);
 
-template <bool Y24>
+template <bool PACKED>
 __global__ __launch_bounds__(256) void combine_norm_kernel(CombineParams p, float eps, uint16_t* __restrict__ norm) {
     __shared__ float s_part[4];
     const int t = blockIdx.x;
@@ -120,17 +117,17 @@ __global__ __launch_bounds__(256) void combine_norm_kernel(CombineParams p, floa
     // of absent terms get an offset past their view and return zeros
     const __amdgpu_buffer_rsrc_t rview =
         buffer_view(p.residual ? p.residual + (size_t)t * p.d : p.y, p.residual ? (uint32_t)p.d * 4 : 0u);
-    const __amdgpu_buffer_rsrc_t yview = buffer_view(p.y, (uint32_t)((kT + p.T) * p.d * (Y24 ? 3 : 4)));
+    const __amdgpu_buffer_rsrc_t yview = buffer_view(p.y, (uint32_t)((kT + p.T) * p.d * (PACKED ? 2 : 4)));
     float4 r[kNormChunks], sh[kNormChunks], yv[kNormChunks][kCombineMaxK];
 #pragma unroll
     for (int i = 0; i < kNormChunks; ++i) {
         const int c = threadIdx.x * 4 + 1024 * i;
         const bool in = c < p.d;
         r[i] = __builtin_bit_cast(float4, buffer_load16(rview, in ? (uint32_t)c * 4 : kOffNone));
-        sh[i] = y_view4<Y24>(yview, in && p.has_shared ? (uint32_t)((kT + t) * p.d + c) : kOffNone);
+        sh[i] = y_view4<PACKED>(yview, in && p.has_shared ? (uint32_t)((kT + t) * p.d + c) : kOffNone);
 #pragma unroll
         for (int j = 0; j < kCombineMaxK; ++j)
-            yv[i][j] = y_view4<Y24>(yview, in && j < p.k ? (uint32_t)((size_t)slot[j] * p.d + c) : kOffNone);
+            yv[i][j] = y_view4<PACKED>(yview, in && j < p.k ? (uint32_t)((size_t)slot[j] * p.d + c) : kOffNone);
     }
     float4 v[kNormChunks];
     float ss = 0.f;
@@ -183,7 +180,7 @@ bool combine_norm_ok(const Dims& dm) {
            (size_t)(dm.k + 1) * dm.T * dm.d * 4 < (size_t)kOffNone;
 }
 
-hipError_t launch_combine_norm(const LayerArgs& a, const Workspace& w, bool y24, float eps, void* norm,
+hipError_t launch_combine_norm(const LayerArgs& a, const Workspace& w, bool packed, float eps, void* norm,
                                hipStream_t s) {
     CombineParams p;
     p.T = a.dm.T;
@@ -195,7 +192,7 @@ hipError_t launch_combine_norm(const LayerArgs& a, const Workspace& w, bool y24,
     p.out = a.out;
     p.out_f32 = 1;
     p.has_shared = a.dm.fs > 0 ? 1 : 0;
-    if (y24)
+    if (packed)
         hipLaunchKernelGGL(combine_norm_kernel<true>, dim3(a.dm.T), dim3(256), 0, s, p, eps,
                            static_cast<uint16_t*>(norm));
     else

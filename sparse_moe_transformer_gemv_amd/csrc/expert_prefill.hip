@@ -12,7 +12,7 @@
 // design for CDNA4 matrix cores, not a port of those.
 //
 //   gate/up:  H[r][j] = SiLU(X_r . G_j) * (X_r . U_j)   (bf16 out, fp32 math)
-//   down:     Y[r][n] = w_r * (H_r . D_n)                (24-bit out, fp32 math)
+//   down:     Y[r][n] = w_r * (H_r . D_n)                (packed out, fp32 math)
 //
 // Tile 256 rows x 256 B rows, 8 waves as 2 (M) x 4 (N), each wave 128 x 64 =
 // 8 x 4 MFMA 16x16x32 tiles (128 fp32 accumulators per lane), two waves per
@@ -23,11 +23,12 @@
 // output columns of one row in each lane.  For gate/up (bf16 h) the weight
 // rows of each pair of column tiles are interleaved so that a lane holds 8;
 // down keeps each tile's order, so the 4 lanes of a row store 16 contiguous
-// columns; the results leave as 16-byte (h) or 12-byte (y) stores straight
-// from registers.  y is fp32 rounded to its upper 24 bits (f32_to_f24: 15
-// fraction bits, relative error at most 2^-16), which keeps the combine's sum of
-// seven rows well inside the layer's tolerance while moving three quarters of
-// the bytes of fp32 rows through the down stores and the combine loads.
+// columns; the results leave as 16-byte (h) or 8-byte (y) stores straight from
+// registers.  y is stored 2 bytes per element as block floating point over 4
+// columns (pack_bfp4: a shared exponent and 14-bit mantissas, error at most
+// 2^-12 of the block's largest magnitude), which keeps the combine's sum of
+// seven rows well inside the layer's tolerance while moving half the bytes of
+// fp32 rows through the down stores and the combine loads.
 //
 // K advances in pairs of 32-wide sub-stages through two 64 KiB LDS buffers,
 // filled straight from global memory with direct-to-LDS 16-byte loads of whole
@@ -88,7 +89,6 @@ constexpr int kThreads = 512;
 // these reads from the direct-to-LDS loads still in flight into the other buffer
 // and would otherwise wait for all of them (vmcnt 0) first.
 typedef __attribute__((ext_vector_type(4))) uint32_t frag_t;
-typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -485,8 +485,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
     // 4 q .. 4 q + 3 of B tile ni for output row 16 mi + row16.  Gate/up: out_col()
     // made the two tiles of a pair 8 consecutive features, one 16-byte bf16 store
     // (8 bytes for a lone tile), 64 contiguous bytes per row and instruction.
-    // Down: columns 16 ni + 4 q .. + 3, one 12-byte store of four 24-bit values
-    // per tile, 48 contiguous bytes per row and instruction.  Every store is issued (rows past the group's end get an
+    // Down: columns 16 ni + 4 q .. + 3, one 8-byte store of their block per
+    // tile, 32 contiguous bytes per row and instruction.  Every store is issued (rows past the group's end get an
     // offset past the view), so a wave always issues the same number. ----
     float wv[8];
     if (MODE == MODE_DOWN) {
@@ -539,19 +539,20 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
             }
         }
     } else {
-        const __amdgpu_buffer_rsrc_t yview = buffer_view(static_cast<unsigned char*>(p.ws.y) + (size_t)(g.w + m0) * d * 3,
-                                                         (uint32_t)((size_t)rows * d * 3));
+        const __amdgpu_buffer_rsrc_t yview = buffer_view(static_cast<uint16_t*>(p.ws.y) + (size_t)(g.w + m0) * d,
+                                                         (uint32_t)((size_t)rows * d * 2));
         const int col = nb0 + 16 * NI * wn + 4 * q;
 #pragma unroll
         for (int mi = 0; mi < 8; ++mi) {
             const int m = 128 * wm + 16 * mi + row16;
             const float ws = (is_shared ? 1.f : wv[mi]) * ts_a;  // ts_a: the down tensor scale (1 for bf16)
-            const uint32_t off = m < rows ? (uint32_t)(((size_t)m * d + col) * 3) : kOffNone;
+            const uint32_t off = m < rows ? (uint32_t)(((size_t)m * d + col) * 2) : kOffNone;
 #pragma unroll
             for (int t4 = 0; t4 < NI; ++t4) {
                 const floatx4_t& a = acc[mi][t4];
-                __builtin_amdgcn_raw_buffer_store_b96(pack_f24x4(ws * a[0], ws * a[1], ws * a[2], ws * a[3]), yview,
-                                                      (int)(off == kOffNone ? kOffNone : off + 48 * t4), 0, 0);
+                const uint2 b = pack_bfp4(ws * a[0], ws * a[1], ws * a[2], ws * a[3]);
+                __builtin_amdgcn_raw_buffer_store_b64((u32x2_t){b.x, b.y}, yview,
+                                                      (int)(off == kOffNone ? kOffNone : off + 32 * t4), 0, 0);
             }
         }
     }

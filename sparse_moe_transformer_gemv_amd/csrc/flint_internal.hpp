@@ -42,8 +42,8 @@ struct Workspace {
                          // flags (zero between launches) and a sticky fault word
     void* h;             // [(k+1)*Tm][fmax] x 8 B: fp32 (decode VALU), three exact bf16 planes (decode
                          // MFMA), two f16 planes (NVFP4), or bf16 (prefill)
-    void* y;             // [(k+1)*Tm][d] weighted expert outputs: fp32 rows (decode), 24-bit rows
-                         // (prefill, 3 bytes per element, f32_to_f24)
+    void* y;             // [(k+1)*Tm][d] weighted expert outputs: fp32 rows (decode), or 2 bytes per
+                         // element in 4-column blocks (prefill, pack_bfp4)
     int max_tiles;
     size_t ticket_bytes;  // the tickets occupy [0, ticket_bytes) of the allocation
     size_t float_off;     // floating-point data from here to the end
@@ -106,14 +106,14 @@ int fused_decode_grid(const Dims& dm, int n_cu);
 hipError_t launch_decode_fused(const LayerArgs& a, const Workspace& w, int nblocks, hipStream_t s);
 hipError_t launch_gateup_prefill(const LayerArgs& a, const Workspace& w, int n_cu, hipStream_t s);
 hipError_t launch_down_prefill(const LayerArgs& a, const Workspace& w, int n_cu, hipStream_t s);
-// y24: the y rows are 24-bit (the prefill down kernels' format), else fp32
-hipError_t launch_combine(const LayerArgs& a, const Workspace& w, bool y24, hipStream_t s);
+// packed: the y rows are in the prefill down kernels' block format (pack_bfp4), else fp32
+hipError_t launch_combine(const LayerArgs& a, const Workspace& w, bool packed, hipStream_t s);
 hipError_t launch_rmsnorm(int T, int d, const float* in, float eps, void* out, hipStream_t s);
 constexpr int kCombineMaxK = 8;  // the largest top_k a configuration may ask for
 // The combine and the next layer's pre-norm in one launch (out fp32, norm bf16);
 // combine_norm_ok: the shapes it takes
 bool combine_norm_ok(const Dims& dm);
-hipError_t launch_combine_norm(const LayerArgs& a, const Workspace& w, bool y24, float eps, void* norm,
+hipError_t launch_combine_norm(const LayerArgs& a, const Workspace& w, bool packed, float eps, void* norm,
                                hipStream_t s);
 // p[0 .. n) = v (a plain kernel, no memset node, so it is safe under graph capture)
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
@@ -352,6 +352,7 @@ __device__ __forceinline__ void topk_token_lds(const float* lrow, int E, int k, 
 // rows of a 16-row MFMA tile that hold no token.  Offsets are 32-bit; kOffNone
 // is past the end of every view (views stay below 2 GiB).
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 constexpr uint32_t kOffNone = 0x80000000u;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -371,24 +372,36 @@ __device__ __forceinline__ void buffer_store16_agent(uint4 v, __amdgpu_buffer_rs
     __builtin_amdgcn_raw_buffer_store_b128((u32x4_t){v.x, v.y, v.z, v.w}, r, (int)off, 0, kCpolAgent);
 }
 
-// 24-bit y elements (the prefill path's weighted expert rows): an fp32 value
-// rounded to nearest-even at its upper 24 bits (sign, 8 exponent bits, 15
-// fraction bits; relative error at most 2^-16), 3 bytes each, 4 consecutive
-// columns in 12 bytes.  A NaN stays a NaN (quiet bit set before the cut); a
-// finite value past the format's largest rounds to infinity.
-typedef __attribute__((ext_vector_type(3))) uint32_t u32x3_t;
-__device__ __forceinline__ uint32_t f32_to_f24(float v) {
-    const uint32_t u = __float_as_uint(v);
-    return v != v ? (u | 0x400000u) >> 8 : (u + 0x7Fu + ((u >> 8) & 1u)) >> 8;
+// Packed y elements (the prefill path's weighted expert rows): block floating
+// point over 4 consecutive columns in 8 bytes, one 8-bit exponent E shared by
+// four 14-bit two's-complement mantissas q, value = q * 2^(E - 139).  E is the
+// fp32 exponent field of the block's largest magnitude (at least 13), so every
+// |q| <= 2^13 - 1 and each value's error is at most 2^-12 of that largest
+// magnitude (half a step of 2^(E - 139), a whole step where the top is clamped);
+// a block whose largest magnitude is below 2^-114 is stored with E = 13, its
+// error under 2^-126.
+// Bits: [0,8) E, [8,22) q0, [22,36) q1, [36,50) q2, [50,64) q3.  A block holding
+// a NaN or an infinity is stored with E = 255 and reads back as four NaNs.
+__device__ __forceinline__ uint2 pack_bfp4(float a, float b, float c, float d) {
+    const uint32_t m = max(max(__float_as_uint(a) & 0x7FFFFFFFu, __float_as_uint(b) & 0x7FFFFFFFu),
+                           max(__float_as_uint(c) & 0x7FFFFFFFu, __float_as_uint(d) & 0x7FFFFFFFu));
+    if (m >= 0x7F800000u) return make_uint2(255u, 0u);
+    const uint32_t E = max(m >> 23, 13u);
+    const float s = __uint_as_float((266u - E) << 23);  // 2^(139 - E)
+    // |v| s < 2^13, so rounding can reach 2^13 only at the top: clamp there
+    const int q0 = min(max(__float2int_rn(a * s), -8191), 8191), q1 = min(max(__float2int_rn(b * s), -8191), 8191);
+    const int q2 = min(max(__float2int_rn(c * s), -8191), 8191), q3 = min(max(__float2int_rn(d * s), -8191), 8191);
+    return make_uint2(E | (((uint32_t)q0 & 0x3FFFu) << 8) | (((uint32_t)q1 & 0x3FFu) << 22),
+                      (((uint32_t)q1 >> 10) & 0xFu) | (((uint32_t)q2 & 0x3FFFu) << 4) | ((uint32_t)q3 << 18));
 }
-__device__ __forceinline__ u32x3_t pack_f24x4(float a, float b, float c, float d) {
-    const uint32_t x = f32_to_f24(a), y = f32_to_f24(b), z = f32_to_f24(c), w = f32_to_f24(d);
-    return (u32x3_t){x | (y << 24), (y >> 8) | (z << 16), (z >> 16) | (w << 8)};
-}
-__device__ __forceinline__ float4 unpack_f24x4(u32x3_t v) {
-    return make_float4(__uint_as_float(v.x << 8), __uint_as_float(__builtin_amdgcn_alignbyte(v.y, v.x, 3) << 8),
-                       __uint_as_float(__builtin_amdgcn_alignbyte(v.z, v.y, 2) << 8),
-                       __uint_as_float(v.z & 0xFFFFFF00u));
+__device__ __forceinline__ float4 unpack_bfp4(uint2 v) {
+    const uint32_t E = v.x & 0xFFu;
+    const float s = E == 255u ? __uint_as_float(0x7FC00000u) : __uint_as_float((E - 12u) << 23);  // 2^(E - 139)
+    const int q0 = (int)(v.x << 10) >> 18;
+    const int q1 = (int)(__builtin_amdgcn_alignbit(v.y, v.x, 22) << 18) >> 18;
+    const int q2 = (int)(v.y << 14) >> 18;
+    const int q3 = (int)v.y >> 18;
+    return make_float4((float)q0 * s, (float)q1 * s, (float)q2 * s, (float)q3 * s);
 }
 // MFMA operand types (gfx950 v_mfma_f32_16x16x32_bf16).  Lane l of a wave
 // supplies A row (l & 15) and B column (l & 15), each with the 8 consecutive

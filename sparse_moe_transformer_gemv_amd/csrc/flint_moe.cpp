@@ -268,12 +268,12 @@ struct Timer {
 // flint_moe_forward_noalloc over the static scratch).
 // The combine launch, or with norm_out the combine and the next layer's
 // pre-norm (one launch where the shape allows, else the combine and then the
-// RMSNorm kernel).  y24: the y rows come from the prefill down kernels (24-bit).
-hipError_t combine_step(flint_moe* h, const LayerArgs& a, bool y24, hipStream_t stream, float eps, void* norm_out) {
+// RMSNorm kernel).  packed: the y rows come from the prefill down kernels (block format).
+hipError_t combine_step(flint_moe* h, const LayerArgs& a, bool packed, hipStream_t stream, float eps, void* norm_out) {
     Timer tm(h, FLINT_KERNEL_COMBINE, stream);
-    if (!norm_out) return launch_combine(a, h->ws, y24, stream);
-    if (combine_norm_ok(a.dm)) return launch_combine_norm(a, h->ws, y24, eps, norm_out, stream);
-    hipError_t e = launch_combine(a, h->ws, y24, stream);
+    if (!norm_out) return launch_combine(a, h->ws, packed, stream);
+    if (combine_norm_ok(a.dm)) return launch_combine_norm(a, h->ws, packed, eps, norm_out, stream);
+    hipError_t e = launch_combine(a, h->ws, packed, stream);
     if (e == hipSuccess) e = launch_rmsnorm(a.dm.T, a.dm.d, static_cast<const float*>(a.out), eps, norm_out, stream);
     return e;
 }
