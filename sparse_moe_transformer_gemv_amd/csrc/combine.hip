@@ -45,34 +45,93 @@ __device__ __forceinline__ float4 y_view4(__amdgpu_buffer_rsrc_t v, uint32_t e) 
         return __builtin_bit_cast(float4, buffer_load16(v, e == kOffNone ? kOffNone : e * 4));
 }
 
-template <bool PACKED>
+// One block of 256 threads per (token, 256 CPT columns); CPT = 8 columns per
+// thread for packed rows (two 8-byte blocks in one 16-byte load), 4 for fp32
+// rows.  Every load of the thread's columns (residual, shared row, the K
+// routed rows) is issued before the first add.
+template <bool PACKED, int K>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
+    constexpr int CPT = PACKED ? 8 : 4;
     const int t = blockIdx.y;
-    const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+    const int c = (blockIdx.x * 256 + threadIdx.x) * CPT;
     if (c >= p.d) return;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    if (p.residual) {
-        float4 r = *reinterpret_cast<const float4*>(p.residual + (size_t)t * p.d + c);
-        acc[0] = r.x; acc[1] = r.y; acc[2] = r.z; acc[3] = r.w;
+    const size_t kT = (size_t)K * p.T;
+    int slot[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) slot[j] = p.pair_pos[(size_t)t * K + j];
+    // rows of a layer without a shared expert are never written: that load reads
+    // the first routed row instead and its values are dropped
+    const size_t srow = p.has_shared ? kT + t : (size_t)slot[0];
+    const float* rrow = p.residual ? p.residual + (size_t)t * p.d : static_cast<const float*>(p.y);
+    float4 r[CPT / 4], sh[CPT / 4], yv[K][CPT / 4];
+#pragma unroll
+    for (int i = 0; i < CPT / 4; ++i) r[i] = *reinterpret_cast<const float4*>(rrow + c + 4 * i);
+    if constexpr (PACKED) {
+        const uint16_t* y = static_cast<const uint16_t*>(p.y);
+        const uint4 s4 = *reinterpret_cast<const uint4*>(y + srow * p.d + c);
+        uint4 v4[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) v4[j] = *reinterpret_cast<const uint4*>(y + (size_t)slot[j] * p.d + c);
+        sh[0] = unpack_bfp4(make_uint2(s4.x, s4.y));
+        sh[1] = unpack_bfp4(make_uint2(s4.z, s4.w));
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            yv[j][0] = unpack_bfp4(make_uint2(v4[j].x, v4[j].y));
+            yv[j][1] = unpack_bfp4(make_uint2(v4[j].z, v4[j].w));
+        }
+    } else {
+        const float* y = static_cast<const float*>(p.y);
+        sh[0] = *reinterpret_cast<const float4*>(y + srow * p.d + c);
+#pragma unroll
+        for (int j = 0; j < K; ++j) yv[j][0] = *reinterpret_cast<const float4*>(y + (size_t)slot[j] * p.d + c);
     }
-    const size_t kT = (size_t)p.k * p.T;
-    if (p.has_shared) {
-        const float4 v = y_row4<PACKED>(p.y, kT + t, p.d, c);
-        acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
-    }
-    for (int j = 0; j < p.k; ++j) {
-        const int slot = p.pair_pos[(size_t)t * p.k + j];
-        const float4 v = y_row4<PACKED>(p.y, (size_t)slot, p.d, c);
-        acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
+    // residual, shared row, routed rows in pair order
+    float acc[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT / 4; ++i) {
+        float* a = acc + 4 * i;
+        if (p.residual) {
+            a[0] = r[i].x; a[1] = r[i].y; a[2] = r[i].z; a[3] = r[i].w;
+        } else {
+            a[0] = a[1] = a[2] = a[3] = 0.f;
+        }
+        if (p.has_shared) {
+            a[0] += sh[i].x; a[1] += sh[i].y; a[2] += sh[i].z; a[3] += sh[i].w;
+        }
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            a[0] += yv[j][i].x; a[1] += yv[j][i].y; a[2] += yv[j][i].z; a[3] += yv[j][i].w;
+        }
     }
     if (p.out_f32) {
-        *reinterpret_cast<float4*>(static_cast<float*>(p.out) + (size_t)t * p.d + c) =
-            make_float4(acc[0], acc[1], acc[2], acc[3]);
+        float* o = static_cast<float*>(p.out) + (size_t)t * p.d + c;
+#pragma unroll
+        for (int i = 0; i < CPT / 4; ++i)
+            *reinterpret_cast<float4*>(o + 4 * i) = make_float4(acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]);
     } else {
-        uint2 o;
-        o.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
-        o.y = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + (size_t)t * p.d + c) = o;
+        uint16_t* o = static_cast<uint16_t*>(p.out) + (size_t)t * p.d + c;
+        if constexpr (CPT == 8) {
+            *reinterpret_cast<uint4*>(o) = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                                      pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+        } else {
+            *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+        }
+    }
+}
+
+template <bool PACKED>
+static void launch_combine_k(const CombineParams& p, hipStream_t s) {
+    constexpr int CPT = PACKED ? 8 : 4;
+    const dim3 grid((p.d + 256 * CPT - 1) / (256 * CPT), p.T);
+    switch (p.k) {
+    case 1: hipLaunchKernelGGL((combine_kernel<PACKED, 1>), grid, dim3(256), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((combine_kernel<PACKED, 2>), grid, dim3(256), 0, s, p); break;
+    case 3: hipLaunchKernelGGL((combine_kernel<PACKED, 3>), grid, dim3(256), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((combine_kernel<PACKED, 4>), grid, dim3(256), 0, s, p); break;
+    case 5: hipLaunchKernelGGL((combine_kernel<PACKED, 5>), grid, dim3(256), 0, s, p); break;
+    case 6: hipLaunchKernelGGL((combine_kernel<PACKED, 6>), grid, dim3(256), 0, s, p); break;
+    case 7: hipLaunchKernelGGL((combine_kernel<PACKED, 7>), grid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((combine_kernel<PACKED, 8>), grid, dim3(256), 0, s, p); break;
     }
 }
 
@@ -87,9 +146,8 @@ hipError_t launch_combine(const LayerArgs& a, const Workspace& w, bool packed, h
     p.out = a.out;
     p.out_f32 = (a.residual != nullptr || a.dm.act == DT_F32) ? 1 : 0;
     p.has_shared = a.dm.fs > 0 ? 1 : 0;
-    dim3 grid((a.dm.d + 1023) / 1024, a.dm.T);
-    if (packed) hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, s, p);
+    if (packed) launch_combine_k<true>(p, s);
+    else launch_combine_k<false>(p, s);
     return hipGetLastError();
 }
 
