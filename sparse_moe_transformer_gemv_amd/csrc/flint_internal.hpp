@@ -33,6 +33,7 @@ struct Workspace {
     int4* groups;        // [E+1] active groups {expert (E = shared), first sorted index, rows, first slot}
     int* n_groups;       // [1]
     int2* tiles;         // [max_tiles] prefill m-tiles {group, first row}
+    int* bhist;          // [ceil(Tm/16)][256] prefill: chosen experts per 16-token block (top-k kernel, read by the sort)
     int* n_tiles;        // [1]
     int* counter;        // [1 + ceil(Tm/16)] last-block tickets, zero between launches
     int* dcount;         // [ceil(d/16)] decode down tickets (combine folded in), zero between launches

@@ -195,6 +195,7 @@ size_t carve(const flint_moe_config& c, char* base, Workspace* w) {
     w->groups = static_cast<int4*>(take((E + 1) * 16));
     w->n_groups = static_cast<int*>(take(4));
     w->tiles = static_cast<int2*>(take(max_tiles * 8));
+    w->bhist = static_cast<int*>(take((Tm + 15) / 16 * 256 * 4));
     w->n_tiles = static_cast<int*>(take(4));
     w->float_off = off;
     // floating-point data

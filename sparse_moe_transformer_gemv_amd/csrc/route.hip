@@ -886,11 +886,14 @@ hipError_t launch_router_gemm(const LayerArgs& a, const Workspace& w, hipStream_
     return hipGetLastError();
 }
 
-// Prefill top-k: 8 waves per block, two tokens per wave (16 per block).
+// Prefill top-k: 8 waves per block, two tokens per wave (16 per block).  The
+// block also counts its chosen experts (Workspace::bhist row blockIdx.x), so
+// the sort reads 16-token block counts instead of counting every pair again.
 __global__ __launch_bounds__(512) void topk_kernel(RouteDecodeParams p) {
     // the block's 16 logit rows into LDS (16-byte loads, all issued before the
     // first LDS store), then one wavefront per token (topk_token_lds)
     __shared__ __attribute__((aligned(16))) float s_logit[16 * 256];
+    __shared__ int s_hist[256];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int t0 = blockIdx.x * 16, nt = min(16, p.T - t0);
     // rounded up within the logits buffer's 256-byte padding
@@ -899,6 +902,7 @@ __global__ __launch_bounds__(512) void topk_kernel(RouteDecodeParams p) {
     uint4 lg[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) lg[i] = buffer_load16(lv, (uint32_t)(tid + 512 * i) * 16);
+    if (tid < 256) s_hist[tid] = 0;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const uint32_t o = (uint32_t)(tid + 512 * i) * 16;
@@ -913,8 +917,11 @@ __global__ __launch_bounds__(512) void topk_kernel(RouteDecodeParams p) {
         if (lane < p.k) {
             p.ws.sel[t * p.k + lane] = e;
             p.ws.wts[t * p.k + lane] = w;
+            atomicAdd(&s_hist[e], 1);
         }
     }
+    __syncthreads();
+    if (tid < 256) p.ws.bhist[(size_t)blockIdx.x * 256 + tid] = s_hist[tid];
 }
 
 hipError_t launch_topk(const LayerArgs& a, const Workspace& w, hipStream_t s) {
@@ -925,58 +932,68 @@ hipError_t launch_topk(const LayerArgs& a, const Workspace& w, hipStream_t s) {
 
 struct SortParams {
     int T, E, k, has_shared, bm;
+    int cb;  // 16-token top-k blocks per sort block
     Workspace ws;
 };
 
 // ---------------------------------------------------------------------------
-// Prefill counting sort, one launch of ceil(P / kSortBlock) blocks.  Block b
-// places the pairs [kSortBlock b, kSortBlock (b + 1)); pair i is read by
-// thread i mod kSortBlock of every block, so each block counts all P keys
-// itself (per expert: the pairs in earlier blocks and in later ones) with no
-// hand-off between blocks.  Counting uses a histogram per wavefront in LDS, so
-// atomics collide only inside a wavefront.  The block's own pairs are ranked
-// among equal keys by ballots over the 8 key bits.  The order is stable (pairs
-// of one expert keep pair order), so the result does not depend on timing.
-// Block 0 also writes the counts, offsets, group list and tile list.  The
-// scattered writes of the permutation are spread over the blocks: from one
-// block they cost a cache line per distinct expert per 64 pairs, one
-// instruction after another.
+// Prefill counting sort, one launch.  Sort block b places the pairs of the
+// top-k blocks [cb b, cb (b + 1)) (cb 16-token blocks, 16 k cb <= kSortBlock
+// pairs, one per thread).  The per-expert counts come from the top-k blocks'
+// own counts (Workspace::bhist, rows of 256): the pairs in earlier blocks give each
+// expert's start for this block, all of them the totals, so no pair key is
+// read twice and no hand-off between blocks is needed.  The block's own pairs
+// are ranked among equal keys by ballots over the 8 key bits, then placed in
+// wave order.  The order is stable (pairs of one expert keep pair order), so
+// the result does not depend on timing.  Block 0 also writes the counts,
+// offsets, group list and tile list.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kSortBlock) void sort_kernel(SortParams p) {
-    constexpr int NW = kSortBlock / 64, KU = 32;
-    __shared__ int s_pre[NW][256];   // per wave: pairs per expert in blocks before b
-    __shared__ int s_post[NW][256];  // per wave: pairs per expert in blocks after b
-    __shared__ int s_base[NW][256];  // per wave: this block's pairs per expert, then their first positions
+    constexpr int NW = kSortBlock / 64, U = 16;
+    __shared__ int s_cnt[NW][2][256];  // per wave's rows of the block counts: pairs before this block, all pairs
+    __shared__ int s_base[NW][256];    // per wave: this block's pairs per expert, then their first positions
     __shared__ int s_tot[256];
     __shared__ int s_before[256];
     __shared__ int s_off[257];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int E = p.E, P = p.k * p.T, nb = (int)gridDim.x, b = (int)blockIdx.x;
-    for (int j = tid; j < NW * 256; j += kSortBlock) {
-        (&s_pre[0][0])[j] = 0;
-        (&s_post[0][0])[j] = 0;
-        (&s_base[0][0])[j] = 0;
-    }
-    // this block's own pair, requested with the first batch of keys
-    const int i = b * kSortBlock + tid;
-    const bool valid = i < P;
+    const int E = p.E, P = p.k * p.T, b = (int)blockIdx.x;
+    const int nblk = (p.T + 15) / 16, first_blk = b * p.cb, pb = p.cb * 16 * p.k;
+    for (int j = tid; j < NW * 256; j += kSortBlock) (&s_base[0][0])[j] = 0;
+    // this block's own pair, requested before the block counts
+    const int i = b * pb + tid;
+    const bool valid = tid < pb && i < P;
     const int key = valid ? p.ws.sel[i] : 0;
     const float wt = valid ? p.ws.wts[i] : 0.f;
-    __syncthreads();
-    for (int j0 = 0; j0 < nb; j0 += KU) {
-        int kv[KU];
+    {
+        // wave w sums the count rows w, w + NW, ...; lane: experts 4 lane .. + 3
+        // (16-byte loads of rows 256 entries long, U in flight)
+        int4 before = make_int4(0, 0, 0, 0), tot = make_int4(0, 0, 0, 0);
+        for (int c0 = w; c0 < nblk; c0 += NW * U) {
+            int4 v[U];
 #pragma unroll
-        for (int u = 0; u < KU; ++u) {
-            const int ii = (j0 + u) * kSortBlock + tid;
-            kv[u] = (j0 + u < nb && ii < P) ? p.ws.sel[ii] : -1;
-        }
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + NW * u;
+                v[u] = c < nblk ? *reinterpret_cast<const int4*>(p.ws.bhist + (size_t)c * 256 + 4 * lane)
+                                : make_int4(0, 0, 0, 0);
+            }
 #pragma unroll
-        for (int u = 0; u < KU; ++u) {
-            const int j = j0 + u;
-            if (j >= nb) break;  // uniform
-            if (kv[u] >= 0 && j != b) atomicAdd(j < b ? &s_pre[w][kv[u]] : &s_post[w][kv[u]], 1);
+            for (int u = 0; u < U; ++u) {
+                tot.x += v[u].x;
+                tot.y += v[u].y;
+                tot.z += v[u].z;
+                tot.w += v[u].w;
+                if (c0 + NW * u < first_blk) {
+                    before.x += v[u].x;
+                    before.y += v[u].y;
+                    before.z += v[u].z;
+                    before.w += v[u].w;
+                }
+            }
         }
+        *reinterpret_cast<int4*>(&s_cnt[w][0][4 * lane]) = before;
+        *reinterpret_cast<int4*>(&s_cnt[w][1][4 * lane]) = tot;
     }
+    __syncthreads();
     // lanes of this wave holding the same expert as this lane
     unsigned long long m = __ballot(valid);
 #pragma unroll
@@ -988,15 +1005,15 @@ __global__ __launch_bounds__(kSortBlock) void sort_kernel(SortParams p) {
     const int rank = __popcll(m & ((1ull << lane) - 1ull));
     // the highest lane of each group of equal keys records its size
     if (valid && (m >> lane) == 1ull) s_base[w][key] = __popcll(m);
-    __syncthreads();
     if (tid < E) {
-        int before = 0, rest = 0;
-        for (int ww = 0; ww < NW; ++ww) {
-            before += s_pre[ww][tid];
-            rest += s_post[ww][tid] + s_base[ww][tid];
+        int before = 0, tot = 0;
+#pragma unroll
+        for (int q = 0; q < NW; ++q) {
+            before += s_cnt[q][0][tid];
+            tot += s_cnt[q][1][tid];
         }
         s_before[tid] = before;
-        s_tot[tid] = before + rest;
+        s_tot[tid] = tot;
     }
     __syncthreads();
     // exclusive scan of the totals (wave 0, 4 experts per lane)
@@ -1052,9 +1069,12 @@ __global__ __launch_bounds__(kSortBlock) void sort_kernel(SortParams p) {
     if (b == 0 && w == 0) write_groups(s_off, E, p.T, p.k, p.has_shared != 0, p.bm, p.ws, lane);
 }
 
+// Needs the top-k kernel's block counts (launch_topk) of the same batch.
 hipError_t launch_sort(const LayerArgs& a, const Workspace& w, int bm, hipStream_t s) {
-    SortParams p{a.dm.T, a.dm.E, a.dm.k, a.dm.fs > 0, bm, w};
-    const dim3 grid((a.dm.k * a.dm.T + kSortBlock - 1) / kSortBlock);
+    const int cb = kSortBlock / (16 * a.dm.k);  // k <= 8, so cb >= 8
+    SortParams p{a.dm.T, a.dm.E, a.dm.k, a.dm.fs > 0, bm, cb, w};
+    const int nblk = (a.dm.T + 15) / 16;
+    const dim3 grid((nblk + cb - 1) / cb);
     hipLaunchKernelGGL(sort_kernel, grid, dim3(kSortBlock), 0, s, p);
     return hipGetLastError();
 }
