@@ -551,8 +551,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
             for (int t4 = 0; t4 < NI; ++t4) {
                 const floatx4_t& a = acc[mi][t4];
                 const uint2 b = pack_bfp4(ws * a[0], ws * a[1], ws * a[2], ws * a[3]);
-                __builtin_amdgcn_raw_buffer_store_b64((u32x2_t){b.x, b.y}, yview,
-                                                      (int)(off == kOffNone ? kOffNone : off + 32 * t4), 0, 0);
+                // (a row past the group's end stays past the view with the column offset added)
+                __builtin_amdgcn_raw_buffer_store_b64((u32x2_t){b.x, b.y}, yview, (int)(off + 32 * t4), 0, 0);
             }
         }
     }

@@ -383,17 +383,31 @@ __device__ __forceinline__ void buffer_store16_agent(uint4 v, __amdgpu_buffer_rs
 // error under 2^-126.
 // Bits: [0,8) E, [8,22) q0, [22,36) q1, [36,50) q2, [50,64) q3.  A block holding
 // a NaN or an infinity is stored with E = 255 and reads back as four NaNs.
-__device__ __forceinline__ uint2 pack_bfp4(float a, float b, float c, float d) {
-    const uint32_t m = max(max(__float_as_uint(a) & 0x7FFFFFFFu, __float_as_uint(b) & 0x7FFFFFFFu),
-                           max(__float_as_uint(c) & 0x7FFFFFFFu, __float_as_uint(d) & 0x7FFFFFFFu));
-    if (m >= 0x7F800000u) return make_uint2(255u, 0u);
-    const uint32_t E = max(m >> 23, 13u);
-    const float s = __uint_as_float((266u - E) << 23);  // 2^(139 - E)
-    // |v| s < 2^13, so rounding can reach 2^13 only at the top: clamp there
-    const int q0 = min(max(__float2int_rn(a * s), -8191), 8191), q1 = min(max(__float2int_rn(b * s), -8191), 8191);
-    const int q2 = min(max(__float2int_rn(c * s), -8191), 8191), q3 = min(max(__float2int_rn(d * s), -8191), 8191);
-    return make_uint2(E | (((uint32_t)q0 & 0x3FFFu) << 8) | (((uint32_t)q1 & 0x3FFu) << 22),
-                      (((uint32_t)q1 >> 10) & 0xFu) | (((uint32_t)q2 & 0x3FFFu) << 4) | ((uint32_t)q3 << 18));
+// Written without branches (the epilogue that calls it runs 32 blocks per lane
+// back to back): each value is scaled by 2^(139 - E), which is exact, and
+// rounded to an integer, ties to even, by adding 1.5 x 2^23, whose sum has a
+// unit of 1 and so holds the integer in the low bits of its mantissa (two's
+// complement there, the offset having 22 zero low bits); the clamp to +-8191
+// acts on that sum.  A fused multiply-add of the two steps gives the same
+// sum, the product being exact.  Also compiled for the host, where a test
+// checks it bit for bit against the format's plain definition.
+__host__ __device__ __forceinline__ uint2 pack_bfp4(float a, float b, float c, float d) {
+    const uint32_t ma = __builtin_bit_cast(uint32_t, a) & 0x7FFFFFFFu, mb = __builtin_bit_cast(uint32_t, b) & 0x7FFFFFFFu;
+    const uint32_t mc = __builtin_bit_cast(uint32_t, c) & 0x7FFFFFFFu, md = __builtin_bit_cast(uint32_t, d) & 0x7FFFFFFFu;
+    const uint32_t mab = ma > mb ? ma : mb, mcd = mc > md ? mc : md;
+    const uint32_t m = mab > mcd ? mab : mcd;
+    const uint32_t e8 = m >> 23;  // 255 for a NaN or an infinity
+    const uint32_t E = e8 > 13u ? e8 : 13u;
+    const float s = __builtin_bit_cast(float, (266u - E) << 23);  // 2^(139 - E)
+    constexpr float kM = 12582912.0f, kLo = kM - 8191.0f, kHi = kM + 8191.0f;
+    const uint32_t q0 = __builtin_bit_cast(uint32_t, fminf(fmaxf(a * s + kM, kLo), kHi));
+    const uint32_t q1 = __builtin_bit_cast(uint32_t, fminf(fmaxf(b * s + kM, kLo), kHi));
+    const uint32_t q2 = __builtin_bit_cast(uint32_t, fminf(fmaxf(c * s + kM, kLo), kHi));
+    const uint32_t q3 = __builtin_bit_cast(uint32_t, fminf(fmaxf(d * s + kM, kLo), kHi));
+    const uint32_t w0 = E | ((q0 & 0x3FFFu) << 8) | (q1 << 22);
+    const uint32_t w1 = ((q1 >> 10) & 0xFu) | ((q2 & 0x3FFFu) << 4) | (q3 << 18);
+    const bool bad = E == 255u;
+    return make_uint2(bad ? 255u : w0, bad ? 0u : w1);
 }
 __device__ __forceinline__ float4 unpack_bfp4(uint2 v) {
     const uint32_t E = v.x & 0xFFu;
