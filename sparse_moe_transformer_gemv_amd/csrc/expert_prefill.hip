@@ -20,11 +20,11 @@
 // gate rows then the matching 32 up rows of features 32q..32q+31, so each wave
 // holds matching gate and up columns and applies SwiGLU in registers.  The
 // MFMAs take the weights as their first operand, which leaves 4 consecutive
-// output columns of one row in each lane.  For gate/up (bf16 h) the weight
-// rows of each pair of column tiles are interleaved so that a lane holds 8;
-// down keeps each tile's order, so the 4 lanes of a row store 16 contiguous
-// columns; the results leave as 16-byte (h) or 8-byte (y) stores straight from
-// registers.  y is stored 2 bytes per element as block floating point over 4
+// output columns of one row in each lane.  The weight rows of each pair of
+// column tiles are interleaved so that a lane holds 8 consecutive columns, and
+// the results leave as 16-byte stores straight from registers (8 bf16 h
+// values, or two packed y blocks), 64 contiguous bytes of a row per
+// instruction.  y is stored 2 bytes per element as block floating point over 4
 // columns (pack_bfp4: a shared exponent and 14-bit mantissas, error at most
 // 2^-12 of the block's largest magnitude), which keeps the combine's sum of
 // seven rows well inside the layer's tolerance while moving half the bytes of
@@ -262,9 +262,12 @@ __device__ __forceinline__ int b_row(const PrefillParams& p, const TileRef& t, i
         const int F = t.g.x == p.dm.E ? p.dm.fs : p.dm.f;
         return (tn >= NI / 2 ? F : 0) + t.nb0 + HS * wb + out_col<NI / 2>(tn % (NI / 2), jr);
     }
-    // down writes fp32: tiles keep their own order (column 16 tn + jr), so each
-    // store instruction covers 64 contiguous bytes of a row
-    return t.nb0 + 16 * NI * wb + 16 * tn + jr;
+    // down: B rows interleaved as for gate/up, so that lane q of a wave holds
+    // columns 8 q .. 8 q + 7 of each 32-column half of its block (tiles 2 h and
+    // 2 h + 1 give half h): the packed y blocks of two tiles leave as one
+    // 16-byte store, 64 contiguous bytes of a row per instruction (8-byte
+    // stores of one tile each, 32 bytes per row, cost the down GEMM 12 us more)
+    return t.nb0 + 16 * NI * wb + 32 * (tn >> 1) + 8 * (jr >> 2) + 4 * (tn & 1) + (jr & 3);
 }
 template <int MODE, int NI>
 __device__ __forceinline__ void b_offsets(const PrefillParams& p, const TileRef& t, uint32_t (&boff)[NI]) {
@@ -283,7 +286,7 @@ __device__ __forceinline__ void b_offsets(const PrefillParams& p, const TileRef&
 // them stores (the down kernel's weight loads come before the next tile's
 // loads): the next tile's first wait lets exactly these stay in flight.
 template <int MODE>
-constexpr int epilogue_stores() { return MODE == MODE_GATEUP ? 8 : 32; }
+constexpr int epilogue_stores() { return MODE == MODE_GATEUP ? 8 : 16; }
 // s_waitcnt immediate for vmcnt(n) alone (gfx9 encoding: vmcnt in bits 3..0
 // and 15..14, expcnt and lgkmcnt at their no-wait values)
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
@@ -485,8 +488,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
     // 4 q .. 4 q + 3 of B tile ni for output row 16 mi + row16.  Gate/up: out_col()
     // made the two tiles of a pair 8 consecutive features, one 16-byte bf16 store
     // (8 bytes for a lone tile), 64 contiguous bytes per row and instruction.
-    // Down: columns 16 ni + 4 q .. + 3, one 8-byte store of their block per
-    // tile, 32 contiguous bytes per row and instruction.  Every store is issued (rows past the group's end get an
+    // Down: tiles 2 h and 2 h + 1 give columns 32 h + 8 q .. + 7 (b_row), two
+    // packed blocks, one 16-byte store, 64 contiguous bytes per row and
+    // instruction.  Every store is issued (rows past the group's end get an
     // offset past the view), so a wave always issues the same number. ----
     float wv[8];
     if (MODE == MODE_DOWN) {
@@ -541,18 +545,24 @@ __device__ __forceinline__ void prefill_tile(const PrefillParams& p, unsigned ch
     } else {
         const __amdgpu_buffer_rsrc_t yview = buffer_view(static_cast<uint16_t*>(p.ws.y) + (size_t)(g.w + m0) * d,
                                                          (uint32_t)((size_t)rows * d * 2));
-        const int col = nb0 + 16 * NI * wn + 4 * q;
+        const int col = nb0 + 16 * NI * wn + 8 * q;  // this lane's first run of 8 columns (b_row)
+        // (the run of tiles t4, t4 + 1 starts 32 t4 / 2 columns further: 32 t4 bytes)
 #pragma unroll
         for (int mi = 0; mi < 8; ++mi) {
             const int m = 128 * wm + 16 * mi + row16;
             const float ws = (is_shared ? 1.f : wv[mi]) * ts_a;  // ts_a: the down tensor scale (1 for bf16)
             const uint32_t off = m < rows ? (uint32_t)(((size_t)m * d + col) * 2) : kOffNone;
 #pragma unroll
-            for (int t4 = 0; t4 < NI; ++t4) {
+            for (int t4 = 0; t4 < NI; t4 += 2) {
                 const floatx4_t& a = acc[mi][t4];
-                const uint2 b = pack_bfp4(ws * a[0], ws * a[1], ws * a[2], ws * a[3]);
-                // (a row past the group's end stays past the view with the column offset added)
-                __builtin_amdgcn_raw_buffer_store_b64((u32x2_t){b.x, b.y}, yview, (int)(off + 32 * t4), 0, 0);
+                const floatx4_t& c = acc[mi][t4 + 1];
+                const uint2 b0 = pack_bfp4(ws * a[0], ws * a[1], ws * a[2], ws * a[3]);
+                const uint2 b1 = pack_bfp4(ws * c[0], ws * c[1], ws * c[2], ws * c[3]);
+                // (a row past the group's end stays past the view with the column offset added).  No
+                // non-temporal hint: with it the combine, which reads y next, found it in HBM rather
+                // than in the caches (4 us slower)
+                __builtin_amdgcn_raw_buffer_store_b128((u32x4_t){b0.x, b0.y, b1.x, b1.y}, yview, (int)(off + 32 * t4), 0,
+                                                       0);
             }
         }
     }
