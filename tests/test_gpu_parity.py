@@ -138,6 +138,13 @@ def test_prefill_path_k8_odd_experts():
     _case(2, 333, flags=FLINT_FORCE_PREFILL_PATH, d=256, E=100, k=8, f=128, fs=128)
 
 
+def test_prefill_sort_beyond_4096_tokens():
+    # more than 256 sixteen-token blocks of expert counts, so every sort block
+    # reads them in more than one pass, with a ragged last block and the Zipf
+    # bias; every token's output against the oracle
+    _case(2, 5000, d=256, E=64, f=128, fs=128)
+
+
 def test_f32_activations_bf16_weights():
     _case(1, 9, d=192, E=48, f=32, fs=64, act=synth.F32)
 
